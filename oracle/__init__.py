@@ -1,0 +1,115 @@
+"""CPU oracle of the Ulysses all_to_all_4D head/sequence exchange.
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are its only callers.  The product path
+(``ulysses_all_re_amd``) never imports it, and it imports nothing from there.
+
+The arithmetic lives in ``ua2a_oracle.c`` as plain nested loops (see the
+header of that file for the page and method each loop follows); this module
+only builds that file with gcc, loads it with ctypes and marshals numpy
+arrays.
+
+Shapes follow the FastVideo ``ulysses_a2a`` page (method ``run_armed``): the
+w rank tensors are stacked rank-major in one array,
+    mode 0 input  [w, B, S_local, H, D]      -> output [w, B, S_local*w, H//w, D]
+    mode 1 input  [w, B, S_global, H_local, D] -> output [w, B, S_global//w, H_local*w, D]
+and elements are moved as raw bit patterns (any numpy dtype of 1, 2, 4 or 8
+bytes; bf16 travels as uint16/int16).
+
+Parity pins (tests/test_oracle_pins.py): closed-form shapes, w = 1 identity,
+mode1(mode0(x)) == x and mode0(mode1(y)) == y, chunked == unchunked,
+agreement with an all-to-all over torch.distributed's gloo backend in w
+processes, agreement with numpy reshape/transpose, hand-derived worked
+examples under tests/golden/, bijection of the element multiset.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ua2a_oracle.c")
+LIBRARY = os.path.join(_HERE, "libua2a_oracle.so")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc into oracle/libua2a_oracle.so."""
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-Werror",
+           "-shared", "-fPIC", SOURCE, "-o", LIBRARY + ".tmp"]
+    subprocess.check_call(cmd)
+    os.replace(LIBRARY + ".tmp", LIBRARY)
+    return LIBRARY
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        build()
+    lib = ctypes.CDLL(LIBRARY)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    for name in ("ua2a_oracle_mode0", "ua2a_oracle_mode1"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, i64, i64, i64, i64, i32, vp, vp]
+        fn.restype = ctypes.c_int
+    lib.ua2a_oracle_chunked.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp]
+    lib.ua2a_oracle_chunked.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class OracleError(ValueError):
+    """Raised when the oracle rejects its arguments (code from ua2a_oracle.c)."""
+
+    def __init__(self, code: int):
+        super().__init__(f"oracle rejected the call (code {code})")
+        self.code = code
+
+
+def local_shape(x_shape, mode: int, w: int):
+    """(B, S_local, H, D) of a rank-stacked input, derived the way run_armed does."""
+    if len(x_shape) != 5 or x_shape[0] != w:
+        raise ValueError(f"expected a rank-stacked [w={w}, B, S, H, D] array, got {tuple(x_shape)}")
+    _, B, S, Hx, D = x_shape
+    if mode == 0:
+        return B, S, Hx, D
+    if mode == 1:
+        if S % w:
+            raise ValueError("mode 1 needs S_global divisible by w")
+        return B, S // w, Hx * w, D
+    raise ValueError("mode must be 0 or 1")
+
+
+def exchange(x: np.ndarray, mode: int, w: int, chunked: bool = False) -> np.ndarray:
+    """Run the oracle on a rank-stacked array and return a fresh output array."""
+    x = np.ascontiguousarray(x)
+    B, S_local, H, D = local_shape(x.shape, mode, w)
+    if H % w:
+        raise OracleError(-2)
+    if mode == 0:
+        out = np.empty((w, B, S_local * w, H // w, D), dtype=x.dtype)
+    else:
+        out = np.empty((w, B, S_local, H, D), dtype=x.dtype)
+    lib = _load()
+    e = x.dtype.itemsize
+    ip, op = x.ctypes.data, out.ctypes.data
+    if chunked:
+        rc = lib.ua2a_oracle_chunked(mode, w, B, S_local, H, D, e, ip, op)
+    elif mode == 0:
+        rc = lib.ua2a_oracle_mode0(w, B, S_local, H, D, e, ip, op)
+    else:
+        rc = lib.ua2a_oracle_mode1(w, B, S_local, H, D, e, ip, op)
+    if rc != 0:
+        raise OracleError(rc)
+    return out
+
+
+def raw_call(fn_name: str, *args) -> int:
+    """Call one oracle entry point with raw arguments (for argument-check tests)."""
+    return getattr(_load(), fn_name)(*args)
