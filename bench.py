@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Throughput of the Ulysses all_to_all_4D exchange on one MI355X.
+
+One step = one mode-0 exchange (scatter heads, gather sequence) followed by
+one mode-1 exchange (its inverse) of the video-DiT-scale workload: w = 8
+virtual ranks, B = 1, S_local = 9450 (75 600 tokens in all), H = 40 heads
+(5 per rank), D = 128, bf16, N(0,1) seeded synthetic data, all ranks stacked
+in one HBM allocation per tensor (FastVideo "ulysses_a2a" API page, method
+run_armed, for the two modes).  Inputs are resident in HBM before the timed
+region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+prints ONE JSON line.  `value` is achieved HBM read+write GB/s over the K
+timed steps (algorithmic bytes: every element read once and written once per
+exchange, 2 * 774 144 000 B per exchange, two exchanges per step).  The
+`roofline` object is for the mode-0 permutation kernel, timed with HIP events
+recorded on the stream the kernel is launched on.  `cpu_baseline` times the
+plain CPU oracle on the host (single thread) on a bounded sample of the same
+workload.  A device-to-device copy of the same byte count is timed beside it
+(`memcpy_GBps`).
+
+    python bench.py --traffic-from DIR
+
+reads the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then
+WRITE_SIZE) under DIR and writes profiles/traffic_direct_video_dit.json, which
+later runs report as roofline.traffic while the kernel sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
+WORKLOAD = "video_dit"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_direct_video_dit.json")
+DIRECT_KERNEL = "ua2a_direct_kernel"
+COPY_KERNEL_HINT = "copyBuffer"     # the runtime's device-to-device copy kernel
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the library sources: traffic counters are valid only for this build."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "ulysses_all_re_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "include", "ua2a.h")]:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None          # counters were taken on another build of the kernel
+    return t
+
+
+def cpu_baseline(x_cpu, w, steps, moved_bytes):
+    """The oracle as it stands, single-threaded, on `steps` full round trips."""
+    import oracle
+    xb = x_cpu.view(__import__("torch").int16).numpy()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        y = oracle.exchange(xb, 0, w)
+        oracle.exchange(y, 1, w)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(2 * moved_bytes * steps / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{steps} full {WORKLOAD} round trips (mode 0 then mode 1, "
+                  f"{2 * moved_bytes * steps} algorithmic bytes) through the C nested-loop "
+                  f"oracle, one thread, {dt:.2f} s",
+    }
+
+
+def run(args):
+    import torch
+
+    import ulysses_all_re_amd as ua
+    from workloads import CONFIGS, make_tensor
+
+    c = CONFIGS[WORKLOAD]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lay = ua.ua2a_layout(w, B, S, H, D, 2)
+    moved = lay["moved_bytes"]                     # per exchange: read + write
+    log(f"workload {WORKLOAD} w={w} B={B} S_local={S} H={H} D={D} bf16, "
+        f"{lay['tensor_bytes']} B per tensor")
+    x_cpu = make_tensor((w, B, S, H, D), c["dtype"], c["dist"], c["seed0"])
+    x = x_cpu.to(dev)
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16, blocks=args.blocks, device=dev)
+    y = torch.empty(plan.out_shape(0), dtype=torch.bfloat16, device=dev)
+    z = torch.empty(plan.out_shape(1), dtype=torch.bfloat16, device=dev)
+    info0 = plan.describe(x, 0, out=y)
+    info1 = plan.describe(y, 1, out=z)
+    log(f"mode 0 launch {info0}")
+    log(f"mode 1 launch {info1}")
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        plan.exchange(x, 0, out=y, stream=stream)
+        plan.exchange(y, 1, out=z, stream=stream)
+    torch.cuda.synchronize(dev)
+    if not torch.equal(z.view(torch.int16), x.view(torch.int16)):
+        raise SystemExit("round trip did not return the input; refusing to report a number")
+    log(f"warmup done ({args.warmup} steps), round trip bit-exact")
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+    torch.cuda.synchronize(dev)
+    ev[0].record(stream)
+    for i in range(K):
+        plan.exchange(x, 0, out=y, stream=stream)
+        ev[2 * i + 1].record(stream)
+        plan.exchange(y, 1, out=z, stream=stream)
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize(dev)
+    total_ms = ev[0].elapsed_time(ev[-1])
+    t0 = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(K)]
+    t1 = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(K)]
+    log(f"timed {K} steps in {total_ms:.3f} ms")
+
+    # device-to-device copy of the same byte count, timed the same way
+    cp = torch.empty_like(x)
+    for _ in range(3):
+        cp.copy_(x)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize(dev)
+    cev[0].record(stream)
+    for i in range(K):
+        cp.copy_(x)
+        cev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    tc = [cev[i].elapsed_time(cev[i + 1]) for i in range(K)]
+
+    def gbps(ms):
+        return moved / (ms * 1e-3) / 1e9
+
+    def med(v):
+        s = sorted(v)
+        return s[len(s) // 2]
+
+    avg0, avg1 = sum(t0) / K, sum(t1) / K
+    value = 2 * moved * K / (total_ms * 1e-3) / 1e9
+    traffic = load_traffic()
+    roofline = {
+        "bound": "hbm",
+        "kernel": f"ua2a_direct_kernel<{info0['vector_bytes']}, mode 0>",
+        "achieved": round(gbps(avg0), 1),
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(gbps(avg0) / PEAK_HBM_GBPS, 4),
+        "traffic": traffic["mode0_bytes_per_launch"] if traffic else None,
+        "algorithmic_bytes": moved,
+        "avg_launch_us": round(avg0 * 1e3, 2),
+    }
+    result = {
+        "metric": "achieved HBM GB/s (read+write) and % of peak, mode0/mode1, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "w": w, "B": B, "S_local": S, "S_global": S * w,
+                   "H": H, "D": D, "elem": "bf16", "step": "mode 0 then mode 1",
+                   "bytes_per_step": 2 * moved},
+        "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "mode0": {"GBps_avg": round(gbps(avg0), 1), "GBps_median": round(gbps(med(t0)), 1),
+                  "us_avg": round(avg0 * 1e3, 2), "us_min": round(min(t0) * 1e3, 2),
+                  "pct_peak": round(100 * gbps(avg0) / PEAK_HBM_GBPS, 2), "launch": info0},
+        "mode1": {"GBps_avg": round(gbps(avg1), 1), "GBps_median": round(gbps(med(t1)), 1),
+                  "us_avg": round(avg1 * 1e3, 2), "us_min": round(min(t1) * 1e3, 2),
+                  "pct_peak": round(100 * gbps(avg1) / PEAK_HBM_GBPS, 2), "launch": info1},
+        "memcpy_GBps": round(gbps(sum(tc) / K), 1),
+        "roofline": roofline,
+        "roofline_mode1": {"achieved": round(gbps(avg1), 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(gbps(avg1) / PEAK_HBM_GBPS, 4),
+                           "traffic": traffic["mode1_bytes_per_launch"] if traffic else None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: {args.cpu_steps} oracle round trips")
+        result["cpu_baseline"] = cpu_baseline(x_cpu, w, args.cpu_steps, moved)
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------- counter post-processing
+
+def _read_counter_rows(d):
+    rows = []
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        with open(p, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def traffic_from(d):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this bench into bytes per launch.
+
+    Each counter reads KiB per dispatch.  It is scaled by what the same counter
+    reads for the runtime's device-to-device copy of a known size (the memcpy
+    leg of this bench: tensor_bytes read and tensor_bytes written).
+    """
+    import ulysses_all_re_amd as ua
+    from workloads import CONFIGS
+    c = CONFIGS[WORKLOAD]
+    lay = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], 2)
+    rows = _read_counter_rows(d)
+    if not rows:
+        raise SystemExit(f"no counter_collection CSV under {d}")
+    kcol = next(k for k in rows[0] if k.lower() in ("kernel_name", "kernel-name", "kernelname"))
+    ncol = next(k for k in rows[0] if k.lower() in ("counter_name", "counter-name"))
+    vcol = next(k for k in rows[0] if k.lower() in ("counter_value", "counter-value"))
+    vals = {}
+    for r in rows:
+        name = r[kcol]
+        key = ("mode1" if "ELb1E" in name else "mode0") if DIRECT_KERNEL in name else \
+              ("copy" if COPY_KERNEL_HINT in name else None)
+        if key is None:
+            continue
+        vals.setdefault((key, r[ncol]), []).append(float(r[vcol]))
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    known = lay["tensor_bytes"]
+    fetch_f = avg[("copy", "FETCH_SIZE")] * 1024 / known
+    write_f = avg[("copy", "WRITE_SIZE")] * 1024 / known
+    out = {"source_hash": source_hash(), "workload": WORKLOAD, "counters_dir": d,
+           "copy_scale": {"FETCH_SIZE": round(fetch_f, 4), "WRITE_SIZE": round(write_f, 4),
+                          "known_bytes_each_way": known}}
+    for m in ("mode0", "mode1"):
+        fk = avg[(m, "FETCH_SIZE")] * 1024 / fetch_f
+        wk = avg[(m, "WRITE_SIZE")] * 1024 / write_f
+        out[f"{m}_fetch_bytes"] = round(fk)
+        out[f"{m}_write_bytes"] = round(wk)
+        out[f"{m}_bytes_per_launch"] = round(fk + wk)
+        out[f"{m}_raw_kib"] = {"FETCH_SIZE": avg[(m, "FETCH_SIZE")], "WRITE_SIZE": avg[(m, "WRITE_SIZE")]}
+    out["algorithmic_bytes_per_launch"] = lay["moved_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+    print(json.dumps(out, indent=2))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--blocks", type=int, default=0, help="grid-size hint (0 = library default)")
+    ap.add_argument("--cpu-steps", type=int, default=4,
+                    help="oracle round trips timed for cpu_baseline (about 2.5 s each)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", metavar="DIR", default=None)
+    args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("this exchange runs all w virtual ranks on ONE GPU; there is no multi-GPU "
+               f"configuration to measure (asked for --gpus {args.gpus}, WORLD_SIZE={world})")
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(msg, file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

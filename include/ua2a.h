@@ -1,0 +1,179 @@
+/*
+ * ua2a.h -- C ABI of the MI355X (gfx950) Ulysses all_to_all_4D exchange.
+ *
+ * The operation (FastVideo "ulysses_a2a" API page, method run_armed):
+ *   w ranks each hold x[B, S_local, H, D].
+ *   mode 0 ("scatter heads, gather sequence"): rank r ends with
+ *       out_r[b][j*S_local + s][h][d] = x_j[b][s][r*(H/w) + h][d]
+ *     i.e. [B, S_local*w, H/w, D]: the full sequence, gathered from all
+ *     ranks in rank order, for its own contiguous block of H/w heads.
+ *   mode 1 (the inverse, same page): rank j holds y_j[B, S_global, H/w, D]
+ *     with S_global = S_local*w and ends with [B, S_local, H, D]:
+ *       out_j[b][s][r*(H/w) + h][d] = y_r[b][j*S_local + s][h][d].
+ *   chunked (same method, chunked branch): the exchange is issued once per
+ *     batch plane, each plane passing through a window sized for one plane;
+ *     the result is identical to the unchunked call.
+ *
+ * All w "virtual ranks" live on ONE device, stacked rank-major in one
+ * allocation per tensor:
+ *   mode-0 side ("head-complete")     [w][B][S_local][H][D]
+ *   mode-1 side ("sequence-gathered") [w][B][S_local*w][H/w][D]
+ * Both are dense, row-major, no padding.  Elements are moved as raw
+ * elem_bytes-byte patterns (bf16/fp16 = 2, fp32 = 4, ...): the result is a
+ * bit-exact permutation of the input for every dtype.
+ *
+ * Conventions for every function below:
+ *   - return 0 (UA2A_OK) or a negative UA2A_ERR_* code; nothing throws;
+ *   - no function synchronises the host with the device;
+ *   - ua2a_exchange allocates nothing and launches only on the given stream;
+ *   - pointers named in/out/window are device pointers on the plan's
+ *     device, owned by the caller, and are only borrowed by the library.
+ */
+#ifndef UA2A_H
+#define UA2A_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+#define UA2A_OK                0
+#define UA2A_ERR_INVALID_ARG  (-1) /* null pointer, mode/chunked not 0/1, bad elem_bytes, bad path */
+#define UA2A_ERR_SHAPE        (-2) /* a dimension < 1, H % w != 0, or a size beyond the limits below */
+#define UA2A_ERR_ALIGN        (-3) /* a tensor or window pointer not aligned to elem_bytes */
+#define UA2A_ERR_ALIAS        (-4) /* byte ranges of in, out and window overlap */
+#define UA2A_ERR_CAPACITY     (-5) /* chunked call with no window or one smaller than one plane */
+#define UA2A_ERR_DEVICE       (-6) /* the calling thread's current device is not the plan's */
+#define UA2A_ERR_HIP          (-7) /* a HIP runtime or launch call failed: the plan is now disabled */
+#define UA2A_ERR_DISABLED     (-8) /* the plan was disabled by an earlier UA2A_ERR_HIP */
+#define UA2A_ERR_NOMEM        (-9) /* host allocation of the plan object failed */
+
+/* Limits: w <= 65536; every one of B, S_local, H, D <= 2^31 - 1; one
+ * rank-stacked tensor <= 2^47 bytes (128 TiB). */
+
+typedef struct ua2a_plan_s* ua2a_plan_t;
+
+/* Sizes derived from a shape (host only; see ua2a_layout). */
+typedef struct ua2a_layout_s {
+    int64_t H_local;       /* H / w: heads each rank keeps in mode 0 */
+    int64_t S_global;      /* S_local * w */
+    int64_t run_bytes;     /* H_local * D * elem_bytes: one token's slice of one head block,
+                              the unit that stays contiguous on both sides */
+    int64_t tensor_elems;  /* w * B * S_local * H * D (input and output alike) */
+    int64_t tensor_bytes;  /* tensor_elems * elem_bytes */
+    int64_t window_bytes;  /* w * S_local * H * D * elem_bytes: one batch plane of every rank,
+                              the least window a chunked call accepts */
+    int64_t moved_bytes;   /* 2 * tensor_bytes: every element read once and written once */
+} ua2a_layout_t;
+
+/* Which kernel family runs an exchange (ua2a_plan_set_path, ua2a_describe). */
+#define UA2A_PATH_AUTO    0  /* the library chooses (default) */
+#define UA2A_PATH_DIRECT  1  /* one pass, each lane moves whole vectors of a run */
+#define UA2A_PATH_LDS     2  /* rows staged through LDS, both sides moved as contiguous spans */
+
+/* What an exchange would launch (ua2a_describe). */
+typedef struct ua2a_launch_info_s {
+    int32_t path;          /* UA2A_PATH_DIRECT or UA2A_PATH_LDS */
+    int32_t vector_bytes;  /* bytes per lane access of the permutation kernel (1..16) */
+    int32_t grid;          /* workgroups of the permutation kernel per launch */
+    int32_t block;         /* threads per workgroup */
+    int64_t tiles;         /* work tiles per launch */
+    int32_t launches;      /* kernel launches per exchange (2*B when chunked: B permutes + B copies) */
+    int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
+} ua2a_launch_info_t;
+
+/*
+ * ua2a_layout: validate a shape and fill *layout.  Host only, no device call.
+ *   w           virtual ranks (>= 1)
+ *   B, S_local, H, D   the mode-0-side (local) shape, as the page passes it to
+ *               the native call in both modes (mode 1 derives S_local and H
+ *               from [B, S_global, H_local, D] first)
+ *   elem_bytes  1, 2, 4 or 8
+ * Errors: INVALID_ARG (layout NULL, elem_bytes), SHAPE.
+ */
+int ua2a_layout(int32_t w, int64_t B, int64_t S_local, int64_t H, int64_t D,
+                int32_t elem_bytes, ua2a_layout_t* layout);
+
+/*
+ * ua2a_plan: create a plan for one shape on one device.  Host only: it makes
+ * no HIP call and allocates only the small host-side plan object.
+ *   blocks      grid-size hint for the permutation kernel (the page passes
+ *               `blocks` to the native op); 0 = choose from the device's
+ *               compute-unit count.  The result never depends on it.
+ *   window, window_bytes  caller-owned device buffer used by chunked calls
+ *               as the one-plane receive window of all w ranks; it may be
+ *               NULL/0 if chunked is never requested.  The plan borrows it:
+ *               the caller keeps it alive and unchanged until ua2a_destroy.
+ *               A bigger window needs a new plan (windows never shrink or
+ *               grow in place, as on the page, where growth re-builds).
+ *   device      HIP device ordinal the plan launches on.
+ * Errors: INVALID_ARG (plan_out NULL, device < 0, blocks < 0, window_bytes
+ * < 0, window NULL with window_bytes > 0), SHAPE, ALIGN (window not
+ * elem_bytes-aligned), NOMEM.  *plan_out is NULL on error.
+ */
+int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
+              int64_t H, int64_t D, int32_t elem_bytes, int32_t blocks,
+              void* window, int64_t window_bytes, int32_t device);
+
+/*
+ * ua2a_exchange: enqueue one exchange on `stream` (a hipStream_t; NULL = the
+ * device's null stream) and return without waiting.
+ *   mode     0 or 1 (see the top of this file)
+ *   chunked  0: one permutation launch over all B planes;
+ *            1: per plane p, a permutation of plane p of every rank into the
+ *               window, then a copy of the window into plane p of `out`;
+ *               plane p+1 reuses the window only after plane p's copy, by
+ *               stream order.  Needs window_bytes >= layout.window_bytes.
+ *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]
+ *   out      the other layout; must not overlap `in` or the window.
+ * Both tensors must be elem_bytes-aligned; 16-byte alignment (and run_bytes
+ * a multiple of 16) selects the widest vectors.  The calling thread's current
+ * device must be the plan's device.  One plan serves one stream at a time:
+ * calls on one plan must not run concurrently from several threads.
+ * Errors: INVALID_ARG, ALIGN, ALIAS, CAPACITY, DEVICE (no state change);
+ * HIP (the launch failed; the plan becomes disabled, see
+ * ua2a_plan_last_error); DISABLED (an earlier HIP error).
+ */
+int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked,
+                  const void* in, void* out, void* stream);
+
+/*
+ * ua2a_destroy: release the plan object.  It always consumes the plan, also
+ * a disabled one, and never touches the window or device memory (the page's
+ * disposer likewise consumes its handle even when cleanup reports an error).
+ * NULL is accepted and ignored.  Returns UA2A_OK.
+ */
+int ua2a_destroy(ua2a_plan_t plan);
+
+/* ua2a_status_string: static English text for a status code (never NULL). */
+const char* ua2a_status_string(int32_t status);
+
+/* ua2a_plan_last_error: why the plan is disabled, or "" if it is not (or
+ * plan is NULL).  The string lives as long as the plan. */
+const char* ua2a_plan_last_error(ua2a_plan_t plan);
+
+/*
+ * ua2a_plan_set_path: force a kernel family for later exchanges (for
+ * measurement); UA2A_PATH_AUTO restores the default choice.  Forcing
+ * UA2A_PATH_LDS on a shape whose rows do not fit the LDS tile makes
+ * exchanges fall back to UA2A_PATH_DIRECT (ua2a_describe reports which).
+ * Errors: INVALID_ARG.
+ */
+int ua2a_plan_set_path(ua2a_plan_t plan, int32_t path);
+
+/*
+ * ua2a_describe: report in *info what ua2a_exchange(plan, mode, chunked,
+ * in, out, ...) would launch, after the same argument checks (same error
+ * codes, minus DEVICE and HIP).  Host only; the pointers are only inspected
+ * for alignment and overlap, never dereferenced.
+ */
+int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked,
+                  const void* in, const void* out, ua2a_launch_info_t* info);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UA2A_H */

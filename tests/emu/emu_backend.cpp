@@ -1,0 +1,152 @@
+// Host emulation of the ua2a device backend -- TEST ONLY.
+//
+// Linked with the library's own host logic (ua2a_host.cpp) into
+// tests/emu/libua2a_emu.so, it replaces the HIP launches by running the
+// kernels' per-thread bodies (ua2a_bodies.h) on the CPU: every tile, every
+// thread of the workgroup, the LDS kernel's fill phase for all threads
+// before its drain phase (what the workgroup barrier guarantees on the GPU).
+// Buffers are ordinary host memory, so the same C ABI can be exercised on a
+// machine with no GPU, under AddressSanitizer, and compared with the oracle.
+#include <string.h>
+
+#include <vector>
+
+#include "ua2a_bodies.h"
+#include "ua2a_internal.h"
+
+namespace ua2a {
+
+namespace {
+int g_fail_next = 0;          // test hook: fail the next launch with this code
+int g_device = 0;             // device the emulation reports as current
+int g_launches = 0;           // launches since the last reset
+int g_kernel_counts[3] = {0, 0, 0};
+uint32_t g_last_grid = 0;
+
+template <int VB, bool M1>
+void run_direct(const DirectGeom& g)
+{
+    for (uint32_t t = 0; t < g.num_tiles; ++t)
+        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
+            direct_tile_body<VB, M1, kDirectUnroll>(g, t, tid);
+}
+
+template <int G, bool M1>
+void run_lds(const LdsGeom& g)
+{
+    // exactly lds_bytes, so any access past the reserved LDS is a heap
+    // overflow that AddressSanitizer reports
+    std::vector<uint8_t> lds(g.lds_bytes);
+    for (uint32_t t = 0; t < g.num_tiles; ++t) {
+        memset(lds.data(), 0xA5, lds.size());
+        const LdsTile d = lds_tile(g, t);
+        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
+            lds_fill<G, M1, kLdsUnroll>(g, d, tid, lds.data());
+        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
+            lds_drain<G, M1>(g, d, tid, lds.data());
+    }
+}
+
+template <int VB>
+void run_copy(const CopyGeom& g)
+{
+    for (uint32_t t = 0; t < g.num_tiles; ++t)
+        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
+            copy_tile_body<VB, kDirectUnroll>(g, t, tid);
+}
+
+template <bool M1>
+int dispatch_direct(const DirectGeom& g, int vb)
+{
+    switch (vb) {
+    case 16: run_direct<16, M1>(g); return 0;
+    case 8: run_direct<8, M1>(g); return 0;
+    case 4: run_direct<4, M1>(g); return 0;
+    case 2: run_direct<2, M1>(g); return 0;
+    case 1: run_direct<1, M1>(g); return 0;
+    default: return 1;
+    }
+}
+
+template <bool M1>
+int dispatch_lds(const LdsGeom& g, int gw)
+{
+    switch (gw) {
+    case 16: run_lds<16, M1>(g); return 0;
+    case 8: run_lds<8, M1>(g); return 0;
+    case 4: run_lds<4, M1>(g); return 0;
+    case 2: run_lds<2, M1>(g); return 0;
+    case 1: run_lds<1, M1>(g); return 0;
+    default: return 1;
+    }
+}
+
+int dispatch_copy(const CopyGeom& g, int vb)
+{
+    switch (vb) {
+    case 16: run_copy<16>(g); return 0;
+    case 8: run_copy<8>(g); return 0;
+    case 4: run_copy<4>(g); return 0;
+    case 2: run_copy<2>(g); return 0;
+    case 1: run_copy<1>(g); return 0;
+    default: return 1;
+    }
+}
+}  // namespace
+
+int backend_current_device(int32_t* device)
+{
+    *device = g_device;
+    return 0;
+}
+
+int backend_cu_count(int32_t, int32_t* cus)
+{
+    *cus = 256;
+    return 0;
+}
+
+const char* backend_error_name(int) { return "emulated launch failure"; }
+
+int backend_launch(const Launch& L, void*)
+{
+    if (g_fail_next) {
+        const int e = g_fail_next;
+        g_fail_next = 0;
+        return e;
+    }
+    ++g_launches;
+    ++g_kernel_counts[static_cast<int>(L.kernel)];
+    g_last_grid = L.grid;
+    if (L.grid < 1) return 2;
+    switch (L.kernel) {
+    case Kernel::Direct:
+        return L.mode ? dispatch_direct<true>(L.direct, L.width) : dispatch_direct<false>(L.direct, L.width);
+    case Kernel::Lds:
+        if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.row)
+            return 3;
+        return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);
+    case Kernel::Copy:
+        return dispatch_copy(L.copy, L.width);
+    }
+    return 4;
+}
+
+}  // namespace ua2a
+
+extern "C" {
+
+void ua2a_emu_fail_next_launch(int code) { ua2a::g_fail_next = code; }
+void ua2a_emu_set_device(int device) { ua2a::g_device = device; }
+
+void ua2a_emu_reset_counts(void)
+{
+    ua2a::g_launches = 0;
+    ua2a::g_kernel_counts[0] = ua2a::g_kernel_counts[1] = ua2a::g_kernel_counts[2] = 0;
+}
+
+int ua2a_emu_launches(void) { return ua2a::g_launches; }
+int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
+unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
+
+}  // extern "C"

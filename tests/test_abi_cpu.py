@@ -1,0 +1,91 @@
+"""The real libua2a.so on the CPU: it loads, exports every entry point that
+include/ua2a.h declares, and its host-only calls (layout, plan, describe,
+status strings) behave -- without touching a GPU (no exchange is issued)."""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import ulysses_all_re_amd as ua
+from workloads import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ua2a.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ua2a_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ua.LIBRARY):
+        from ulysses_all_re_amd import build
+        build.build()
+    return ua.load_library()
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared() == sorted(ua.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    syms = subprocess.check_output(["nm", "-D", "--defined-only", ua.LIBRARY], text=True)
+    exported = {line.split()[-1] for line in syms.splitlines() if " T " in line}
+    for name in declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_targets_gfx950(lib):
+    # the embedded code object names its target
+    assert b"gfx950" in open(ua.LIBRARY, "rb").read()
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_layout_of_the_workloads(lib, name):
+    c = CONFIGS[name]
+    e = {"bf16": 2, "fp16": 2, "fp32": 4}[c["dtype"]]
+    lay = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], e)
+    n = c["w"] * c["B"] * c["S_local"] * c["H"] * c["D"]
+    assert lay["tensor_elems"] == n and lay["tensor_bytes"] == n * e
+    assert lay["H_local"] == c["H"] // c["w"] and lay["S_global"] == c["S_local"] * c["w"]
+    assert lay["run_bytes"] == c["H"] // c["w"] * c["D"] * e
+    assert lay["window_bytes"] == n * e // c["B"]
+    assert lay["moved_bytes"] == 2 * n * e
+
+
+def test_host_only_calls(lib):
+    # plan and describe make no device call; the pointers are never dereferenced
+    h = ua.ua2a_plan(8, 1, 9450, 40, 128, 2, 0, 0, 0, 0)
+    try:
+        base = 1 << 40
+        info = ua.ua2a_describe(h, 0, 0, base, base + (1 << 30))
+        assert info["path"] == ua.UA2A_PATH_DIRECT and info["vector_bytes"] == 16
+        assert info["block"] == 256 and info["launches"] == 1 and info["grid"] >= 1
+        ua.ua2a_plan_set_path(h, ua.UA2A_PATH_LDS)
+        assert ua.ua2a_describe(h, 1, 0, base, base + (1 << 30))["path"] == ua.UA2A_PATH_LDS
+        with pytest.raises(ua.UA2AError) as e:
+            ua.ua2a_describe(h, 0, 1, base, base + (1 << 30))
+        assert e.value.code == ua.UA2A_ERR_CAPACITY
+        with pytest.raises(ua.UA2AError) as e:
+            ua.ua2a_describe(h, 0, 0, base, base + 16)
+        assert e.value.code == ua.UA2A_ERR_ALIAS
+        assert ua.ua2a_plan_last_error(h) == ""
+    finally:
+        ua.ua2a_destroy(h)
+    with pytest.raises(ua.UA2AError) as e:
+        ua.ua2a_plan(3, 1, 8, 4, 16, 2)
+    assert e.value.code == ua.UA2A_ERR_SHAPE
+    assert "window" in ua.ua2a_status_string(ua.UA2A_ERR_CAPACITY)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(ua, "_lib", None)
+    monkeypatch.setattr(ua, "LIBRARY", str(tmp_path / "libua2a.so"))
+    with pytest.raises(RuntimeError, match="no non-HIP implementation"):
+        ua.load_library()

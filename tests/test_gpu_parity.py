@@ -1,0 +1,266 @@
+"""GPU parity: the HIP exchange, called through the C ABI, against the CPU oracle.
+
+Every comparison is byte for byte (the exchange is a pure permutation, so the
+bar is bit-exactness for every dtype).  Covers the five workloads at their
+full sizes, both modes, the chunked path, the short-run and unaligned tail
+paths, both kernel families, misaligned bases, grid-size hints, poisoned
+outputs and guard bands, back-to-back launches on one stream, a non-default
+stream, and the argument checks.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ulysses_all_re_amd as ua
+from workloads import BITS_VIEW, CONFIGS, TAIL_SHAPES, make_tensor
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+POISON = -1          # 0xFF.. bit pattern written into outputs before each run
+PATHS = {"auto": ua.UA2A_PATH_AUTO, "direct": ua.UA2A_PATH_DIRECT, "lds": ua.UA2A_PATH_LDS}
+
+
+def note(msg):
+    """Name the case on stdout before it touches the GPU."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ua.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def bits(t):
+    return t.view(BITS_VIEW[t.element_size()])
+
+
+def oracle_out(x_cpu, mode, w, chunked=False):
+    xb = bits(x_cpu).numpy()
+    return torch.from_numpy(oracle.exchange(xb, mode, w, chunked=chunked))
+
+
+def poisoned(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    b = bits(t)
+    b.fill_(255 if b.dtype == torch.uint8 else POISON)     # all-ones bit pattern
+    return t
+
+
+def assert_same_bits(got_dev, want_bits_cpu, what):
+    got = bits(got_dev.cpu())
+    if not torch.equal(got, want_bits_cpu):
+        bad = (got != want_bits_cpu).nonzero()
+        raise AssertionError(f"{what}: {bad.shape[0]} elements differ; first at {bad[0].tolist()}")
+
+
+def cfg_shape(c):
+    return c["w"], c["B"], c["S_local"], c["H"], c["D"]
+
+
+def in_shape(w, B, S, H, D, mode):
+    return (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "video_dit", "chunked", "awkward"])
+def test_workload_parity(name):
+    c = CONFIGS[name]
+    w, B, S, H, D = cfg_shape(c)
+    dt = ua_dtype = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[c["dtype"]]
+    lay = ua.ua2a_layout(w, B, S, H, D, torch.empty((), dtype=dt).element_size())
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV) if c["chunked"] else None
+    plan = ua.Plan(w, B, S, H, D, ua_dtype, window=window)
+    chunk_opts = (False, True) if c["chunked"] else (False,)
+    x0 = make_tensor(in_shape(w, B, S, H, D, 0), c["dtype"], c["dist"], c["seed0"])
+    want0 = oracle_out(x0, 0, w)
+    x0d = x0.to(DEV)
+    for chunked in chunk_opts:
+        note(f"{name} mode0 chunked={chunked} shape={tuple(x0.shape)} path={plan.describe(x0d, 0, chunked)}")
+        y = plan.exchange(x0d, 0, chunked, out=poisoned(plan.out_shape(0), dt))
+        torch.cuda.synchronize()
+        assert_same_bits(y, want0, f"{name} mode 0 chunked={chunked}")
+        # round trip: mode 1 on mode 0's output gives the input back
+        note(f"{name} mode1 round trip chunked={chunked}")
+        z = plan.exchange(y, 1, chunked, out=poisoned(plan.out_shape(1), dt))
+        torch.cuda.synchronize()
+        assert_same_bits(z, bits(x0), f"{name} round trip chunked={chunked}")
+    del want0, y, z
+    # mode 1 on an independent input
+    dist = c["dist"] if c["dist"] != "index" else "index_bits"
+    x1 = make_tensor(in_shape(w, B, S, H, D, 1), c["dtype"], dist, c["seed1"])
+    want1 = oracle_out(x1, 1, w)
+    x1d = x1.to(DEV)
+    for chunked in chunk_opts:
+        note(f"{name} mode1 chunked={chunked} shape={tuple(x1.shape)}")
+        u = plan.exchange(x1d, 1, chunked, out=poisoned(plan.out_shape(1), dt))
+        torch.cuda.synchronize()
+        assert_same_bits(u, want1, f"{name} mode 1 chunked={chunked}")
+    plan.close()
+
+
+def test_awkward_exact_provenance():
+    """The awkward workload with every element a distinct int32 bit pattern."""
+    c = CONFIGS["awkward"]
+    w, B, S, H, D = cfg_shape(c)
+    x = make_tensor((w, B, S, H, D), "fp32", "index_bits")
+    plan = ua.Plan(w, B, S, H, D, torch.float32)
+    note("awkward index_bits mode0")
+    y = plan.exchange(x.to(DEV), 0).cpu()
+    got = bits(y).numpy()
+    # decode where each element came from and check it against the oracle's placement
+    assert np.array_equal(got, oracle.exchange(bits(x).numpy(), 0, w))
+    assert np.array_equal(np.sort(got.ravel()), np.arange(x.numel(), dtype=np.int32))
+    plan.close()
+
+
+# ------------------------------------------------- tail shapes, both paths
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("shape", TAIL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_tail_shapes(shape, path):
+    w, B, S, H, D, dtype = shape
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32,
+          "f64": torch.float64, "u8": torch.uint8}[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=window)
+    plan.set_path(PATHS[path])
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 11 + mode)
+        want = oracle_out(x, mode, w)
+        xd = x.to(DEV)
+        for chunked in (False, True):
+            note(f"tail {shape} {path} mode={mode} chunked={chunked} {plan.describe(xd, mode, chunked)}")
+            y = plan.exchange(xd, mode, chunked, out=poisoned(plan.out_shape(mode), dt))
+            torch.cuda.synchronize()
+            assert_same_bits(y, want, f"tail {shape} {path} mode {mode} chunked={chunked}")
+    plan.close()
+
+
+@pytest.mark.parametrize("offsets", [(1, 0), (0, 1), (1, 3), (5, 7)])
+@pytest.mark.parametrize("shape", [(4, 1, 1024, 24, 128, "bf16"), (3, 1, 5, 3, 7, "bf16"),
+                                   (2, 2, 300, 4, 16, "bf16")], ids=lambda s: "x".join(map(str, s)))
+def test_misaligned_bases(shape, offsets):
+    """Tensors that start one or more elements past an aligned address, with guard bands."""
+    w, B, S, H, D, dtype = shape
+    dt = torch.bfloat16
+    plan = ua.Plan(w, B, S, H, D, dt)
+    n = w * B * S * H * D
+    for path in ("auto", "direct", "lds"):
+        plan.set_path(PATHS[path])
+        for mode in (0, 1):
+            x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "normal", 21 + mode)
+            want = oracle_out(x, mode, w)
+            xin = torch.zeros(n + 64, dtype=dt, device=DEV)
+            xin[offsets[0]:offsets[0] + n] = x.reshape(-1).to(DEV)
+            outbuf = poisoned((n + 64,), dt)
+            xi = xin[offsets[0]:offsets[0] + n].view(in_shape(w, B, S, H, D, mode))
+            yo = outbuf[offsets[1]:offsets[1] + n].view(plan.out_shape(mode))
+            note(f"misaligned {shape} {offsets} {path} mode={mode} {plan.describe(xi, mode, out=yo)}")
+            plan.exchange(xi, mode, out=yo)
+            torch.cuda.synchronize()
+            assert_same_bits(yo, want, f"misaligned {shape} {offsets} {path} mode {mode}")
+            guard = bits(outbuf.cpu())
+            assert (guard[:offsets[1]] == POISON).all() and (guard[offsets[1] + n:] == POISON).all()
+    plan.close()
+
+
+# ------------------------------------------------------ launch-shape freedom
+
+@pytest.mark.parametrize("blocks", [1, 7, 64, 0])
+def test_blocks_hint_gives_identical_bytes(blocks):
+    w, B, S, H, D = cfg_shape(CONFIGS["mid"])
+    x = make_tensor((w, B, S, H, D), "bf16", "normal", 0)
+    want = oracle_out(x, 0, w)
+    xd = x.to(DEV)
+    for path in ("direct", "lds"):
+        plan = ua.Plan(w, B, S, H, D, torch.bfloat16, blocks=blocks)
+        plan.set_path(PATHS[path])
+        note(f"blocks={blocks} path={path} {plan.describe(xd, 0)}")
+        y = plan.exchange(xd, 0, out=poisoned(plan.out_shape(0), torch.bfloat16))
+        torch.cuda.synchronize()
+        assert_same_bits(y, want, f"blocks={blocks} {path}")
+        z = plan.exchange(y, 1)
+        torch.cuda.synchronize()
+        assert_same_bits(z, bits(x), f"blocks={blocks} {path} round trip")
+        plan.close()
+
+
+def test_back_to_back_on_one_stream_and_side_stream():
+    """mode 0 -> mode 1 -> mode 0 queued without host syncs, on a non-default stream."""
+    w, B, S, H, D = cfg_shape(CONFIGS["chunked"])
+    x = make_tensor((w, B, S, H, D), "fp16", "uniform", 0)
+    want = oracle_out(x, 0, w)
+    lay = ua.ua2a_layout(w, B, S, H, D, 2)
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, torch.float16, window=window)
+    s = torch.cuda.Stream()
+    xd = x.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        note("back-to-back chunked/unchunked on a side stream")
+        y = plan.exchange(xd, 0, True)
+        z = plan.exchange(y, 1, False)
+        y2 = plan.exchange(z, 0, False)
+        z2 = plan.exchange(y2, 1, True)
+    s.synchronize()
+    assert_same_bits(y, want, "chunked mode 0")
+    assert_same_bits(y2, want, "mode 0 after round trip")
+    assert_same_bits(z2, bits(x), "second round trip")
+    plan.close()
+
+
+def test_window_is_reused_and_left_alone_outside_its_size():
+    """Chunked planes share one window; bytes past the one-plane size stay untouched."""
+    w, B, S, H, D = 4, 3, 100, 8, 32
+    lay = ua.ua2a_layout(w, B, S, H, D, 2)
+    win = torch.full((lay["window_bytes"] + 4096,), 0x77, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16, window=win)
+    x = make_tensor((w, B, S, H, D), "bf16", "normal", 4)
+    note("window reuse")
+    y = plan.exchange(x.to(DEV), 0, True)
+    torch.cuda.synchronize()
+    assert_same_bits(y, oracle_out(x, 0, w), "chunked via shared window")
+    assert (win[lay["window_bytes"]:].cpu() == 0x77).all()
+    plan.close()
+
+
+# ------------------------------------------------------------- argument checks
+
+def test_argument_checks_on_device_tensors():
+    w, B, S, H, D = 2, 1, 8, 4, 16
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    x = torch.zeros((w, B, S, H, D), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ua.UA2AError) as e:
+        ua.ua2a_exchange(plan.handle, 0, 0, x.data_ptr(), x.data_ptr() + 2, 0)
+    assert e.value.code == ua.UA2A_ERR_ALIAS
+    with pytest.raises(ua.UA2AError) as e:
+        plan.exchange(x, 0, chunked=True)
+    assert e.value.code == ua.UA2A_ERR_CAPACITY
+    with pytest.raises(ua.UA2AError) as e:
+        ua.ua2a_exchange(plan.handle, 0, 0, x.data_ptr() + 1, x.data_ptr() + 4096, 0)
+    assert e.value.code == ua.UA2A_ERR_ALIGN
+    with pytest.raises(ValueError):
+        plan.exchange(x.transpose(2, 3), 0)
+    with pytest.raises(TypeError):
+        plan.exchange(x.float(), 0)
+    assert plan.last_error() == ""
+    # the plan still works after rejected calls
+    y = plan.exchange(x, 0)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+    plan.close()

@@ -1,0 +1,243 @@
+"""Python binding of the MI355X Ulysses all_to_all_4D exchange library (libua2a.so).
+
+Argument marshalling only: every byte of the exchange is moved by the HIP
+kernels in libua2a.so.  PyTorch is used for device memory and streams.
+
+The functions mirror the C ABI of include/ua2a.h one to one
+(``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``, ``ua2a_destroy``,
+``ua2a_status_string``, ``ua2a_plan_last_error``, ``ua2a_plan_set_path``,
+``ua2a_describe``) and raise :class:`UA2AError` on a non-zero status.
+:class:`Plan` wraps them for torch tensors laid out rank-stacked:
+
+    mode 0 input  [w, B, S_local, H, D]        -> output [w, B, S_local*w, H//w, D]
+    mode 1 input  [w, B, S_local*w, H//w, D]   -> output [w, B, S_local, H, D]
+
+(FastVideo ``ulysses_a2a`` API page, method ``run_armed``: mode 0 scatters
+heads and gathers the sequence, mode 1 is its inverse, chunked runs the same
+exchange one batch plane at a time through a window sized for one plane.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG_DIR, "libua2a.so")
+
+UA2A_OK = 0
+UA2A_ERR_INVALID_ARG = -1
+UA2A_ERR_SHAPE = -2
+UA2A_ERR_ALIGN = -3
+UA2A_ERR_ALIAS = -4
+UA2A_ERR_CAPACITY = -5
+UA2A_ERR_DEVICE = -6
+UA2A_ERR_HIP = -7
+UA2A_ERR_DISABLED = -8
+UA2A_ERR_NOMEM = -9
+
+UA2A_PATH_AUTO = 0
+UA2A_PATH_DIRECT = 1
+UA2A_PATH_LDS = 2
+
+# every symbol include/ua2a.h declares
+EXPORTED = (
+    "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_destroy", "ua2a_status_string",
+    "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
+)
+
+
+class ua2a_layout_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "H_local", "S_global", "run_bytes", "tensor_elems", "tensor_bytes",
+        "window_bytes", "moved_bytes")]
+
+
+class ua2a_launch_info_t(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
+                ("lds_rows", ctypes.c_int32)]
+
+
+class UA2AError(RuntimeError):
+    """A non-zero ua2a status."""
+
+    def __init__(self, code: int, what: str, detail: str = ""):
+        msg = f"{what}: {ua2a_status_string(code)} ({code})"
+        if detail:
+            msg += f": {detail}"
+        super().__init__(msg)
+        self.code = code
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libua2a.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(
+            f"{LIBRARY} is missing: build it with `python -m ulysses_all_re_amd.build` "
+            "(the exchange has no non-HIP implementation)")
+    _lib = declare_signatures(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def declare_signatures(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set ctypes argument/return types of the C ABI on a loaded library."""
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    sig = {
+        "ua2a_layout": ([i32, i64, i64, i64, i64, i32, ctypes.POINTER(ua2a_layout_t)], ctypes.c_int),
+        "ua2a_plan": ([ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32, vp, i64, i32], ctypes.c_int),
+        "ua2a_exchange": ([vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        "ua2a_destroy": ([vp], ctypes.c_int),
+        "ua2a_status_string": ([i32], ctypes.c_char_p),
+        "ua2a_plan_last_error": ([vp], ctypes.c_char_p),
+        "ua2a_plan_set_path": ([vp, i32], ctypes.c_int),
+        "ua2a_describe": ([vp, i32, i32, vp, vp, ctypes.POINTER(ua2a_launch_info_t)], ctypes.c_int),
+    }
+    for name, (argtypes, restype) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return lib
+
+
+# ------------------------------------------------------------ C ABI mirror
+
+def ua2a_status_string(status: int) -> str:
+    return load_library().ua2a_status_string(status).decode()
+
+
+def ua2a_layout(w: int, B: int, S_local: int, H: int, D: int, elem_bytes: int) -> dict:
+    lay = ua2a_layout_t()
+    rc = load_library().ua2a_layout(w, B, S_local, H, D, elem_bytes, ctypes.byref(lay))
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_layout")
+    return {name: getattr(lay, name) for name, _ in ua2a_layout_t._fields_}
+
+
+def ua2a_plan(w: int, B: int, S_local: int, H: int, D: int, elem_bytes: int, blocks: int = 0,
+              window: int = 0, window_bytes: int = 0, device: int = 0) -> int:
+    """Create a plan; returns the opaque handle (an int)."""
+    h = ctypes.c_void_p()
+    rc = load_library().ua2a_plan(ctypes.byref(h), w, B, S_local, H, D, elem_bytes, blocks,
+                                  window or None, window_bytes, device)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_plan")
+    return h.value
+
+
+def ua2a_plan_last_error(plan: int) -> str:
+    return load_library().ua2a_plan_last_error(plan).decode()
+
+
+def ua2a_exchange(plan: int, mode: int, chunked: int, inp: int, out: int, stream: int = 0) -> None:
+    """Enqueue one exchange on `stream` (raw device pointers and a hipStream_t)."""
+    rc = load_library().ua2a_exchange(plan, mode, chunked, inp or None, out or None, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_exchange", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_destroy(plan: int) -> None:
+    load_library().ua2a_destroy(plan)
+
+
+def ua2a_plan_set_path(plan: int, path: int) -> None:
+    rc = load_library().ua2a_plan_set_path(plan, path)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_plan_set_path")
+
+
+def ua2a_describe(plan: int, mode: int, chunked: int, inp: int, out: int) -> dict:
+    info = ua2a_launch_info_t()
+    rc = load_library().ua2a_describe(plan, mode, chunked, inp or None, out or None,
+                                      ctypes.byref(info))
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_describe")
+    return {name: getattr(info, name) for name, _ in ua2a_launch_info_t._fields_}
+
+
+# ------------------------------------------------------------- torch wrapper
+
+class Plan:
+    """A ua2a plan bound to torch tensors on one device.
+
+    ``window``: optional device tensor used as the one-plane window of
+    chunked exchanges (at least ``layout['window_bytes']`` bytes); the plan
+    keeps a reference to it for its own lifetime.
+    """
+
+    def __init__(self, w: int, B: int, S_local: int, H: int, D: int, dtype, blocks: int = 0,
+                 window=None, device=None):
+        import torch
+        self.w, self.B, self.S_local, self.H, self.D = w, B, S_local, H, D
+        self.dtype = dtype
+        self.elem_bytes = torch.empty((), dtype=dtype).element_size()
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
+                                   else torch.device(device).index or 0)
+        self.layout = ua2a_layout(w, B, S_local, H, D, self.elem_bytes)
+        self.window = window
+        wptr, wbytes = 0, 0
+        if window is not None:
+            if window.device != self.device:
+                raise ValueError(f"window is on {window.device}, plan is on {self.device}")
+            wptr, wbytes = window.data_ptr(), window.numel() * window.element_size()
+        self.handle = ua2a_plan(w, B, S_local, H, D, self.elem_bytes, blocks, wptr, wbytes,
+                                self.device.index)
+
+    def in_shape(self, mode: int):
+        w, B, S, H, D = self.w, self.B, self.S_local, self.H, self.D
+        return (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+
+    def out_shape(self, mode: int):
+        return self.in_shape(1 - mode)
+
+    def _check(self, t, shape, what):
+        if t.dtype != self.dtype:
+            raise TypeError(f"{what} has dtype {t.dtype}, plan expects {self.dtype}")
+        if t.device != self.device:
+            raise ValueError(f"{what} is on {t.device}, plan is on {self.device}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+
+    def exchange(self, x, mode: int, chunked: bool = False, out=None, stream=None):
+        """Enqueue the exchange on `stream` (default: torch's current stream) and return out."""
+        import torch
+        self._check(x, self.in_shape(mode), "input")
+        if out is None:
+            out = torch.empty(self.out_shape(mode), dtype=self.dtype, device=self.device)
+        else:
+            self._check(out, self.out_shape(mode), "output")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        with torch.cuda.device(self.device):
+            ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
+                          stream.cuda_stream)
+        return out
+
+    def describe(self, x, mode: int, chunked: bool = False, out=None) -> dict:
+        optr = out.data_ptr() if out is not None else x.data_ptr() + self.layout["tensor_bytes"]
+        return ua2a_describe(self.handle, mode, int(chunked), x.data_ptr(), optr)
+
+    def set_path(self, path: int) -> None:
+        ua2a_plan_set_path(self.handle, path)
+
+    def last_error(self) -> str:
+        return ua2a_plan_last_error(self.handle)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            ua2a_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,327 @@
+// Index geometry of the Ulysses all_to_all_4D exchange kernels.
+//
+// The exchange (FastVideo "ulysses_a2a" API page, method run_armed) moves
+// one "run" -- the H/w * D elements of one token in one head block -- at a
+// time: a run is contiguous on both sides, so the whole permutation is a copy
+// of runs between two layouts of the rank-stacked tensors:
+//
+//   P side ("head-complete", mode-0 input / mode-1 output)
+//       [j = token owner][b][s][r = head block][run]
+//   A side ("sequence-gathered", mode-0 output / mode-1 input)
+//       [r = head block][b][j*S_local + s][run]
+//
+// Mode 0 copies P -> A, mode 1 copies A -> P.  Every offset below is built
+// from explicit rank and plane strides, so the same kernels serve the
+// unchunked exchange (dense strides over all B planes) and the chunked one
+// (one plane of every rank, into or out of a one-plane window).
+//
+// Everything here is __host__ __device__ so the kernels and a host-side
+// emulation of their index math (used by the tests to check bounds and
+// parity on a machine with no GPU) evaluate the very same expressions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define UA2A_HD __host__ __device__ __forceinline__
+
+namespace ua2a {
+
+constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
+
+// ------------------------------------------------------------------------
+// Division of a 32-bit unsigned n by an invariant d >= 1 via a multiply-high
+// and a shift (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, the round-up variant with an N+1-bit
+// multiplier): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+//     q = (mulhi32(n, m) + n) >> l   for every 0 <= n < 2^32.
+// The sum is formed in 64 bits so it cannot overflow.
+struct Div32 {
+    uint32_t d;
+    uint32_t m;
+    uint32_t s;
+};
+
+inline Div32 make_div32(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return Div32{d, static_cast<uint32_t>(m), l};
+}
+
+UA2A_HD uint32_t fdiv(uint32_t n, Div32 f)
+{
+    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> 32);
+    return static_cast<uint32_t>((static_cast<uint64_t>(hi) + n) >> f.s);
+}
+
+UA2A_HD uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// ------------------------------------------------------------------------
+// Direct path: each lane moves whole VB-byte vectors of a run.  Units of
+// every stride/offset in DirectGeom are vectors of VB bytes.
+//
+// Work tile = up to rows_per_tile consecutive tokens s of one "slab"
+// (r, b, j): rows * vr vectors, contiguous on the A side; on the P side the
+// same rows sit p_row vectors apart.  Tiles are numbered
+//     t = ((r * nb + b) * w + j) * tiles_per_slab + tt
+// i.e. in A-side memory order.
+struct DirectGeom {
+    const uint8_t* src;        // mode 0: P side; mode 1: A side
+    uint8_t* dst;              // the other side
+    int64_t a_rank, a_plane;   // A-side strides
+    int64_t p_rank, p_plane;   // P-side strides
+    uint32_t p_row;            // w * vr: one token of all heads
+    uint32_t vr;               // vectors per run
+    uint32_t s_local;          // tokens per rank
+    uint32_t rows_per_tile;
+    uint32_t tiles_per_slab;   // ceil(s_local / rows_per_tile)
+    uint32_t num_tiles;        // w * nb * w * tiles_per_slab
+    uint32_t w, nb;            // ranks; planes covered by this launch
+    Div32 d_vr, d_tps, d_w, d_nb;
+};
+
+struct DirectTile {
+    int64_t a_base;   // A-side vector offset of the tile's first vector
+    int64_t p_base;   // P-side vector offset of the tile's first vector
+    uint32_t nvec;    // vectors in this tile (rows * vr; the last tile of a slab is short)
+};
+
+UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
+{
+    const uint32_t slab = fdiv(t, g.d_tps);
+    const uint32_t tt = t - slab * g.tiles_per_slab;
+    const uint32_t rb = fdiv(slab, g.d_w);
+    const uint32_t j = slab - rb * g.w;
+    const uint32_t r = fdiv(rb, g.d_nb);
+    const uint32_t b = rb - r * g.nb;
+    const uint32_t s0 = tt * g.rows_per_tile;
+    const uint32_t rows = umin32(g.rows_per_tile, g.s_local - s0);
+    DirectTile d;
+    d.a_base = static_cast<int64_t>(r) * g.a_rank + static_cast<int64_t>(b) * g.a_plane +
+               (static_cast<int64_t>(j) * g.s_local + s0) * g.vr;
+    d.p_base = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
+               static_cast<int64_t>(s0) * g.p_row + static_cast<int64_t>(r) * g.vr;
+    d.nvec = rows * g.vr;
+    return d;
+}
+
+// Offsets of the tile's delta-th vector (delta < nvec) on both sides.
+UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t delta,
+                           int64_t& a_off, int64_t& p_off)
+{
+    const uint32_t q = fdiv(delta, g.d_vr);       // row within the tile
+    const uint32_t o = delta - q * g.vr;          // vector within the run
+    a_off = d.a_base + delta;
+    p_off = d.p_base + static_cast<int64_t>(static_cast<uint64_t>(q) * g.p_row) + o;
+}
+
+// ------------------------------------------------------------------------
+// LDS path: a workgroup stages rows [s0, s0 + rows) of one (j, b) -- a
+// contiguous span of rows * w * run bytes on the P side -- in LDS, laid out
+// exactly as on the P side but shifted by `head` = the span's address mod 16
+// so that 16-byte global chunks map to 16-byte aligned LDS slots.  The w
+// A-side spans of the tile (one per head block r, rows * run bytes each) are
+// then moved in G-byte pieces, G = the alignment shared by run and both
+// base pointers.  All units here are bytes.
+//     t = (j * nb + b) * tiles_per_plane + tt      (P-side memory order)
+struct LdsGeom {
+    uint8_t* p_ptr;            // base of the P-side tensor (read in mode 0, written in mode 1)
+    uint8_t* a_ptr;            // base of the A-side tensor (written in mode 0, read in mode 1)
+    int64_t a_rank, a_plane;
+    int64_t p_rank, p_plane;
+    uint32_t run;              // bytes per run
+    uint32_t row;              // w * run
+    uint32_t s_local;
+    uint32_t rows_per_tile;
+    uint32_t tiles_per_plane;  // ceil(s_local / rows_per_tile)
+    uint32_t num_tiles;        // w * nb * tiles_per_plane
+    uint32_t w, nb;
+    uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * row)
+    Div32 d_tpp, d_nb, d_run;
+};
+
+struct LdsTile {
+    int64_t p_start;   // byte offset of the P span (from p_ptr)
+    int64_t a_start0;  // byte offset of the A span of head block r = 0 (from a_ptr)
+    uint32_t p_len;    // rows * row
+    uint32_t a_len;    // rows * run (each of the w A spans)
+    uint32_t head;     // (p_ptr + p_start) mod 16: LDS position of the span's first byte
+};
+
+UA2A_HD LdsTile lds_tile(const LdsGeom& g, uint32_t t)
+{
+    const uint32_t jb = fdiv(t, g.d_tpp);
+    const uint32_t tt = t - jb * g.tiles_per_plane;
+    const uint32_t j = fdiv(jb, g.d_nb);
+    const uint32_t b = jb - j * g.nb;
+    const uint32_t s0 = tt * g.rows_per_tile;
+    const uint32_t rows = umin32(g.rows_per_tile, g.s_local - s0);
+    LdsTile d;
+    d.p_start = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
+                static_cast<int64_t>(s0) * g.row;
+    d.a_start0 = static_cast<int64_t>(b) * g.a_plane +
+                 (static_cast<int64_t>(j) * g.s_local + s0) * g.run;
+    d.p_len = rows * g.row;
+    d.a_len = rows * g.run;
+    d.head = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g.p_ptr + d.p_start) & 15u);
+    return d;
+}
+
+// LDS byte position of byte p (0 <= p < a_len) of head block r's A span.
+UA2A_HD uint32_t lds_pos_of_a(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t p)
+{
+    const uint32_t k = fdiv(p, g.d_run);          // row within the tile
+    const uint32_t off = p - k * g.run;           // byte within the run
+    return d.head + k * g.row + r * g.run + off;
+}
+
+// Byte-sized pieces the LDS path moves between LDS and the A side.
+typedef uint32_t u32x4 __attribute__((vector_size(16)));
+
+template <int N> struct Piece;
+template <> struct Piece<16> { typedef u32x4 T; };
+template <> struct Piece<8> { typedef uint64_t T; };
+template <> struct Piece<4> { typedef uint32_t T; };
+template <> struct Piece<2> { typedef uint16_t T; };
+template <> struct Piece<1> { typedef uint8_t T; };
+
+UA2A_HD uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// A 16-byte chunk at byte `lo` of a span that starts `head` bytes into its
+// 16-aligned first chunk and is `len` bytes long lies wholly in the span.
+UA2A_HD bool chunk_full(uint32_t lo, uint32_t head, uint32_t len)
+{
+    return lo >= head && lo + 16 <= head + len;
+}
+
+// Chunks (16-byte, aligned) that a span touches.
+UA2A_HD uint32_t span_chunks(uint32_t head, uint32_t len) { return (head + len + 15) >> 4; }
+
+// Copy the in-span G-byte pieces of a partial chunk between two buffers
+// that share the span's alignment (global P span <-> its LDS image, both
+// indexed from the 16-aligned chunk base).
+template <int G>
+UA2A_HD void copy_partial_chunk(const uint8_t* from, uint8_t* to, uint32_t lo, uint32_t head,
+                                uint32_t len)
+{
+    typedef typename Piece<G>::T T;
+    const uint32_t x1 = umin32(lo + 16, head + len);
+    for (uint32_t x = umax32(lo, head); x < x1; x += G)
+        *reinterpret_cast<T*>(to + x) = *reinterpret_cast<const T*>(from + x);
+}
+
+// Gather the 16 bytes of a full A-span chunk of head block r from LDS;
+// p0 = byte position of the chunk's first byte in the A span.  Positions
+// advance by G and wrap into the next row at the end of each run.
+template <int G>
+UA2A_HD u32x4 gather_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t p0,
+                             const uint8_t* lds)
+{
+    typedef typename Piece<G>::T T;
+    union {
+        u32x4 v;
+        T p[16 / G];
+    } buf;
+    uint32_t k = fdiv(p0, g.d_run);
+    uint32_t off = p0 - k * g.run;
+    uint32_t pos = d.head + k * g.row + r * g.run + off;
+#pragma unroll
+    for (int i = 0; i < 16 / G; ++i) {
+        buf.p[i] = *reinterpret_cast<const T*>(lds + pos);
+        off += G;
+        pos += G;
+        if (off == g.run) {          // next row of the tile, same head block
+            off = 0;
+            pos += g.row - g.run;
+        }
+    }
+    return buf.v;
+}
+
+// Scatter the 16 bytes of a full A-span chunk of head block r into LDS.
+template <int G>
+UA2A_HD void scatter_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t p0,
+                             u32x4 v, uint8_t* lds)
+{
+    typedef typename Piece<G>::T T;
+    union {
+        u32x4 v;
+        T p[16 / G];
+    } buf;
+    buf.v = v;
+    uint32_t k = fdiv(p0, g.d_run);
+    uint32_t off = p0 - k * g.run;
+    uint32_t pos = d.head + k * g.row + r * g.run + off;
+#pragma unroll
+    for (int i = 0; i < 16 / G; ++i) {
+        *reinterpret_cast<T*>(lds + pos) = buf.p[i];
+        off += G;
+        pos += G;
+        if (off == g.run) {
+            off = 0;
+            pos += g.row - g.run;
+        }
+    }
+}
+
+// Partial A-span chunk (the first or last of a span): move its in-span
+// G-byte pieces one by one.  achunk0 = the span's 16-aligned first chunk
+// in global memory, ahead = the span's offset inside it.
+template <int G>
+UA2A_HD void a_partial_from_lds(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t lo,
+                                uint32_t ahead, const uint8_t* lds, uint8_t* achunk0)
+{
+    typedef typename Piece<G>::T T;
+    const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
+    for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
+        *reinterpret_cast<T*>(achunk0 + x) =
+            *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead));
+}
+
+template <int G>
+UA2A_HD void a_partial_to_lds(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t lo,
+                              uint32_t ahead, const uint8_t* achunk0, uint8_t* lds)
+{
+    typedef typename Piece<G>::T T;
+    const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
+    for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
+        *reinterpret_cast<T*>(lds + lds_pos_of_a(g, d, r, x - ahead)) =
+            *reinterpret_cast<const T*>(achunk0 + x);
+}
+
+// ------------------------------------------------------------------------
+// Plain strided block copy (window <-> one plane of every rank in the
+// chunked exchange): `count` blocks of span vectors, block k at
+// src + k*src_stride -> dst + k*dst_stride.  Units: VB-byte vectors.
+struct CopyGeom {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t src_stride, dst_stride;
+    int64_t span;              // vectors per block
+    uint32_t tile_vecs;
+    uint32_t tiles_per_span;   // ceil(span / tile_vecs)
+    uint32_t num_tiles;        // count * tiles_per_span
+    Div32 d_tps;
+};
+
+struct CopyTile {
+    int64_t src_base, dst_base;
+    uint32_t nvec;
+};
+
+UA2A_HD CopyTile copy_tile(const CopyGeom& g, uint32_t t)
+{
+    const uint32_t k = fdiv(t, g.d_tps);
+    const uint32_t tt = t - k * g.tiles_per_span;
+    const int64_t first = static_cast<int64_t>(tt) * g.tile_vecs;
+    const int64_t left = g.span - first;
+    CopyTile c;
+    c.src_base = static_cast<int64_t>(k) * g.src_stride + first;
+    c.dst_base = static_cast<int64_t>(k) * g.dst_stride + first;
+    c.nvec = left < static_cast<int64_t>(g.tile_vecs) ? static_cast<uint32_t>(left) : g.tile_vecs;
+    return c;
+}
+
+}  // namespace ua2a

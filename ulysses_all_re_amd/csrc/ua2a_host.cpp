@@ -1,0 +1,447 @@
+// Host side of the ua2a C ABI: shape validation, plans, per-call argument
+// checks, kernel-path choice and launch geometry.  It calls the device only
+// through the backend hooks of ua2a_internal.h.
+//
+// Semantics follow the FastVideo "ulysses_a2a" API page, method run_armed
+// (shapes of mode 0 / mode 1, per-plane chunked loop, one window sized for a
+// plane); the argument checks follow the launch-validation practice of the
+// b12x PCIe two-shot collectives page (validate every input and caller-owned
+// output before launching; reject overlapping storage by byte range, not by
+// pointer equality).
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ua2a_internal.h"
+
+using namespace ua2a;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxRowBytes = int64_t(1) << 31;      // H * D * elem_bytes
+constexpr int64_t kMaxRuns = (int64_t(1) << 32) - 1;     // w * w * B * S_local
+constexpr int64_t kMaxTensorBytes = int64_t(1) << 44;    // 16 TiB
+
+// Largest power of two <= 16 that divides x (16 for x == 0).
+uint32_t pow2_align(uint64_t x)
+{
+    uint32_t a = 16;
+    while (a > 1 && (x % a) != 0) a >>= 1;
+    return a;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && pa < pb + static_cast<uintptr_t>(nb) &&
+           pb < pa + static_cast<uintptr_t>(na);
+}
+
+// Multiply with an overflow check against `limit` (all operands >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out)
+{
+    if (a != 0 && b > limit / a) return false;
+    *out = a * b;
+    return *out <= limit;
+}
+
+uint32_t grid_for(uint32_t tiles, int32_t hint, int32_t cus, uint32_t per_cu)
+{
+    uint64_t g = hint > 0 ? static_cast<uint64_t>(hint)
+                          : static_cast<uint64_t>(cus > 0 ? cus : kAssumedCus) * per_cu;
+    if (g > tiles) g = tiles;
+    if (g < 1) g = 1;
+    return static_cast<uint32_t>(g);
+}
+
+// Everything one exchange launches.  For a chunked exchange, perm and copy
+// describe plane 0; plane p adds p * plane_bytes to the pointers named below.
+struct Prepared {
+    int32_t path;            // UA2A_PATH_DIRECT or UA2A_PATH_LDS
+    int32_t chunked;
+    Launch perm;
+    Launch copy;
+    int64_t plane_bytes;     // S_local * H * D * elem_bytes
+    int32_t launches;
+};
+
+DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_t* a_ptr,
+                       int mode, int64_t p_rank, int64_t p_plane, int64_t a_rank,
+                       int64_t a_plane, uint32_t nb)
+{
+    DirectGeom g;
+    memset(&g, 0, sizeof g);
+    const int64_t run = p->layout.run_bytes;
+    g.src = mode == 0 ? p_ptr : a_ptr;
+    g.dst = mode == 0 ? a_ptr : p_ptr;
+    g.a_rank = a_rank / vb;
+    g.a_plane = a_plane / vb;
+    g.p_rank = p_rank / vb;
+    g.p_plane = p_plane / vb;
+    g.vr = static_cast<uint32_t>(run / vb);
+    g.p_row = static_cast<uint32_t>(p->w) * g.vr;
+    g.s_local = static_cast<uint32_t>(p->S_local);
+    uint32_t rows = g.vr >= kDirectTileVectors ? 1u : kDirectTileVectors / g.vr;
+    if (rows > g.s_local) rows = g.s_local;
+    g.rows_per_tile = rows;
+    g.tiles_per_slab = (g.s_local + rows - 1) / rows;
+    g.w = static_cast<uint32_t>(p->w);
+    g.nb = nb;
+    g.num_tiles = g.w * g.w * nb * g.tiles_per_slab;   // bounded by the run limit
+    g.d_vr = make_div32(g.vr);
+    g.d_tps = make_div32(g.tiles_per_slab);
+    g.d_w = make_div32(g.w);
+    g.d_nb = make_div32(nb);
+    return g;
+}
+
+// Rows of one (j, b) that fit the LDS tile, 0 if not even one does.
+uint32_t lds_rows(const ua2a_plan_s* p)
+{
+    const int64_t row = p->layout.run_bytes * p->w;
+    if (row + 16 > kLdsTileBytes) return 0;
+    int64_t rows = (kLdsTileBytes - 16) / row;
+    if (rows > p->S_local) rows = p->S_local;
+    return static_cast<uint32_t>(rows);
+}
+
+LdsGeom make_lds(const ua2a_plan_s* p, uint8_t* p_ptr, uint8_t* a_ptr, int64_t p_rank,
+                 int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
+{
+    LdsGeom g;
+    memset(&g, 0, sizeof g);
+    g.p_ptr = p_ptr;
+    g.a_ptr = a_ptr;
+    g.a_rank = a_rank;
+    g.a_plane = a_plane;
+    g.p_rank = p_rank;
+    g.p_plane = p_plane;
+    g.run = static_cast<uint32_t>(p->layout.run_bytes);
+    g.row = g.run * static_cast<uint32_t>(p->w);
+    g.s_local = static_cast<uint32_t>(p->S_local);
+    g.rows_per_tile = lds_rows(p);
+    g.tiles_per_plane = (g.s_local + g.rows_per_tile - 1) / g.rows_per_tile;
+    g.w = static_cast<uint32_t>(p->w);
+    g.nb = nb;
+    g.num_tiles = g.w * nb * g.tiles_per_plane;
+    g.lds_bytes = (16 + g.rows_per_tile * g.row + 15) & ~15u;
+    g.d_tpp = make_div32(g.tiles_per_plane);
+    g.d_nb = make_div32(nb);
+    g.d_run = make_div32(g.run);
+    return g;
+}
+
+CopyGeom make_copy(uint32_t vb, const uint8_t* src, uint8_t* dst, int64_t src_stride,
+                   int64_t dst_stride, int64_t span_bytes, uint32_t count)
+{
+    CopyGeom g;
+    memset(&g, 0, sizeof g);
+    g.src = src;
+    g.dst = dst;
+    g.src_stride = src_stride / vb;
+    g.dst_stride = dst_stride / vb;
+    g.span = span_bytes / vb;
+    g.tile_vecs = kCopyTileVectors;
+    g.tiles_per_span = static_cast<uint32_t>((g.span + g.tile_vecs - 1) / g.tile_vecs);
+    g.num_tiles = count * g.tiles_per_span;
+    g.d_tps = make_div32(g.tiles_per_span);
+    return g;
+}
+
+int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in,
+               const void* out)
+{
+    if (p == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (p->disabled) return UA2A_ERR_DISABLED;
+    if ((mode != 0 && mode != 1) || (chunked != 0 && chunked != 1)) return UA2A_ERR_INVALID_ARG;
+    if (in == nullptr || out == nullptr) return UA2A_ERR_INVALID_ARG;
+    const uintptr_t e = static_cast<uintptr_t>(p->elem_bytes);
+    if (reinterpret_cast<uintptr_t>(in) % e || reinterpret_cast<uintptr_t>(out) % e)
+        return UA2A_ERR_ALIGN;
+    const int64_t n = p->layout.tensor_bytes;
+    if (overlaps(in, n, out, n)) return UA2A_ERR_ALIAS;
+    if (chunked) {
+        if (p->window == nullptr || p->window_bytes < p->layout.window_bytes)
+            return UA2A_ERR_CAPACITY;
+        const int64_t wn = p->layout.window_bytes;
+        if (overlaps(p->window, wn, in, n) || overlaps(p->window, wn, out, n))
+            return UA2A_ERR_ALIAS;
+    }
+    return UA2A_OK;
+}
+
+void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in, void* out,
+             int32_t cus, Prepared* pr)
+{
+    memset(pr, 0, sizeof *pr);
+    const int64_t run = p->layout.run_bytes;
+    const int64_t plane = p->S_local * p->H * p->D * p->elem_bytes;   // one plane of one rank
+    const int64_t rank_bytes = plane * p->B;
+    uint8_t* inb = const_cast<uint8_t*>(static_cast<const uint8_t*>(in));
+    uint8_t* outb = static_cast<uint8_t*>(out);
+
+    uint32_t g = pow2_align(static_cast<uint64_t>(run));
+    g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(in)));
+    g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(out)));
+    if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
+
+    const uint32_t rows = lds_rows(p);
+    int32_t path;
+    if (p->path == UA2A_PATH_DIRECT)
+        path = UA2A_PATH_DIRECT;
+    else if (p->path == UA2A_PATH_LDS)
+        path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
+    else if (g == 16 && run >= kDirectMinRun)
+        path = UA2A_PATH_DIRECT;
+    else
+        path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
+
+    // Which tensor is the P side ([j][b][s][H][D]) and which the A side
+    // ([r][b][S_global][H/w][D]); strides in bytes.
+    uint8_t *p_ptr, *a_ptr;
+    int64_t p_rank, p_plane, a_rank, a_plane;
+    uint32_t nb;
+    if (!chunked) {
+        p_ptr = mode == 0 ? inb : outb;
+        a_ptr = mode == 0 ? outb : inb;
+        p_rank = a_rank = rank_bytes;
+        p_plane = a_plane = plane;
+        nb = static_cast<uint32_t>(p->B);
+    } else {
+        // plane 0 of every rank <-> the window ([w][one plane] in the layout
+        // of the exchange's output side)
+        nb = 1;
+        if (mode == 0) {
+            p_ptr = inb;       p_rank = rank_bytes;
+            a_ptr = p->window; a_rank = plane;
+        } else {
+            a_ptr = inb;       a_rank = rank_bytes;
+            p_ptr = p->window; p_rank = plane;
+        }
+        p_plane = a_plane = 0;
+    }
+
+    pr->path = path;
+    pr->chunked = chunked;
+    pr->plane_bytes = plane;
+    Launch& L = pr->perm;
+    L.mode = mode;
+    if (path == UA2A_PATH_DIRECT) {
+        L.kernel = Kernel::Direct;
+        L.width = static_cast<int32_t>(g);
+        L.direct = make_direct(p, g, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb);
+        L.grid = grid_for(L.direct.num_tiles, p->blocks, cus, kDirectBlocksPerCu);
+    } else {
+        L.kernel = Kernel::Lds;
+        L.width = static_cast<int32_t>(g);
+        L.lds = make_lds(p, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
+        L.lds_bytes = L.lds.lds_bytes;
+        L.grid = grid_for(L.lds.num_tiles, p->blocks, cus, kLdsBlocksPerCu);
+    }
+    pr->launches = 1;
+    if (chunked) {
+        // window -> plane 0 of every rank of `out`: w blocks of one plane
+        uint32_t vb = pow2_align(static_cast<uint64_t>(plane));
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out)));
+        Launch& C = pr->copy;
+        C.kernel = Kernel::Copy;
+        C.width = static_cast<int32_t>(vb);
+        C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
+                           static_cast<uint32_t>(p->w));
+        C.grid = grid_for(C.copy.num_tiles, 0, cus, kCopyBlocksPerCu);
+        pr->launches = static_cast<int32_t>(2 * p->B);
+    }
+}
+
+// Shift plane-0 launches of a chunked exchange to plane `pl`.
+void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch* copy)
+{
+    *perm = pr.perm;
+    *copy = pr.copy;
+    const int64_t off = pl * pr.plane_bytes;
+    // the input side walks the planes; the window side stays put
+    if (perm->kernel == Kernel::Direct)
+        perm->direct.src += off;
+    else if (mode == 0)
+        perm->lds.p_ptr += off;
+    else
+        perm->lds.a_ptr += off;
+    copy->copy.dst += off;
+}
+
+void disable(ua2a_plan_s* p, const char* what, int err)
+{
+    p->disabled = 1;
+    snprintf(p->reason, sizeof p->reason, "%s failed: %s (%d)", what, backend_error_name(err), err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ua2a_layout(int32_t w, int64_t B, int64_t S_local, int64_t H, int64_t D,
+                int32_t elem_bytes, ua2a_layout_t* layout)
+{
+    if (layout == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+        return UA2A_ERR_INVALID_ARG;
+    if (w < 1 || w > 65536 || B < 1 || S_local < 1 || H < 1 || D < 1) return UA2A_ERR_SHAPE;
+    if (B > kMaxDim || S_local > kMaxDim || H > kMaxDim || D > kMaxDim) return UA2A_ERR_SHAPE;
+    if (H % w != 0) return UA2A_ERR_SHAPE;
+    int64_t row, runs, elems, bytes, t;
+    if (!mul_ok(H, D, kMaxRowBytes, &t) || !mul_ok(t, elem_bytes, kMaxRowBytes, &row))
+        return UA2A_ERR_SHAPE;
+    if (!mul_ok(int64_t(w) * w, B, kMaxRuns, &t) || !mul_ok(t, S_local, kMaxRuns, &runs))
+        return UA2A_ERR_SHAPE;
+    if (!mul_ok(runs / w, row / elem_bytes, kMaxTensorBytes, &elems) ||
+        !mul_ok(elems, elem_bytes, kMaxTensorBytes, &bytes))
+        return UA2A_ERR_SHAPE;
+    layout->H_local = H / w;
+    layout->S_global = S_local * w;
+    layout->run_bytes = (H / w) * D * elem_bytes;
+    layout->tensor_elems = elems;
+    layout->tensor_bytes = bytes;
+    layout->window_bytes = int64_t(w) * S_local * row;
+    layout->moved_bytes = 2 * bytes;
+    return UA2A_OK;
+}
+
+int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local, int64_t H,
+              int64_t D, int32_t elem_bytes, int32_t blocks, void* window,
+              int64_t window_bytes, int32_t device)
+{
+    if (plan_out == nullptr) return UA2A_ERR_INVALID_ARG;
+    *plan_out = nullptr;
+    ua2a_layout_t lay;
+    const int rc = ua2a_layout(w, B, S_local, H, D, elem_bytes, &lay);
+    if (rc != UA2A_OK) return rc;
+    if (device < 0 || blocks < 0 || window_bytes < 0) return UA2A_ERR_INVALID_ARG;
+    if (window == nullptr && window_bytes > 0) return UA2A_ERR_INVALID_ARG;
+    if (window != nullptr && reinterpret_cast<uintptr_t>(window) % elem_bytes)
+        return UA2A_ERR_ALIGN;
+    ua2a_plan_s* p = static_cast<ua2a_plan_s*>(calloc(1, sizeof(ua2a_plan_s)));
+    if (p == nullptr) return UA2A_ERR_NOMEM;
+    p->w = w;
+    p->B = B;
+    p->S_local = S_local;
+    p->H = H;
+    p->D = D;
+    p->elem_bytes = elem_bytes;
+    p->layout = lay;
+    p->blocks = blocks;
+    p->window = static_cast<uint8_t*>(window);
+    p->window_bytes = window == nullptr ? 0 : window_bytes;
+    p->device = device;
+    p->path = UA2A_PATH_AUTO;
+    *plan_out = p;
+    return UA2A_OK;
+}
+
+int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* in, void* out,
+                  void* stream)
+{
+    int rc = check_call(plan, mode, chunked, in, out);
+    if (rc != UA2A_OK) return rc;
+    int32_t dev = -1;
+    int err = backend_current_device(&dev);
+    if (err != 0) {
+        disable(plan, "querying the current device", err);
+        return UA2A_ERR_HIP;
+    }
+    if (dev != plan->device) return UA2A_ERR_DEVICE;
+    if (plan->cus == 0) {
+        int32_t cus = 0;
+        err = backend_cu_count(plan->device, &cus);
+        if (err != 0) {
+            disable(plan, "querying the compute-unit count", err);
+            return UA2A_ERR_HIP;
+        }
+        plan->cus = cus > 0 ? cus : kAssumedCus;
+    }
+    Prepared pr;
+    prepare(plan, mode, chunked, in, out, plan->cus, &pr);
+    if (!chunked) {
+        err = backend_launch(pr.perm, stream);
+        if (err != 0) {
+            disable(plan, "launching the exchange kernel", err);
+            return UA2A_ERR_HIP;
+        }
+        return UA2A_OK;
+    }
+    // Chunked: per plane, permute into the window, then copy the window out.
+    // Stream order makes plane p's copy finish before plane p+1 overwrites
+    // the window.
+    for (int64_t pl = 0; pl < plan->B; ++pl) {
+        Launch perm, copy;
+        to_plane(pr, mode, pl, &perm, &copy);
+        err = backend_launch(perm, stream);
+        if (err == 0) err = backend_launch(copy, stream);
+        if (err != 0) {
+            disable(plan, "launching a chunked-plane kernel", err);
+            return UA2A_ERR_HIP;
+        }
+    }
+    return UA2A_OK;
+}
+
+int ua2a_destroy(ua2a_plan_t plan)
+{
+    free(plan);
+    return UA2A_OK;
+}
+
+const char* ua2a_status_string(int32_t status)
+{
+    switch (status) {
+    case UA2A_OK: return "ok";
+    case UA2A_ERR_INVALID_ARG: return "invalid argument";
+    case UA2A_ERR_SHAPE: return "unsupported shape (dimension < 1, H not divisible by w, or beyond the size limits)";
+    case UA2A_ERR_ALIGN: return "pointer not aligned to the element size";
+    case UA2A_ERR_ALIAS: return "input, output and window byte ranges overlap";
+    case UA2A_ERR_CAPACITY: return "chunked exchange needs a window of at least one batch plane of every rank";
+    case UA2A_ERR_DEVICE: return "current device is not the plan's device";
+    case UA2A_ERR_HIP: return "HIP runtime or launch failure; the plan is disabled";
+    case UA2A_ERR_DISABLED: return "plan disabled by an earlier HIP failure";
+    case UA2A_ERR_NOMEM: return "out of host memory";
+    default: return "unknown status";
+    }
+}
+
+const char* ua2a_plan_last_error(ua2a_plan_t plan)
+{
+    if (plan == nullptr || !plan->disabled) return "";
+    return plan->reason;
+}
+
+int ua2a_plan_set_path(ua2a_plan_t plan, int32_t path)
+{
+    if (plan == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (path != UA2A_PATH_AUTO && path != UA2A_PATH_DIRECT && path != UA2A_PATH_LDS)
+        return UA2A_ERR_INVALID_ARG;
+    plan->path = path;
+    return UA2A_OK;
+}
+
+int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* in,
+                  const void* out, ua2a_launch_info_t* info)
+{
+    if (info == nullptr) return UA2A_ERR_INVALID_ARG;
+    const int rc = check_call(plan, mode, chunked, in, out);
+    if (rc != UA2A_OK) return rc;
+    Prepared pr;
+    prepare(plan, mode, chunked, in, const_cast<void*>(out), plan->cus, &pr);
+    memset(info, 0, sizeof *info);
+    info->path = pr.path;
+    info->vector_bytes = pr.perm.width;
+    info->grid = static_cast<int32_t>(pr.perm.grid);
+    info->block = kBlock;
+    info->tiles = pr.perm.kernel == Kernel::Direct ? pr.perm.direct.num_tiles : pr.perm.lds.num_tiles;
+    info->launches = pr.launches;
+    info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
+    return UA2A_OK;
+}
+
+}  // extern "C"

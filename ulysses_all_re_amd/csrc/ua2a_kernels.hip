@@ -1,0 +1,150 @@
+// gfx950 (MI355X, CDNA4) kernels of the Ulysses all_to_all_4D exchange and
+// the HIP backend that launches them.
+//
+// The exchange is pure data movement (FastVideo "ulysses_a2a" API page,
+// method run_armed: mode 0 [B,S_local,H,D] -> [B,S_local*w,H/w,D] per rank,
+// mode 1 the inverse), so it is bound by HBM bandwidth: no MFMA, every byte
+// read once and written once.  Three kernels:
+//
+//  * ua2a_direct_kernel  -- each lane moves whole vectors (16 bytes when the
+//    run and both bases allow) of a run; consecutive lanes touch consecutive
+//    vectors of a tile, so one side is fully contiguous per wave and the
+//    other is contiguous for a whole run.  Each lane keeps kDirectUnroll
+//    vectors in flight (loads first, then stores).  Used for runs of at
+//    least a few cache lines.
+//  * ua2a_lds_kernel     -- for short or unaligned runs: a workgroup stages
+//    a contiguous span of P-side rows in LDS and moves both sides as 16-byte
+//    aligned chunks, re-ordering runs inside LDS in G-byte pieces.
+//  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
+//    to move the one-plane window into the output.
+//
+// The per-thread bodies (ua2a_bodies.h) and their index math
+// (ua2a_geometry.h) are shared with a host emulation used by the tests.
+#include <hip/hip_runtime.h>
+
+#include "ua2a_bodies.h"
+#include "ua2a_internal.h"
+
+namespace ua2a {
+
+template <int VB, bool MODE1>
+__global__ __launch_bounds__(kBlock) void ua2a_direct_kernel(DirectGeom g)
+{
+    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
+        direct_tile_body<VB, MODE1, kDirectUnroll>(g, t, threadIdx.x);
+}
+
+template <int G, bool MODE1>
+__global__ __launch_bounds__(kBlock) void ua2a_lds_kernel(LdsGeom g)
+{
+    extern __shared__ u32x4 ua2a_lds_raw[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
+    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
+        const LdsTile d = lds_tile(g, t);
+        lds_fill<G, MODE1, kLdsUnroll>(g, d, threadIdx.x, lds);
+        __syncthreads();
+        lds_drain<G, MODE1>(g, d, threadIdx.x, lds);
+        __syncthreads();   // the next tile overwrites the LDS image
+    }
+}
+
+template <int VB>
+__global__ __launch_bounds__(kBlock) void ua2a_copy_kernel(CopyGeom g)
+{
+    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
+        copy_tile_body<VB, kDirectUnroll>(g, t, threadIdx.x);
+}
+
+namespace {
+
+template <bool MODE1>
+const void* direct_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_direct_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_direct_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_direct_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_direct_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_direct_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
+template <bool MODE1>
+const void* lds_fn(int g)
+{
+    switch (g) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_lds_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_lds_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_lds_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_lds_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_lds_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
+const void* copy_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_copy_kernel<16>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_copy_kernel<8>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_copy_kernel<4>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_copy_kernel<2>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_copy_kernel<1>);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+int backend_current_device(int32_t* device)
+{
+    int d = -1;
+    const hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess) return static_cast<int>(e);
+    *device = d;
+    return 0;
+}
+
+int backend_cu_count(int32_t device, int32_t* cus)
+{
+    int v = 0;
+    const hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return static_cast<int>(e);
+    *cus = v;
+    return 0;
+}
+
+const char* backend_error_name(int err) { return hipGetErrorName(static_cast<hipError_t>(err)); }
+
+int backend_launch(const Launch& L, void* stream)
+{
+    const void* fn = nullptr;
+    void* arg = nullptr;
+    DirectGeom dg = L.direct;
+    LdsGeom lg = L.lds;
+    CopyGeom cg = L.copy;
+    size_t shmem = 0;
+    switch (L.kernel) {
+    case Kernel::Direct:
+        fn = L.mode ? direct_fn<true>(L.width) : direct_fn<false>(L.width);
+        arg = &dg;
+        break;
+    case Kernel::Lds:
+        fn = L.mode ? lds_fn<true>(L.width) : lds_fn<false>(L.width);
+        arg = &lg;
+        shmem = L.lds_bytes;
+        break;
+    case Kernel::Copy:
+        fn = copy_fn(L.width);
+        arg = &cg;
+        break;
+    }
+    if (fn == nullptr) return static_cast<int>(hipErrorInvalidValue);
+    void* args[] = {arg};
+    const hipError_t e = hipLaunchKernel(fn, dim3(L.grid), dim3(kBlock), args, shmem,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? 0 : static_cast<int>(e);
+}
+
+}  // namespace ua2a
