@@ -50,8 +50,10 @@ extern "C" {
 #define UA2A_ERR_DISABLED     (-8) /* the plan was disabled by an earlier UA2A_ERR_HIP */
 #define UA2A_ERR_NOMEM        (-9) /* host allocation of the plan object failed */
 
-/* Limits: w <= 65536; every one of B, S_local, H, D <= 2^31 - 1; one
- * rank-stacked tensor <= 2^47 bytes (128 TiB). */
+/* Limits (UA2A_ERR_SHAPE beyond them): w <= 65536; each of B, S_local, H,
+ * D <= 2^31 - 1; one token of all heads (H*D*elem_bytes) <= 2^31 bytes; one
+ * batch plane of one rank (S_local*H*D*elem_bytes) < 2^32 bytes;
+ * w*w*B*S_local < 2^32; one rank-stacked tensor <= 2^38 bytes (256 GiB). */
 
 typedef struct ua2a_plan_s* ua2a_plan_t;
 
@@ -99,9 +101,11 @@ int ua2a_layout(int32_t w, int64_t B, int64_t S_local, int64_t H, int64_t D,
 /*
  * ua2a_plan: create a plan for one shape on one device.  Host only: it makes
  * no HIP call and allocates only the small host-side plan object.
- *   blocks      grid-size hint for the permutation kernel (the page passes
- *               `blocks` to the native op); 0 = choose from the device's
- *               compute-unit count.  The result never depends on it.
+ *   blocks      grid-size cap for the permutation kernel (the page passes
+ *               `blocks` to the native op); 0 = one workgroup per work tile
+ *               (the fastest shape on MI355X).  With a smaller cap each
+ *               workgroup loops over several tiles.  The result never
+ *               depends on it.
  *   window, window_bytes  caller-owned device buffer used by chunked calls
  *               as the one-plane receive window of all w ranks; it may be
  *               NULL/0 if chunked is never requested.  The plan borrows it:

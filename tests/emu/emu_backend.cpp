@@ -27,8 +27,8 @@ template <int VB, bool M1>
 void run_direct(const DirectGeom& g)
 {
     for (uint32_t t = 0; t < g.num_tiles; ++t)
-        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
-            direct_tile_body<VB, M1, kDirectUnroll>(g, t, tid);
+        for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+            direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, t, tid);
 }
 
 template <int G, bool M1>
@@ -40,10 +40,10 @@ void run_lds(const LdsGeom& g)
     for (uint32_t t = 0; t < g.num_tiles; ++t) {
         memset(lds.data(), 0xA5, lds.size());
         const LdsTile d = lds_tile(g, t);
-        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
-            lds_fill<G, M1, kLdsUnroll>(g, d, tid, lds.data());
-        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
-            lds_drain<G, M1>(g, d, tid, lds.data());
+        for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+            lds_fill<PlainMem, G, M1, kLdsBlock, kLdsUnroll>(g, d, tid, lds.data());
+        for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+            lds_drain<PlainMem, G, M1, kLdsBlock>(g, d, tid, lds.data());
     }
 }
 
@@ -51,8 +51,8 @@ template <int VB>
 void run_copy(const CopyGeom& g)
 {
     for (uint32_t t = 0; t < g.num_tiles; ++t)
-        for (uint32_t tid = 0; tid < static_cast<uint32_t>(kBlock); ++tid)
-            copy_tile_body<VB, kDirectUnroll>(g, t, tid);
+        for (uint32_t tid = 0; tid < kCopyBlock; ++tid)
+            copy_tile_body<PlainMem, VB, kCopyBlock, kDirectUnroll>(g, t, tid);
 }
 
 template <bool M1>
@@ -100,12 +100,6 @@ int backend_current_device(int32_t* device)
     return 0;
 }
 
-int backend_cu_count(int32_t, int32_t* cus)
-{
-    *cus = 256;
-    return 0;
-}
-
 const char* backend_error_name(int) { return "emulated launch failure"; }
 
 int backend_launch(const Launch& L, void*)
@@ -119,6 +113,9 @@ int backend_launch(const Launch& L, void*)
     ++g_kernel_counts[static_cast<int>(L.kernel)];
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
+    const uint32_t want_block = L.kernel == Kernel::Direct ? kDirectBlock
+                              : L.kernel == Kernel::Lds ? kLdsBlock : kCopyBlock;
+    if (L.block != want_block) return 5;
     switch (L.kernel) {
     case Kernel::Direct:
         return L.mode ? dispatch_direct<true>(L.direct, L.width) : dispatch_direct<false>(L.direct, L.width);

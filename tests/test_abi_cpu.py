@@ -66,7 +66,8 @@ def test_host_only_calls(lib):
         base = 1 << 40
         info = ua.ua2a_describe(h, 0, 0, base, base + (1 << 30))
         assert info["path"] == ua.UA2A_PATH_DIRECT and info["vector_bytes"] == 16
-        assert info["block"] == 256 and info["launches"] == 1 and info["grid"] >= 1
+        assert info["block"] == 64 and info["launches"] == 1
+        assert info["grid"] == info["tiles"] == 8 * 8 * -(-9450 * 80 // 64)   # 1 KiB tiles per slab
         ua.ua2a_plan_set_path(h, ua.UA2A_PATH_LDS)
         assert ua.ua2a_describe(h, 1, 0, base, base + (1 << 30))["path"] == ua.UA2A_PATH_LDS
         with pytest.raises(ua.UA2AError) as e:

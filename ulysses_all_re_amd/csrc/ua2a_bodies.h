@@ -12,31 +12,40 @@
 
 namespace ua2a {
 
-// Direct path: lanes move whole VB-byte vectors; U vectors per lane are
-// loaded before any is stored so each lane keeps U requests in flight.
-template <int VB, bool MODE1, uint32_t U>
+// Global-memory access policy of the bodies.  The kernels use one that
+// marks accesses non-temporal (streamed once, not worth keeping in cache);
+// the host emulation uses PlainMem.
+struct PlainMem {
+    template <class T>
+    UA2A_HD static T ld(const T* p) { return *p; }
+    template <class T>
+    UA2A_HD static void st(T* p, T v) { *p = v; }
+};
+
+// Direct path: the BS lanes move whole VB-byte vectors of the tile; U
+// vectors per lane are loaded before any is stored.
+template <class Mem, int VB, bool MODE1, uint32_t BS, uint32_t U>
 UA2A_HD void direct_tile_body(const DirectGeom& g, uint32_t t, uint32_t tid)
 {
     typedef typename Piece<VB>::T T;
     const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
     T* __restrict__ dst = reinterpret_cast<T*>(g.dst);
-    const DirectTile d = direct_tile(g, t);
-    for (uint32_t base = tid; base < d.nvec; base += kBlock * U) {
+    const DirectTile d = direct_tile<MODE1>(g, t);
+    for (uint32_t base = tid; base < d.nvec; base += BS * U) {
         T v[U];
         int64_t to[U];
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k) {
-            const uint32_t delta = base + k * kBlock;
+            const uint32_t delta = base + k * BS;
             if (delta < d.nvec) {
-                int64_t a, p;
-                direct_vector(g, d, delta, a, p);
-                v[k] = src[MODE1 ? a : p];
-                to[k] = MODE1 ? p : a;
+                int64_t from;
+                direct_vector<MODE1>(g, d, d.u0 + delta, from, to[k]);
+                v[k] = Mem::ld(src + from);
             }
         }
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k)
-            if (base + k * kBlock < d.nvec) dst[to[k]] = v[k];
+            if (base + k * BS < d.nvec) Mem::st(dst + to[k], v[k]);
     }
 }
 
@@ -44,23 +53,23 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, uint32_t t, uint32_t tid)
 //   mode 0: the P span itself (contiguous 16-byte chunks);
 //   mode 1: the w A spans, each read as contiguous chunks and scattered
 //           into its runs' places in the image in G-byte pieces.
-template <int G, bool MODE1, uint32_t U>
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U>
 UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t* lds)
 {
     if (!MODE1) {
         const uint8_t* pchunk0 = g.p_ptr + d.p_start - d.head;   // 16-aligned
         const uint32_t pch = span_chunks(d.head, d.p_len);
-        for (uint32_t c0 = tid; c0 < pch; c0 += kBlock * U) {
+        for (uint32_t c0 = tid; c0 < pch; c0 += BS * U) {
             u32x4 v[U];
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t c = c0 + k * kBlock;
+                const uint32_t c = c0 + k * BS;
                 if (c < pch && chunk_full(c * 16, d.head, d.p_len))
-                    v[k] = *reinterpret_cast<const u32x4*>(pchunk0 + c * 16);
+                    v[k] = Mem::ld(reinterpret_cast<const u32x4*>(pchunk0 + c * 16));
             }
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t c = c0 + k * kBlock;
+                const uint32_t c = c0 + k * BS;
                 if (c >= pch) continue;
                 if (chunk_full(c * 16, d.head, d.p_len))
                     *reinterpret_cast<u32x4*>(lds + c * 16) = v[k];
@@ -74,17 +83,17 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
             const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
             const uint8_t* achunk0 = aspan - ahead;
             const uint32_t ach = span_chunks(ahead, d.a_len);
-            for (uint32_t c0 = tid; c0 < ach; c0 += kBlock * U) {
+            for (uint32_t c0 = tid; c0 < ach; c0 += BS * U) {
                 u32x4 v[U];
 #pragma unroll
                 for (uint32_t k = 0; k < U; ++k) {
-                    const uint32_t c = c0 + k * kBlock;
+                    const uint32_t c = c0 + k * BS;
                     if (c < ach && chunk_full(c * 16, ahead, d.a_len))
-                        v[k] = *reinterpret_cast<const u32x4*>(achunk0 + c * 16);
+                        v[k] = Mem::ld(reinterpret_cast<const u32x4*>(achunk0 + c * 16));
                 }
 #pragma unroll
                 for (uint32_t k = 0; k < U; ++k) {
-                    const uint32_t c = c0 + k * kBlock;
+                    const uint32_t c = c0 + k * BS;
                     if (c >= ach) continue;
                     if (chunk_full(c * 16, ahead, d.a_len))
                         scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k], lds);
@@ -100,7 +109,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
 //   mode 0: each of the w A spans, gathered from the image, written as
 //           contiguous 16-byte chunks;
 //   mode 1: the P span, copied out of the image as contiguous chunks.
-template <int G, bool MODE1>
+template <class Mem, int G, bool MODE1, uint32_t BS>
 UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const uint8_t* lds)
 {
     if (!MODE1) {
@@ -109,10 +118,10 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
             const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
             uint8_t* achunk0 = aspan - ahead;
             const uint32_t ach = span_chunks(ahead, d.a_len);
-            for (uint32_t c = tid; c < ach; c += kBlock) {
+            for (uint32_t c = tid; c < ach; c += BS) {
                 const uint32_t lo = c * 16;
                 if (chunk_full(lo, ahead, d.a_len))
-                    *reinterpret_cast<u32x4*>(achunk0 + lo) = gather_a_chunk<G>(g, d, r, lo - ahead, lds);
+                    Mem::st(reinterpret_cast<u32x4*>(achunk0 + lo), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
                 else
                     a_partial_from_lds<G>(g, d, r, lo, ahead, lds, achunk0);
             }
@@ -120,10 +129,10 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
     } else {
         uint8_t* pchunk0 = g.p_ptr + d.p_start - d.head;
         const uint32_t pch = span_chunks(d.head, d.p_len);
-        for (uint32_t c = tid; c < pch; c += kBlock) {
+        for (uint32_t c = tid; c < pch; c += BS) {
             const uint32_t lo = c * 16;
             if (chunk_full(lo, d.head, d.p_len))
-                *reinterpret_cast<u32x4*>(pchunk0 + lo) = *reinterpret_cast<const u32x4*>(lds + lo);
+                Mem::st(reinterpret_cast<u32x4*>(pchunk0 + lo), *reinterpret_cast<const u32x4*>(lds + lo));
             else
                 copy_partial_chunk<G>(lds, pchunk0, lo, d.head, d.p_len);
         }
@@ -131,21 +140,21 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
 }
 
 // Strided block copy (chunked exchange: window -> planes of the output).
-template <int VB, uint32_t U>
+template <class Mem, int VB, uint32_t BS, uint32_t U>
 UA2A_HD void copy_tile_body(const CopyGeom& g, uint32_t t, uint32_t tid)
 {
     typedef typename Piece<VB>::T T;
     const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
     T* __restrict__ dst = reinterpret_cast<T*>(g.dst);
     const CopyTile c = copy_tile(g, t);
-    for (uint32_t base = tid; base < c.nvec; base += kBlock * U) {
+    for (uint32_t base = tid; base < c.nvec; base += BS * U) {
         T v[U];
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k)
-            if (base + k * kBlock < c.nvec) v[k] = src[c.src_base + base + k * kBlock];
+            if (base + k * BS < c.nvec) v[k] = Mem::ld(src + c.src_base + base + k * BS);
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k)
-            if (base + k * kBlock < c.nvec) dst[c.dst_base + base + k * kBlock] = v[k];
+            if (base + k * BS < c.nvec) Mem::st(dst + c.dst_base + base + k * BS, v[k]);
     }
 }
 

@@ -27,7 +27,12 @@
 
 namespace ua2a {
 
-constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
+// Threads per workgroup.  Direct and copy kernels: one wave64 per
+// workgroup (measured fastest on MI355X for these streams); LDS kernel: four
+// waves sharing one LDS tile.
+constexpr uint32_t kDirectBlock = 64;
+constexpr uint32_t kCopyBlock = 64;
+constexpr uint32_t kLdsBlock = 256;
 
 // ------------------------------------------------------------------------
 // Division of a 32-bit unsigned n by an invariant d >= 1 via a multiply-high
@@ -59,62 +64,84 @@ UA2A_HD uint32_t fdiv(uint32_t n, Div32 f)
 UA2A_HD uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
 
 // ------------------------------------------------------------------------
-// Direct path: each lane moves whole VB-byte vectors of a run.  Units of
-// every stride/offset in DirectGeom are vectors of VB bytes.
-//
-// Work tile = up to rows_per_tile consecutive tokens s of one "slab"
-// (r, b, j): rows * vr vectors, contiguous on the A side; on the P side the
-// same rows sit p_row vectors apart.  Tiles are numbered
-//     t = ((r * nb + b) * w + j) * tiles_per_slab + tt
-// i.e. in A-side memory order.
+// Direct path: each lane moves whole VB-byte vectors.  The work is cut along
+// the side the exchange WRITES, so the stores of every workgroup form one
+// contiguous stretch (on MI355X the write stream is what limits a copy; the
+// reads then cover whole runs, each contiguous):
+//   mode 0 writes the A side, slab = (r, b, j): s_local * vr vectors
+//          contiguous; t = ((r * nb + b) * w + j) * tiles_per_slab + tt
+//   mode 1 writes the P side, slab = (j, b): s_local * p_row vectors
+//          contiguous; t = (j * nb + b) * tiles_per_slab + tt
+// A tile is tile_vecs consecutive vectors of one slab (the last tile of a
+// slab is short).  Units of every stride/offset: VB-byte vectors.
 struct DirectGeom {
     const uint8_t* src;        // mode 0: P side; mode 1: A side
     uint8_t* dst;              // the other side
     int64_t a_rank, a_plane;   // A-side strides
     int64_t p_rank, p_plane;   // P-side strides
-    uint32_t p_row;            // w * vr: one token of all heads
     uint32_t vr;               // vectors per run
+    uint32_t p_row;            // w * vr: one token of all heads
     uint32_t s_local;          // tokens per rank
-    uint32_t rows_per_tile;
-    uint32_t tiles_per_slab;   // ceil(s_local / rows_per_tile)
-    uint32_t num_tiles;        // w * nb * w * tiles_per_slab
     uint32_t w, nb;            // ranks; planes covered by this launch
-    Div32 d_vr, d_tps, d_w, d_nb;
+    uint32_t slab_vecs;        // vectors per slab (< 2^32, checked by the host)
+    uint32_t tile_vecs;
+    uint32_t tiles_per_slab;   // ceil(slab_vecs / tile_vecs)
+    uint32_t num_tiles;        // slabs * tiles_per_slab
+    Div32 d_vr, d_prow, d_tps, d_w, d_nb;
 };
 
 struct DirectTile {
-    int64_t a_base;   // A-side vector offset of the tile's first vector
-    int64_t p_base;   // P-side vector offset of the tile's first vector
-    uint32_t nvec;    // vectors in this tile (rows * vr; the last tile of a slab is short)
+    int64_t dst_slab;   // write-side offset of the slab's first vector
+    int64_t src_slab;   // read-side offset that the per-vector terms are added to
+    uint32_t u0;        // first vector of the tile within its slab
+    uint32_t nvec;      // vectors in this tile
 };
 
+template <bool MODE1>
 UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
 {
     const uint32_t slab = fdiv(t, g.d_tps);
     const uint32_t tt = t - slab * g.tiles_per_slab;
-    const uint32_t rb = fdiv(slab, g.d_w);
-    const uint32_t j = slab - rb * g.w;
-    const uint32_t r = fdiv(rb, g.d_nb);
-    const uint32_t b = rb - r * g.nb;
-    const uint32_t s0 = tt * g.rows_per_tile;
-    const uint32_t rows = umin32(g.rows_per_tile, g.s_local - s0);
     DirectTile d;
-    d.a_base = static_cast<int64_t>(r) * g.a_rank + static_cast<int64_t>(b) * g.a_plane +
-               (static_cast<int64_t>(j) * g.s_local + s0) * g.vr;
-    d.p_base = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
-               static_cast<int64_t>(s0) * g.p_row + static_cast<int64_t>(r) * g.vr;
-    d.nvec = rows * g.vr;
+    d.u0 = tt * g.tile_vecs;
+    d.nvec = umin32(g.tile_vecs, g.slab_vecs - d.u0);
+    if (!MODE1) {
+        const uint32_t rb = fdiv(slab, g.d_w);
+        const uint32_t j = slab - rb * g.w;
+        const uint32_t r = fdiv(rb, g.d_nb);
+        const uint32_t b = rb - r * g.nb;
+        d.dst_slab = static_cast<int64_t>(r) * g.a_rank + static_cast<int64_t>(b) * g.a_plane +
+                     static_cast<int64_t>(j) * g.s_local * g.vr;
+        d.src_slab = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
+                     static_cast<int64_t>(r) * g.vr;
+    } else {
+        const uint32_t j = fdiv(slab, g.d_nb);
+        const uint32_t b = slab - j * g.nb;
+        d.dst_slab = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane;
+        d.src_slab = static_cast<int64_t>(b) * g.a_plane +
+                     static_cast<int64_t>(j) * g.s_local * g.vr;
+    }
     return d;
 }
 
-// Offsets of the tile's delta-th vector (delta < nvec) on both sides.
-UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t delta,
-                           int64_t& a_off, int64_t& p_off)
+// Read- and write-side offsets of vector u (< slab_vecs) of the tile's slab.
+template <bool MODE1>
+UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t u,
+                           int64_t& src_off, int64_t& dst_off)
 {
-    const uint32_t q = fdiv(delta, g.d_vr);       // row within the tile
-    const uint32_t o = delta - q * g.vr;          // vector within the run
-    a_off = d.a_base + delta;
-    p_off = d.p_base + static_cast<int64_t>(static_cast<uint64_t>(q) * g.p_row) + o;
+    dst_off = d.dst_slab + u;
+    if (!MODE1) {
+        const uint32_t s = fdiv(u, g.d_vr);          // token of the sending rank
+        const uint32_t o = u - s * g.vr;             // vector within the run
+        src_off = d.src_slab + static_cast<int64_t>(static_cast<uint64_t>(s) * g.p_row) + o;
+    } else {
+        const uint32_t s = fdiv(u, g.d_prow);        // token of the receiving rank
+        const uint32_t rem = u - s * g.p_row;
+        const uint32_t r = fdiv(rem, g.d_vr);        // head block = rank that sent it
+        const uint32_t o = rem - r * g.vr;
+        src_off = d.src_slab + static_cast<int64_t>(r) * g.a_rank +
+                  static_cast<int64_t>(static_cast<uint64_t>(s) * g.vr) + o;
+    }
 }
 
 // ------------------------------------------------------------------------

@@ -21,7 +21,8 @@ namespace {
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxRowBytes = int64_t(1) << 31;      // H * D * elem_bytes
 constexpr int64_t kMaxRuns = (int64_t(1) << 32) - 1;     // w * w * B * S_local
-constexpr int64_t kMaxTensorBytes = int64_t(1) << 44;    // 16 TiB
+constexpr int64_t kMaxPlaneBytes = (int64_t(1) << 32) - 1;   // S_local * H * D * elem_bytes
+constexpr int64_t kMaxTensorBytes = int64_t(1) << 38;    // 256 GiB
 
 // Largest power of two <= 16 that divides x (16 for x == 0).
 uint32_t pow2_align(uint64_t x)
@@ -47,11 +48,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out)
     return *out <= limit;
 }
 
-uint32_t grid_for(uint32_t tiles, int32_t hint, int32_t cus, uint32_t per_cu)
+// One tile per workgroup unless the caller's hint caps the grid (the
+// kernels then loop over their tiles grid-stride).
+uint32_t grid_for(uint32_t tiles, int32_t hint)
 {
-    uint64_t g = hint > 0 ? static_cast<uint64_t>(hint)
-                          : static_cast<uint64_t>(cus > 0 ? cus : kAssumedCus) * per_cu;
-    if (g > tiles) g = tiles;
+    uint64_t g = tiles;
+    if (hint > 0 && static_cast<uint64_t>(hint) < g) g = static_cast<uint64_t>(hint);
     if (g < 1) g = 1;
     return static_cast<uint32_t>(g);
 }
@@ -83,14 +85,17 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     g.vr = static_cast<uint32_t>(run / vb);
     g.p_row = static_cast<uint32_t>(p->w) * g.vr;
     g.s_local = static_cast<uint32_t>(p->S_local);
-    uint32_t rows = g.vr >= kDirectTileVectors ? 1u : kDirectTileVectors / g.vr;
-    if (rows > g.s_local) rows = g.s_local;
-    g.rows_per_tile = rows;
-    g.tiles_per_slab = (g.s_local + rows - 1) / rows;
     g.w = static_cast<uint32_t>(p->w);
     g.nb = nb;
-    g.num_tiles = g.w * g.w * nb * g.tiles_per_slab;   // bounded by the run limit
+    // slabs are cut along the written side: (r, b, j) runs in mode 0, (j, b) rows in mode 1
+    const uint64_t slab_vecs = static_cast<uint64_t>(g.s_local) * (mode == 0 ? g.vr : g.p_row);
+    const uint64_t slabs = static_cast<uint64_t>(g.w) * nb * (mode == 0 ? g.w : 1u);
+    g.slab_vecs = static_cast<uint32_t>(slab_vecs);   // < 2^32 by the plane-size limit
+    g.tile_vecs = kTileBytes / vb;      // 1 KiB of data whatever the vector width
+    g.tiles_per_slab = static_cast<uint32_t>((slab_vecs + g.tile_vecs - 1) / g.tile_vecs);
+    g.num_tiles = static_cast<uint32_t>(slabs * g.tiles_per_slab);   // bounded by the tensor limit
     g.d_vr = make_div32(g.vr);
+    g.d_prow = make_div32(g.p_row);
     g.d_tps = make_div32(g.tiles_per_slab);
     g.d_w = make_div32(g.w);
     g.d_nb = make_div32(nb);
@@ -143,7 +148,7 @@ CopyGeom make_copy(uint32_t vb, const uint8_t* src, uint8_t* dst, int64_t src_st
     g.src_stride = src_stride / vb;
     g.dst_stride = dst_stride / vb;
     g.span = span_bytes / vb;
-    g.tile_vecs = kCopyTileVectors;
+    g.tile_vecs = kTileBytes / vb;
     g.tiles_per_span = static_cast<uint32_t>((g.span + g.tile_vecs - 1) / g.tile_vecs);
     g.num_tiles = count * g.tiles_per_span;
     g.d_tps = make_div32(g.tiles_per_span);
@@ -173,7 +178,7 @@ int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* 
 }
 
 void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in, void* out,
-             int32_t cus, Prepared* pr)
+             Prepared* pr)
 {
     memset(pr, 0, sizeof *pr);
     const int64_t run = p->layout.run_bytes;
@@ -230,15 +235,17 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     L.mode = mode;
     if (path == UA2A_PATH_DIRECT) {
         L.kernel = Kernel::Direct;
+        L.block = kDirectBlock;
         L.width = static_cast<int32_t>(g);
         L.direct = make_direct(p, g, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb);
-        L.grid = grid_for(L.direct.num_tiles, p->blocks, cus, kDirectBlocksPerCu);
+        L.grid = grid_for(L.direct.num_tiles, p->blocks);
     } else {
         L.kernel = Kernel::Lds;
+        L.block = kLdsBlock;
         L.width = static_cast<int32_t>(g);
         L.lds = make_lds(p, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
         L.lds_bytes = L.lds.lds_bytes;
-        L.grid = grid_for(L.lds.num_tiles, p->blocks, cus, kLdsBlocksPerCu);
+        L.grid = grid_for(L.lds.num_tiles, p->blocks);
     }
     pr->launches = 1;
     if (chunked) {
@@ -248,10 +255,11 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out)));
         Launch& C = pr->copy;
         C.kernel = Kernel::Copy;
+        C.block = kCopyBlock;
         C.width = static_cast<int32_t>(vb);
         C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
-        C.grid = grid_for(C.copy.num_tiles, 0, cus, kCopyBlocksPerCu);
+        C.grid = grid_for(C.copy.num_tiles, 0);
         pr->launches = static_cast<int32_t>(2 * p->B);
     }
 }
@@ -299,6 +307,8 @@ int ua2a_layout(int32_t w, int64_t B, int64_t S_local, int64_t H, int64_t D,
     if (!mul_ok(runs / w, row / elem_bytes, kMaxTensorBytes, &elems) ||
         !mul_ok(elems, elem_bytes, kMaxTensorBytes, &bytes))
         return UA2A_ERR_SHAPE;
+    int64_t plane;
+    if (!mul_ok(S_local, row, kMaxPlaneBytes, &plane)) return UA2A_ERR_SHAPE;
     layout->H_local = H / w;
     layout->S_global = S_local * w;
     layout->run_bytes = (H / w) * D * elem_bytes;
@@ -352,17 +362,8 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
         return UA2A_ERR_HIP;
     }
     if (dev != plan->device) return UA2A_ERR_DEVICE;
-    if (plan->cus == 0) {
-        int32_t cus = 0;
-        err = backend_cu_count(plan->device, &cus);
-        if (err != 0) {
-            disable(plan, "querying the compute-unit count", err);
-            return UA2A_ERR_HIP;
-        }
-        plan->cus = cus > 0 ? cus : kAssumedCus;
-    }
     Prepared pr;
-    prepare(plan, mode, chunked, in, out, plan->cus, &pr);
+    prepare(plan, mode, chunked, in, out, &pr);
     if (!chunked) {
         err = backend_launch(pr.perm, stream);
         if (err != 0) {
@@ -432,12 +433,12 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     const int rc = check_call(plan, mode, chunked, in, out);
     if (rc != UA2A_OK) return rc;
     Prepared pr;
-    prepare(plan, mode, chunked, in, const_cast<void*>(out), plan->cus, &pr);
+    prepare(plan, mode, chunked, in, const_cast<void*>(out), &pr);
     memset(info, 0, sizeof *info);
     info->path = pr.path;
     info->vector_bytes = pr.perm.width;
     info->grid = static_cast<int32_t>(pr.perm.grid);
-    info->block = kBlock;
+    info->block = static_cast<int32_t>(pr.perm.block);
     info->tiles = pr.perm.kernel == Kernel::Direct ? pr.perm.direct.num_tiles : pr.perm.lds.num_tiles;
     info->launches = pr.launches;
     info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;

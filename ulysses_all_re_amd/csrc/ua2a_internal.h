@@ -15,30 +15,28 @@ struct ua2a_plan_s {
     int64_t window_bytes;
     int32_t device;
     int32_t path;              // UA2A_PATH_*
-    int32_t cus;               // compute units of `device`, 0 until first queried
     int32_t disabled;          // sticky after a backend failure
     char reason[256];          // why it is disabled
 };
 
 namespace ua2a {
 
-// Tunables of the host logic (bytes / vectors / workgroups).
-constexpr uint32_t kDirectTileVectors = 4096;   // target vectors per direct-path tile
-constexpr uint32_t kDirectUnroll = 4;           // vectors in flight per lane (direct, copy)
+// Tunables (bytes / vectors / workgroups).  Measured on MI355X: one vector
+// per lane per pass, single-wave workgroups, one 1 KiB tile per workgroup
+// and non-temporal accesses move the most bytes per second; deeper per-lane
+// unrolling, bigger workgroups or persistent grids are slower there.
+constexpr uint32_t kDirectUnroll = 1;           // vectors per lane per pass (direct, copy)
+constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
 constexpr uint32_t kLdsUnroll = 4;              // 16-byte chunks in flight per lane (LDS fill)
 constexpr uint32_t kDirectMinRun = 256;         // auto path: direct only for runs >= this (bytes)
 constexpr uint32_t kLdsTileBytes = 32768;       // LDS per workgroup on the LDS path
-constexpr uint32_t kCopyTileVectors = 4096;     // vectors per copy-kernel tile
-constexpr uint32_t kDirectBlocksPerCu = 8;      // auto grid caps (workgroups per CU)
-constexpr uint32_t kLdsBlocksPerCu = 4;
-constexpr uint32_t kCopyBlocksPerCu = 8;
-constexpr int32_t kAssumedCus = 256;            // used by ua2a_describe before the first exchange
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
     Kernel kernel;
+    uint32_t block;      // threads per workgroup
     int32_t width;       // Direct/Copy: bytes per lane vector; Lds: LDS piece bytes G
     int32_t mode;        // Direct/Lds: 0 or 1
     uint32_t grid;
@@ -52,7 +50,6 @@ struct Launch {
 // (tests only) implements it over ordinary memory.  Each returns 0 or a
 // backend error code that backend_error_name() can name.
 int backend_current_device(int32_t* device);
-int backend_cu_count(int32_t device, int32_t* cus);
 int backend_launch(const Launch& launch, void* stream);
 const char* backend_error_name(int err);
 

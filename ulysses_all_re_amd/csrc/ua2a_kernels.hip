@@ -6,12 +6,12 @@
 // mode 1 the inverse), so it is bound by HBM bandwidth: no MFMA, every byte
 // read once and written once.  Three kernels:
 //
-//  * ua2a_direct_kernel  -- each lane moves whole vectors (16 bytes when the
-//    run and both bases allow) of a run; consecutive lanes touch consecutive
-//    vectors of a tile, so one side is fully contiguous per wave and the
-//    other is contiguous for a whole run.  Each lane keeps kDirectUnroll
-//    vectors in flight (loads first, then stores).  Used for runs of at
-//    least a few cache lines.
+//  * ua2a_direct_kernel  -- each lane moves one whole vector (16 bytes when
+//    the run and both bases allow) per pass; a workgroup covers one tile of
+//    consecutive vectors of the side being WRITTEN (the A side in mode 0,
+//    the P side in mode 1), so its stores are contiguous and its loads are
+//    whole runs.  One tile per workgroup.  Used for runs of at least a few
+//    cache lines.
 //  * ua2a_lds_kernel     -- for short or unaligned runs: a workgroup stages
 //    a contiguous span of P-side rows in LDS and moves both sides as 16-byte
 //    aligned chunks, re-ordering runs inside LDS in G-byte pieces.
@@ -27,32 +27,41 @@
 
 namespace ua2a {
 
+// Every byte is read once and written once: mark the global accesses
+// non-temporal so the streams do not displace other data in L2 / MALL.
+struct StreamMem {
+    template <class T>
+    __device__ static T ld(const T* p) { return __builtin_nontemporal_load(p); }
+    template <class T>
+    __device__ static void st(T* p, T v) { __builtin_nontemporal_store(v, p); }
+};
+
 template <int VB, bool MODE1>
-__global__ __launch_bounds__(kBlock) void ua2a_direct_kernel(DirectGeom g)
+__global__ __launch_bounds__(kDirectBlock) void ua2a_direct_kernel(DirectGeom g)
 {
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
-        direct_tile_body<VB, MODE1, kDirectUnroll>(g, t, threadIdx.x);
+        direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(g, t, threadIdx.x);
 }
 
 template <int G, bool MODE1>
-__global__ __launch_bounds__(kBlock) void ua2a_lds_kernel(LdsGeom g)
+__global__ __launch_bounds__(kLdsBlock) void ua2a_lds_kernel(LdsGeom g)
 {
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
         const LdsTile d = lds_tile(g, t);
-        lds_fill<G, MODE1, kLdsUnroll>(g, d, threadIdx.x, lds);
+        lds_fill<StreamMem, G, MODE1, kLdsBlock, kLdsUnroll>(g, d, threadIdx.x, lds);
         __syncthreads();
-        lds_drain<G, MODE1>(g, d, threadIdx.x, lds);
+        lds_drain<StreamMem, G, MODE1, kLdsBlock>(g, d, threadIdx.x, lds);
         __syncthreads();   // the next tile overwrites the LDS image
     }
 }
 
 template <int VB>
-__global__ __launch_bounds__(kBlock) void ua2a_copy_kernel(CopyGeom g)
+__global__ __launch_bounds__(kCopyBlock) void ua2a_copy_kernel(CopyGeom g)
 {
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
-        copy_tile_body<VB, kDirectUnroll>(g, t, threadIdx.x);
+        copy_tile_body<StreamMem, VB, kCopyBlock, kDirectUnroll>(g, t, threadIdx.x);
 }
 
 namespace {
@@ -106,15 +115,6 @@ int backend_current_device(int32_t* device)
     return 0;
 }
 
-int backend_cu_count(int32_t device, int32_t* cus)
-{
-    int v = 0;
-    const hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
-    if (e != hipSuccess) return static_cast<int>(e);
-    *cus = v;
-    return 0;
-}
-
 const char* backend_error_name(int err) { return hipGetErrorName(static_cast<hipError_t>(err)); }
 
 int backend_launch(const Launch& L, void* stream)
@@ -142,7 +142,7 @@ int backend_launch(const Launch& L, void* stream)
     }
     if (fn == nullptr) return static_cast<int>(hipErrorInvalidValue);
     void* args[] = {arg};
-    const hipError_t e = hipLaunchKernel(fn, dim3(L.grid), dim3(kBlock), args, shmem,
+    const hipError_t e = hipLaunchKernel(fn, dim3(L.grid), dim3(L.block), args, shmem,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : static_cast<int>(e);
 }
