@@ -74,10 +74,11 @@ def load_traffic():
     return t
 
 
-def cpu_baseline(x_cpu, w, steps, moved_bytes):
+def cpu_baseline(x_cpu, w, steps, moved_bytes, workload):
     """The oracle as it stands, single-threaded, on `steps` full round trips."""
     import oracle
-    xb = x_cpu.view(__import__("torch").int16).numpy()
+    from workloads import BITS_VIEW
+    xb = x_cpu.view(BITS_VIEW[x_cpu.element_size()]).numpy()
     t0 = time.perf_counter()
     for _ in range(steps):
         y = oracle.exchange(xb, 0, w)
@@ -88,7 +89,7 @@ def cpu_baseline(x_cpu, w, steps, moved_bytes):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{steps} full {WORKLOAD} round trips (mode 0 then mode 1, "
+        "sample": f"{steps} full {workload} round trips (mode 0 then mode 1, "
                   f"{2 * moved_bytes * steps} algorithmic bytes) through the C nested-loop "
                   f"oracle, one thread, {dt:.2f} s",
     }
@@ -98,32 +99,47 @@ def run(args):
     import torch
 
     import ulysses_all_re_amd as ua
-    from workloads import CONFIGS, make_tensor
+    from workloads import CONFIGS, DTYPES, MEASURE, make_tensor
 
-    c = CONFIGS[WORKLOAD]
+    name = args.workload
+    c = {**CONFIGS, **MEASURE}[name]
     w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dt = DTYPES[c["dtype"]]
+    e = torch.empty((), dtype=dt).element_size()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    lay = ua.ua2a_layout(w, B, S, H, D, 2)
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
     moved = lay["moved_bytes"]                     # per exchange: read + write
-    log(f"workload {WORKLOAD} w={w} B={B} S_local={S} H={H} D={D} bf16, "
-        f"{lay['tensor_bytes']} B per tensor")
-    x_cpu = make_tensor((w, B, S, H, D), c["dtype"], c["dist"], c["seed0"])
+    chunked = bool(args.chunked)
+    log(f"workload {name} w={w} B={B} S_local={S} H={H} D={D} {c['dtype']}, "
+        f"{lay['tensor_bytes']} B per tensor, chunked={chunked}")
+    dist = "index_bits" if c["dist"] == "index" else c["dist"]
+    x_cpu = make_tensor((w, B, S, H, D), c["dtype"], dist, c["seed0"])
     x = x_cpu.to(dev)
-    plan = ua.Plan(w, B, S, H, D, torch.bfloat16, blocks=args.blocks, device=dev)
-    y = torch.empty(plan.out_shape(0), dtype=torch.bfloat16, device=dev)
-    z = torch.empty(plan.out_shape(1), dtype=torch.bfloat16, device=dev)
-    info0 = plan.describe(x, 0, out=y)
-    info1 = plan.describe(y, 1, out=z)
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=dev) if chunked else None
+    plan = ua.Plan(w, B, S, H, D, dt, blocks=args.blocks, window=window, device=dev)
+    plan.set_path({"auto": ua.UA2A_PATH_AUTO, "direct": ua.UA2A_PATH_DIRECT,
+                   "lds": ua.UA2A_PATH_LDS}[args.path])
+    y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
+    z = torch.empty(plan.out_shape(1), dtype=dt, device=dev)
+    info0 = plan.describe(x, 0, chunked, out=y)
+    info1 = plan.describe(y, 1, chunked, out=z)
     log(f"mode 0 launch {info0}")
     log(f"mode 1 launch {info1}")
     stream = torch.cuda.current_stream(dev)
+    bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[e]
+
+    def ex0():
+        plan.exchange(x, 0, chunked, out=y, stream=stream)
+
+    def ex1():
+        plan.exchange(y, 1, chunked, out=z, stream=stream)
 
     for _ in range(args.warmup):
-        plan.exchange(x, 0, out=y, stream=stream)
-        plan.exchange(y, 1, out=z, stream=stream)
+        ex0()
+        ex1()
     torch.cuda.synchronize(dev)
-    if not torch.equal(z.view(torch.int16), x.view(torch.int16)):
+    if not torch.equal(z.view(bits), x.view(bits)):
         raise SystemExit("round trip did not return the input; refusing to report a number")
     log(f"warmup done ({args.warmup} steps), round trip bit-exact")
 
@@ -141,31 +157,34 @@ def run(args):
         return a.elapsed_time(b)
 
     def step():
-        plan.exchange(x, 0, out=y, stream=stream)
-        plan.exchange(y, 1, out=z, stream=stream)
+        ex0()
+        ex1()
 
     # the timed region: K whole steps, nothing else on the stream
     total_ms = timed(step, K)
     log(f"timed {K} steps in {total_ms:.3f} ms")
-    # per-kernel averages for the roofline: each kernel launched K times back to back
-    avg0 = timed(lambda: plan.exchange(x, 0, out=y, stream=stream), K) / K
-    avg1 = timed(lambda: plan.exchange(y, 1, out=z, stream=stream), K) / K
+    # per-exchange averages for the roofline: each mode K times back to back
+    avg0 = timed(ex0, K) / K
+    avg1 = timed(ex1, K) / K
     # device-to-device copy of the same byte count, timed the same way
     cp = torch.empty_like(x)
     timed(lambda: cp.copy_(x), 3)
     avgc = timed(lambda: cp.copy_(x), K) / K
-    log(f"per launch: mode 0 {avg0 * 1e3:.1f} us, mode 1 {avg1 * 1e3:.1f} us, copy {avgc * 1e3:.1f} us")
+    log(f"per exchange: mode 0 {avg0 * 1e3:.1f} us, mode 1 {avg1 * 1e3:.1f} us, "
+        f"copy {avgc * 1e3:.1f} us")
 
     def gbps(ms):
         return moved / (ms * 1e-3) / 1e9
 
     value = 2 * moved * K / (total_ms * 1e-3) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic() if (name == WORKLOAD and not chunked and args.path == "auto") else None
     dom_mode, dom_avg = (0, avg0) if avg0 >= avg1 else (1, avg1)
+    dom_info = info0 if dom_mode == 0 else info1
+    kname = "ua2a_direct_kernel" if dom_info["path"] == ua.UA2A_PATH_DIRECT else "ua2a_lds_kernel"
     roofline = {
         "bound": "hbm",
-        "kernel": f"ua2a_direct_kernel<{(info0 if dom_mode == 0 else info1)['vector_bytes']}, "
-                  f"mode {dom_mode}>",
+        "kernel": f"{kname}<{dom_info['vector_bytes']}, mode {dom_mode}>"
+                  + (" + ua2a_copy_kernel, per plane" if chunked else ""),
         "achieved": round(gbps(dom_avg), 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
@@ -176,7 +195,7 @@ def run(args):
     }
 
     def mode_entry(avg, info, m):
-        return {"GBps": round(gbps(avg), 1), "us_per_launch": round(avg * 1e3, 2),
+        return {"GBps": round(gbps(avg), 1), "us_per_exchange": round(avg * 1e3, 2),
                 "pct_peak": round(100 * gbps(avg) / PEAK_HBM_GBPS, 2),
                 "traffic_bytes": traffic[f"mode{m}_bytes_per_launch"] if traffic else None,
                 "launch": info}
@@ -192,11 +211,13 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": c["dtype"],
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "w": w, "B": B, "S_local": S, "S_global": S * w,
-                   "H": H, "D": D, "elem": "bf16", "step": "mode 0 then mode 1",
-                   "bytes_per_step": 2 * moved},
+        "config": {"workload": name, "w": w, "B": B, "S_local": S, "S_global": S * w,
+                   "H": H, "D": D, "elem": c["dtype"], "run_bytes": lay["run_bytes"],
+                   "chunked": chunked, "path": args.path, "step": "mode 0 then mode 1",
+                   "bytes_per_step": 2 * moved,
+                   "cache_resident": lay["tensor_bytes"] * 2 <= 256 * 2 ** 20},
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "mode0": mode_entry(avg0, info0, 0),
         "mode1": mode_entry(avg1, info1, 1),
@@ -204,9 +225,12 @@ def run(args):
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if chunked:
+        # what the window path actually moves: permute into the window + copy out of it
+        result["window_path_bytes_per_exchange"] = 2 * moved
     if not args.no_cpu_baseline:
         log(f"cpu baseline: {args.cpu_steps} oracle round trips")
-        result["cpu_baseline"] = cpu_baseline(x_cpu, w, args.cpu_steps, moved)
+        result["cpu_baseline"] = cpu_baseline(x_cpu, w, args.cpu_steps, moved, name)
     plan.close()
     print(json.dumps(result), flush=True)
 
@@ -301,9 +325,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--blocks", type=int, default=0, help="grid-size hint (0 = library default)")
-    ap.add_argument("--cpu-steps", type=int, default=4,
-                    help="oracle round trips timed for cpu_baseline (about 2.5 s each)")
+    ap.add_argument("--blocks", type=int, default=0, help="grid-size cap (0 = library default)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="workload to time (default: the video-DiT exchange the metric is quoted on)")
+    ap.add_argument("--chunked", action="store_true", help="time the chunked (per-plane window) path")
+    ap.add_argument("--path", choices=("auto", "direct", "lds"), default="auto",
+                    help="force a kernel family (default: the library's choice)")
+    ap.add_argument("--cpu-steps", type=int, default=12,
+                    help="oracle round trips timed for cpu_baseline (about 1 s each on the "
+                         "video-DiT workload, so about 12 s in all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE CSVs under DIR into traffic bytes")

@@ -34,6 +34,15 @@ CONFIGS = {
                     seed0=None, seed1=None, chunked=False),
 }
 
+# Measurement-only shapes for the short-run (LDS) and unaligned-run paths,
+# sized past the 256 MB on-package cache so they measure HBM.
+MEASURE = {
+    "short_run": dict(w=8, B=1, S_local=131072, H=8, D=32, dtype="bf16", dist="normal",
+                      seed0=0, seed1=1, chunked=False),     # run 64 B, 537 MB per tensor
+    "odd_run": dict(w=4, B=1, S_local=2097152, H=4, D=7, dtype="bf16", dist="normal",
+                    seed0=0, seed1=1, chunked=False),       # run 14 B, 470 MB per tensor
+}
+
 # Shapes whose per-rank run (H/w * D elements) is not a multiple of 16 bytes,
 # or is shorter than a 128-byte cache line: (w, B, S_local, H, D, dtype).
 TAIL_SHAPES = [
