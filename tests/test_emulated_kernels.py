@@ -38,6 +38,8 @@ SHAPES = [
     (4, 1, 40, 8, 128, 2),     # run 512 B: direct path, several tiles
     (3, 2, 33, 12, 80, 4),     # awkward-shaped, run 1280 B
     (8, 1, 13, 40, 128, 2),    # video-DiT head layout, short sequence
+    (2, 1, 37, 2, 1024, 2),    # 4 KiB rows: grouped tile order in mode 0, padding tiles
+    (4, 2, 13, 8, 256, 2),     # 4 KiB rows, two planes
 ] + [s[:5] + ({"bf16": 2, "fp16": 2, "fp32": 4, "f64": 8, "u8": 1}[s[5]],) for s in TAIL_SHAPES]
 
 
@@ -286,6 +288,26 @@ def test_chunked_failure_mid_plane_disables(emu):
     emu.ua2a_emu_fail_next_launch(7)
     assert emu.ua2a_exchange(h, 0, 1, a.ptr, b.ptr, None) == ua.UA2A_ERR_HIP
     assert emu.ua2a_exchange(h, 0, 1, a.ptr, b.ptr, None) == ua.UA2A_ERR_DISABLED
+    emu.ua2a_destroy(h)
+
+
+def test_grouped_tile_order_covers_every_vector(emu):
+    """Mode 0 on 4 KiB-multiple rows uses the interleaved order; padding tiles stay empty."""
+    shape = (2, 3, 37, 2, 1024, 2)        # row 4096 B, 74 tiles per slab, groups of 8
+    for mode in (0, 1):
+        x, y, info, bufs = emu_exchange(emu, shape, mode, seed=9)
+        assert np.array_equal(y, oracle_bytes(x, shape, mode))
+        assert all(b.guards_intact() for b in bufs)
+    w, B, S = shape[:3]
+    slabs, tps = w * B * w, -(-S * 128 // 64)
+    lay = ua2a_layout(emu, *shape)
+    a, b = Buf(lay.tensor_bytes), Buf(lay.tensor_bytes)
+    rc, h = _plan(emu, shape)
+    info = ua.ua2a_launch_info_t()
+    assert emu.ua2a_describe(h, 0, 0, a.ptr, b.ptr, ctypes.byref(info)) == 0
+    assert info.tiles == slabs * -(-tps // 8) * 8          # padded to whole groups
+    assert emu.ua2a_describe(h, 1, 0, a.ptr, b.ptr, ctypes.byref(info)) == 0
+    assert info.tiles == w * B * -(-S * 2 * 128 // 64)       # mode 1: slab after slab
     emu.ua2a_destroy(h)
 
 

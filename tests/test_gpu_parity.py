@@ -179,6 +179,23 @@ def test_misaligned_bases(shape, offsets):
     plan.close()
 
 
+@pytest.mark.parametrize("shape", [(8, 1, 2048, 8, 256), (4, 2, 513, 8, 512), (2, 3, 37, 2, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_power_of_two_rows(shape):
+    """Token rows that are a multiple of 4 KiB take the interleaved tile order in mode 0."""
+    w, B, S, H, D = shape
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), "bf16", "normal", 31 + mode)
+        want = oracle_out(x, mode, w)
+        xd = x.to(DEV)
+        note(f"pow2 rows {shape} mode={mode} {plan.describe(xd, mode)}")
+        y = plan.exchange(xd, mode, out=poisoned(plan.out_shape(mode), torch.bfloat16))
+        torch.cuda.synchronize()
+        assert_same_bits(y, want, f"pow2 rows {shape} mode {mode}")
+    plan.close()
+
+
 # ------------------------------------------------------ launch-shape freedom
 
 @pytest.mark.parametrize("blocks", [1, 7, 64, 0])

@@ -78,28 +78,36 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
             }
         }
     } else {
-        for (uint32_t r = 0; r < g.w; ++r) {
-            const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
-            const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-            const uint8_t* achunk0 = aspan - ahead;
-            const uint32_t ach = span_chunks(ahead, d.a_len);
-            for (uint32_t c0 = tid; c0 < ach; c0 += BS * U) {
-                u32x4 v[U];
+        // the w spans' chunks as one flat index space, so every lane has work
+        // even when one span is shorter than the workgroup
+        const uint32_t stride = span_chunks(15, d.a_len);     // chunks of the longest span
+        const uint32_t total = g.w * stride;
+        for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
+            u32x4 v[U] = {};
 #pragma unroll
-                for (uint32_t k = 0; k < U; ++k) {
-                    const uint32_t c = c0 + k * BS;
-                    if (c < ach && chunk_full(c * 16, ahead, d.a_len))
-                        v[k] = Mem::ld(reinterpret_cast<const u32x4*>(achunk0 + c * 16));
-                }
+            for (uint32_t k = 0; k < U; ++k) {
+                const uint32_t i = i0 + k * BS;
+                if (i >= total) continue;
+                const uint32_t r = i / stride;
+                const uint32_t c = i - r * stride;
+                const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
+                const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+                if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
+                    v[k] = Mem::ld(reinterpret_cast<const u32x4*>(aspan - ahead + c * 16));
+            }
 #pragma unroll
-                for (uint32_t k = 0; k < U; ++k) {
-                    const uint32_t c = c0 + k * BS;
-                    if (c >= ach) continue;
-                    if (chunk_full(c * 16, ahead, d.a_len))
-                        scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k], lds);
-                    else
-                        a_partial_to_lds<G>(g, d, r, c * 16, ahead, achunk0, lds);
-                }
+            for (uint32_t k = 0; k < U; ++k) {
+                const uint32_t i = i0 + k * BS;
+                if (i >= total) continue;
+                const uint32_t r = i / stride;
+                const uint32_t c = i - r * stride;
+                const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
+                const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+                if (c >= span_chunks(ahead, d.a_len)) continue;
+                if (chunk_full(c * 16, ahead, d.a_len))
+                    scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k], lds);
+                else
+                    a_partial_to_lds<G>(g, d, r, c * 16, ahead, aspan - ahead, lds);
             }
         }
     }
@@ -113,18 +121,20 @@ template <class Mem, int G, bool MODE1, uint32_t BS>
 UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const uint8_t* lds)
 {
     if (!MODE1) {
-        for (uint32_t r = 0; r < g.w; ++r) {
+        // the w spans' chunks as one flat index space (see lds_fill)
+        const uint32_t stride = span_chunks(15, d.a_len);
+        const uint32_t total = g.w * stride;
+        for (uint32_t i = tid; i < total; i += BS) {
+            const uint32_t r = i / stride;
+            const uint32_t c = i - r * stride;
             uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
             const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-            uint8_t* achunk0 = aspan - ahead;
-            const uint32_t ach = span_chunks(ahead, d.a_len);
-            for (uint32_t c = tid; c < ach; c += BS) {
-                const uint32_t lo = c * 16;
-                if (chunk_full(lo, ahead, d.a_len))
-                    Mem::st(reinterpret_cast<u32x4*>(achunk0 + lo), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
-                else
-                    a_partial_from_lds<G>(g, d, r, lo, ahead, lds, achunk0);
-            }
+            if (c >= span_chunks(ahead, d.a_len)) continue;
+            const uint32_t lo = c * 16;
+            if (chunk_full(lo, ahead, d.a_len))
+                Mem::st(reinterpret_cast<u32x4*>(aspan - ahead + lo), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
+            else
+                a_partial_from_lds<G>(g, d, r, lo, ahead, lds, aspan - ahead);
         }
     } else {
         uint8_t* pchunk0 = g.p_ptr + d.p_start - d.head;

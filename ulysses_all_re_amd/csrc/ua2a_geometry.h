@@ -74,6 +74,14 @@ UA2A_HD uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
 //          contiguous; t = (j * nb + b) * tiles_per_slab + tt
 // A tile is tile_vecs consecutive vectors of one slab (the last tile of a
 // slab is short).  Units of every stride/offset: VB-byte vectors.
+//
+// Tile order.  By default tiles run slab after slab.  With group = F > 0
+// they run in groups of F tiles of one slab, the groups of all slabs
+// interleaved (t = ((hi * slabs + slab) * F + lo), tt = hi * F + lo); the
+// host picks this for mode 0 when a P-side row is a multiple of 4 KiB, where
+// slab after slab would keep every active workgroup reading the same column
+// of power-of-two-strided rows.  Padding tiles (tt >= tiles_per_slab) are
+// empty.
 struct DirectGeom {
     const uint8_t* src;        // mode 0: P side; mode 1: A side
     uint8_t* dst;              // the other side
@@ -86,8 +94,10 @@ struct DirectGeom {
     uint32_t slab_vecs;        // vectors per slab (< 2^32, checked by the host)
     uint32_t tile_vecs;
     uint32_t tiles_per_slab;   // ceil(slab_vecs / tile_vecs)
-    uint32_t num_tiles;        // slabs * tiles_per_slab
-    Div32 d_vr, d_prow, d_tps, d_w, d_nb;
+    uint32_t num_tiles;        // slabs * tiles_per_slab (grouped: slabs * ceil(tps / F) * F)
+    uint32_t group;            // 0: slab after slab; F > 0: groups of F tiles interleaved
+    uint32_t slabs;
+    Div32 d_vr, d_prow, d_tps, d_w, d_nb, d_group, d_slabs;
 };
 
 struct DirectTile {
@@ -100,9 +110,24 @@ struct DirectTile {
 template <bool MODE1>
 UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
 {
-    const uint32_t slab = fdiv(t, g.d_tps);
-    const uint32_t tt = t - slab * g.tiles_per_slab;
+    uint32_t slab, tt;
+    if (g.group == 0) {
+        slab = fdiv(t, g.d_tps);
+        tt = t - slab * g.tiles_per_slab;
+    } else {
+        const uint32_t grp = fdiv(t, g.d_group);
+        const uint32_t lo = t - grp * g.group;
+        const uint32_t hi = fdiv(grp, g.d_slabs);
+        slab = grp - hi * g.slabs;
+        tt = hi * g.group + lo;
+    }
     DirectTile d;
+    if (tt >= g.tiles_per_slab) {      // padding tile of the grouped order
+        d.u0 = 0;
+        d.nvec = 0;
+        d.dst_slab = d.src_slab = 0;
+        return d;
+    }
     d.u0 = tt * g.tile_vecs;
     d.nvec = umin32(g.tile_vecs, g.slab_vecs - d.u0);
     if (!MODE1) {

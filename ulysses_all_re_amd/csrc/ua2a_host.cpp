@@ -93,26 +93,42 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     g.slab_vecs = static_cast<uint32_t>(slab_vecs);   // < 2^32 by the plane-size limit
     g.tile_vecs = kTileBytes / vb;      // 1 KiB of data whatever the vector width
     g.tiles_per_slab = static_cast<uint32_t>((slab_vecs + g.tile_vecs - 1) / g.tile_vecs);
-    g.num_tiles = static_cast<uint32_t>(slabs * g.tiles_per_slab);   // bounded by the tensor limit
+    g.slabs = static_cast<uint32_t>(slabs);
+    // mode 0 reads one column of P rows per slab: interleave slabs when the
+    // row stride is a multiple of 4 KiB (measured: slab after slab camps there)
+    const int64_t row_bytes = run * p->w;
+    g.group = (mode == 0 && slabs > 1 && row_bytes % kDirectGroupRowAlign == 0) ? kDirectGroup : 0;
+    if (g.group) {
+        const uint64_t groups = (g.tiles_per_slab + g.group - 1) / g.group;
+        g.num_tiles = static_cast<uint32_t>(groups * g.group * slabs);
+    } else {
+        g.num_tiles = static_cast<uint32_t>(slabs * g.tiles_per_slab);   // bounded by the tensor limit
+    }
     g.d_vr = make_div32(g.vr);
     g.d_prow = make_div32(g.p_row);
     g.d_tps = make_div32(g.tiles_per_slab);
     g.d_w = make_div32(g.w);
     g.d_nb = make_div32(nb);
+    g.d_group = make_div32(g.group ? g.group : 1);
+    g.d_slabs = make_div32(g.slabs);
     return g;
 }
 
-// Rows of one (j, b) that fit the LDS tile, 0 if not even one does.
-uint32_t lds_rows(const ua2a_plan_s* p)
+// Rows of one (j, b) per LDS tile: as many as fit the mode's target size,
+// at least one, and 0 (no LDS path) if one row plus the alignment slack
+// exceeds the largest tile a workgroup may hold.
+uint32_t lds_rows(const ua2a_plan_s* p, int mode)
 {
     const int64_t row = p->layout.run_bytes * p->w;
-    if (row + 16 > kLdsTileBytes) return 0;
-    int64_t rows = (kLdsTileBytes - 16) / row;
+    if (row + 16 > kLdsTileMax) return 0;
+    const int64_t target = mode == 0 ? kLdsTileMode0 : kLdsTileMode1;
+    int64_t rows = (target - 16) / row;
+    if (rows < 1) rows = 1;
     if (rows > p->S_local) rows = p->S_local;
     return static_cast<uint32_t>(rows);
 }
 
-LdsGeom make_lds(const ua2a_plan_s* p, uint8_t* p_ptr, uint8_t* a_ptr, int64_t p_rank,
+LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint8_t* p_ptr, uint8_t* a_ptr, int64_t p_rank,
                  int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
 {
     LdsGeom g;
@@ -126,7 +142,7 @@ LdsGeom make_lds(const ua2a_plan_s* p, uint8_t* p_ptr, uint8_t* a_ptr, int64_t p
     g.run = static_cast<uint32_t>(p->layout.run_bytes);
     g.row = g.run * static_cast<uint32_t>(p->w);
     g.s_local = static_cast<uint32_t>(p->S_local);
-    g.rows_per_tile = lds_rows(p);
+    g.rows_per_tile = lds_rows(p, mode);
     g.tiles_per_plane = (g.s_local + g.rows_per_tile - 1) / g.rows_per_tile;
     g.w = static_cast<uint32_t>(p->w);
     g.nb = nb;
@@ -192,14 +208,14 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(out)));
     if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
 
-    const uint32_t rows = lds_rows(p);
+    const uint32_t rows = lds_rows(p, mode);
     int32_t path;
     if (p->path == UA2A_PATH_DIRECT)
         path = UA2A_PATH_DIRECT;
     else if (p->path == UA2A_PATH_LDS)
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
-    else if (g == 16 && run >= kDirectMinRun)
-        path = UA2A_PATH_DIRECT;
+    else if (g == 16 && run % 128 == 0 && (run >= kDirectMinRun || mode == 0))
+        path = UA2A_PATH_DIRECT;      // whole cache lines per run: no staging needed
     else
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
 
@@ -243,7 +259,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.kernel = Kernel::Lds;
         L.block = kLdsBlock;
         L.width = static_cast<int32_t>(g);
-        L.lds = make_lds(p, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
+        L.lds = make_lds(p, mode, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
         L.lds_bytes = L.lds.lds_bytes;
         L.grid = grid_for(L.lds.num_tiles, p->blocks);
     }

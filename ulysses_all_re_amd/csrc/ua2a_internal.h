@@ -27,9 +27,13 @@ namespace ua2a {
 // unrolling, bigger workgroups or persistent grids are slower there.
 constexpr uint32_t kDirectUnroll = 1;           // vectors per lane per pass (direct, copy)
 constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
-constexpr uint32_t kLdsUnroll = 4;              // 16-byte chunks in flight per lane (LDS fill)
-constexpr uint32_t kDirectMinRun = 256;         // auto path: direct only for runs >= this (bytes)
-constexpr uint32_t kLdsTileBytes = 32768;       // LDS per workgroup on the LDS path
+constexpr uint32_t kLdsUnroll = 1;              // 16-byte chunks per lane per pass (LDS fill)
+constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: direct only for runs >= this (bytes)
+constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
+constexpr uint32_t kDirectGroupRowAlign = 4096;
+constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
+constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
+constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2 };
 
