@@ -160,6 +160,28 @@ def run(args):
         ex0()
         ex1()
 
+    if args.graph:
+        # one step captured once as a HIP graph; the timed region replays it
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            plan.exchange(x, 0, chunked, out=y, stream=side)
+            plan.exchange(y, 1, chunked, out=z, stream=side)
+        torch.cuda.synchronize(dev)
+        bits_z = z.view(bits)
+        bits_z.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        if not torch.equal(z.view(bits), x.view(bits)):
+            raise SystemExit("graph replay did not return the input; refusing to report a number")
+        step = graph.replay
+        log("timing graph replays of one step")
+
     # the timed region: K whole steps, nothing else on the stream
     total_ms = timed(step, K)
     log(f"timed {K} steps in {total_ms:.3f} ms")
@@ -215,7 +237,8 @@ def run(args):
         "data": "synthetic",
         "config": {"workload": name, "w": w, "B": B, "S_local": S, "S_global": S * w,
                    "H": H, "D": D, "elem": c["dtype"], "run_bytes": lay["run_bytes"],
-                   "chunked": chunked, "path": args.path, "step": "mode 0 then mode 1",
+                   "chunked": chunked, "path": args.path, "graph": bool(args.graph),
+                   "step": "mode 0 then mode 1",
                    "bytes_per_step": 2 * moved,
                    "cache_resident": lay["tensor_bytes"] * 2 <= 256 * 2 ** 20},
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
@@ -329,6 +352,8 @@ def main():
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload to time (default: the video-DiT exchange the metric is quoted on)")
     ap.add_argument("--chunked", action="store_true", help="time the chunked (per-plane window) path")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step as a HIP graph and time its replays")
     ap.add_argument("--path", choices=("auto", "direct", "lds"), default="auto",
                     help="force a kernel family (default: the library's choice)")
     ap.add_argument("--cpu-steps", type=int, default=12,
