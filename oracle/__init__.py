@@ -16,6 +16,10 @@ w rank tensors are stacked rank-major in one array,
 and elements are moved as raw bit patterns (any numpy dtype of 1, 2, 4 or 8
 bytes; bf16 travels as uint16/int16).
 
+``source_indices`` gives, for chosen output positions, the input position
+each one comes from (the same definitions, one element at a time), for
+checking outputs too large to copy whole to the host.
+
 Parity pins (tests/test_oracle_pins.py): closed-form shapes, w = 1 identity,
 mode1(mode0(x)) == x and mode0(mode1(y)) == y, chunked == unchunked,
 agreement with an all-to-all over torch.distributed's gloo backend in w
@@ -60,6 +64,10 @@ def _load():
         fn.restype = ctypes.c_int
     lib.ua2a_oracle_chunked.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp]
     lib.ua2a_oracle_chunked.restype = ctypes.c_int
+    lib.ua2a_oracle_source_index.argtypes = [i32, i32, i64, i64, i64, i64, i64]
+    lib.ua2a_oracle_source_index.restype = i64
+    lib.ua2a_oracle_source_indices.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp]
+    lib.ua2a_oracle_source_indices.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -108,6 +116,18 @@ def exchange(x: np.ndarray, mode: int, w: int, chunked: bool = False) -> np.ndar
     if rc != 0:
         raise OracleError(rc)
     return out
+
+
+def source_indices(mode: int, w: int, B: int, S_local: int, H: int, D: int,
+                   out_index: np.ndarray) -> np.ndarray:
+    """Input positions of the elements the exchange writes at `out_index` (int64 array)."""
+    idx = np.ascontiguousarray(out_index, dtype=np.int64)
+    src = np.empty_like(idx)
+    rc = _load().ua2a_oracle_source_indices(mode, w, B, S_local, H, D, idx.ctypes.data,
+                                             idx.size, src.ctypes.data)
+    if rc != 0:
+        raise OracleError(rc)
+    return src
 
 
 def raw_call(fn_name: str, *args) -> int:

@@ -138,3 +138,53 @@ int ua2a_oracle_chunked(int32_t mode, int32_t w, int64_t B, int64_t S_local,
     free(window);
     return rc;
 }
+
+/* Flat position in the rank-stacked input of the element that the exchange
+ * (mode 0 or 1) writes at flat position out_index of the output: the
+ * definitions above, for one element at a time (used to check outputs too
+ * large for a whole CPU copy).  -1 on a bad argument or an index out of
+ * range. */
+int64_t ua2a_oracle_source_index(int32_t mode, int32_t w, int64_t B, int64_t S_local,
+                                 int64_t H, int64_t D, int64_t out_index)
+{
+    if (w < 1 || B < 1 || S_local < 1 || H < 1 || D < 1 || H % w != 0) return -1;
+    if (mode != 0 && mode != 1) return -1;
+    const int64_t Hl = H / w;
+    const int64_t S_global = S_local * w;
+    if (out_index < 0 || out_index >= (int64_t)w * B * S_local * H * D) return -1;
+    int64_t i = out_index;
+    const int64_t d = i % D;
+    i /= D;
+    if (mode == 0) {                       /* out[r][b][t][h][d], t = j*S_local + s */
+        const int64_t h = i % Hl;
+        i /= Hl;
+        const int64_t t = i % S_global;
+        i /= S_global;
+        const int64_t b = i % B;
+        const int64_t r = i / B;
+        const int64_t j = t / S_local, s = t % S_local;
+        return (((j * B + b) * S_local + s) * H + (r * Hl + h)) * D + d;
+    }
+    /* mode 1: out[j][b][s][hh][d], hh = r*Hl + h */
+    const int64_t hh = i % H;
+    i /= H;
+    const int64_t s = i % S_local;
+    i /= S_local;
+    const int64_t b = i % B;
+    const int64_t j = i / B;
+    const int64_t r = hh / Hl, h = hh % Hl;
+    return (((r * B + b) * S_global + (j * S_local + s)) * Hl + h) * D + d;
+}
+
+/* ua2a_oracle_source_index for n output positions. Returns 0, or -1 if any
+ * argument or index is out of range. */
+int ua2a_oracle_source_indices(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64_t H,
+                               int64_t D, const int64_t* out_index, int64_t n, int64_t* src)
+{
+    if (out_index == NULL || src == NULL || n < 0) return -1;
+    for (int64_t k = 0; k < n; ++k) {
+        src[k] = ua2a_oracle_source_index(mode, w, B, S_local, H, D, out_index[k]);
+        if (src[k] < 0) return -1;
+    }
+    return 0;
+}

@@ -196,6 +196,38 @@ def test_power_of_two_rows(shape):
     plan.close()
 
 
+def test_large_tensor_sampled():
+    """16 GiB per tensor (2^31 eight-byte elements): byte offsets far past 2^32.
+    Each element holds its own input position, so a sampled output position
+    must hold exactly what the element oracle says it came from."""
+    w, B, S, H, D = 8, 2, 32768, 64, 64
+    n = w * B * S * H * D
+    assert n == 2 ** 31
+    lay = ua.ua2a_layout(w, B, S, H, D, 8)
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, torch.int64, window=window)
+    x = torch.arange(n, dtype=torch.int64, device=DEV).view(w, B, S, H, D)
+    gen = torch.Generator("cpu").manual_seed(12)
+    idx = torch.cat([torch.arange(4096), torch.randint(0, n, (200000,), generator=gen),
+                     torch.arange(n - 4096, n)])
+    for mode in (0, 1):
+        for chunked in (False, True):
+            note(f"large sampled mode={mode} chunked={chunked} {plan.describe(x, mode, chunked)}")
+            src = x if mode == 0 else x.view(plan.in_shape(1))
+            y = plan.exchange(src, mode, chunked)
+            torch.cuda.synchronize()
+            got = y.view(-1)[idx.to(DEV)].cpu().numpy()
+            want = oracle.source_indices(mode, w, B, S, H, D, idx.numpy())
+            assert np.array_equal(got, want), (mode, chunked)
+            del y
+    note("large round trip")
+    y = plan.exchange(x, 0)
+    z = plan.exchange(y, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(z, x)
+    plan.close()
+
+
 # ------------------------------------------------------ launch-shape freedom
 
 @pytest.mark.parametrize("blocks", [1, 7, 64, 0])

@@ -315,3 +315,27 @@ def test_argument_errors():
     assert oracle.raw_call("ua2a_oracle_chunked", 2, 2, 1, 2, 4, 1, 2, p, p + 2048) == -1  # mode 2
     with pytest.raises(oracle.OracleError):
         oracle.exchange(np.zeros((2, 1, 2, 3, 1), np.int16), 0, 2)
+
+
+# ------------------------------------------------- per-element source index
+
+@pytest.mark.parametrize("shape", SHAPES + [(2, 2, 37, 2, 1024)])
+def test_source_index_agrees_with_the_whole_oracle(shape):
+    """Every output position, both modes: the element oracle names the input
+    position the whole-tensor oracle copied there (index-valued inputs)."""
+    w, B, S, H, D = shape
+    n = w * B * S * H * D
+    for mode, in_shape in ((0, shape), (1, mode1_shape(*shape))):
+        x = np.arange(n, dtype=np.int64).reshape(in_shape)
+        y = oracle.exchange(x, mode, w).ravel()
+        src = oracle.source_indices(mode, w, B, S, H, D, np.arange(n, dtype=np.int64))
+        assert np.array_equal(src, y)
+
+
+def test_source_index_rejects_out_of_range():
+    assert oracle.raw_call("ua2a_oracle_source_index", 0, 2, 1, 8, 4, 16, 2 * 8 * 4 * 16) == -1
+    assert oracle.raw_call("ua2a_oracle_source_index", 0, 2, 1, 8, 4, 16, -1) == -1
+    assert oracle.raw_call("ua2a_oracle_source_index", 2, 2, 1, 8, 4, 16, 0) == -1
+    assert oracle.raw_call("ua2a_oracle_source_index", 0, 2, 1, 8, 3, 16, 0) == -1
+    with pytest.raises(oracle.OracleError):
+        oracle.source_indices(0, 2, 1, 8, 4, 16, np.array([5000], dtype=np.int64))

@@ -222,7 +222,15 @@ class Plan:
         return out
 
     def describe(self, x, mode: int, chunked: bool = False, out=None) -> dict:
-        optr = out.data_ptr() if out is not None else x.data_ptr() + self.layout["tensor_bytes"]
+        """What exchange(x, mode, chunked, out) would launch.  Without `out`, a
+        16-byte-aligned stand-in address past `x` and the window is checked."""
+        if out is not None:
+            optr = out.data_ptr()
+        else:
+            end = x.data_ptr() + self.layout["tensor_bytes"]
+            if self.window is not None:
+                end = max(end, self.window.data_ptr() + self.window.numel() * self.window.element_size())
+            optr = (end + 255) // 256 * 256
         return ua2a_describe(self.handle, mode, int(chunked), x.data_ptr(), optr)
 
     def set_path(self, path: int) -> None:
