@@ -320,16 +320,19 @@ def traffic_from(d):
     print(json.dumps(out, indent=2))
 
 
-def summarize_trace(d):
+def summarize_trace(d, workload):
     """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run."""
     paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {d}")
+    import torch
+
     import ulysses_all_re_amd as ua
-    from workloads import CONFIGS
-    c = CONFIGS[WORKLOAD]
-    moved = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], 2)["moved_bytes"]
-    print("| kernel | calls | avg us | min us | max us | GB/s at avg (2 x tensor bytes) |")
+    from workloads import CONFIGS, DTYPES, MEASURE
+    c = {**CONFIGS, **MEASURE}[workload]
+    e = torch.empty((), dtype=DTYPES[c["dtype"]]).element_size()
+    moved = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], e)["moved_bytes"]
+    print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {moved // 2} B) |")
     print("|---|---|---|---|---|---|")
     with open(paths[0], newline="") as f:
         for r in csv.DictReader(f):
@@ -337,7 +340,7 @@ def summarize_trace(d):
             if len(name) > 70:
                 name = name[:67] + "..."
             avg = float(r["AverageNs"])
-            big = DIRECT_KERNEL in r["Name"] or COPY_KERNEL_HINT in r["Name"]
+            big = "ua2a_" in r["Name"] or COPY_KERNEL_HINT in r["Name"]
             rate = f"{moved / (avg * 1e-9) / 1e9:.1f}" if big else ""
             print(f"| `{name}` | {r['Calls']} | {avg / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                   f"{float(r['MaxNs']) / 1e3:.2f} | {rate} |")
@@ -369,7 +372,7 @@ def main():
         traffic_from(args.traffic_from)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.workload)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

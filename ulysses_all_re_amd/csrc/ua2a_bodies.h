@@ -79,7 +79,9 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
         }
     } else {
         // the w spans' chunks as one flat index space, so every lane has work
-        // even when one span is shorter than the workgroup
+        // even when one span is shorter than the workgroup; neighbouring lanes
+        // take neighbouring chunks of one span (measured faster than putting
+        // the head block fastest, which spreads a wave over w regions)
         const uint32_t stride = span_chunks(15, d.a_len);     // chunks of the longest span
         const uint32_t total = g.w * stride;
         for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
