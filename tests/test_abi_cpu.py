@@ -90,3 +90,10 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ua, "LIBRARY", str(tmp_path / "libua2a.so"))
     with pytest.raises(RuntimeError, match="no non-HIP implementation"):
         ua.load_library()
+
+
+def test_c_consumer_compiles_against_the_header(lib):
+    """include/ua2a.h is plain C99 and libua2a.so links from C (the GPU test runs it)."""
+    from tests.c_abi import build as cbuild
+    path = cbuild.build()
+    assert os.path.exists(path)

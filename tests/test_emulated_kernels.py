@@ -392,3 +392,35 @@ def test_emulated_kernels_under_asan(tmp_path):
                          timeout=600)
     assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-6000:]
     assert "asan-ok" in res.stdout
+
+
+# ------------------------------------------------------- property-based sweep
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+@st.composite
+def exchange_cases(draw):
+    w = draw(st.integers(1, 6))
+    hl = draw(st.integers(1, 5))
+    e = draw(st.sampled_from([1, 2, 4, 8]))
+    B = draw(st.integers(1, 3))
+    S = draw(st.integers(1, 40))
+    D = draw(st.integers(1, 48))
+    mode = draw(st.integers(0, 1))
+    chunked = draw(st.booleans())
+    path = draw(st.sampled_from([ua.UA2A_PATH_AUTO, ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS]))
+    mis = tuple(draw(st.integers(0, 15)) // e * e for _ in range(3))
+    blocks = draw(st.sampled_from([0, 1, 3, 1000]))
+    return (w, B, S, w * hl, D, e), mode, chunked, path, mis, blocks
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(case=exchange_cases())
+def test_emulated_random_cases_match_oracle(emu, case):
+    shape, mode, chunked, path, mis, blocks = case
+    x, y, info, bufs = emu_exchange(emu, shape, mode, chunked, path, *mis, seed=sum(shape),
+                                    blocks=blocks)
+    assert np.array_equal(y, oracle_bytes(x, shape, mode)), (case, info.path, info.vector_bytes)
+    assert all(b.guards_intact() for b in bufs), case

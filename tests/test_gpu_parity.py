@@ -228,6 +228,54 @@ def test_large_tensor_sampled():
     plan.close()
 
 
+def _random_cases(n, seed):
+    """Seeded random shapes, element sizes, paths, modes and misalignments."""
+    rng = np.random.default_rng(seed)
+    dts = [("u8", torch.uint8), ("bf16", torch.bfloat16), ("fp32", torch.float32),
+           ("f64", torch.float64)]
+    cases = []
+    for _ in range(n):
+        w = int(rng.integers(1, 9))
+        hl = int(rng.integers(1, 7))
+        name, dt = dts[int(rng.integers(0, len(dts)))]
+        e = torch.empty((), dtype=dt).element_size()
+        B, S, D = int(rng.integers(1, 4)), int(rng.integers(1, 700)), int(rng.integers(1, 200))
+        S = max(1, min(S, (32 << 20) // (w * B * w * hl * D * e)))    # at most ~32 MB per tensor
+        cases.append(dict(w=w, B=B, S=S, H=w * hl, D=D, name=name, dt=dt, e=e,
+                          mode=int(rng.integers(0, 2)), chunked=bool(rng.integers(0, 2)),
+                          path=["auto", "direct", "lds"][int(rng.integers(0, 3))],
+                          mis_in=int(rng.integers(0, 4)), mis_out=int(rng.integers(0, 4))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(60, 2024), ids=lambda c: (
+    f"w{c['w']}B{c['B']}S{c['S']}H{c['H']}D{c['D']}{c['name']}m{c['mode']}"
+    f"{'c' if c['chunked'] else ''}{c['path']}{c['mis_in']}{c['mis_out']}"))
+def test_random_cases(case):
+    w, B, S, H, D, dt = case["w"], case["B"], case["S"], case["H"], case["D"], case["dt"]
+    n = w * B * S * H * D
+    mode = case["mode"]
+    lay = ua.ua2a_layout(w, B, S, H, D, case["e"])
+    window = torch.empty(lay["window_bytes"] + 64, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=window)
+    plan.set_path(PATHS[case["path"]])
+    x = make_tensor(in_shape(w, B, S, H, D, mode), case["name"], "bytes", n % 9973)
+    want = oracle_out(x, mode, w)
+    xin = torch.zeros(n + 8, dtype=dt, device=DEV)
+    xin[case["mis_in"]:case["mis_in"] + n] = x.reshape(-1).to(DEV)
+    outbuf = poisoned((n + 8,), dt)
+    xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
+    yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
+    note(f"random {case} {plan.describe(xi, mode, case['chunked'], out=yo)}")
+    plan.exchange(xi, mode, case["chunked"], out=yo)
+    torch.cuda.synchronize()
+    assert_same_bits(yo, want, f"random case {case}")
+    guard = bits(outbuf.cpu())
+    full = 255 if guard.dtype == torch.uint8 else POISON
+    assert (guard[:case["mis_out"]] == full).all() and (guard[case["mis_out"] + n:] == full).all()
+    plan.close()
+
+
 # ------------------------------------------------------ launch-shape freedom
 
 @pytest.mark.parametrize("blocks", [1, 7, 64, 0])
