@@ -114,6 +114,22 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     return g;
 }
 
+// Whether the direct path's reads cover whole, aligned 128-byte lines, so
+// that staging through LDS cannot save traffic (measured rule, 16-byte
+// vectors).  Mode 0 reads one run per token: whole lines when the run is a
+// multiple of 128 bytes, or when w = 1 (the runs are then adjacent).  Mode 1
+// reads, per 1 KiB tile, one contiguous stretch per head block: a whole run
+// when a token row exceeds the tile, else 1024 / w bytes of consecutive
+// runs; it wants at least 256 line-aligned bytes per stretch.
+bool direct_reads_whole_lines(int mode, int64_t w, int64_t run)
+{
+    if (w == 1) return run % 16 == 0;
+    if (mode == 0) return run % 128 == 0;
+    const int64_t row = w * run;
+    if (row > kTileBytes) return run % 128 == 0 && run >= kDirectMinRun;
+    return kTileBytes % row == 0 && kTileBytes / w >= kDirectMinRun;
+}
+
 // Rows of one (j, b) per LDS tile: as many as fit the mode's target size,
 // at least one, and 0 (no LDS path) if one row plus the alignment slack
 // exceeds the largest tile a workgroup may hold.
@@ -214,8 +230,8 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         path = UA2A_PATH_DIRECT;
     else if (p->path == UA2A_PATH_LDS)
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
-    else if (g == 16 && run % 128 == 0 && (run >= kDirectMinRun || mode == 0))
-        path = UA2A_PATH_DIRECT;      // whole cache lines per run: no staging needed
+    else if (g == 16 && direct_reads_whole_lines(mode, p->w, run))
+        path = UA2A_PATH_DIRECT;
     else
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
 

@@ -28,7 +28,7 @@ namespace ua2a {
 constexpr uint32_t kDirectUnroll = 1;           // vectors per lane per pass (direct, copy)
 constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
 constexpr uint32_t kLdsUnroll = 1;              // 16-byte chunks per lane per pass (LDS fill)
-constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: direct only for runs >= this (bytes)
+constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least contiguous read per head block
 constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
 constexpr uint32_t kDirectGroupRowAlign = 4096;
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
