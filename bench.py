@@ -45,7 +45,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 WORKLOAD = "video_dit"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_direct_video_dit.json")
-DIRECT_KERNEL = "ua2a_direct_kernel"
+DIRECT_KERNEL = "ua2a_direct"        # ua2a_direct_kernel (1-D grid) and ua2a_direct3d_kernel
 COPY_KERNEL_HINT = "copyBuffer"     # the runtime's device-to-device copy kernel
 
 
@@ -202,7 +202,10 @@ def run(args):
     traffic = load_traffic() if (name == WORKLOAD and not chunked and args.path == "auto") else None
     dom_mode, dom_avg = (0, avg0) if avg0 >= avg1 else (1, avg1)
     dom_info = info0 if dom_mode == 0 else info1
-    kname = "ua2a_direct_kernel" if dom_info["path"] == ua.UA2A_PATH_DIRECT else "ua2a_lds_kernel"
+    if dom_info["path"] == ua.UA2A_PATH_DIRECT:
+        kname = "ua2a_direct3d_kernel" if dom_info["grid_dims"] == 3 else "ua2a_direct_kernel"
+    else:
+        kname = "ua2a_lds_kernel"
     roofline = {
         "bound": "hbm",
         "kernel": f"{kname}<{dom_info['vector_bytes']}, mode {dom_mode}>"
@@ -349,8 +352,9 @@ def summarize_trace(d, workload):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed steps (about 0.5 ms each on the default workload)")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--blocks", type=int, default=0, help="grid-size cap (0 = library default)")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload to time (default: the video-DiT exchange the metric is quoted on)")

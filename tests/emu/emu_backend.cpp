@@ -24,11 +24,25 @@ int g_kernel_counts[3] = {0, 0, 0};
 uint32_t g_last_grid = 0;
 
 template <int VB, bool M1>
-void run_direct(const DirectGeom& g)
+void run_direct(const Launch& L)
 {
-    for (uint32_t t = 0; t < g.num_tiles; ++t)
+    const DirectGeom& g = L.direct;
+    if (L.grid3d) {
+        for (uint32_t z = 0; z < L.grid_z; ++z)
+            for (uint32_t y = 0; y < L.grid_y; ++y)
+                for (uint32_t x = 0; x < L.grid; ++x) {
+                    const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
+                    for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+                        direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+                }
+        return;
+    }
+    // a capped grid loops grid-stride; every tile is visited exactly once either way
+    for (uint32_t t = 0; t < g.num_tiles; ++t) {
+        const DirectTile d = direct_tile<M1>(g, t);
         for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-            direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, t, tid);
+            direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+    }
 }
 
 template <int G, bool M1>
@@ -56,14 +70,14 @@ void run_copy(const CopyGeom& g)
 }
 
 template <bool M1>
-int dispatch_direct(const DirectGeom& g, int vb)
+int dispatch_direct(const Launch& L, int vb)
 {
     switch (vb) {
-    case 16: run_direct<16, M1>(g); return 0;
-    case 8: run_direct<8, M1>(g); return 0;
-    case 4: run_direct<4, M1>(g); return 0;
-    case 2: run_direct<2, M1>(g); return 0;
-    case 1: run_direct<1, M1>(g); return 0;
+    case 16: run_direct<16, M1>(L); return 0;
+    case 8: run_direct<8, M1>(L); return 0;
+    case 4: run_direct<4, M1>(L); return 0;
+    case 2: run_direct<2, M1>(L); return 0;
+    case 1: run_direct<1, M1>(L); return 0;
     default: return 1;
     }
 }
@@ -118,8 +132,18 @@ int backend_launch(const Launch& L, void*)
     if (L.block != want_block) return 5;
     switch (L.kernel) {
     case Kernel::Direct:
-        return L.mode ? dispatch_direct<true>(L.direct, L.width) : dispatch_direct<false>(L.direct, L.width);
+        if (L.grid3d) {
+            // the 3-D grid must cover every tile exactly once
+            const uint64_t slabs = static_cast<uint64_t>(L.direct.w) * L.direct.nb * (L.mode ? 1u : L.direct.w);
+            if (L.grid != L.direct.tiles_per_slab || static_cast<uint64_t>(L.grid_y) * L.grid_z != slabs ||
+                L.direct.group != 0)
+                return 6;
+        } else if (L.grid_y != 1 || L.grid_z != 1) {
+            return 7;
+        }
+        return L.mode ? dispatch_direct<true>(L, L.width) : dispatch_direct<false>(L, L.width);
     case Kernel::Lds:
+        if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.row)
             return 3;
         return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);

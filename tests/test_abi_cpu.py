@@ -68,8 +68,10 @@ def test_host_only_calls(lib):
         assert info["path"] == ua.UA2A_PATH_DIRECT and info["vector_bytes"] == 16
         assert info["block"] == 64 and info["launches"] == 1
         assert info["grid"] == info["tiles"] == 8 * 8 * -(-9450 * 80 // 64)   # 1 KiB tiles per slab
+        assert info["grid_dims"] == 3                      # one tile per workgroup, 3-D grid
         ua.ua2a_plan_set_path(h, ua.UA2A_PATH_LDS)
-        assert ua.ua2a_describe(h, 1, 0, base, base + (1 << 30))["path"] == ua.UA2A_PATH_LDS
+        lds = ua.ua2a_describe(h, 1, 0, base, base + (1 << 30))
+        assert lds["path"] == ua.UA2A_PATH_LDS and lds["grid_dims"] == 1
         with pytest.raises(ua.UA2AError) as e:
             ua.ua2a_describe(h, 0, 1, base, base + (1 << 30))
         assert e.value.code == ua.UA2A_ERR_CAPACITY
@@ -83,6 +85,15 @@ def test_host_only_calls(lib):
         ua.ua2a_plan(3, 1, 8, 4, 16, 2)
     assert e.value.code == ua.UA2A_ERR_SHAPE
     assert "window" in ua.ua2a_status_string(ua.UA2A_ERR_CAPACITY)
+
+
+def test_grid_cap_uses_the_flat_grid(lib):
+    h = ua.ua2a_plan(8, 1, 9450, 40, 128, 2, 1000)        # blocks = 1000
+    try:
+        info = ua.ua2a_describe(h, 0, 0, 1 << 40, (1 << 40) + (1 << 30))
+        assert info["grid"] == 1000 and info["grid_dims"] == 1
+    finally:
+        ua.ua2a_destroy(h)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

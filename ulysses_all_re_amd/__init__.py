@@ -56,7 +56,7 @@ class ua2a_launch_info_t(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
-                ("lds_rows", ctypes.c_int32)]
+                ("lds_rows", ctypes.c_int32), ("grid_dims", ctypes.c_int32)]
 
 
 class UA2AError(RuntimeError):
@@ -216,9 +216,13 @@ class Plan:
             self._check(out, self.out_shape(mode), "output")
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        with torch.cuda.device(self.device):
+        if torch.cuda.current_device() == self.device.index:
             ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
                           stream.cuda_stream)
+        else:
+            with torch.cuda.device(self.device):
+                ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
+                              stream.cuda_stream)
         return out
 
     def describe(self, x, mode: int, chunked: bool = False, out=None) -> dict:

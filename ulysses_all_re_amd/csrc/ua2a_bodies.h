@@ -25,12 +25,11 @@ struct PlainMem {
 // Direct path: the BS lanes move whole VB-byte vectors of the tile; U
 // vectors per lane are loaded before any is stored.
 template <class Mem, int VB, bool MODE1, uint32_t BS, uint32_t U>
-UA2A_HD void direct_tile_body(const DirectGeom& g, uint32_t t, uint32_t tid)
+UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t tid)
 {
     typedef typename Piece<VB>::T T;
     const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
     T* __restrict__ dst = reinterpret_cast<T*>(g.dst);
-    const DirectTile d = direct_tile<MODE1>(g, t);
     for (uint32_t base = tid; base < d.nvec; base += BS * U) {
         T v[U];
         int64_t to[U];

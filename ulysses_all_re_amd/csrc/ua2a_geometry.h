@@ -155,6 +155,33 @@ UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
     return d;
 }
 
+// The same tile on a 3-D grid, where the hardware supplies the coordinates
+// (no scalar division per workgroup): x = tile within its slab,
+//   mode 0: y = j, z = r * nb + b;      mode 1: y = b, z = j.
+// Used for the default slab-after-slab order when the grid fits.
+template <bool MODE1>
+UA2A_HD DirectTile direct_tile_3d(const DirectGeom& g, uint32_t x, uint32_t y, uint32_t z)
+{
+    DirectTile d;
+    d.u0 = x * g.tile_vecs;
+    d.nvec = umin32(g.tile_vecs, g.slab_vecs - d.u0);
+    if (!MODE1) {
+        const uint32_t j = y;
+        const uint32_t r = fdiv(z, g.d_nb);
+        const uint32_t b = z - r * g.nb;
+        d.dst_slab = static_cast<int64_t>(r) * g.a_rank + static_cast<int64_t>(b) * g.a_plane +
+                     static_cast<int64_t>(j) * g.s_local * g.vr;
+        d.src_slab = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
+                     static_cast<int64_t>(r) * g.vr;
+    } else {
+        const uint32_t b = y, j = z;
+        d.dst_slab = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane;
+        d.src_slab = static_cast<int64_t>(b) * g.a_plane +
+                     static_cast<int64_t>(j) * g.s_local * g.vr;
+    }
+    return d;
+}
+
 // Read- and write-side offsets of vector u (< slab_vecs) of the tile's slab.
 template <bool MODE1>
 UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t u,

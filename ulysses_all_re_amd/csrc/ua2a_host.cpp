@@ -265,12 +265,25 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     pr->plane_bytes = plane;
     Launch& L = pr->perm;
     L.mode = mode;
+    L.grid_y = L.grid_z = 1;
     if (path == UA2A_PATH_DIRECT) {
         L.kernel = Kernel::Direct;
         L.block = kDirectBlock;
         L.width = static_cast<int32_t>(g);
         L.direct = make_direct(p, g, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb);
         L.grid = grid_for(L.direct.num_tiles, p->blocks);
+        // default order, no grid cap: one tile per workgroup on a 3-D grid
+        // whose coordinates are the tile's (x = tile in slab; mode 0: y = j,
+        // z = r*nb + b; mode 1: y = b, z = j), sparing each workgroup the
+        // scalar division of a flat tile index
+        const uint32_t ny = mode == 0 ? static_cast<uint32_t>(p->w) : nb;
+        const uint32_t nz = mode == 0 ? static_cast<uint32_t>(p->w) * nb : static_cast<uint32_t>(p->w);
+        if (p->blocks == 0 && L.direct.group == 0 && ny <= kMaxGridYZ && nz <= kMaxGridYZ) {
+            L.grid3d = 1;
+            L.grid = L.direct.tiles_per_slab;
+            L.grid_y = ny;
+            L.grid_z = nz;
+        }
     } else {
         L.kernel = Kernel::Lds;
         L.block = kLdsBlock;
@@ -288,6 +301,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         Launch& C = pr->copy;
         C.kernel = Kernel::Copy;
         C.block = kCopyBlock;
+        C.grid_y = C.grid_z = 1;
         C.width = static_cast<int32_t>(vb);
         C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
@@ -469,11 +483,13 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     memset(info, 0, sizeof *info);
     info->path = pr.path;
     info->vector_bytes = pr.perm.width;
-    info->grid = static_cast<int32_t>(pr.perm.grid);
+    info->grid = static_cast<int32_t>(static_cast<uint64_t>(pr.perm.grid) * pr.perm.grid_y *
+                                      pr.perm.grid_z);
     info->block = static_cast<int32_t>(pr.perm.block);
     info->tiles = pr.perm.kernel == Kernel::Direct ? pr.perm.direct.num_tiles : pr.perm.lds.num_tiles;
     info->launches = pr.launches;
     info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
+    info->grid_dims = pr.perm.grid3d ? 3 : 1;
     return UA2A_OK;
 }
 

@@ -31,6 +31,7 @@ constexpr uint32_t kLdsUnroll = 1;              // 16-byte chunks per lane per p
 constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least contiguous read per head block
 constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
 constexpr uint32_t kDirectGroupRowAlign = 4096;
+constexpr uint32_t kMaxGridYZ = 65535;          // largest y / z grid extent used
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
@@ -41,9 +42,12 @@ enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2 };
 struct Launch {
     Kernel kernel;
     uint32_t block;      // threads per workgroup
+    uint32_t grid_y;     // 3-D grid of the direct kernel (1 otherwise)
+    uint32_t grid_z;
+    int32_t grid3d;      // direct kernel: one tile per workgroup on (grid, grid_y, grid_z)
     int32_t width;       // Direct/Copy: bytes per lane vector; Lds: LDS piece bytes G
     int32_t mode;        // Direct/Lds: 0 or 1
-    uint32_t grid;
+    uint32_t grid;       // workgroups along x
     uint32_t lds_bytes;  // dynamic LDS (Lds kernel only)
     DirectGeom direct;
     LdsGeom lds;

@@ -40,7 +40,16 @@ template <int VB, bool MODE1>
 __global__ __launch_bounds__(kDirectBlock) void ua2a_direct_kernel(DirectGeom g)
 {
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
-        direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(g, t, threadIdx.x);
+        direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
+            g, direct_tile<MODE1>(g, t), threadIdx.x);
+}
+
+// One tile per workgroup on a 3-D grid (see direct_tile_3d).
+template <int VB, bool MODE1>
+__global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom g)
+{
+    direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
+        g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
 }
 
 template <int G, bool MODE1>
@@ -75,6 +84,19 @@ const void* direct_fn(int vb)
     case 4: return reinterpret_cast<const void*>(&ua2a_direct_kernel<4, MODE1>);
     case 2: return reinterpret_cast<const void*>(&ua2a_direct_kernel<2, MODE1>);
     case 1: return reinterpret_cast<const void*>(&ua2a_direct_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
+template <bool MODE1>
+const void* direct3d_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<1, MODE1>);
     default: return nullptr;
     }
 }
@@ -127,7 +149,10 @@ int backend_launch(const Launch& L, void* stream)
     size_t shmem = 0;
     switch (L.kernel) {
     case Kernel::Direct:
-        fn = L.mode ? direct_fn<true>(L.width) : direct_fn<false>(L.width);
+        if (L.grid3d)
+            fn = L.mode ? direct3d_fn<true>(L.width) : direct3d_fn<false>(L.width);
+        else
+            fn = L.mode ? direct_fn<true>(L.width) : direct_fn<false>(L.width);
         arg = &dg;
         break;
     case Kernel::Lds:
@@ -142,7 +167,7 @@ int backend_launch(const Launch& L, void* stream)
     }
     if (fn == nullptr) return static_cast<int>(hipErrorInvalidValue);
     void* args[] = {arg};
-    const hipError_t e = hipLaunchKernel(fn, dim3(L.grid), dim3(L.block), args, shmem,
+    const hipError_t e = hipLaunchKernel(fn, dim3(L.grid, L.grid_y, L.grid_z), dim3(L.block), args, shmem,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : static_cast<int>(e);
 }
