@@ -96,6 +96,28 @@ def test_grid_cap_uses_the_flat_grid(lib):
         ua.ua2a_destroy(h)
 
 
+@pytest.mark.parametrize("shape,mode,path,blocks", [
+    ((8, 32, 2 ** 17, 8, 256, 2), 0, ua.UA2A_PATH_AUTO, 0),     # 128 GiB, 4 KiB rows: flat grouped order
+    ((8, 511, 2 ** 17, 8, 32, 2), 1, ua.UA2A_PATH_LDS, 0),      # 255 GiB through the LDS kernel
+    ((8, 32, 2 ** 17, 8, 256, 2), 1, ua.UA2A_PATH_AUTO, 2 ** 31 - 1),   # huge blocks hint
+])
+def test_huge_launches_stay_within_a_dispatch(lib, shape, mode, path, blocks):
+    """A flat launch keeps grid x block at most 2^31 work-items (a dispatch
+    packet counts them in 32 bits); the kernels loop over the other tiles."""
+    w, B, S, H, D, e = shape
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    h = ua.ua2a_plan(w, B, S, H, D, e, blocks)
+    try:
+        ua.ua2a_plan_set_path(h, path)
+        base = 1 << 44
+        info = ua.ua2a_describe(h, mode, 0, base, base + lay["tensor_bytes"])
+        assert info["grid_dims"] == 1
+        assert info["tiles"] * info["block"] > 2 ** 32          # would not fit uncapped
+        assert info["grid"] * info["block"] <= 2 ** 31
+    finally:
+        ua.ua2a_destroy(h)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ua, "_lib", None)
     monkeypatch.setattr(ua, "LIBRARY", str(tmp_path / "libua2a.so"))

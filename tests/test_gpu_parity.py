@@ -228,6 +228,45 @@ def test_large_tensor_sampled():
     plan.close()
 
 
+def test_capped_grid_at_64_gib():
+    """64 GiB per tensor with 4 KiB token rows: mode 0 runs the flat grouped
+    order with 2^26 tiles, more than one dispatch can count in lanes, so the
+    grid is capped and every workgroup loops over several tiles."""
+    w, B, S, H, D = 8, 16, 2 ** 17, 8, 64          # 8-byte elements, 512-byte runs
+    n = w * B * S * H * D
+    free, _ = torch.cuda.mem_get_info()
+    if free < 140 * 2 ** 30:
+        pytest.skip(f"needs about 130 GiB of free device memory, {free / 2 ** 30:.0f} GiB free")
+    torch.cuda.empty_cache()
+    plan = ua.Plan(w, B, S, H, D, torch.int64)
+    x = torch.empty(n, dtype=torch.int64, device=DEV)
+    step = 2 ** 27                                 # torch's own fill kernels stay small
+    for a in range(0, n, step):
+        x[a:a + step] = torch.arange(a, min(n, a + step), dtype=torch.int64, device=DEV)
+    x = x.view(w, B, S, H, D)
+    info = plan.describe(x, 0)
+    assert info["grid_dims"] == 1 and info["grid"] * info["block"] <= 2 ** 31 < info["tiles"] * 64
+    note(f"64 GiB mode 0 {info}")
+    y = plan.exchange(x, 0)
+    torch.cuda.synchronize()
+    gen = torch.Generator("cpu").manual_seed(64)
+    idx = torch.cat([torch.arange(4096), torch.randint(0, n, (200000,), generator=gen),
+                     torch.arange(n - 4096, n)])
+    got = y.view(-1)[idx.to(DEV)].cpu().numpy()
+    assert np.array_equal(got, oracle.source_indices(0, w, B, S, H, D, idx.numpy()))
+    del x
+    note("64 GiB mode 1 round trip")
+    z = plan.exchange(y, 1)
+    torch.cuda.synchronize()
+    del y
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        assert torch.equal(z.view(-1)[a:b], torch.arange(a, b, dtype=torch.int64, device=DEV)), a
+    del z
+    plan.close()
+    torch.cuda.empty_cache()
+
+
 def _random_cases(n, seed):
     """Seeded random shapes, element sizes, paths, modes and misalignments."""
     rng = np.random.default_rng(seed)

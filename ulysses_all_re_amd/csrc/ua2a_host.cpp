@@ -48,12 +48,15 @@ bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out)
     return *out <= limit;
 }
 
-// One tile per workgroup unless the caller's hint caps the grid (the
-// kernels then loop over their tiles grid-stride).
-uint32_t grid_for(uint32_t tiles, int32_t hint)
+// One tile per workgroup unless the caller's hint caps the grid, and never
+// more work-items along x than a dispatch packet counts (32 bits); a capped
+// grid's kernels loop over their tiles grid-stride.
+uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
 {
     uint64_t g = tiles;
     if (hint > 0 && static_cast<uint64_t>(hint) < g) g = static_cast<uint64_t>(hint);
+    const uint64_t cap = kMaxGridWorkItems / block;
+    if (g > cap) g = cap;
     if (g < 1) g = 1;
     return static_cast<uint32_t>(g);
 }
@@ -271,7 +274,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.block = kDirectBlock;
         L.width = static_cast<int32_t>(g);
         L.direct = make_direct(p, g, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb);
-        L.grid = grid_for(L.direct.num_tiles, p->blocks);
+        L.grid = grid_for(L.direct.num_tiles, p->blocks, kDirectBlock);
         // default order, no grid cap: one tile per workgroup on a 3-D grid
         // whose coordinates are the tile's (x = tile in slab; mode 0: y = j,
         // z = r*nb + b; mode 1: y = b, z = j), sparing each workgroup the
@@ -290,7 +293,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.width = static_cast<int32_t>(g);
         L.lds = make_lds(p, mode, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
         L.lds_bytes = L.lds.lds_bytes;
-        L.grid = grid_for(L.lds.num_tiles, p->blocks);
+        L.grid = grid_for(L.lds.num_tiles, p->blocks, kLdsBlock);
     }
     pr->launches = 1;
     if (chunked) {
@@ -305,7 +308,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         C.width = static_cast<int32_t>(vb);
         C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
-        C.grid = grid_for(C.copy.num_tiles, 0);
+        C.grid = grid_for(C.copy.num_tiles, 0, kCopyBlock);
         pr->launches = static_cast<int32_t>(2 * p->B);
     }
 }

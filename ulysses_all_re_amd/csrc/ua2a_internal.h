@@ -32,6 +32,7 @@ constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least cont
 constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
 constexpr uint32_t kDirectGroupRowAlign = 4096;
 constexpr uint32_t kMaxGridYZ = 65535;          // largest y / z grid extent used
+constexpr uint64_t kMaxGridWorkItems = (uint64_t(1) << 31);   // x extent of a launch, in lanes
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
