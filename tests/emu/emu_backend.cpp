@@ -167,6 +167,13 @@ void ua2a_emu_reset_counts(void)
 }
 
 int ua2a_emu_launches(void) { return ua2a::g_launches; }
+
+/* The kernels' magic-number division, for checking against exact division. */
+void ua2a_emu_fdiv(uint32_t d, const uint32_t* n, uint32_t* q, int count)
+{
+    const ua2a::Div32 f = ua2a::make_div32(d);
+    for (int i = 0; i < count; ++i) q[i] = ua2a::fdiv(n[i], f);
+}
 int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
 unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 

@@ -185,6 +185,29 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
     assert dst.view.tobytes() == x.tobytes()
 
 
+# ------------------------------------------------------ magic-number division
+
+def test_fdiv_matches_exact_division(emu):
+    """The kernels' multiply-high division against exact integer division."""
+    fn = emu.ua2a_emu_fdiv
+    fn.argtypes = [ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    rng = np.random.default_rng(5)
+    top = 2 ** 32 - 1
+    divisors = ([1, 2, 3, 5, 7, 10, 14, 40, 80, 96, 640, 1000, 2 ** 16 - 1, 2 ** 16, 2 ** 16 + 1,
+                 2 ** 31 - 1, 2 ** 31, 2 ** 31 + 1, top - 1, top] +
+                [1 << k for k in range(32)] + rng.integers(1, top, 300, dtype=np.uint64).tolist())
+    n = np.concatenate([np.arange(0, 4096), top - np.arange(0, 4096),
+                        rng.integers(0, top, 20000, dtype=np.uint64)]).astype(np.uint32)
+    q = np.empty_like(n)
+    for d in divisors:
+        edges = np.array([d - 1, d, d + 1, 2 * d - 1, 2 * d, (top // d) * d, (top // d) * d - 1],
+                         dtype=np.uint64)
+        nn = np.concatenate([n, np.clip(edges, 0, top).astype(np.uint32)])
+        qq = np.empty_like(nn)
+        fn(int(d), nn.ctypes.data, qq.ctypes.data, nn.size)
+        assert np.array_equal(qq, (nn.astype(np.uint64) // np.uint64(d)).astype(np.uint32)), d
+
+
 # ------------------------------------------------------------- error handling
 
 def _plan(lib, shape=(2, 2, 4, 4, 8, 2), window=None, wbytes=0, device=0):
