@@ -16,6 +16,9 @@ w rank tensors are stacked rank-major in one array,
 and elements are moved as raw bit patterns (any numpy dtype of 1, 2, 4 or 8
 bytes; bf16 travels as uint16/int16).
 
+``exchange_ranks`` runs the exchange between separate per-rank arrays,
+restricted to a range of sending ranks.
+
 ``source_indices`` gives, for chosen output positions, the input position
 each one comes from (the same definitions, one element at a time), for
 checking outputs too large to copy whole to the host.
@@ -24,7 +27,9 @@ Parity pins (tests/test_oracle_pins.py): closed-form shapes, w = 1 identity,
 mode1(mode0(x)) == x and mode0(mode1(y)) == y, chunked == unchunked,
 agreement with an all-to-all over torch.distributed's gloo backend in w
 processes, agreement with numpy reshape/transpose, hand-derived worked
-examples under tests/golden/, bijection of the element multiset.
+examples under tests/golden/, bijection of the element multiset; for the
+per-rank form, the numpy permutation masked by the source rank of every
+element, and the union of single-sender calls.
 """
 from __future__ import annotations
 
@@ -64,6 +69,8 @@ def _load():
         fn.restype = ctypes.c_int
     lib.ua2a_oracle_chunked.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp]
     lib.ua2a_oracle_chunked.restype = ctypes.c_int
+    lib.ua2a_oracle_ranks.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp, i32, i32]
+    lib.ua2a_oracle_ranks.restype = ctypes.c_int
     lib.ua2a_oracle_source_index.argtypes = [i32, i32, i64, i64, i64, i64, i64]
     lib.ua2a_oracle_source_index.restype = i64
     lib.ua2a_oracle_source_indices.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp]
@@ -116,6 +123,41 @@ def exchange(x: np.ndarray, mode: int, w: int, chunked: bool = False) -> np.ndar
     if rc != 0:
         raise OracleError(rc)
     return out
+
+
+def exchange_ranks(xs, outs, mode: int, first: int = 0, count=None) -> None:
+    """The exchange between separate per-rank arrays, in place into `outs`.
+
+    xs[k] is rank k's input without the leading rank axis (mode 0:
+    [B, S_local, H, D]; mode 1: [B, S_global, H_local, D]); only the entries of
+    the sending ranks [first, first + count) are read and the others may be
+    None.  outs[k] is rank k's output, fully given: only elements whose source
+    rank is a sender are written.
+    """
+    w = len(outs)
+    count = w - first if count is None else count
+    if len(xs) != w:
+        raise ValueError("xs and outs must both hold one entry per rank")
+    senders = [xs[k] for k in range(first, first + count)]
+    if not senders or any(x is None for x in senders):
+        raise OracleError(-1)
+    ref = senders[0]
+    if any(x.shape != ref.shape or x.dtype != ref.dtype or not x.flags.c_contiguous for x in senders):
+        raise ValueError("sender inputs must share one shape and dtype and be C-contiguous")
+    B, S_local, H, D = local_shape((w, *ref.shape), mode, w)
+    if H % w:
+        raise OracleError(-2)
+    out_shape = (B, S_local * w, H // w, D) if mode == 0 else (B, S_local, H, D)
+    for o in outs:
+        if o.shape != out_shape or o.dtype != ref.dtype or not o.flags.c_contiguous:
+            raise ValueError(f"every output must be a C-contiguous {out_shape} {ref.dtype} array")
+    vp = ctypes.c_void_p
+    in_tab = (vp * w)(*[None if x is None else x.ctypes.data for x in xs])
+    out_tab = (vp * w)(*[o.ctypes.data for o in outs])
+    rc = _load().ua2a_oracle_ranks(mode, w, B, S_local, H, D, ref.dtype.itemsize,
+                                   ctypes.cast(in_tab, vp), ctypes.cast(out_tab, vp), first, count)
+    if rc != 0:
+        raise OracleError(rc)
 
 
 def source_indices(mode: int, w: int, B: int, S_local: int, H: int, D: int,

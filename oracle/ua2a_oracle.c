@@ -139,6 +139,60 @@ int ua2a_oracle_chunked(int32_t mode, int32_t w, int64_t B, int64_t S_local,
     return rc;
 }
 
+/* Per-rank allocations, restricted to the runs that ranks [first,
+ * first+count) send.  in[k] and out[k] are the separate tensors of rank k
+ * (the rank-stacked layouts above without the leading w); in[] is indexed by
+ * the sending rank (mode 0: token owner j, mode 1: head-block owner r), out[]
+ * by the receiving rank.  Only senders' inputs are read (other entries may be
+ * NULL); output elements whose source rank lies outside the range are left
+ * untouched.  Same page and method as the unrestricted exchange, read for a
+ * device communicator whose ranks each own their buffers; (0, w) is the
+ * whole exchange. */
+int ua2a_oracle_ranks(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64_t H,
+                      int64_t D, int32_t elem_bytes, const void* const* in, void* const* out,
+                      int32_t first, int32_t count)
+{
+    if (in == NULL || out == NULL) return -1;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return -1;
+    if (mode != 0 && mode != 1) return -1;
+    if (w < 1 || B < 1 || S_local < 1 || H < 1 || D < 1 || H % w != 0) return -2;
+    if (first < 0 || count < 1 || first + count > w) return -1;
+    for (int32_t k = first; k < first + count; ++k)
+        if (in[k] == NULL) return -1;
+    for (int32_t k = 0; k < w; ++k)
+        if (out[k] == NULL) return -1;
+    const int64_t Hl = H / w;
+    const int64_t S_global = S_local * w;
+    const size_t e = (size_t)elem_bytes;
+
+    if (mode == 0) {
+        for (int64_t r = 0; r < w; ++r)                          /* receiving rank */
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t j = first; j < first + count; ++j)  /* sending rank */
+                    for (int64_t s = 0; s < S_local; ++s)
+                        for (int64_t h = 0; h < Hl; ++h)
+                            for (int64_t d = 0; d < D; ++d) {
+                                int64_t si = ((b * S_local + s) * H + (r * Hl + h)) * D + d;
+                                int64_t di = ((b * S_global + (j * S_local + s)) * Hl + h) * D + d;
+                                memcpy((unsigned char*)out[r] + (size_t)di * e,
+                                       (const unsigned char*)in[j] + (size_t)si * e, e);
+                            }
+    } else {
+        for (int64_t j = 0; j < w; ++j)                          /* receiving rank */
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t s = 0; s < S_local; ++s)
+                    for (int64_t r = first; r < first + count; ++r)   /* sending rank */
+                        for (int64_t h = 0; h < Hl; ++h)
+                            for (int64_t d = 0; d < D; ++d) {
+                                int64_t si = ((b * S_global + (j * S_local + s)) * Hl + h) * D + d;
+                                int64_t di = ((b * S_local + s) * H + (r * Hl + h)) * D + d;
+                                memcpy((unsigned char*)out[j] + (size_t)di * e,
+                                       (const unsigned char*)in[r] + (size_t)si * e, e);
+                            }
+    }
+    return 0;
+}
+
 /* Flat position in the rank-stacked input of the element that the exchange
  * (mode 0 or 1) writes at flat position out_index of the output: the
  * definitions above, for one element at a time (used to check outputs too

@@ -339,3 +339,64 @@ def test_source_index_rejects_out_of_range():
     assert oracle.raw_call("ua2a_oracle_source_index", 0, 2, 1, 8, 3, 16, 0) == -1
     with pytest.raises(oracle.OracleError):
         oracle.source_indices(0, 2, 1, 8, 4, 16, np.array([5000], dtype=np.int64))
+
+
+# ------------------------------------------------- per-rank allocations
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ranks_sender_ranges_match_masked_numpy(shape, mode):
+    """Per-rank form, every sender range: an output element holds the numpy
+    permutation's value when the rank it comes from is a sender, else its
+    fill is untouched.  Index-valued inputs name each element's source rank
+    (value // elements per rank); non-senders' inputs are passed as None."""
+    w, B, S, H, D = shape
+    n = w * B * S * H * D
+    in_shape = shape if mode == 0 else mode1_shape(*shape)
+    x = np.arange(n, dtype=np.int64).reshape(in_shape)
+    full = numpy_mode0(x, w) if mode == 0 else numpy_mode1(x, w)
+    src_rank = full // (n // w)
+    for first in range(w):
+        for count in range(1, w - first + 1):
+            xs = [x[k].copy() if first <= k < first + count else None for k in range(w)]
+            outs = [np.full(full.shape[1:], -1, np.int64) for _ in range(w)]
+            oracle.exchange_ranks(xs, outs, mode, first, count)
+            sel = (src_rank >= first) & (src_rank < first + count)
+            assert np.array_equal(np.stack(outs), np.where(sel, full, -1)), (first, count)
+
+
+@pytest.mark.parametrize("itemsize", [1, 2, 4, 8])
+@pytest.mark.parametrize("shape", SHAPES + [s[:5] for s in TAIL_SHAPES])
+def test_ranks_single_senders_compose_the_whole_exchange(shape, itemsize):
+    """One call per sending rank, each writing only its own runs, together
+    give the numpy permutation (random bits, every dtype size)."""
+    w = shape[0]
+    for mode, in_shape in ((0, shape), (1, mode1_shape(*shape))):
+        x = rand_bits(in_shape, itemsize, 8 + mode)
+        full = numpy_mode0(x, w) if mode == 0 else numpy_mode1(x, w)
+        outs = [np.zeros(full.shape[1:], x.dtype) for _ in range(w)]
+        for j in range(w):
+            oracle.exchange_ranks([x[k].copy() for k in range(w)], outs, mode, j, 1)
+        assert np.array_equal(np.stack(outs), full)
+
+
+def test_ranks_argument_errors():
+    w = 2
+    x = [np.zeros((1, 2, 4, 3), np.int16) for _ in range(w)]
+    o = [np.zeros((1, 4, 2, 3), np.int16) for _ in range(w)]
+    oracle.exchange_ranks(x, o, 0, 0, 2)
+    vp = ctypes.c_void_p
+    ins = (vp * 2)(x[0].ctypes.data, x[1].ctypes.data)
+    outs = (vp * 2)(o[0].ctypes.data, o[1].ctypes.data)
+    nulls = (vp * 2)(None, None)
+    f = "ua2a_oracle_ranks"
+    i, q = ctypes.cast(ins, vp), ctypes.cast(outs, vp)
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, q, 0, 2) == 0
+    assert oracle.raw_call(f, 2, 2, 1, 2, 4, 3, 2, i, q, 0, 2) == -1     # mode
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 3, i, q, 0, 2) == -1     # elem_bytes
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, q, 1, 2) == -1     # first + count > w
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, q, 0, 0) == -1     # count < 1
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, ctypes.cast(nulls, vp), q, 0, 1) == -1   # sender NULL
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, ctypes.cast(nulls, vp), 0, 1) == -1   # output NULL
+    assert oracle.raw_call(f, 0, 2, 1, 2, 3, 3, 2, i, q, 0, 2) == -2     # H % w
+    assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, None, q, 0, 2) == -1  # no table
