@@ -120,26 +120,54 @@ def run(args):
     plan = ua.Plan(w, B, S, H, D, dt, blocks=args.blocks, window=window, device=dev)
     plan.set_path({"auto": ua.UA2A_PATH_AUTO, "direct": ua.UA2A_PATH_DIRECT,
                    "lds": ua.UA2A_PATH_LDS}[args.path])
-    y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
-    z = torch.empty(plan.out_shape(1), dtype=dt, device=dev)
-    info0 = plan.describe(x, 0, chunked, out=y)
-    info1 = plan.describe(y, 1, chunked, out=z)
-    log(f"mode 0 launch {info0}")
-    log(f"mode 1 launch {info1}")
     stream = torch.cuda.current_stream(dev)
     bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[e]
 
-    def ex0():
-        plan.exchange(x, 0, chunked, out=y, stream=stream)
+    def round_trip_bits():
+        if args.ranks is None:
+            return z.view(bits)
+        return torch.stack([t.view(bits) for t in zs])
 
-    def ex1():
-        plan.exchange(y, 1, chunked, out=z, stream=stream)
+    if args.ranks is None:
+        y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
+        z = torch.empty(plan.out_shape(1), dtype=dt, device=dev)
+        info0 = plan.describe(x, 0, chunked, out=y)
+        info1 = plan.describe(y, 1, chunked, out=z)
+
+        def ex0():
+            plan.exchange(x, 0, chunked, out=y, stream=stream)
+
+        def ex1():
+            plan.exchange(y, 1, chunked, out=z, stream=stream)
+    else:
+        # per-rank allocations: every rank's tensors are allocations of their own
+        if chunked:
+            raise SystemExit("--ranks has no chunked form")
+        xs = [x[k].clone() for k in range(w)]
+        ys = [torch.empty(plan.out_shape(0)[1:], dtype=dt, device=dev) for _ in range(w)]
+        zs = [torch.empty(plan.out_shape(1)[1:], dtype=dt, device=dev) for _ in range(w)]
+        senders = [(0, w)] if args.ranks == "all" else [(j, 1) for j in range(w)]
+        calls0 = [plan.bind_ranks(xs, 0, ys, f, n, stream) for f, n in senders]
+        calls1 = [plan.bind_ranks(ys, 1, zs, f, n, stream) for f, n in senders]
+        info0 = plan.describe_ranks(xs, ys, 0, *senders[0])
+        info1 = plan.describe_ranks(ys, zs, 1, *senders[0])
+        info0["launches"] = info1["launches"] = len(senders)
+
+        def ex0():
+            for call in calls0:
+                call()
+
+        def ex1():
+            for call in calls1:
+                call()
+    log(f"mode 0 launch {info0}")
+    log(f"mode 1 launch {info1}")
 
     for _ in range(args.warmup):
         ex0()
         ex1()
     torch.cuda.synchronize(dev)
-    if not torch.equal(z.view(bits), x.view(bits)):
+    if not torch.equal(round_trip_bits(), x.view(bits)):
         raise SystemExit("round trip did not return the input; refusing to report a number")
     log(f"warmup done ({args.warmup} steps), round trip bit-exact")
 
@@ -160,6 +188,8 @@ def run(args):
         ex0()
         ex1()
 
+    if args.graph and args.ranks is not None:
+        raise SystemExit("--graph times the rank-stacked exchange only")
     if args.graph:
         # one step captured once as a HIP graph; the timed region replays it
         side = torch.cuda.Stream(dev)
@@ -200,16 +230,21 @@ def run(args):
 
     value = 2 * moved * K / (total_ms * 1e-3) / 1e9
     traffic = load_traffic() if (name == WORKLOAD and not chunked and args.path == "auto") else None
+    if args.ranks is not None:
+        traffic = None
     dom_mode, dom_avg = (0, avg0) if avg0 >= avg1 else (1, avg1)
     dom_info = info0 if dom_mode == 0 else info1
-    if dom_info["path"] == ua.UA2A_PATH_DIRECT:
+    if args.ranks is not None:
+        kname = "ua2a_ranks_kernel"
+    elif dom_info["path"] == ua.UA2A_PATH_DIRECT:
         kname = "ua2a_direct3d_kernel" if dom_info["grid_dims"] == 3 else "ua2a_direct_kernel"
     else:
         kname = "ua2a_lds_kernel"
     roofline = {
         "bound": "hbm",
         "kernel": f"{kname}<{dom_info['vector_bytes']}, mode {dom_mode}>"
-                  + (" + ua2a_copy_kernel, per plane" if chunked else ""),
+                  + (" + ua2a_copy_kernel, per plane" if chunked else "")
+                  + (f", {w} launches of one sender each" if args.ranks == "one" else ""),
         "achieved": round(gbps(dom_avg), 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
@@ -241,6 +276,7 @@ def run(args):
         "config": {"workload": name, "w": w, "B": B, "S_local": S, "S_global": S * w,
                    "H": H, "D": D, "elem": c["dtype"], "run_bytes": lay["run_bytes"],
                    "chunked": chunked, "path": args.path, "graph": bool(args.graph),
+                   "ranks": args.ranks,
                    "step": "mode 0 then mode 1",
                    "bytes_per_step": 2 * moved,
                    "cache_resident": lay["tensor_bytes"] * 2 <= 256 * 2 ** 20},
@@ -361,6 +397,10 @@ def main():
     ap.add_argument("--chunked", action="store_true", help="time the chunked (per-plane window) path")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph and time its replays")
+    ap.add_argument("--ranks", choices=("all", "one"), default=None,
+                    help="per-rank allocations (ua2a_exchange_ranks): one launch with every "
+                         "sender, or one launch per sender (what each device of a multi-device "
+                         "exchange runs)")
     ap.add_argument("--path", choices=("auto", "direct", "lds"), default="auto",
                     help="force a kernel family (default: the library's choice)")
     ap.add_argument("--cpu-steps", type=int, default=12,

@@ -25,7 +25,8 @@
  * Conventions for every function below:
  *   - return 0 (UA2A_OK) or a negative UA2A_ERR_* code; nothing throws;
  *   - no function synchronises the host with the device;
- *   - ua2a_exchange allocates nothing and launches only on the given stream;
+ *   - ua2a_exchange and ua2a_exchange_ranks allocate nothing and launch
+ *     only on the given stream;
  *   - pointers named in/out/window are device pointers on the plan's
  *     device, owned by the caller, and are only borrowed by the library.
  */
@@ -84,7 +85,7 @@ typedef struct ua2a_launch_info_s {
     int64_t tiles;         /* work tiles per launch */
     int32_t launches;      /* kernel launches per exchange (2*B when chunked: B permutes + B copies) */
     int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
-    int32_t grid_dims;     /* 3: direct path, one tile per workgroup on a 3-D grid; else 1 */
+    int32_t grid_dims;     /* 3: a 3-D grid (direct path by default, every per-rank launch); else 1 */
 } ua2a_launch_info_t;
 
 /*
@@ -145,6 +146,40 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked,
                   const void* in, void* out, void* stream);
 
 /*
+ * ua2a_exchange_ranks: the same exchange when each rank's tensors are
+ * allocations of their own, as when every rank of the page's device
+ * communicator owns its buffers and its registered window (FastVideo
+ * "ulysses_a2a" API page: run_armed, and close for the per-rank windows),
+ * optionally restricted to the runs that a range of ranks SENDS.
+ *   in_ptrs   host array of w device pointers, indexed by sending rank:
+ *             mode 0: in_ptrs[j] -> x_j [B][S_local][H][D];
+ *             mode 1: in_ptrs[r] -> y_r [B][S_local*w][H/w][D].
+ *             Only entries first .. first+count-1 are read (others may be NULL).
+ *   out_ptrs  host array of w device pointers, indexed by receiving rank,
+ *             all used: mode 0: out_ptrs[r] -> [B][S_local*w][H/w][D];
+ *             mode 1: out_ptrs[j] -> [B][S_local][H][D].
+ *   first, count  sending ranks [first, first + count), 0 <= first,
+ *             1 <= count, first + count <= w.  Only runs from those senders
+ *             are written: mode 0, the token block [j*S_local, (j+1)*S_local)
+ *             of every out_ptrs[r] for each sender j; mode 1, the head block
+ *             [r*H/w, (r+1)*H/w) of every token of every out_ptrs[j] for each
+ *             sender r.  Every other output byte is left as it was.  (0, w)
+ *             is the whole exchange; (j, 1) is the part that rank j pushes
+ *             to its peers in a multi-device exchange.
+ * The tables are read during the call only (copied into the launch); the
+ * tensors are borrowed as in ua2a_exchange.  Each used pointer must be
+ * elem_bytes-aligned; outputs may overlap neither each other nor a used
+ * input.  One launch of the direct kernel scheme (never the LDS path; the
+ * plan's window and chunked mode do not apply).  w <= 64 (the tables travel
+ * in the kernel argument).
+ * Errors: INVALID_ARG (NULL table or used entry, mode, first/count out of
+ * range), SHAPE (w > 64), ALIGN, ALIAS, DEVICE (no state change); HIP
+ * (the plan becomes disabled); DISABLED.
+ */
+int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
+                        void* const* out_ptrs, int32_t first, int32_t count, void* stream);
+
+/*
  * ua2a_destroy: release the plan object.  It always consumes the plan, also
  * a disabled one, and never touches the window or device memory (the page's
  * disposer likewise consumes its handle even when cleanup reports an error).
@@ -176,6 +211,15 @@ int ua2a_plan_set_path(ua2a_plan_t plan, int32_t path);
  */
 int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked,
                   const void* in, const void* out, ua2a_launch_info_t* info);
+
+/*
+ * ua2a_describe_ranks: as ua2a_describe, for ua2a_exchange_ranks with the
+ * same arguments (same checks; host only, pointers never dereferenced).
+ * info->tiles counts the launch's work tiles, grid its workgroups.
+ */
+int ua2a_describe_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
+                        void* const* out_ptrs, int32_t first, int32_t count,
+                        ua2a_launch_info_t* info);
 
 #ifdef __cplusplus
 }

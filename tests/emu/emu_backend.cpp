@@ -20,7 +20,7 @@ namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[3] = {0, 0, 0};
+int g_kernel_counts[4] = {0, 0, 0, 0};
 uint32_t g_last_grid = 0;
 
 template <int VB, bool M1>
@@ -67,6 +67,37 @@ void run_copy(const CopyGeom& g)
     for (uint32_t t = 0; t < g.num_tiles; ++t)
         for (uint32_t tid = 0; tid < kCopyBlock; ++tid)
             copy_tile_body<PlainMem, VB, kCopyBlock, kDirectUnroll>(g, t, tid);
+}
+
+// Every workgroup of the launch's grid runs the kernel's loops over the
+// slab grid exactly as on the device.
+template <int VB, bool M1, bool TWO>
+void run_ranks(const Launch& L)
+{
+    const RanksGeom& g = L.ranks;
+    for (uint32_t bz = 0; bz < L.grid_z; ++bz)
+        for (uint32_t by = 0; by < L.grid_y; ++by)
+            for (uint32_t bx = 0; bx < L.grid; ++bx)
+                for (uint32_t z = bz; z < g.nz; z += L.grid_z)
+                    for (uint32_t y = by; y < g.ny; y += L.grid_y)
+                        for (uint32_t x = bx; x < g.tiles_per_slab; x += L.grid) {
+                            const RanksTile d = ranks_tile<M1, TWO>(g, x, y, z);
+                            for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+                                ranks_tile_body<PlainMem, VB, M1, TWO, kDirectBlock>(g, d, tid);
+                        }
+}
+
+template <bool M1, bool TWO>
+int dispatch_ranks(const Launch& L, int vb)
+{
+    switch (vb) {
+    case 16: run_ranks<16, M1, TWO>(L); return 0;
+    case 8: run_ranks<8, M1, TWO>(L); return 0;
+    case 4: run_ranks<4, M1, TWO>(L); return 0;
+    case 2: run_ranks<2, M1, TWO>(L); return 0;
+    case 1: run_ranks<1, M1, TWO>(L); return 0;
+    default: return 1;
+    }
 }
 
 template <bool M1>
@@ -127,8 +158,8 @@ int backend_launch(const Launch& L, void*)
     ++g_kernel_counts[static_cast<int>(L.kernel)];
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
-    const uint32_t want_block = L.kernel == Kernel::Direct ? kDirectBlock
-                              : L.kernel == Kernel::Lds ? kLdsBlock : kCopyBlock;
+    const uint32_t want_block = L.kernel == Kernel::Lds ? kLdsBlock
+                              : L.kernel == Kernel::Copy ? kCopyBlock : kDirectBlock;
     if (L.block != want_block) return 5;
     switch (L.kernel) {
     case Kernel::Direct:
@@ -149,6 +180,14 @@ int backend_launch(const Launch& L, void*)
         return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);
     case Kernel::Copy:
         return dispatch_copy(L.copy, L.width);
+    case Kernel::Ranks:
+        // the hardware's limits on a dispatch's extents
+        if (L.grid_y < 1 || L.grid_z < 1 || L.grid_y > 65535 || L.grid_z > 65535 ||
+            static_cast<uint64_t>(L.grid) * L.block > (uint64_t(1) << 31))
+            return 8;
+        if (!L.mode) return dispatch_ranks<false, false>(L, L.width);
+        return L.ranks.two_runs ? dispatch_ranks<true, true>(L, L.width)
+                                : dispatch_ranks<true, false>(L, L.width);
     }
     return 4;
 }
@@ -163,10 +202,12 @@ void ua2a_emu_set_device(int device) { ua2a::g_device = device; }
 void ua2a_emu_reset_counts(void)
 {
     ua2a::g_launches = 0;
-    ua2a::g_kernel_counts[0] = ua2a::g_kernel_counts[1] = ua2a::g_kernel_counts[2] = 0;
+    for (int& c : ua2a::g_kernel_counts) c = 0;
 }
 
 int ua2a_emu_launches(void) { return ua2a::g_launches; }
+int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
+unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 
 /* The kernels' magic-number division, for checking against exact division. */
 void ua2a_emu_fdiv(uint32_t d, const uint32_t* n, uint32_t* q, int count)
@@ -174,7 +215,5 @@ void ua2a_emu_fdiv(uint32_t d, const uint32_t* n, uint32_t* q, int count)
     const ua2a::Div32 f = ua2a::make_div32(d);
     for (int i = 0; i < count; ++i) q[i] = ua2a::fdiv(n[i], f);
 }
-int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
-unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 
 }  // extern "C"

@@ -1,0 +1,228 @@
+"""GPU parity of the per-rank exchange (ua2a_exchange_ranks) against the CPU oracle.
+
+Each rank's input and output is a tensor of its own (a separate device
+allocation); outputs start poisoned so that the runs of non-sending ranks
+can be checked to stay untouched.  Byte-for-byte comparisons throughout.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ulysses_all_re_amd as ua
+from workloads import BITS_VIEW, CONFIGS, TAIL_SHAPES, make_tensor
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32,
+          "f64": torch.float64, "u8": torch.uint8}
+
+
+def note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ua.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def bits(t):
+    return t.view(BITS_VIEW[t.element_size()])
+
+
+def poison_bits(dtype):
+    return 255 if torch.empty((), dtype=dtype).element_size() == 1 else -1
+
+
+def stacked_shapes(w, B, S, H, D, mode):
+    a, b = (w, B, S, H, D), (w, B, S * w, H // w, D)
+    return (a, b) if mode == 0 else (b, a)
+
+
+def run_case(plan, x_stacked, mode, first, count, offsets=None):
+    """Per-rank exchange of the ranks of `x_stacked` (CPU) on the device;
+    returns (device outputs as CPU bit tensors, oracle outputs)."""
+    w = plan.w
+    dt = x_stacked.dtype
+    ish, osh = stacked_shapes(plan.w, plan.B, plan.S_local, plan.H, plan.D, mode)
+    pb = poison_bits(dt)
+    if offsets is None:
+        xs = [x_stacked[k].to(DEV) if first <= k < first + count else None for k in range(w)]
+        outs = []
+        for _ in range(w):
+            o = torch.empty(osh[1:], dtype=dt, device=DEV)
+            bits(o).fill_(pb)
+            outs.append(o)
+    else:
+        # every rank's tensors at its own element offset inside a larger allocation
+        n = int(np.prod(ish[1:]))
+        xs, outs = [], []
+        for k in range(w):
+            oi, oo = offsets[k]
+            if first <= k < first + count:
+                buf = torch.empty(n + oi, dtype=dt, device=DEV)
+                buf[oi:].copy_(x_stacked[k].reshape(-1).to(DEV))
+                xs.append(buf[oi:].view(ish[1:]))
+            else:
+                xs.append(None)
+            ob = torch.empty(n + oo, dtype=dt, device=DEV)
+            bits(ob).fill_(pb)
+            outs.append(ob[oo:].view(osh[1:]))
+    plan.exchange_ranks(xs, mode, outs=outs, first=first, count=count)
+    torch.cuda.synchronize()
+    got = [bits(o.cpu()) for o in outs]
+    xb = bits(x_stacked).numpy()
+    want = [np.full(osh[1:], pb, dtype=xb.dtype) for _ in range(w)]
+    oracle.exchange_ranks([xb[k] if first <= k < first + count else None for k in range(w)],
+                          want, mode, first, count)
+    return got, [torch.from_numpy(a) for a in want]
+
+
+def assert_ranks_equal(got, want, what):
+    for k, (g, t) in enumerate(zip(got, want)):
+        if not torch.equal(g, t):
+            bad = (g != t).nonzero()
+            raise AssertionError(f"{what}: rank {k}: {bad.shape[0]} elements differ; first at {bad[0].tolist()}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "video_dit", "chunked", "awkward"])
+def test_workload_ranks_parity(name):
+    """Each workload, both modes: the whole exchange (all senders), the first
+    and last sender alone, and every sender one call at a time."""
+    c = CONFIGS[name]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dt = DTYPES[c["dtype"]]
+    plan = ua.Plan(w, B, S, H, D, dt)
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        dist = c["dist"] if (c["dist"] != "index" or mode == 0) else "index_bits"
+        x = make_tensor(ish, c["dtype"], dist, c["seed0"] if mode == 0 else c["seed1"])
+        for first, count in ((0, w), (0, 1), (w - 1, 1)):
+            note(f"ranks {name} mode{mode} senders=[{first},{first + count}) shape={tuple(ish)}")
+            got, want = run_case(plan, x, mode, first, count)
+            assert_ranks_equal(got, want, f"{name} mode {mode} senders [{first}, {first + count})")
+        # one call per sender into the same outputs gives the whole exchange
+        note(f"ranks {name} mode{mode} composed from single senders")
+        _, osh = stacked_shapes(w, B, S, H, D, mode)
+        xs = [x[k].to(DEV) for k in range(w)]
+        outs = [torch.zeros(osh[1:], dtype=dt, device=DEV) for _ in range(w)]
+        for j in range(w):
+            plan.exchange_ranks(xs, mode, outs=outs, first=j, count=1)
+        whole = plan.exchange_ranks(xs, mode)
+        torch.cuda.synchronize()
+        for k in range(w):
+            assert torch.equal(bits(outs[k]), bits(whole[k])), (name, mode, k)
+        del xs, outs, whole
+    plan.close()
+
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_ranks_tail_shapes(shape):
+    w, B, S, H, D, dname = shape
+    dt = DTYPES[dname]
+    plan = ua.Plan(w, B, S, H, D, dt)
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        x = make_tensor(ish, dname, "bytes", 11 + mode)
+        for first, count in ((0, w), (w - 1, 1)):
+            note(f"ranks tail {shape} mode{mode} senders=[{first},{first + count})")
+            got, want = run_case(plan, x, mode, first, count)
+            assert_ranks_equal(got, want, f"tail {shape} mode {mode}")
+    plan.close()
+
+
+@pytest.mark.parametrize("shape", [(4, 1, 1024, 24, 128, "bf16"), (3, 1, 5, 3, 7, "bf16"),
+                                   (8, 1, 300, 40, 128, "bf16"), (2, 2, 9, 6, 5, "fp32")],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ranks_misaligned_bases(shape):
+    """Per-rank tensors at different element offsets from their allocations."""
+    w, B, S, H, D, dname = shape
+    dt = DTYPES[dname]
+    plan = ua.Plan(w, B, S, H, D, dt)
+    offsets = [((k % 3) + 1, (2 * k + 1) % 5) for k in range(w)]
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        x = make_tensor(ish, dname, "bytes", 21 + mode)
+        note(f"ranks misaligned {shape} mode{mode}")
+        got, want = run_case(plan, x, mode, 0, w, offsets)
+        assert_ranks_equal(got, want, f"misaligned {shape} mode {mode}")
+    plan.close()
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        w = int(rng.integers(1, 17))
+        hl = int(rng.integers(1, 6))
+        D = int(rng.choice([1, 3, 8, 16, 40, 64, 80, 128, 129]))
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(1, 700))
+        dname = str(rng.choice(["bf16", "fp32", "u8", "f64"]))
+        mode = int(rng.integers(0, 2))
+        first = int(rng.integers(0, w))
+        count = int(rng.integers(1, w - first + 1))
+        cases.append((w, B, S, w * hl, D, dname, mode, first, count))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(30, 77), ids=lambda c: "x".join(map(str, c)))
+def test_ranks_random_cases(case):
+    w, B, S, H, D, dname, mode, first, count = case
+    dt = DTYPES[dname]
+    plan = ua.Plan(w, B, S, H, D, dt)
+    ish, _ = stacked_shapes(w, B, S, H, D, mode)
+    x = make_tensor(ish, dname, "bytes", sum(case[:5]))
+    note(f"ranks random {case}")
+    got, want = run_case(plan, x, mode, first, count)
+    assert_ranks_equal(got, want, f"random {case}")
+    plan.close()
+
+
+def test_ranks_largest_table():
+    w = 64
+    plan = ua.Plan(w, 1, 33, 64, 16, torch.bfloat16)
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, 1, 33, 64, 16, mode)
+        x = make_tensor(ish, "bf16", "bytes", 31 + mode)
+        for first, count in ((0, 64), (40, 9)):
+            note(f"ranks w=64 mode{mode} senders=[{first},{first + count})")
+            got, want = run_case(plan, x, mode, first, count)
+            assert_ranks_equal(got, want, f"w=64 mode {mode}")
+    plan.close()
+
+
+def test_ranks_argument_checks_on_device_tensors():
+    plan = ua.Plan(2, 1, 8, 4, 16, torch.bfloat16)
+    xs = [torch.zeros(1, 8, 4, 16, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    with pytest.raises(TypeError):
+        plan.exchange_ranks([x.float() for x in xs], 0)
+    with pytest.raises(ValueError):
+        plan.exchange_ranks(xs[:1], 0)
+    with pytest.raises(ValueError):
+        plan.exchange_ranks([xs[0], None], 0)
+    with pytest.raises(ValueError):
+        plan.exchange_ranks(xs, 0, first=1, count=2)
+    outs = [torch.empty(1, 16, 2, 16, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    with pytest.raises(ua.UA2AError) as e:
+        plan.exchange_ranks(xs, 0, outs=[outs[0], outs[0]])
+    assert e.value.code == ua.UA2A_ERR_ALIAS
+    with pytest.raises(ua.UA2AError) as e:
+        plan.exchange_ranks(xs, 0, outs=[outs[0], xs[1].view(1, 16, 2, 16)])
+    assert e.value.code == ua.UA2A_ERR_ALIAS
+    # a non-sender's input is neither read nor checked
+    plan.exchange_ranks([xs[0], None], 0, outs=outs, first=0, count=1)
+    torch.cuda.synchronize()
+    plan.close()

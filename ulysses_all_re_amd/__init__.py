@@ -4,9 +4,10 @@ Argument marshalling only: every byte of the exchange is moved by the HIP
 kernels in libua2a.so.  PyTorch is used for device memory and streams.
 
 The functions mirror the C ABI of include/ua2a.h one to one
-(``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``, ``ua2a_destroy``,
-``ua2a_status_string``, ``ua2a_plan_last_error``, ``ua2a_plan_set_path``,
-``ua2a_describe``) and raise :class:`UA2AError` on a non-zero status.
+(``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``, ``ua2a_exchange_ranks``,
+``ua2a_destroy``, ``ua2a_status_string``, ``ua2a_plan_last_error``,
+``ua2a_plan_set_path``, ``ua2a_describe``, ``ua2a_describe_ranks``) and raise
+:class:`UA2AError` on a non-zero status.
 :class:`Plan` wraps them for torch tensors laid out rank-stacked:
 
     mode 0 input  [w, B, S_local, H, D]        -> output [w, B, S_local*w, H//w, D]
@@ -15,6 +16,9 @@ The functions mirror the C ABI of include/ua2a.h one to one
 (FastVideo ``ulysses_a2a`` API page, method ``run_armed``: mode 0 scatters
 heads and gathers the sequence, mode 1 is its inverse, chunked runs the same
 exchange one batch plane at a time through a window sized for one plane.)
+``Plan.exchange_ranks`` runs it between per-rank tensors (one allocation
+each, the ranks' shapes without the leading w), optionally only for the runs
+a range of ranks sends.
 """
 from __future__ import annotations
 
@@ -41,9 +45,12 @@ UA2A_PATH_LDS = 2
 
 # every symbol include/ua2a.h declares
 EXPORTED = (
-    "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_destroy", "ua2a_status_string",
-    "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
+    "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_ranks", "ua2a_destroy",
+    "ua2a_status_string", "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
+    "ua2a_describe_ranks",
 )
+
+MAX_RANK_TABLE = 64     # largest w that ua2a_exchange_ranks accepts
 
 
 class ua2a_layout_t(ctypes.Structure):
@@ -98,6 +105,9 @@ def declare_signatures(lib: ctypes.CDLL) -> ctypes.CDLL:
         "ua2a_plan_last_error": ([vp], ctypes.c_char_p),
         "ua2a_plan_set_path": ([vp, i32], ctypes.c_int),
         "ua2a_describe": ([vp, i32, i32, vp, vp, ctypes.POINTER(ua2a_launch_info_t)], ctypes.c_int),
+        "ua2a_exchange_ranks": ([vp, i32, vp, vp, i32, i32, vp], ctypes.c_int),
+        "ua2a_describe_ranks": ([vp, i32, vp, vp, i32, i32, ctypes.POINTER(ua2a_launch_info_t)],
+                                ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(lib, name)
@@ -140,6 +150,32 @@ def ua2a_exchange(plan: int, mode: int, chunked: int, inp: int, out: int, stream
     rc = load_library().ua2a_exchange(plan, mode, chunked, inp or None, out or None, stream or None)
     if rc != UA2A_OK:
         raise UA2AError(rc, "ua2a_exchange", ua2a_plan_last_error(plan) if plan else "")
+
+
+def _table(ptrs):
+    """A C array of device pointers (None or 0 for an unused entry)."""
+    return (ctypes.c_void_p * len(ptrs))(*[p or None for p in ptrs])
+
+
+def ua2a_exchange_ranks(plan: int, mode: int, in_ptrs, out_ptrs, first: int, count: int,
+                        stream: int = 0) -> None:
+    """Enqueue the exchange between per-rank allocations (lists of raw device
+    pointers, indexed by sending / receiving rank) for senders [first, first+count)."""
+    rc = load_library().ua2a_exchange_ranks(plan, mode, _table(in_ptrs) if in_ptrs is not None else None,
+                                            _table(out_ptrs) if out_ptrs is not None else None,
+                                            first, count, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_exchange_ranks", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_describe_ranks(plan: int, mode: int, in_ptrs, out_ptrs, first: int, count: int) -> dict:
+    info = ua2a_launch_info_t()
+    rc = load_library().ua2a_describe_ranks(plan, mode, _table(in_ptrs) if in_ptrs is not None else None,
+                                            _table(out_ptrs) if out_ptrs is not None else None,
+                                            first, count, ctypes.byref(info))
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_describe_ranks")
+    return {name: getattr(info, name) for name, _ in ua2a_launch_info_t._fields_}
 
 
 def ua2a_destroy(plan: int) -> None:
@@ -224,6 +260,76 @@ class Plan:
                 ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
                               stream.cuda_stream)
         return out
+
+    def _check_ranks(self, xs, outs, mode: int, first: int, count: int) -> None:
+        w = self.w
+        if len(xs) != w:
+            raise ValueError(f"xs needs one entry per rank ({w}), got {len(xs)}")
+        if not (0 <= first and 1 <= count and first + count <= w):
+            raise ValueError(f"sender range [{first}, {first + count}) is not within [0, {w})")
+        for k in range(first, first + count):
+            if xs[k] is None:
+                raise ValueError(f"sending rank {k} has no input")
+            self._check(xs[k], self.in_shape(mode)[1:], f"input of rank {k}")
+        if len(outs) != w:
+            raise ValueError(f"outs needs one entry per rank ({w}), got {len(outs)}")
+        for k, o in enumerate(outs):
+            self._check(o, self.out_shape(mode)[1:], f"output of rank {k}")
+
+    def exchange_ranks(self, xs, mode: int, outs=None, first: int = 0, count=None, stream=None):
+        """Exchange between per-rank tensors: xs[k] is rank k's input (the
+        rank-stacked shape without its leading w), indexed by sending rank;
+        only xs[first : first+count] are read and the other entries may be
+        None.  Returns outs (allocated with torch.empty when None), indexed by
+        receiving rank; only the runs from the senders are written."""
+        import torch
+        count = self.w - first if count is None else count
+        if outs is None:
+            outs = [torch.empty(self.out_shape(mode)[1:], dtype=self.dtype, device=self.device)
+                    for _ in range(self.w)]
+        self._check_ranks(xs, outs, mode, first, count)
+        in_ptrs = [None if x is None else x.data_ptr() for x in xs]
+        out_ptrs = [o.data_ptr() for o in outs]
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        if torch.cuda.current_device() == self.device.index:
+            ua2a_exchange_ranks(self.handle, mode, in_ptrs, out_ptrs, first, count, stream.cuda_stream)
+        else:
+            with torch.cuda.device(self.device):
+                ua2a_exchange_ranks(self.handle, mode, in_ptrs, out_ptrs, first, count,
+                                    stream.cuda_stream)
+        return outs
+
+    def bind_ranks(self, xs, mode: int, outs, first: int = 0, count=None, stream=None):
+        """Check a per-rank call once (nothing is launched) and return a
+        no-argument function that issues it on the current device -- the same
+        tensors, senders and stream every time -- for loops where per-call
+        checks would cost more than the launch.  The function keeps the
+        tensors alive."""
+        import torch
+        count = self.w - first if count is None else count
+        self._check_ranks(xs, outs, mode, first, count)
+        self.describe_ranks(xs, outs, mode, first, count)     # the library's own checks
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        lib = load_library()
+        in_tab = _table([None if x is None else x.data_ptr() for x in xs])
+        out_tab = _table([o.data_ptr() for o in outs])
+        handle, sptr = self.handle, stream.cuda_stream
+
+        def call():
+            rc = lib.ua2a_exchange_ranks(handle, mode, in_tab, out_tab, first, count, sptr)
+            if rc != UA2A_OK:
+                raise UA2AError(rc, "ua2a_exchange_ranks", ua2a_plan_last_error(handle))
+
+        call.tensors = (list(xs), list(outs))
+        return call
+
+    def describe_ranks(self, xs, outs, mode: int, first: int = 0, count=None) -> dict:
+        """What exchange_ranks(xs, mode, outs, first, count) would launch."""
+        count = self.w - first if count is None else count
+        return ua2a_describe_ranks(self.handle, mode, [None if x is None else x.data_ptr() for x in xs],
+                                   [o.data_ptr() for o in outs], first, count)
 
     def describe(self, x, mode: int, chunked: bool = False, out=None) -> dict:
         """What exchange(x, mode, chunked, out) would launch.  Without `out`, a

@@ -48,6 +48,21 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
     }
 }
 
+// Per-rank allocations: as direct_tile_body, the tensors taken from the
+// geometry's pointer tables (per tile, or per vector in mode 1).
+template <class Mem, int VB, bool MODE1, bool TWO, uint32_t BS>
+UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t tid)
+{
+    typedef typename Piece<VB>::T T;
+    T* dst = reinterpret_cast<T*>(d.dst);
+    for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
+        const uint8_t* sp;
+        int64_t from, to;
+        ranks_vector<MODE1, TWO>(g, d, d.u0 + delta, sp, from, to);
+        Mem::st(dst + to, Mem::ld(reinterpret_cast<const T*>(sp) + from));
+    }
+}
+
 // LDS path, first phase: global -> LDS image of the tile's P rows.
 //   mode 0: the P span itself (contiguous 16-byte chunks);
 //   mode 1: the w A spans, each read as contiguous chunks and scattered

@@ -203,6 +203,118 @@ UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t u,
 }
 
 // ------------------------------------------------------------------------
+// Per-rank allocations: the same exchange when every rank's tensor is an
+// allocation of its own, reached through tables of base pointers, moving only
+// the runs whose SENDING rank (mode 0: the token owner j, mode 1: the head
+// block r) lies in [first, first + count).  With count = 1 this is what one
+// device of a multi-device exchange pushes to its peers; with count = w it is
+// the whole exchange.  Tiles are still cut along the written side:
+//   mode 0: slab = (r, b, j = first + y): the s_local runs that j sends to r,
+//           contiguous in out[r]; each run is read from row s of in[j];
+//   mode 1: slab = (j, b): the rows of out[j], of which the launch writes the
+//           seg = count * vr vectors of head blocks first .. first+count-1
+//           (the whole row when count = w); each vector's run comes from the
+//           sender's table entry.
+// Slab grid: x = tile within the slab; mode 0: y = j - first, z = r * nb + b;
+// mode 1: y = b, z = j.  Units: VB-byte vectors.
+//
+// Mode 1 reads each vector's run from its sender's tensor.  When every tile
+// lies in at most two runs (one sender, or runs of at least a tile) the
+// workgroup loads the two table entries once, with wave-uniform indices, and
+// each lane picks one (TWO = true); otherwise each lane loads its own entry
+// before its data.  The two forms are separate kernels: code that indexes the
+// table both ways makes the compiler copy the whole kernel argument into
+// per-lane scratch memory.
+constexpr uint32_t kMaxRankTable = 64;     // table entries carried in the kernel argument
+
+struct RanksGeom {
+    const uint8_t* src[kMaxRankTable];   // per rank: base of the tensor read
+    uint8_t* dst[kMaxRankTable];         // per rank: base of the tensor written
+    int64_t a_plane, p_plane;            // one batch plane of one rank, each side
+    uint32_t vr;                         // vectors per run
+    uint32_t p_row;                      // w * vr
+    uint32_t seg;                        // count * vr: vectors a mode-1 slab writes per token
+    uint32_t s_local, w, nb, first, count;
+    uint32_t slab_vecs, tile_vecs, tiles_per_slab;
+    uint32_t ny, nz;                     // slab grid extents along y and z
+    uint32_t two_runs;                   // mode 1: every tile lies in at most two runs
+    Div32 d_vr, d_seg, d_nb, d_count;
+};
+
+struct RanksTile {
+    uint8_t* dst;        // the written tensor (table entry of the receiving rank)
+    const uint8_t* src0; // mode 0: the read tensor; mode 1, TWO: sender of the tile's first run
+    const uint8_t* src1; // mode 1, TWO: sender of the tile's last run
+    uint32_t k0;         // mode 1, TWO: sender index (from first) of the tile's first run
+    int64_t dst_off;     // offset of the slab's first written vector
+    int64_t src_off;     // read-side term shared by the slab
+    uint32_t u0;         // first vector of the tile within its slab
+    uint32_t nvec;       // vectors in this tile
+};
+
+// Sender index k (0 <= k < count) of vector u of a mode-1 slab: the slab's
+// runs are numbered s * count + k along it.
+UA2A_HD uint32_t ranks_sender(const RanksGeom& g, uint32_t u)
+{
+    const uint32_t run = fdiv(u, g.d_vr);
+    return run - fdiv(run, g.d_count) * g.count;
+}
+
+template <bool MODE1, bool TWO>
+UA2A_HD RanksTile ranks_tile(const RanksGeom& g, uint32_t x, uint32_t y, uint32_t z)
+{
+    RanksTile d;
+    d.u0 = x * g.tile_vecs;
+    d.nvec = umin32(g.tile_vecs, g.slab_vecs - d.u0);
+    if (!MODE1) {
+        const uint32_t j = g.first + y;
+        const uint32_t r = fdiv(z, g.d_nb);
+        const uint32_t b = z - r * g.nb;
+        d.dst = g.dst[r];
+        d.src0 = d.src1 = g.src[j];
+        d.k0 = 0;
+        d.dst_off = static_cast<int64_t>(b) * g.a_plane + static_cast<int64_t>(j) * g.s_local * g.vr;
+        d.src_off = static_cast<int64_t>(b) * g.p_plane + static_cast<int64_t>(r) * g.vr;
+    } else {
+        const uint32_t b = y, j = z;
+        d.dst = g.dst[j];
+        d.dst_off = static_cast<int64_t>(b) * g.p_plane + static_cast<int64_t>(g.first) * g.vr;
+        d.src_off = static_cast<int64_t>(b) * g.a_plane + static_cast<int64_t>(j) * g.s_local * g.vr;
+        d.src0 = d.src1 = nullptr;
+        d.k0 = 0;
+        if (TWO) {
+            d.k0 = ranks_sender(g, d.u0);
+            d.src0 = g.src[g.first + d.k0];
+            d.src1 = g.src[g.first + ranks_sender(g, d.u0 + d.nvec - 1)];
+        }
+    }
+    return d;
+}
+
+// Read tensor and offsets of vector u (< slab_vecs) of the tile's slab.
+template <bool MODE1, bool TWO>
+UA2A_HD void ranks_vector(const RanksGeom& g, const RanksTile& d, uint32_t u, const uint8_t*& src,
+                          int64_t& src_off, int64_t& dst_off)
+{
+    if (!MODE1) {
+        const uint32_t s = fdiv(u, g.d_vr);          // token of the sending rank
+        const uint32_t o = u - s * g.vr;
+        src = d.src0;
+        src_off = d.src_off + static_cast<int64_t>(static_cast<uint64_t>(s) * g.p_row) + o;
+        dst_off = d.dst_off + u;
+    } else {
+        const uint32_t s = fdiv(u, g.d_seg);         // token of the receiving rank
+        const uint32_t rem = u - s * g.seg;
+        const uint32_t k = fdiv(rem, g.d_vr);        // sender = head block first + k
+        const uint32_t o = rem - k * g.vr;
+        src = TWO ? (k == d.k0 ? d.src0 : d.src1) : g.src[g.first + k];
+        src_off = d.src_off + static_cast<int64_t>(static_cast<uint64_t>(s) * g.vr) + o;
+        dst_off = d.dst_off + static_cast<int64_t>(static_cast<uint64_t>(s) * g.p_row) +
+                  static_cast<int64_t>(k) * g.vr + o;
+    }
+}
+
+// ------------------------------------------------------------------------
 // LDS path: a workgroup stages rows [s0, s0 + rows) of one (j, b) -- a
 // contiguous span of rows * w * run bytes on the P side -- in LDS, laid out
 // exactly as on the P side but shifted by `head` = the span's address mod 16

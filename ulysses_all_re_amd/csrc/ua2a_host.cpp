@@ -329,6 +329,97 @@ void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch
     copy->copy.dst += off;
 }
 
+// Per-rank tables: only the entries a call uses are looked at -- the inputs
+// of the sending ranks and every output (each receives runs from every
+// sender).  Outputs may overlap neither each other nor a used input.
+int check_ranks_call(const ua2a_plan_s* p, int32_t mode, const void* const* in,
+                     void* const* out, int32_t first, int32_t count)
+{
+    if (p == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (p->disabled) return UA2A_ERR_DISABLED;
+    if (mode != 0 && mode != 1) return UA2A_ERR_INVALID_ARG;
+    if (in == nullptr || out == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (p->w > static_cast<int32_t>(kMaxRankTable)) return UA2A_ERR_SHAPE;
+    if (first < 0 || count < 1 || first > p->w - count) return UA2A_ERR_INVALID_ARG;
+    const int32_t last = first + count;
+    for (int32_t k = first; k < last; ++k)
+        if (in[k] == nullptr) return UA2A_ERR_INVALID_ARG;
+    for (int32_t k = 0; k < p->w; ++k)
+        if (out[k] == nullptr) return UA2A_ERR_INVALID_ARG;
+    const uintptr_t e = static_cast<uintptr_t>(p->elem_bytes);
+    for (int32_t k = first; k < last; ++k)
+        if (reinterpret_cast<uintptr_t>(in[k]) % e) return UA2A_ERR_ALIGN;
+    for (int32_t k = 0; k < p->w; ++k)
+        if (reinterpret_cast<uintptr_t>(out[k]) % e) return UA2A_ERR_ALIGN;
+    const int64_t n = p->layout.tensor_bytes / p->w;     // one rank's tensor
+    for (int32_t k = 0; k < p->w; ++k) {
+        for (int32_t k2 = k + 1; k2 < p->w; ++k2)
+            if (overlaps(out[k], n, out[k2], n)) return UA2A_ERR_ALIAS;
+        for (int32_t k2 = first; k2 < last; ++k2)
+            if (overlaps(out[k], n, in[k2], n)) return UA2A_ERR_ALIAS;
+    }
+    return UA2A_OK;
+}
+
+// The one launch of a per-rank exchange.  Default grid: one tile per
+// workgroup over (tile, y, z), y and z capped at the hardware extent (the
+// kernel loops past a cap); a `blocks` hint caps the total.
+void prepare_ranks(const ua2a_plan_s* p, int32_t mode, const void* const* in, void* const* out,
+                   int32_t first, int32_t count, Launch* L)
+{
+    memset(L, 0, sizeof *L);
+    const int64_t run = p->layout.run_bytes;
+    const int64_t plane = p->S_local * p->H * p->D * p->elem_bytes;
+    const int32_t last = first + count;
+    uint32_t vb = pow2_align(static_cast<uint64_t>(run));
+    for (int32_t k = first; k < last; ++k)
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(in[k])));
+    for (int32_t k = 0; k < p->w; ++k)
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out[k])));
+
+    RanksGeom& g = L->ranks;
+    for (int32_t k = 0; k < p->w; ++k) {
+        g.dst[k] = static_cast<uint8_t*>(out[k]);
+        g.src[k] = (k >= first && k < last) ? static_cast<const uint8_t*>(in[k]) : nullptr;
+    }
+    g.a_plane = plane / vb;     // S_global * run bytes == S_local * H * D * e
+    g.p_plane = plane / vb;
+    g.vr = static_cast<uint32_t>(run / vb);
+    g.p_row = static_cast<uint32_t>(p->w) * g.vr;
+    g.seg = static_cast<uint32_t>(count) * g.vr;
+    g.s_local = static_cast<uint32_t>(p->S_local);
+    g.w = static_cast<uint32_t>(p->w);
+    g.nb = static_cast<uint32_t>(p->B);
+    g.first = static_cast<uint32_t>(first);
+    g.count = static_cast<uint32_t>(count);
+    g.slab_vecs = g.s_local * (mode == 0 ? g.vr : g.seg);   // < 2^32 by the plane-size limit
+    g.tile_vecs = kTileBytes / vb;
+    g.tiles_per_slab = (g.slab_vecs + g.tile_vecs - 1) / g.tile_vecs;
+    // a tile of tile_vecs consecutive vectors lies in at most two runs when
+    // runs are at least that long; with one sender all its runs share a tensor
+    g.two_runs = (g.count == 1 || g.vr >= g.tile_vecs) ? 1u : 0u;
+    g.ny = mode == 0 ? g.count : g.nb;
+    g.nz = mode == 0 ? g.w * g.nb : g.w;     // w * B < 2^32 by the run-count limit
+    g.d_vr = make_div32(g.vr);
+    g.d_seg = make_div32(g.seg);
+    g.d_nb = make_div32(g.nb);
+    g.d_count = make_div32(g.count);
+
+    L->kernel = Kernel::Ranks;
+    L->block = kDirectBlock;
+    L->width = static_cast<int32_t>(vb);
+    L->mode = mode;
+    L->grid = grid_for(g.tiles_per_slab, p->blocks, kDirectBlock);
+    uint64_t room = p->blocks > 0 ? static_cast<uint64_t>(p->blocks) / L->grid : kMaxGridYZ;
+    if (room < 1) room = 1;
+    L->grid_y = static_cast<uint32_t>(g.ny < room ? g.ny : room);
+    if (L->grid_y > kMaxGridYZ) L->grid_y = kMaxGridYZ;
+    room = p->blocks > 0 ? room / L->grid_y : kMaxGridYZ;
+    if (room < 1) room = 1;
+    L->grid_z = static_cast<uint32_t>(g.nz < room ? g.nz : room);
+    if (L->grid_z > kMaxGridYZ) L->grid_z = kMaxGridYZ;
+}
+
 void disable(ua2a_plan_s* p, const char* what, int err)
 {
     p->disabled = 1;
@@ -437,6 +528,28 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     return UA2A_OK;
 }
 
+int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
+                        void* const* out_ptrs, int32_t first, int32_t count, void* stream)
+{
+    int rc = check_ranks_call(plan, mode, in_ptrs, out_ptrs, first, count);
+    if (rc != UA2A_OK) return rc;
+    int32_t dev = -1;
+    int err = backend_current_device(&dev);
+    if (err != 0) {
+        disable(plan, "querying the current device", err);
+        return UA2A_ERR_HIP;
+    }
+    if (dev != plan->device) return UA2A_ERR_DEVICE;
+    Launch L;
+    prepare_ranks(plan, mode, in_ptrs, out_ptrs, first, count, &L);
+    err = backend_launch(L, stream);
+    if (err != 0) {
+        disable(plan, "launching the per-rank exchange kernel", err);
+        return UA2A_ERR_HIP;
+    }
+    return UA2A_OK;
+}
+
 int ua2a_destroy(ua2a_plan_t plan)
 {
     free(plan);
@@ -493,6 +606,27 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     info->launches = pr.launches;
     info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
     info->grid_dims = pr.perm.grid3d ? 3 : 1;
+    return UA2A_OK;
+}
+
+int ua2a_describe_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
+                        void* const* out_ptrs, int32_t first, int32_t count,
+                        ua2a_launch_info_t* info)
+{
+    if (info == nullptr) return UA2A_ERR_INVALID_ARG;
+    const int rc = check_ranks_call(plan, mode, in_ptrs, out_ptrs, first, count);
+    if (rc != UA2A_OK) return rc;
+    Launch L;
+    prepare_ranks(plan, mode, in_ptrs, out_ptrs, first, count, &L);
+    memset(info, 0, sizeof *info);
+    info->path = UA2A_PATH_DIRECT;
+    info->vector_bytes = L.width;
+    info->grid = static_cast<int32_t>(static_cast<uint64_t>(L.grid) * L.grid_y * L.grid_z);
+    info->block = static_cast<int32_t>(L.block);
+    info->tiles = static_cast<int64_t>(L.ranks.tiles_per_slab) * L.ranks.ny * L.ranks.nz;
+    info->launches = 1;
+    info->lds_rows = 0;
+    info->grid_dims = 3;
     return UA2A_OK;
 }
 

@@ -37,7 +37,7 @@ constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgrou
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
 
-enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2 };
+enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -46,13 +46,14 @@ struct Launch {
     uint32_t grid_y;     // 3-D grid of the direct kernel (1 otherwise)
     uint32_t grid_z;
     int32_t grid3d;      // direct kernel: one tile per workgroup on (grid, grid_y, grid_z)
-    int32_t width;       // Direct/Copy: bytes per lane vector; Lds: LDS piece bytes G
-    int32_t mode;        // Direct/Lds: 0 or 1
+    int32_t width;       // Direct/Copy/Ranks: bytes per lane vector; Lds: LDS piece bytes G
+    int32_t mode;        // Direct/Lds/Ranks: 0 or 1
     uint32_t grid;       // workgroups along x
     uint32_t lds_bytes;  // dynamic LDS (Lds kernel only)
     DirectGeom direct;
     LdsGeom lds;
     CopyGeom copy;
+    RanksGeom ranks;
 };
 
 // Device backend.  The library implements it over HIP; a host emulation

@@ -17,6 +17,8 @@
 //    aligned chunks, re-ordering runs inside LDS in G-byte pieces.
 //  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
 //    to move the one-plane window into the output.
+//  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
+//    allocations (pointer tables) and a range of sending ranks.
 //
 // The per-thread bodies (ua2a_bodies.h) and their index math
 // (ua2a_geometry.h) are shared with a host emulation used by the tests.
@@ -66,6 +68,18 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_kernel(LdsGeom g)
     }
 }
 
+// Per-rank allocations (pointer tables, sender range): one tile per
+// workgroup when the grid covers the slab grid, else each dimension loops.
+template <int VB, bool MODE1, bool TWO>
+__global__ __launch_bounds__(kDirectBlock) void ua2a_ranks_kernel(RanksGeom g)
+{
+    for (uint32_t z = blockIdx.z; z < g.nz; z += gridDim.z)
+        for (uint32_t y = blockIdx.y; y < g.ny; y += gridDim.y)
+            for (uint32_t x = blockIdx.x; x < g.tiles_per_slab; x += gridDim.x)
+                ranks_tile_body<StreamMem, VB, MODE1, TWO, kDirectBlock>(
+                    g, ranks_tile<MODE1, TWO>(g, x, y, z), threadIdx.x);
+}
+
 template <int VB>
 __global__ __launch_bounds__(kCopyBlock) void ua2a_copy_kernel(CopyGeom g)
 {
@@ -110,6 +124,19 @@ const void* lds_fn(int g)
     case 4: return reinterpret_cast<const void*>(&ua2a_lds_kernel<4, MODE1>);
     case 2: return reinterpret_cast<const void*>(&ua2a_lds_kernel<2, MODE1>);
     case 1: return reinterpret_cast<const void*>(&ua2a_lds_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
+template <bool MODE1, bool TWO>
+const void* ranks_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<16, MODE1, TWO>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<8, MODE1, TWO>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<4, MODE1, TWO>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<2, MODE1, TWO>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<1, MODE1, TWO>);
     default: return nullptr;
     }
 }
@@ -163,6 +190,13 @@ int backend_launch(const Launch& L, void* stream)
     case Kernel::Copy:
         fn = copy_fn(L.width);
         arg = &cg;
+        break;
+    case Kernel::Ranks:
+        if (!L.mode)
+            fn = ranks_fn<false, false>(L.width);
+        else
+            fn = L.ranks.two_runs ? ranks_fn<true, true>(L.width) : ranks_fn<true, false>(L.width);
+        arg = const_cast<RanksGeom*>(&L.ranks);
         break;
     }
     if (fn == nullptr) return static_cast<int>(hipErrorInvalidValue);
