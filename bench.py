@@ -359,8 +359,9 @@ def traffic_from(d):
     print(json.dumps(out, indent=2))
 
 
-def summarize_trace(d, workload):
-    """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run."""
+def summarize_trace(d, workload, ranks=None):
+    """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run
+    (with ranks == "one", each exchange launch moves one sender's share, 1/w)."""
     paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -371,7 +372,9 @@ def summarize_trace(d, workload):
     c = {**CONFIGS, **MEASURE}[workload]
     e = torch.empty((), dtype=DTYPES[c["dtype"]]).element_size()
     moved = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], e)["moved_bytes"]
-    print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {moved // 2} B) |")
+    share = moved // c["w"] if ranks == "one" else moved
+    print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {share // 2} B"
+          + (", one sender" if ranks == "one" else "") + ") |")
     print("|---|---|---|---|---|---|")
     with open(paths[0], newline="") as f:
         for r in csv.DictReader(f):
@@ -379,8 +382,11 @@ def summarize_trace(d, workload):
             if len(name) > 70:
                 name = name[:67] + "..."
             avg = float(r["AverageNs"])
-            big = "ua2a_" in r["Name"] or COPY_KERNEL_HINT in r["Name"]
-            rate = f"{moved / (avg * 1e-9) / 1e9:.1f}" if big else ""
+            rate = ""
+            if "ua2a_" in r["Name"]:
+                rate = f"{share / (avg * 1e-9) / 1e9:.1f}"
+            elif COPY_KERNEL_HINT in r["Name"] and ranks is None:   # per-rank runs also clone ranks
+                rate = f"{moved / (avg * 1e-9) / 1e9:.1f}"
             print(f"| `{name}` | {r['Calls']} | {avg / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                   f"{float(r['MaxNs']) / 1e3:.2f} | {rate} |")
 
@@ -416,7 +422,7 @@ def main():
         traffic_from(args.traffic_from)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload)
+        summarize_trace(args.summarize_trace, args.workload, args.ranks)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
