@@ -297,6 +297,117 @@ def run(args):
     print(json.dumps(result), flush=True)
 
 
+def run_overlap(args):
+    """Mode 0 followed by a per-receiver consumer, serial versus pipelined on
+    readiness credits.  The consumer of receiving rank r is one bf16 GEMM on
+    its gathered sequence, [B*S_global, H/w*D] @ [H/w*D, H/w*D] (a stand-in for
+    the projection or attention that follows the exchange; torch.matmul).
+    Serial: exchange, then the w GEMMs, one stream.  Pipelined: the publishing
+    exchange (one part per receiving rank) on the main stream; on a second
+    stream, for each r, a wait for r's credit, then r's GEMM.  Prints one JSON
+    line."""
+    import torch
+
+    import ulysses_all_re_amd as ua
+    from workloads import CONFIGS, DTYPES, MEASURE, make_tensor
+
+    name = args.workload
+    c = {**CONFIGS, **MEASURE}[name]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dt = DTYPES[c["dtype"]]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    plan = ua.Plan(w, B, S, H, D, dt, device=dev)
+    x = make_tensor((w, B, S, H, D), c["dtype"], "normal", c["seed0"]).to(dev)
+    y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
+    k = (H // w) * D
+    rows = B * S * w
+    wgt = (torch.randn(k, k, generator=torch.Generator("cpu").manual_seed(3)) / k ** 0.5).to(dt).to(dev)
+    z = torch.empty(w, rows, k, dtype=dt, device=dev)
+    credits = torch.zeros(w, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    epoch = [0]
+
+    def consume(r):
+        torch.matmul(y[r].view(rows, k), wgt, out=z[r])
+
+    def serial():
+        plan.exchange(x, 0, out=y, stream=main)
+        for r in range(w):
+            consume(r)
+
+    def pipelined():
+        main.wait_stream(side)               # the previous step's consumers are done with y
+        plan.exchange_publish(x, 0, credits, out=y, stream=main)
+        epoch[0] += 1
+        for r in range(w):
+            ua.wait_credits(credits, r, 1, epoch[0], status, stream=side)
+            with torch.cuda.stream(side):
+                consume(r)
+        main.wait_stream(side)
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        a.record(main)
+        for _ in range(n):
+            fn()
+        b.record(main)
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / n
+
+    for _ in range(args.warmup):
+        serial()
+        pipelined()
+    torch.cuda.synchronize(dev)
+    serial()
+    ref = z.clone()
+    z.zero_()
+    pipelined()
+    torch.cuda.synchronize(dev)
+    if int(status.item()) != 0:
+        raise SystemExit("a credit wait timed out; refusing to report a number")
+    if not torch.equal(z, ref):
+        raise SystemExit("pipelined consumers saw different data than serial ones")
+    K = args.steps
+    t_exchange = timed(lambda: plan.exchange(x, 0, out=y, stream=main), K)
+
+    def publish_only():
+        plan.exchange_publish(x, 0, credits, out=y, stream=main)
+        epoch[0] += 1
+
+    t_publish = timed(publish_only, K)
+
+    def consume_all():
+        for r in range(w):
+            consume(r)
+
+    t_consume = timed(consume_all, K)
+    t_serial = timed(serial, K)
+    t_pipe = timed(pipelined, K)
+    if int(status.item()) != 0:
+        raise SystemExit("a credit wait timed out; refusing to report a number")
+    flops = 2.0 * rows * k * k * w
+    result = {
+        "metric": "mode-0 exchange + per-rank consumer, serial vs pipelined on readiness credits",
+        "value": round(t_serial / t_pipe, 4), "unit": "x (serial time / pipelined time)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "higher_is_better": True,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": name, "w": w, "B": B, "S_local": S, "H": H, "D": D,
+                   "consumer": f"per rank: [{rows}, {k}] @ [{k}, {k}] {c['dtype']} GEMM (torch.matmul)",
+                   "parts": w},
+        "ms": {"exchange": round(t_exchange, 4), "exchange_publish": round(t_publish, 4),
+               "consumers": round(t_consume, 4), "serial": round(t_serial, 4),
+               "pipelined": round(t_pipe, 4)},
+        "publish_overhead": round(t_publish / t_exchange - 1, 4),
+        "consumer_TFLOPs": round(flops / (t_consume * 1e-3) / 1e12, 1),
+    }
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
 # ----------------------------------------------------- counter post-processing
 
 def _read_counter_rows(d):
@@ -407,6 +518,9 @@ def main():
                     help="per-rank allocations (ua2a_exchange_ranks): one launch with every "
                          "sender, or one launch per sender (what each device of a multi-device "
                          "exchange runs)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time mode 0 + a per-rank consumer GEMM, serial vs pipelined on "
+                         "readiness credits (its own JSON line)")
     ap.add_argument("--path", choices=("auto", "direct", "lds"), default="auto",
                     help="force a kernel family (default: the library's choice)")
     ap.add_argument("--cpu-steps", type=int, default=12,
@@ -433,6 +547,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    if args.overlap:
+        run_overlap(args)
+        return
     run(args)
 
 

@@ -179,6 +179,53 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked,
 int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
                         void* const* out_ptrs, int32_t first, int32_t count, void* stream);
 
+/* ------------------------------------------------------ readiness credits */
+/*
+ * A consumer of the exchange (attention on a rank's gathered sequence, a
+ * projection on a rank's restored tokens) can start on the receiving ranks
+ * whose output is complete while the rest is still moving: the
+ * publish-then-consume pipelining of the pypto-lib pull request "Perf:
+ * pipeline HCA AllToAll into O-A" (its summary: readiness published by the
+ * exchange, consumers launched from the window, credits released), here with
+ * one credit counter per RECEIVING rank (mode 0: rank r's [B, S_local*w,
+ * H/w, D]; mode 1: rank j's [B, S_local, H, D]).
+ *
+ * Credits are a caller-owned device array of w uint32_t, zeroed by the
+ * caller once before first use; the library only ever adds to them.  Each
+ * publishing exchange adds 1 to every receiver's counter once that
+ * receiver's output is complete and visible device-wide, so after the n-th
+ * call on the same counters receiver k is ready when credits[k] reaches n
+ * (modulo 2^32).  A credits array belongs to one plan and mode.
+ */
+
+/*
+ * ua2a_exchange_publish: ua2a_exchange(plan, mode, 0, in, out, stream) in
+ * `parts` launches (1 <= parts <= w), part k covering receiving ranks
+ * [w*k/parts, w*(k+1)/parts); after each part, a small launch on the same
+ * stream adds 1 to those receivers' credits (w counters, 4-byte aligned, not
+ * overlapping in or out).  parts = w publishes each receiver as soon as its
+ * own part is done.  Always the direct kernel family, never chunked.
+ * Errors: those of ua2a_exchange, plus INVALID_ARG (credits NULL, parts out
+ * of range), ALIGN, ALIAS.
+ */
+int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* out,
+                          uint32_t* credits, int32_t parts, void* stream);
+
+/*
+ * ua2a_wait_credits: enqueue on `stream` one small kernel that returns once
+ * credits[first .. first+count) have all reached `target` (modulo 2^32), so
+ * that work enqueued after it on that stream sees those receivers' bytes.  Run it
+ * on a stream other than the exchange's, enqueued after the exchange.  It
+ * polls each counter at most spin_limit times (with a short sleep between
+ * polls); if one never gets there it stores 1 into *status (a caller-owned,
+ * caller-zeroed device int32) and returns anyway, so it always ends: check
+ * *status after synchronising before trusting what followed it.  No plan is
+ * needed.  Errors: INVALID_ARG (NULL pointer, count < 1, first < 0, range
+ * past 2^32, spin_limit 0), ALIGN, ALIAS (status inside the range), HIP.
+ */
+int ua2a_wait_credits(const uint32_t* credits, int64_t first, int64_t count, uint32_t target,
+                      uint32_t spin_limit, int32_t* status, void* stream);
+
 /*
  * ua2a_destroy: release the plan object.  It always consumes the plan, also
  * a disabled one, and never touches the window or device memory (the page's

@@ -20,8 +20,24 @@ namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[4] = {0, 0, 0, 0};
+int g_kernel_counts[6] = {0, 0, 0, 0, 0, 0};
 uint32_t g_last_grid = 0;
+long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
+bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
+
+// Whether the next direct tile runs.  When the budget runs out the launch
+// stops part-way, as a kernel still in flight would look to a consumer, and
+// nothing later on the stream starts (stream order).
+bool take_tile()
+{
+    if (g_tile_budget < 0) return true;
+    if (g_tile_budget == 0) {
+        g_stalled = true;
+        return false;
+    }
+    --g_tile_budget;
+    return true;
+}
 
 template <int VB, bool M1>
 void run_direct(const Launch& L)
@@ -31,6 +47,7 @@ void run_direct(const Launch& L)
         for (uint32_t z = 0; z < L.grid_z; ++z)
             for (uint32_t y = 0; y < L.grid_y; ++y)
                 for (uint32_t x = 0; x < L.grid; ++x) {
+                    if (!take_tile()) return;
                     const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
                     for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
                         direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
@@ -39,10 +56,22 @@ void run_direct(const Launch& L)
     }
     // a capped grid loops grid-stride; every tile is visited exactly once either way
     for (uint32_t t = 0; t < g.num_tiles; ++t) {
+        if (!take_tile()) return;
         const DirectTile d = direct_tile<M1>(g, t);
         for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
             direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
     }
+}
+
+// The wait kernel with nothing running beside it: a counter short of its
+// target can never move, so the time-out is immediate.
+void run_wait(const WaitGeom& g)
+{
+    for (uint32_t i = 0; i < g.count; ++i)
+        if (!credit_reached(g.credits[g.first + i], g.target)) {
+            *g.status = 1;
+            return;
+        }
 }
 
 template <int G, bool M1>
@@ -156,18 +185,23 @@ int backend_launch(const Launch& L, void*)
     }
     ++g_launches;
     ++g_kernel_counts[static_cast<int>(L.kernel)];
+    if (g_stalled) return 0;       // queued behind an unfinished launch
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
     const uint32_t want_block = L.kernel == Kernel::Lds ? kLdsBlock
-                              : L.kernel == Kernel::Copy ? kCopyBlock : kDirectBlock;
+                              : L.kernel == Kernel::Copy ? kCopyBlock
+                              : (L.kernel == Kernel::Wait || L.kernel == Kernel::Signal) ? kWaitBlock
+                              : kDirectBlock;
     if (L.block != want_block) return 5;
     switch (L.kernel) {
     case Kernel::Direct:
         if (L.grid3d) {
-            // the 3-D grid must cover every tile exactly once
-            const uint64_t slabs = static_cast<uint64_t>(L.direct.w) * L.direct.nb * (L.mode ? 1u : L.direct.w);
-            if (L.grid != L.direct.tiles_per_slab || static_cast<uint64_t>(L.grid_y) * L.grid_z != slabs ||
-                L.direct.group != 0)
+            // the 3-D grid must cover every tile of the launch exactly once (a
+            // part of a publishing exchange covers fewer receivers than w)
+            const uint64_t slabs = static_cast<uint64_t>(L.grid_y) * L.grid_z;
+            if (L.grid != L.direct.tiles_per_slab || L.direct.group != 0 ||
+                slabs * L.direct.tiles_per_slab != L.direct.num_tiles ||
+                L.grid_y != (L.mode ? L.direct.nb : L.direct.w) || L.grid_z % (L.mode ? 1u : L.direct.nb))
                 return 6;
         } else if (L.grid_y != 1 || L.grid_z != 1) {
             return 7;
@@ -180,6 +214,14 @@ int backend_launch(const Launch& L, void*)
         return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);
     case Kernel::Copy:
         return dispatch_copy(L.copy, L.width);
+    case Kernel::Wait:
+        if (L.grid != 1 || L.grid_y != 1 || L.grid_z != 1 || L.wait.spin_limit < 1) return 9;
+        run_wait(L.wait);
+        return 0;
+    case Kernel::Signal:
+        if (L.grid != 1 || L.grid_y != 1 || L.grid_z != 1) return 9;
+        for (uint32_t i = 0; i < L.signal.count; ++i) ++L.signal.credits[L.signal.first + i];
+        return 0;
     case Kernel::Ranks:
         // the hardware's limits on a dispatch's extents
         if (L.grid_y < 1 || L.grid_z < 1 || L.grid_y > 65535 || L.grid_z > 65535 ||
@@ -197,6 +239,11 @@ int backend_launch(const Launch& L, void*)
 extern "C" {
 
 void ua2a_emu_fail_next_launch(int code) { ua2a::g_fail_next = code; }
+void ua2a_emu_set_tile_budget(long long tiles)
+{
+    ua2a::g_tile_budget = tiles;
+    ua2a::g_stalled = false;
+}
 void ua2a_emu_set_device(int device) { ua2a::g_device = device; }
 
 void ua2a_emu_reset_counts(void)

@@ -47,7 +47,7 @@ UA2A_PATH_LDS = 2
 EXPORTED = (
     "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_ranks", "ua2a_destroy",
     "ua2a_status_string", "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
-    "ua2a_describe_ranks",
+    "ua2a_describe_ranks", "ua2a_exchange_publish", "ua2a_wait_credits",
 )
 
 MAX_RANK_TABLE = 64     # largest w that ua2a_exchange_ranks accepts
@@ -108,6 +108,8 @@ def declare_signatures(lib: ctypes.CDLL) -> ctypes.CDLL:
         "ua2a_exchange_ranks": ([vp, i32, vp, vp, i32, i32, vp], ctypes.c_int),
         "ua2a_describe_ranks": ([vp, i32, vp, vp, i32, i32, ctypes.POINTER(ua2a_launch_info_t)],
                                 ctypes.c_int),
+        "ua2a_exchange_publish": ([vp, i32, vp, vp, vp, i32, vp], ctypes.c_int),
+        "ua2a_wait_credits": ([vp, i64, i64, ctypes.c_uint32, ctypes.c_uint32, vp, vp], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(lib, name)
@@ -178,6 +180,41 @@ def ua2a_describe_ranks(plan: int, mode: int, in_ptrs, out_ptrs, first: int, cou
     return {name: getattr(info, name) for name, _ in ua2a_launch_info_t._fields_}
 
 
+def ua2a_exchange_publish(plan: int, mode: int, inp: int, out: int, credits: int, parts: int,
+                          stream: int = 0) -> None:
+    rc = load_library().ua2a_exchange_publish(plan, mode, inp or None, out or None, credits or None,
+                                              parts, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_exchange_publish", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_wait_credits(credits: int, first: int, count: int, target: int, spin_limit: int,
+                      status: int, stream: int = 0) -> None:
+    rc = load_library().ua2a_wait_credits(credits or None, first, count, target & 0xFFFFFFFF,
+                                          spin_limit, status or None, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_wait_credits")
+
+
+def wait_credits(credits, first: int, count: int, target: int, status, spin_limit: int = 1 << 22,
+                 stream=None) -> None:
+    """Enqueue a wait on `stream` (default: torch's current stream) until
+    credits[first : first+count] (a uint32/int32 device tensor, one counter per
+    receiving rank) reach `target`; `status` (an int32 device tensor, zeroed by
+    the caller) becomes 1 on a time-out."""
+    import torch
+    if credits.element_size() != 4 or status.element_size() != 4:
+        raise TypeError("credits and status must be 4-byte integer tensors")
+    if not (credits.is_contiguous() and credits.is_cuda and status.is_cuda):
+        raise ValueError("credits and status must be contiguous device tensors")
+    if first < 0 or count < 1 or first + count > credits.numel():
+        raise ValueError(f"slab range [{first}, {first + count}) is outside the {credits.numel()} counters")
+    if stream is None:
+        stream = torch.cuda.current_stream(credits.device)
+    ua2a_wait_credits(credits.data_ptr(), first, count, target, spin_limit, status.data_ptr(),
+                      stream.cuda_stream)
+
+
 def ua2a_destroy(plan: int) -> None:
     load_library().ua2a_destroy(plan)
 
@@ -232,6 +269,14 @@ class Plan:
     def out_shape(self, mode: int):
         return self.in_shape(1 - mode)
 
+    def _on_device(self, fn, *args):
+        """Call fn(*args) with the plan's device current (the library checks it)."""
+        import torch
+        if torch.cuda.current_device() == self.device.index:
+            return fn(*args)
+        with torch.cuda.device(self.device):
+            return fn(*args)
+
     def _check(self, t, shape, what):
         if t.dtype != self.dtype:
             raise TypeError(f"{what} has dtype {t.dtype}, plan expects {self.dtype}")
@@ -252,13 +297,8 @@ class Plan:
             self._check(out, self.out_shape(mode), "output")
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        if torch.cuda.current_device() == self.device.index:
-            ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
-                          stream.cuda_stream)
-        else:
-            with torch.cuda.device(self.device):
-                ua2a_exchange(self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
-                              stream.cuda_stream)
+        self._on_device(ua2a_exchange, self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
+                        stream.cuda_stream)
         return out
 
     def _check_ranks(self, xs, outs, mode: int, first: int, count: int) -> None:
@@ -292,12 +332,8 @@ class Plan:
         out_ptrs = [o.data_ptr() for o in outs]
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        if torch.cuda.current_device() == self.device.index:
-            ua2a_exchange_ranks(self.handle, mode, in_ptrs, out_ptrs, first, count, stream.cuda_stream)
-        else:
-            with torch.cuda.device(self.device):
-                ua2a_exchange_ranks(self.handle, mode, in_ptrs, out_ptrs, first, count,
-                                    stream.cuda_stream)
+        self._on_device(ua2a_exchange_ranks, self.handle, mode, in_ptrs, out_ptrs, first, count,
+                        stream.cuda_stream)
         return outs
 
     def bind_ranks(self, xs, mode: int, outs, first: int = 0, count=None, stream=None):
@@ -324,6 +360,27 @@ class Plan:
 
         call.tensors = (list(xs), list(outs))
         return call
+
+    def exchange_publish(self, x, mode: int, credits, out=None, parts=None, stream=None):
+        """exchange(x, mode) in `parts` launches (default w) by receiving rank,
+        each followed by a readiness credit for its receivers in `credits` (an
+        int32/uint32 device tensor of w counters)."""
+        import torch
+        self._check(x, self.in_shape(mode), "input")
+        parts = self.w if parts is None else parts
+        if credits.element_size() != 4 or credits.numel() < self.w or not credits.is_contiguous():
+            raise ValueError(f"credits must be a contiguous 4-byte integer tensor of >= {self.w} counters")
+        if credits.device != self.device:
+            raise ValueError(f"credits are on {credits.device}, plan is on {self.device}")
+        if out is None:
+            out = torch.empty(self.out_shape(mode), dtype=self.dtype, device=self.device)
+        else:
+            self._check(out, self.out_shape(mode), "output")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._on_device(ua2a_exchange_publish, self.handle, mode, x.data_ptr(), out.data_ptr(),
+                        credits.data_ptr(), parts, stream.cuda_stream)
+        return out
 
     def describe_ranks(self, xs, outs, mode: int, first: int = 0, count=None) -> dict:
         """What exchange_ranks(xs, mode, outs, first, count) would launch."""

@@ -521,4 +521,31 @@ UA2A_HD CopyTile copy_tile(const CopyGeom& g, uint32_t t)
     return c;
 }
 
+// ------------------------------------------------------------------------
+// Readiness credits, one counter per receiving rank.  A publishing exchange
+// runs in parts (ranges of receiving ranks); after a part's launch has
+// completed, a signal launch adds 1 to the counters of its receivers with
+// release order at device scope, so after n publishing calls a receiver whose
+// output is complete holds n.  The wait kernel polls credits[first ..
+// first+count) with acquire loads until each reaches `target` (compared
+// modulo 2^32) or `spin_limit` polls of one counter have passed; then it sets
+// *status to 1.  Either way it ends.
+struct SignalGeom {
+    uint32_t* credits;
+    uint32_t first, count;     // counters credits[first .. first+count) get 1 each
+};
+
+struct WaitGeom {
+    const uint32_t* credits;
+    uint32_t first, count;
+    uint32_t target;
+    uint32_t spin_limit;       // >= 1
+    int32_t* status;           // set to 1 on a time-out, never cleared here
+};
+
+UA2A_HD bool credit_reached(uint32_t value, uint32_t target)
+{
+    return static_cast<int32_t>(value - target) >= 0;
+}
+
 }  // namespace ua2a

@@ -72,9 +72,12 @@ struct Prepared {
     int32_t launches;
 };
 
+// `recv` receiving ranks from the ones at the given bases (w for a whole
+// exchange; fewer for a part of a publishing one, which may not use the
+// grouped order since that order cycles through all w head blocks).
 DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_t* a_ptr,
                        int mode, int64_t p_rank, int64_t p_plane, int64_t a_rank,
-                       int64_t a_plane, uint32_t nb)
+                       int64_t a_plane, uint32_t nb, uint32_t recv, bool allow_group)
 {
     DirectGeom g;
     memset(&g, 0, sizeof g);
@@ -92,7 +95,7 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     g.nb = nb;
     // slabs are cut along the written side: (r, b, j) runs in mode 0, (j, b) rows in mode 1
     const uint64_t slab_vecs = static_cast<uint64_t>(g.s_local) * (mode == 0 ? g.vr : g.p_row);
-    const uint64_t slabs = static_cast<uint64_t>(g.w) * nb * (mode == 0 ? g.w : 1u);
+    const uint64_t slabs = static_cast<uint64_t>(recv) * nb * (mode == 0 ? g.w : 1u);
     g.slab_vecs = static_cast<uint32_t>(slab_vecs);   // < 2^32 by the plane-size limit
     g.tile_vecs = kTileBytes / vb;      // 1 KiB of data whatever the vector width
     g.tiles_per_slab = static_cast<uint32_t>((slab_vecs + g.tile_vecs - 1) / g.tile_vecs);
@@ -100,7 +103,8 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     // stride is a multiple of 4 KiB, cycle head blocks fastest (measured:
     // slab after slab is up to 20 % slower there)
     const int64_t row_bytes = run * p->w;
-    g.group = (mode == 0 && p->w > 1 && row_bytes % kDirectGroupRowAlign == 0) ? kDirectGroup : 0;
+    g.group = (allow_group && mode == 0 && p->w > 1 && row_bytes % kDirectGroupRowAlign == 0)
+                  ? kDirectGroup : 0;
     if (g.group) {
         g.groups = (g.tiles_per_slab + g.group - 1) / g.group;
         g.num_tiles = static_cast<uint32_t>(static_cast<uint64_t>(g.groups) * g.group * slabs);
@@ -190,6 +194,34 @@ CopyGeom make_copy(uint32_t vb, const uint8_t* src, uint8_t* dst, int64_t src_st
     return g;
 }
 
+// The direct kernel's launch for receiving ranks [0, recv) of the given bases.
+// Default order, no grid cap: one tile per workgroup on a 3-D grid whose
+// coordinates are the tile's (x = tile in slab; mode 0: y = j, z = r*nb + b;
+// mode 1: y = b, z = j), sparing each workgroup the scalar division of a flat
+// tile index.
+void direct_launch(const ua2a_plan_s* p, int mode, uint32_t vb, uint8_t* p_ptr, uint8_t* a_ptr,
+                   int64_t p_rank, int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb,
+                   uint32_t recv, bool allow_group, Launch* L)
+{
+    L->kernel = Kernel::Direct;
+    L->block = kDirectBlock;
+    L->width = static_cast<int32_t>(vb);
+    L->mode = mode;
+    L->grid_y = L->grid_z = 1;
+    L->grid3d = 0;
+    L->direct = make_direct(p, vb, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb, recv,
+                            allow_group);
+    L->grid = grid_for(L->direct.num_tiles, p->blocks, kDirectBlock);
+    const uint32_t ny = mode == 0 ? static_cast<uint32_t>(p->w) : nb;
+    const uint32_t nz = mode == 0 ? recv * nb : recv;
+    if (p->blocks == 0 && L->direct.group == 0 && ny <= kMaxGridYZ && nz <= kMaxGridYZ) {
+        L->grid3d = 1;
+        L->grid = L->direct.tiles_per_slab;
+        L->grid_y = ny;
+        L->grid_z = nz;
+    }
+}
+
 int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in,
                const void* out)
 {
@@ -213,7 +245,7 @@ int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* 
 }
 
 void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in, void* out,
-             Prepared* pr)
+             Prepared* pr, int32_t force_path = UA2A_PATH_AUTO)
 {
     memset(pr, 0, sizeof *pr);
     const int64_t run = p->layout.run_bytes;
@@ -228,10 +260,11 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
 
     const uint32_t rows = lds_rows(p, mode);
+    const int32_t want = force_path != UA2A_PATH_AUTO ? force_path : p->path;
     int32_t path;
-    if (p->path == UA2A_PATH_DIRECT)
+    if (want == UA2A_PATH_DIRECT)
         path = UA2A_PATH_DIRECT;
-    else if (p->path == UA2A_PATH_LDS)
+    else if (want == UA2A_PATH_LDS)
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
     else if (g == 16 && direct_reads_whole_lines(mode, p->w, run))
         path = UA2A_PATH_DIRECT;
@@ -270,23 +303,8 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     L.mode = mode;
     L.grid_y = L.grid_z = 1;
     if (path == UA2A_PATH_DIRECT) {
-        L.kernel = Kernel::Direct;
-        L.block = kDirectBlock;
-        L.width = static_cast<int32_t>(g);
-        L.direct = make_direct(p, g, p_ptr, a_ptr, mode, p_rank, p_plane, a_rank, a_plane, nb);
-        L.grid = grid_for(L.direct.num_tiles, p->blocks, kDirectBlock);
-        // default order, no grid cap: one tile per workgroup on a 3-D grid
-        // whose coordinates are the tile's (x = tile in slab; mode 0: y = j,
-        // z = r*nb + b; mode 1: y = b, z = j), sparing each workgroup the
-        // scalar division of a flat tile index
-        const uint32_t ny = mode == 0 ? static_cast<uint32_t>(p->w) : nb;
-        const uint32_t nz = mode == 0 ? static_cast<uint32_t>(p->w) * nb : static_cast<uint32_t>(p->w);
-        if (p->blocks == 0 && L.direct.group == 0 && ny <= kMaxGridYZ && nz <= kMaxGridYZ) {
-            L.grid3d = 1;
-            L.grid = L.direct.tiles_per_slab;
-            L.grid_y = ny;
-            L.grid_z = nz;
-        }
+        direct_launch(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb,
+                      static_cast<uint32_t>(p->w), true, &L);
     } else {
         L.kernel = Kernel::Lds;
         L.block = kLdsBlock;
@@ -548,6 +566,88 @@ int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
         return UA2A_ERR_HIP;
     }
     return UA2A_OK;
+}
+
+int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* out,
+                          uint32_t* credits, int32_t parts, void* stream)
+{
+    int rc = check_call(plan, mode, 0, in, out);
+    if (rc != UA2A_OK) return rc;
+    if (credits == nullptr || parts < 1 || parts > plan->w) return UA2A_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(credits) % sizeof(uint32_t)) return UA2A_ERR_ALIGN;
+    const int64_t cbytes = int64_t(plan->w) * static_cast<int64_t>(sizeof(uint32_t));
+    const int64_t n = plan->layout.tensor_bytes;
+    if (overlaps(credits, cbytes, in, n) || overlaps(credits, cbytes, out, n)) return UA2A_ERR_ALIAS;
+    int32_t dev = -1;
+    int err = backend_current_device(&dev);
+    if (err != 0) {
+        disable(plan, "querying the current device", err);
+        return UA2A_ERR_HIP;
+    }
+    if (dev != plan->device) return UA2A_ERR_DEVICE;
+    // Part k covers receiving ranks [w*k/parts, w*(k+1)/parts): the direct
+    // kernel on bases moved to its first receiver (mode 0: A rank r0 and head
+    // block r0 of the P rows; mode 1: P rank j0 and token block j0 of the A
+    // side), then a signal launch for those receivers.
+    Prepared pr;
+    prepare(plan, mode, 0, in, out, &pr, UA2A_PATH_DIRECT);
+    const DirectGeom& g0 = pr.perm.direct;
+    const int64_t vb = pr.perm.width;
+    const int64_t plane = plan->S_local * plan->H * plan->D * plan->elem_bytes;
+    const int64_t rank_bytes = plane * plan->B;
+    uint8_t* p_base = const_cast<uint8_t*>(mode == 0 ? g0.src : g0.dst);
+    uint8_t* a_base = const_cast<uint8_t*>(mode == 0 ? g0.dst : g0.src);
+    for (int32_t k = 0; k < parts; ++k) {
+        const int64_t r0 = int64_t(plan->w) * k / parts;
+        const int64_t r1 = int64_t(plan->w) * (k + 1) / parts;
+        uint8_t* pp = p_base + (mode == 0 ? r0 * g0.vr * vb : r0 * rank_bytes);
+        uint8_t* ap = a_base + (mode == 0 ? r0 * rank_bytes : r0 * int64_t(g0.s_local) * g0.vr * vb);
+        Launch L;
+        memset(&L, 0, sizeof L);
+        direct_launch(plan, mode, static_cast<uint32_t>(vb), pp, ap, rank_bytes, plane, rank_bytes,
+                      plane, static_cast<uint32_t>(plan->B), static_cast<uint32_t>(r1 - r0), false, &L);
+        Launch S;
+        memset(&S, 0, sizeof S);
+        S.kernel = Kernel::Signal;
+        S.block = kWaitBlock;
+        S.grid = S.grid_y = S.grid_z = 1;
+        S.signal.credits = credits;
+        S.signal.first = static_cast<uint32_t>(r0);
+        S.signal.count = static_cast<uint32_t>(r1 - r0);
+        err = backend_launch(L, stream);
+        if (err == 0) err = backend_launch(S, stream);
+        if (err != 0) {
+            disable(plan, "launching a part of a publishing exchange", err);
+            return UA2A_ERR_HIP;
+        }
+    }
+    return UA2A_OK;
+}
+
+int ua2a_wait_credits(const uint32_t* credits, int64_t first, int64_t count, uint32_t target,
+                      uint32_t spin_limit, int32_t* status, void* stream)
+{
+    if (credits == nullptr || status == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (first < 0 || count < 1 || first + count > int64_t(UINT32_MAX) || spin_limit < 1)
+        return UA2A_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(credits) % sizeof(uint32_t) ||
+        reinterpret_cast<uintptr_t>(status) % sizeof(int32_t))
+        return UA2A_ERR_ALIGN;
+    if (overlaps(credits + first, count * static_cast<int64_t>(sizeof(uint32_t)), status,
+                 sizeof(int32_t)))
+        return UA2A_ERR_ALIAS;
+    Launch L;
+    memset(&L, 0, sizeof L);
+    L.kernel = Kernel::Wait;
+    L.block = kWaitBlock;
+    L.grid = L.grid_y = L.grid_z = 1;
+    L.wait.credits = credits;
+    L.wait.first = static_cast<uint32_t>(first);
+    L.wait.count = static_cast<uint32_t>(count);
+    L.wait.target = target;
+    L.wait.spin_limit = spin_limit;
+    L.wait.status = status;
+    return backend_launch(L, stream) == 0 ? UA2A_OK : UA2A_ERR_HIP;
 }
 
 int ua2a_destroy(ua2a_plan_t plan)

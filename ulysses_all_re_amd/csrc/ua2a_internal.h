@@ -36,8 +36,9 @@ constexpr uint64_t kMaxGridWorkItems = (uint64_t(1) << 31);   // x extent of a l
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
+constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
-enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3 };
+enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -54,6 +55,8 @@ struct Launch {
     LdsGeom lds;
     CopyGeom copy;
     RanksGeom ranks;
+    WaitGeom wait;
+    SignalGeom signal;
 };
 
 // Device backend.  The library implements it over HIP; a host emulation

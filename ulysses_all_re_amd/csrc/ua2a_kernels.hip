@@ -19,6 +19,9 @@
 //    to move the one-plane window into the output.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks.
+//  * ua2a_signal_kernel  -- adds readiness credits after a part of a
+//    publishing exchange; ua2a_wait_kernel -- one wave that waits for them,
+//    with a bounded number of polls.
 //
 // The per-thread bodies (ua2a_bodies.h) and their index math
 // (ua2a_geometry.h) are shared with a host emulation used by the tests.
@@ -52,6 +55,37 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom 
 {
     direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
         g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
+}
+
+// Readiness credits: runs after a part of a publishing exchange on the same
+// stream, so every byte of that part is visible device-wide when it starts;
+// its release add passes that on to whoever reads the counter with acquire
+// order (the wait kernel), on any XCD.
+__global__ __launch_bounds__(kWaitBlock) void ua2a_signal_kernel(SignalGeom g)
+{
+    for (uint32_t i = threadIdx.x; i < g.count; i += kWaitBlock)
+        __hip_atomic_fetch_add(g.credits + g.first + i, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait for readiness credits (see WaitGeom): each lane polls its counters,
+// sleeping briefly between polls, and gives up after spin_limit polls of one
+// counter.  The kernel always ends.
+__global__ __launch_bounds__(kWaitBlock) void ua2a_wait_kernel(WaitGeom g)
+{
+    bool ok = true;
+    for (uint32_t i = threadIdx.x; i < g.count && ok; i += kWaitBlock) {
+        const uint32_t* c = g.credits + g.first + i;
+        uint32_t polls = 1;
+        while (!credit_reached(__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT),
+                               g.target)) {
+            if (polls++ >= g.spin_limit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    if (!ok) __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int G, bool MODE1>
@@ -190,6 +224,14 @@ int backend_launch(const Launch& L, void* stream)
     case Kernel::Copy:
         fn = copy_fn(L.width);
         arg = &cg;
+        break;
+    case Kernel::Wait:
+        fn = reinterpret_cast<const void*>(&ua2a_wait_kernel);
+        arg = const_cast<WaitGeom*>(&L.wait);
+        break;
+    case Kernel::Signal:
+        fn = reinterpret_cast<const void*>(&ua2a_signal_kernel);
+        arg = const_cast<SignalGeom*>(&L.signal);
         break;
     case Kernel::Ranks:
         if (!L.mode)
