@@ -209,7 +209,8 @@ int backend_launch(const Launch& L, void*)
         return L.mode ? dispatch_direct<true>(L, L.width) : dispatch_direct<false>(L, L.width);
     case Kernel::Lds:
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
-        if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.row)
+        if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
+            L.lds.lrow != L.lds.row + L.lds.pad || (L.lds.pad && L.width != 16))
             return 3;
         return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);
     case Kernel::Copy:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libua2a.so")
 SOURCES = [os.path.join(CSRC, "ua2a_kernels.hip"), os.path.join(CSRC, "ua2a_host.cpp")]
 HEADERS = [os.path.join(INCLUDE, "ua2a.h"), os.path.join(CSRC, "ua2a_geometry.h"),
-           os.path.join(CSRC, "ua2a_internal.h")]
+           os.path.join(CSRC, "ua2a_bodies.h"), os.path.join(CSRC, "ua2a_internal.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

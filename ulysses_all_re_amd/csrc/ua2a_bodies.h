@@ -86,7 +86,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
                 const uint32_t c = c0 + k * BS;
                 if (c >= pch) continue;
                 if (chunk_full(c * 16, d.head, d.p_len))
-                    *reinterpret_cast<u32x4*>(lds + c * 16) = v[k];
+                    *reinterpret_cast<u32x4*>(lds + lds_pos_of_p(g, c * 16)) = v[k];
                 else
                     copy_partial_chunk<G>(pchunk0, lds, c * 16, d.head, d.p_len);
             }
@@ -96,7 +96,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
         // even when one span is shorter than the workgroup; neighbouring lanes
         // take neighbouring chunks of one span (measured faster than putting
         // the head block fastest, which spreads a wave over w regions)
-        const uint32_t stride = span_chunks(15, d.a_len);     // chunks of the longest span
+        const uint32_t stride = d.stride;      // chunk slots of the longest span
         const uint32_t total = g.w * stride;
         for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
             u32x4 v[U] = {};
@@ -104,7 +104,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
             for (uint32_t k = 0; k < U; ++k) {
                 const uint32_t i = i0 + k * BS;
                 if (i >= total) continue;
-                const uint32_t r = i / stride;
+                const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t c = i - r * stride;
                 const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
@@ -115,7 +115,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
             for (uint32_t k = 0; k < U; ++k) {
                 const uint32_t i = i0 + k * BS;
                 if (i >= total) continue;
-                const uint32_t r = i / stride;
+                const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t c = i - r * stride;
                 const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
@@ -138,10 +138,10 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
 {
     if (!MODE1) {
         // the w spans' chunks as one flat index space (see lds_fill)
-        const uint32_t stride = span_chunks(15, d.a_len);
+        const uint32_t stride = d.stride;
         const uint32_t total = g.w * stride;
         for (uint32_t i = tid; i < total; i += BS) {
-            const uint32_t r = i / stride;
+            const uint32_t r = fdiv(i, d.d_stride);
             const uint32_t c = i - r * stride;
             uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
             const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
@@ -158,7 +158,8 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
         for (uint32_t c = tid; c < pch; c += BS) {
             const uint32_t lo = c * 16;
             if (chunk_full(lo, d.head, d.p_len))
-                Mem::st(reinterpret_cast<u32x4*>(pchunk0 + lo), *reinterpret_cast<const u32x4*>(lds + lo));
+                Mem::st(reinterpret_cast<u32x4*>(pchunk0 + lo),
+                        *reinterpret_cast<const u32x4*>(lds + lds_pos_of_p(g, lo)));
             else
                 copy_partial_chunk<G>(lds, pchunk0, lo, d.head, d.p_len);
         }

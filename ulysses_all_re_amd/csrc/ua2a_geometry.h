@@ -317,11 +317,15 @@ UA2A_HD void ranks_vector(const RanksGeom& g, const RanksTile& d, uint32_t u, co
 // ------------------------------------------------------------------------
 // LDS path: a workgroup stages rows [s0, s0 + rows) of one (j, b) -- a
 // contiguous span of rows * w * run bytes on the P side -- in LDS, laid out
-// exactly as on the P side but shifted by `head` = the span's address mod 16
-// so that 16-byte global chunks map to 16-byte aligned LDS slots.  The w
-// A-side spans of the tile (one per head block r, rows * run bytes each) are
-// then moved in G-byte pieces, G = the alignment shared by run and both
-// base pointers.  All units here are bytes.
+// as on the P side but shifted by `head` = the span's address mod 16 so that
+// 16-byte global chunks map to 16-byte aligned LDS slots.  The w A-side spans
+// of the tile (one per head block r, rows * run bytes each) are then moved in
+// G-byte pieces, G = the alignment shared by run and both base pointers.
+// When G = 16 (every span 16-aligned, head = 0) each LDS row is padded to
+// lrow = row + pad bytes with lrow = run modulo 256: the lanes that move one
+// run of consecutive rows then hit disjoint LDS banks, where the bare row
+// stride (a multiple of the bank period for power-of-two rows) made them
+// collide.  All units here are bytes.
 //     t = (j * nb + b) * tiles_per_plane + tt      (P-side memory order)
 struct LdsGeom {
     uint8_t* p_ptr;            // base of the P-side tensor (read in mode 0, written in mode 1)
@@ -330,13 +334,17 @@ struct LdsGeom {
     int64_t p_rank, p_plane;
     uint32_t run;              // bytes per run
     uint32_t row;              // w * run
+    uint32_t pad;              // LDS padding per row (0 unless G = 16)
+    uint32_t lrow;             // row + pad: LDS stride of a row
     uint32_t s_local;
     uint32_t rows_per_tile;
     uint32_t tiles_per_plane;  // ceil(s_local / rows_per_tile)
     uint32_t num_tiles;        // w * nb * tiles_per_plane
     uint32_t w, nb;
-    uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * row)
-    Div32 d_tpp, d_nb, d_run;
+    uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * lrow)
+    uint32_t stride_full;      // 16-byte chunk slots per A span: tile of rows_per_tile rows
+    uint32_t stride_last;      // ... and the plane's last tile
+    Div32 d_tpp, d_nb, d_run, d_row, d_stride_full, d_stride_last;
 };
 
 struct LdsTile {
@@ -345,6 +353,8 @@ struct LdsTile {
     uint32_t p_len;    // rows * row
     uint32_t a_len;    // rows * run (each of the w A spans)
     uint32_t head;     // (p_ptr + p_start) mod 16: LDS position of the span's first byte
+    uint32_t stride;   // chunk slots per A span in the flat (span, chunk) index
+    Div32 d_stride;
 };
 
 UA2A_HD LdsTile lds_tile(const LdsGeom& g, uint32_t t)
@@ -363,7 +373,18 @@ UA2A_HD LdsTile lds_tile(const LdsGeom& g, uint32_t t)
     d.p_len = rows * g.row;
     d.a_len = rows * g.run;
     d.head = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g.p_ptr + d.p_start) & 15u);
+    const bool full = rows == g.rows_per_tile;
+    d.stride = full ? g.stride_full : g.stride_last;
+    d.d_stride = full ? g.d_stride_full : g.d_stride_last;
     return d;
+}
+
+// LDS byte position of P-span byte x (counted from the span's 16-aligned
+// first chunk); with padding, x is a multiple of 16 and rows start at
+// multiples of row.
+UA2A_HD uint32_t lds_pos_of_p(const LdsGeom& g, uint32_t x)
+{
+    return g.pad ? x + fdiv(x, g.d_row) * g.pad : x;
 }
 
 // LDS byte position of byte p (0 <= p < a_len) of head block r's A span.
@@ -371,7 +392,7 @@ UA2A_HD uint32_t lds_pos_of_a(const LdsGeom& g, const LdsTile& d, uint32_t r, ui
 {
     const uint32_t k = fdiv(p, g.d_run);          // row within the tile
     const uint32_t off = p - k * g.run;           // byte within the run
-    return d.head + k * g.row + r * g.run + off;
+    return d.head + k * g.lrow + r * g.run + off;
 }
 
 // Byte-sized pieces the LDS path moves between LDS and the A side.
@@ -423,7 +444,7 @@ UA2A_HD u32x4 gather_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uin
     } buf;
     uint32_t k = fdiv(p0, g.d_run);
     uint32_t off = p0 - k * g.run;
-    uint32_t pos = d.head + k * g.row + r * g.run + off;
+    uint32_t pos = d.head + k * g.lrow + r * g.run + off;
 #pragma unroll
     for (int i = 0; i < 16 / G; ++i) {
         buf.p[i] = *reinterpret_cast<const T*>(lds + pos);
@@ -431,7 +452,7 @@ UA2A_HD u32x4 gather_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uin
         pos += G;
         if (off == g.run) {          // next row of the tile, same head block
             off = 0;
-            pos += g.row - g.run;
+            pos += g.lrow - g.run;
         }
     }
     return buf.v;
@@ -450,7 +471,7 @@ UA2A_HD void scatter_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uin
     buf.v = v;
     uint32_t k = fdiv(p0, g.d_run);
     uint32_t off = p0 - k * g.run;
-    uint32_t pos = d.head + k * g.row + r * g.run + off;
+    uint32_t pos = d.head + k * g.lrow + r * g.run + off;
 #pragma unroll
     for (int i = 0; i < 16 / G; ++i) {
         *reinterpret_cast<T*>(lds + pos) = buf.p[i];
@@ -458,7 +479,7 @@ UA2A_HD void scatter_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uin
         pos += G;
         if (off == g.run) {
             off = 0;
-            pos += g.row - g.run;
+            pos += g.lrow - g.run;
         }
     }
 }

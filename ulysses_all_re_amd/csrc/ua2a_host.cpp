@@ -137,12 +137,22 @@ bool direct_reads_whole_lines(int mode, int64_t w, int64_t run)
     return kTileBytes % row == 0 && kTileBytes / w >= kDirectMinRun;
 }
 
-// Rows of one (j, b) per LDS tile: as many as fit the mode's target size,
-// at least one, and 0 (no LDS path) if one row plus the alignment slack
-// exceeds the largest tile a workgroup may hold.
-uint32_t lds_rows(const ua2a_plan_s* p, int mode)
+// LDS padding per row for piece size G: with G = 16 every span is 16-aligned
+// and a row may be padded so that its LDS stride equals run modulo 256 bytes
+// (consecutive rows' runs on disjoint banks); otherwise rows stay packed.
+uint32_t lds_pad(const ua2a_plan_s* p, uint32_t G)
 {
-    const int64_t row = p->layout.run_bytes * p->w;
+    if (G != 16) return 0;
+    const int64_t run = p->layout.run_bytes, row = run * p->w;
+    return static_cast<uint32_t>((256 - (row - run) % 256) % 256);
+}
+
+// Rows of one (j, b) per LDS tile: as many as fit the mode's target size,
+// at least one, and 0 (no LDS path) if one row plus padding and the
+// alignment slack exceeds the largest tile a workgroup may hold.
+uint32_t lds_rows(const ua2a_plan_s* p, int mode, uint32_t G)
+{
+    const int64_t row = p->layout.run_bytes * p->w + lds_pad(p, G);
     if (row + 16 > kLdsTileMax) return 0;
     const int64_t target = mode == 0 ? kLdsTileMode0 : kLdsTileMode1;
     int64_t rows = (target - 16) / row;
@@ -151,8 +161,8 @@ uint32_t lds_rows(const ua2a_plan_s* p, int mode)
     return static_cast<uint32_t>(rows);
 }
 
-LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint8_t* p_ptr, uint8_t* a_ptr, int64_t p_rank,
-                 int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
+LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uint8_t* a_ptr,
+                 int64_t p_rank, int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
 {
     LdsGeom g;
     memset(&g, 0, sizeof g);
@@ -164,16 +174,29 @@ LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint8_t* p_ptr, uint8_t* a_ptr,
     g.p_plane = p_plane;
     g.run = static_cast<uint32_t>(p->layout.run_bytes);
     g.row = g.run * static_cast<uint32_t>(p->w);
+    g.pad = lds_pad(p, G);
+    g.lrow = g.row + g.pad;
     g.s_local = static_cast<uint32_t>(p->S_local);
-    g.rows_per_tile = lds_rows(p, mode);
+    g.rows_per_tile = lds_rows(p, mode, G);
     g.tiles_per_plane = (g.s_local + g.rows_per_tile - 1) / g.rows_per_tile;
     g.w = static_cast<uint32_t>(p->w);
     g.nb = nb;
     g.num_tiles = g.w * nb * g.tiles_per_plane;
-    g.lds_bytes = (16 + g.rows_per_tile * g.row + 15) & ~15u;
+    g.lds_bytes = (16 + g.rows_per_tile * g.lrow + 15) & ~15u;
+    // chunk slots per A span: exactly its chunks when spans are 16-aligned,
+    // else room for an unaligned start (the longest a span can touch)
+    const uint32_t rows_last = g.s_local - (g.tiles_per_plane - 1) * g.rows_per_tile;
+    const auto slots = [&](uint32_t rows) {
+        return G == 16 ? rows * g.run / 16 : span_chunks(15, rows * g.run);
+    };
+    g.stride_full = slots(g.rows_per_tile);
+    g.stride_last = slots(rows_last);
     g.d_tpp = make_div32(g.tiles_per_plane);
     g.d_nb = make_div32(nb);
     g.d_run = make_div32(g.run);
+    g.d_row = make_div32(g.row);
+    g.d_stride_full = make_div32(g.stride_full);
+    g.d_stride_last = make_div32(g.stride_last);
     return g;
 }
 
@@ -259,7 +282,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(out)));
     if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
 
-    const uint32_t rows = lds_rows(p, mode);
+    const uint32_t rows = lds_rows(p, mode, g);
     const int32_t want = force_path != UA2A_PATH_AUTO ? force_path : p->path;
     int32_t path;
     if (want == UA2A_PATH_DIRECT)
@@ -309,7 +332,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.kernel = Kernel::Lds;
         L.block = kLdsBlock;
         L.width = static_cast<int32_t>(g);
-        L.lds = make_lds(p, mode, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
+        L.lds = make_lds(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
         L.lds_bytes = L.lds.lds_bytes;
         L.grid = grid_for(L.lds.num_tiles, p->blocks, kLdsBlock);
     }
