@@ -35,6 +35,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,14 +54,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    """Hash of the library sources: traffic counters are valid only for this build."""
+def library_hash() -> str:
+    """Hash of the built library (kernels and launch logic; the build is
+    deterministic, so comment-only source edits keep it): traffic counters
+    are valid only for the build they were taken on."""
+    import ulysses_all_re_amd as ua
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "ulysses_all_re_amd", "csrc", "*"))) + \
-            [os.path.join(ROOT, "include", "ua2a.h")]:
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
+    with open(ua.LIBRARY, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -69,8 +70,8 @@ def load_traffic():
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
-        return None          # counters were taken on another build of the kernel
+    if t.get("library_hash") != library_hash():
+        return None          # counters were taken on another build of the kernels
     return t
 
 
@@ -418,6 +419,16 @@ def _read_counter_rows(d):
     return rows
 
 
+def _is_mode1(kernel_name: str) -> bool:
+    """Whether a (demangled or mangled) direct-kernel name is the mode-1 instance:
+    its second template argument, after the vector width."""
+    m = re.search(r"_kernel<\d+, (true|false)", kernel_name)
+    if m:
+        return m.group(1) == "true"
+    m = re.search(r"_kernelILi\d+ELb([01])", kernel_name)
+    return bool(m) and m.group(1) == "1"
+
+
 def traffic_from(d):
     """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this bench into bytes per launch.
 
@@ -438,8 +449,7 @@ def traffic_from(d):
     vals = {}
     for r in rows:
         name = r[kcol]
-        mode1 = "ELb1E" in name or ", true>" in name     # mangled or demangled MODE1 = true
-        key = ("mode1" if mode1 else "mode0") if DIRECT_KERNEL in name else \
+        key = ("mode1" if _is_mode1(name) else "mode0") if DIRECT_KERNEL in name else \
               ("copy" if COPY_KERNEL_HINT in name else None)
         if key is None:
             continue
@@ -453,7 +463,7 @@ def traffic_from(d):
     known = lay["tensor_bytes"]
     fetch_f = avg[("copy", "FETCH_SIZE")] * 1024 / known
     write_f = avg[("copy", "WRITE_SIZE")] * 1024 / known
-    out = {"source_hash": source_hash(), "workload": WORKLOAD, "counters_dir": d,
+    out = {"library_hash": library_hash(), "workload": WORKLOAD, "counters_dir": d,
            "copy_scale": {"FETCH_SIZE": round(fetch_f, 4), "WRITE_SIZE": round(write_f, 4),
                           "known_bytes_each_way": known}}
     for m in ("mode0", "mode1"):

@@ -201,10 +201,11 @@ int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
 /*
  * ua2a_exchange_publish: ua2a_exchange(plan, mode, 0, in, out, stream) in
  * `parts` launches (1 <= parts <= w), part k covering receiving ranks
- * [w*k/parts, w*(k+1)/parts); after each part, a small launch on the same
- * stream adds 1 to those receivers' credits (w counters, 4-byte aligned, not
- * overlapping in or out).  parts = w publishes each receiver as soon as its
- * own part is done.  Always the direct kernel family, never chunked.
+ * [w*k/parts, w*(k+1)/parts); once part k has completed, 1 is added to
+ * those receivers' credits (w counters, 4-byte aligned, not overlapping in or
+ * out) -- by part k+1's launch, or after the last part by one more small
+ * launch on the same stream.  parts = w publishes each receiver as soon as
+ * its own part is done.  Always the direct kernel family, never chunked.
  * Errors: those of ua2a_exchange, plus INVALID_ARG (credits NULL, parts out
  * of range), ALIGN, ALIAS.
  */

@@ -43,6 +43,9 @@ template <int VB, bool M1>
 void run_direct(const Launch& L)
 {
     const DirectGeom& g = L.direct;
+    // a later part of a publishing exchange: its first workgroup adds the
+    // previous part's credits (that part has completed: stream order)
+    for (uint32_t i = 0; i < g.sig_count; ++i) ++g.sig_credits[g.sig_first + i];
     if (L.grid3d) {
         for (uint32_t z = 0; z < L.grid_z; ++z)
             for (uint32_t y = 0; y < L.grid_y; ++y)

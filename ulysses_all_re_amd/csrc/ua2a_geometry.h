@@ -86,6 +86,9 @@ UA2A_HD uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
 struct DirectGeom {
     const uint8_t* src;        // mode 0: P side; mode 1: A side
     uint8_t* dst;              // the other side
+    uint32_t* sig_credits;     // part of a publishing exchange: credits of the PREVIOUS
+    uint32_t sig_first;        //   part, sig_credits[sig_first .. +sig_count) get 1 each
+    uint32_t sig_count;        //   (0: none)
     int64_t a_rank, a_plane;   // A-side strides
     int64_t p_rank, p_plane;   // P-side strides
     uint32_t vr;               // vectors per run

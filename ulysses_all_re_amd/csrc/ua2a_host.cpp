@@ -611,7 +611,9 @@ int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* 
     // Part k covers receiving ranks [w*k/parts, w*(k+1)/parts): the direct
     // kernel on bases moved to its first receiver (mode 0: A rank r0 and head
     // block r0 of the P rows; mode 1: P rank j0 and token block j0 of the A
-    // side), then a signal launch for those receivers.
+    // side).  Part k's credits are added by part k+1's first workgroup, which
+    // starts only after part k has completed; the last part's by a signal
+    // launch.
     Prepared pr;
     prepare(plan, mode, 0, in, out, &pr, UA2A_PATH_DIRECT);
     const DirectGeom& g0 = pr.perm.direct;
@@ -629,20 +631,29 @@ int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* 
         memset(&L, 0, sizeof L);
         direct_launch(plan, mode, static_cast<uint32_t>(vb), pp, ap, rank_bytes, plane, rank_bytes,
                       plane, static_cast<uint32_t>(plan->B), static_cast<uint32_t>(r1 - r0), false, &L);
-        Launch S;
-        memset(&S, 0, sizeof S);
-        S.kernel = Kernel::Signal;
-        S.block = kWaitBlock;
-        S.grid = S.grid_y = S.grid_z = 1;
-        S.signal.credits = credits;
-        S.signal.first = static_cast<uint32_t>(r0);
-        S.signal.count = static_cast<uint32_t>(r1 - r0);
+        if (k > 0) {
+            L.direct.sig_credits = credits;
+            L.direct.sig_first = static_cast<uint32_t>(int64_t(plan->w) * (k - 1) / parts);
+            L.direct.sig_count = static_cast<uint32_t>(r0) - L.direct.sig_first;
+        }
         err = backend_launch(L, stream);
-        if (err == 0) err = backend_launch(S, stream);
         if (err != 0) {
             disable(plan, "launching a part of a publishing exchange", err);
             return UA2A_ERR_HIP;
         }
+    }
+    Launch S;
+    memset(&S, 0, sizeof S);
+    S.kernel = Kernel::Signal;
+    S.block = kWaitBlock;
+    S.grid = S.grid_y = S.grid_z = 1;
+    S.signal.credits = credits;
+    S.signal.first = static_cast<uint32_t>(int64_t(plan->w) * (parts - 1) / parts);
+    S.signal.count = static_cast<uint32_t>(plan->w) - S.signal.first;
+    err = backend_launch(S, stream);
+    if (err != 0) {
+        disable(plan, "launching a part of a publishing exchange", err);
+        return UA2A_ERR_HIP;
     }
     return UA2A_OK;
 }

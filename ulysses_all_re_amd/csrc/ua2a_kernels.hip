@@ -19,9 +19,10 @@
 //    to move the one-plane window into the output.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks.
-//  * ua2a_signal_kernel  -- adds readiness credits after a part of a
-//    publishing exchange; ua2a_wait_kernel -- one wave that waits for them,
-//    with a bounded number of polls.
+//  * ua2a_signal_kernel  -- adds the readiness credits of a publishing
+//    exchange's last part (earlier parts' credits are added by the next
+//    part's first workgroup); ua2a_wait_kernel -- one wave that waits for
+//    them, with a bounded number of polls.
 //
 // The per-thread bodies (ua2a_bodies.h) and their index math
 // (ua2a_geometry.h) are shared with a host emulation used by the tests.
@@ -41,30 +42,42 @@ struct StreamMem {
     __device__ static void st(T* p, T v) { __builtin_nontemporal_store(v, p); }
 };
 
-template <int VB, bool MODE1>
+// Readiness credits of a publishing exchange.  A launch that follows a part
+// on the same stream starts only after that part has completed, so every
+// byte of the part is visible device-wide by then; a release add at device
+// scope passes that on to whoever reads the counter with acquire order (the
+// wait kernel), on any XCD.
+__device__ __forceinline__ void add_credits(uint32_t* credits, uint32_t first, uint32_t count)
+{
+    for (uint32_t i = threadIdx.x; i < count; i += blockDim.x)
+        __hip_atomic_fetch_add(credits + first + i, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// SIG: a later part of a publishing exchange, whose first workgroup adds the
+// previous part's credits (sparing a launch between the two parts).
+template <int VB, bool MODE1, bool SIG>
 __global__ __launch_bounds__(kDirectBlock) void ua2a_direct_kernel(DirectGeom g)
 {
+    if (SIG && blockIdx.x == 0) add_credits(g.sig_credits, g.sig_first, g.sig_count);
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
         direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
             g, direct_tile<MODE1>(g, t), threadIdx.x);
 }
 
 // One tile per workgroup on a 3-D grid (see direct_tile_3d).
-template <int VB, bool MODE1>
+template <int VB, bool MODE1, bool SIG>
 __global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom g)
 {
+    if (SIG && (blockIdx.x | blockIdx.y | blockIdx.z) == 0)
+        add_credits(g.sig_credits, g.sig_first, g.sig_count);
     direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
         g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
 }
 
-// Readiness credits: runs after a part of a publishing exchange on the same
-// stream, so every byte of that part is visible device-wide when it starts;
-// its release add passes that on to whoever reads the counter with acquire
-// order (the wait kernel), on any XCD.
+// The credits of a publishing exchange's last part.
 __global__ __launch_bounds__(kWaitBlock) void ua2a_signal_kernel(SignalGeom g)
 {
-    for (uint32_t i = threadIdx.x; i < g.count; i += kWaitBlock)
-        __hip_atomic_fetch_add(g.credits + g.first + i, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    add_credits(g.credits, g.first, g.count);
 }
 
 // Wait for readiness credits (see WaitGeom): each lane polls its counters,
@@ -123,30 +136,37 @@ __global__ __launch_bounds__(kCopyBlock) void ua2a_copy_kernel(CopyGeom g)
 
 namespace {
 
-template <bool MODE1>
+template <bool MODE1, bool SIG>
 const void* direct_fn(int vb)
 {
     switch (vb) {
-    case 16: return reinterpret_cast<const void*>(&ua2a_direct_kernel<16, MODE1>);
-    case 8: return reinterpret_cast<const void*>(&ua2a_direct_kernel<8, MODE1>);
-    case 4: return reinterpret_cast<const void*>(&ua2a_direct_kernel<4, MODE1>);
-    case 2: return reinterpret_cast<const void*>(&ua2a_direct_kernel<2, MODE1>);
-    case 1: return reinterpret_cast<const void*>(&ua2a_direct_kernel<1, MODE1>);
+    case 16: return reinterpret_cast<const void*>(&ua2a_direct_kernel<16, MODE1, SIG>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_direct_kernel<8, MODE1, SIG>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_direct_kernel<4, MODE1, SIG>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_direct_kernel<2, MODE1, SIG>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_direct_kernel<1, MODE1, SIG>);
     default: return nullptr;
     }
 }
 
-template <bool MODE1>
+template <bool MODE1, bool SIG>
 const void* direct3d_fn(int vb)
 {
     switch (vb) {
-    case 16: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<16, MODE1>);
-    case 8: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<8, MODE1>);
-    case 4: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<4, MODE1>);
-    case 2: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<2, MODE1>);
-    case 1: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<1, MODE1>);
+    case 16: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<16, MODE1, SIG>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<8, MODE1, SIG>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<4, MODE1, SIG>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<2, MODE1, SIG>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_direct3d_kernel<1, MODE1, SIG>);
     default: return nullptr;
     }
+}
+
+template <bool SIG>
+const void* direct_any(const Launch& L)
+{
+    if (L.grid3d) return L.mode ? direct3d_fn<true, SIG>(L.width) : direct3d_fn<false, SIG>(L.width);
+    return L.mode ? direct_fn<true, SIG>(L.width) : direct_fn<false, SIG>(L.width);
 }
 
 template <bool MODE1>
@@ -210,10 +230,7 @@ int backend_launch(const Launch& L, void* stream)
     size_t shmem = 0;
     switch (L.kernel) {
     case Kernel::Direct:
-        if (L.grid3d)
-            fn = L.mode ? direct3d_fn<true>(L.width) : direct3d_fn<false>(L.width);
-        else
-            fn = L.mode ? direct_fn<true>(L.width) : direct_fn<false>(L.width);
+        fn = L.direct.sig_count ? direct_any<true>(L) : direct_any<false>(L);
         arg = &dg;
         break;
     case Kernel::Lds:
