@@ -87,7 +87,7 @@ void run_lds(const LdsGeom& g)
         memset(lds.data(), 0xA5, lds.size());
         const LdsTile d = lds_tile(g, t);
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-            lds_fill<PlainMem, G, M1, kLdsBlock, kLdsUnroll>(g, d, tid, lds.data());
+            lds_fill<PlainMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, d, tid, lds.data());
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
             lds_drain<PlainMem, G, M1, kLdsBlock>(g, d, tid, lds.data());
     }

@@ -147,15 +147,30 @@ uint32_t lds_pad(const ua2a_plan_s* p, uint32_t G)
     return static_cast<uint32_t>((256 - (row - run) % 256) % 256);
 }
 
-// Rows of one (j, b) per LDS tile: as many as fit the mode's target size,
-// at least one, and 0 (no LDS path) if one row plus padding and the
-// alignment slack exceeds the largest tile a workgroup may hold.
+// Rows of one (j, b) per LDS tile: about the mode's target size, rounded to
+// the nearest multiple of 128 / gcd(run, 128) rows so that every tile's A
+// spans (rows * run bytes) are whole 128-byte lines -- otherwise neighbouring
+// tiles share a line at every span boundary, read twice in mode 1 and
+// written in parts in mode 0 -- at least one row and within the largest tile
+// a workgroup may hold; 0 (no LDS path) if one row plus padding and the
+// alignment slack does not fit.
 uint32_t lds_rows(const ua2a_plan_s* p, int mode, uint32_t G)
 {
     const int64_t row = p->layout.run_bytes * p->w + lds_pad(p, G);
     if (row + 16 > kLdsTileMax) return 0;
     const int64_t target = mode == 0 ? kLdsTileMode0 : kLdsTileMode1;
     int64_t rows = (target - 16) / row;
+    int64_t g = p->layout.run_bytes, m = kLineBytes;
+    while (m != 0) {
+        const int64_t t = g % m;
+        g = m;
+        m = t;
+    }
+    const int64_t unit = kLineBytes / g;            // rows per whole number of lines
+    const int64_t fit = (kLdsTileMax - 16) / row;   // most rows a tile may hold
+    const int64_t aligned = (rows + unit / 2) / unit * unit;
+    if (aligned >= unit && aligned <= fit) rows = aligned;
+    else if (rows < unit && unit <= fit) rows = unit;
     if (rows < 1) rows = 1;
     if (rows > p->S_local) rows = p->S_local;
     return static_cast<uint32_t>(rows);

@@ -27,7 +27,7 @@ namespace ua2a {
 // unrolling, bigger workgroups or persistent grids are slower there.
 constexpr uint32_t kDirectUnroll = 1;           // vectors per lane per pass (direct, copy)
 constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
-constexpr uint32_t kLdsUnroll = 1;              // 16-byte chunks per lane per pass (LDS fill)
+constexpr uint32_t kLdsUnroll = 2;              // 16-byte chunks per lane per pass (LDS fill, G = 16)
 constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least contiguous read per head block
 constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
 constexpr uint32_t kDirectGroupRowAlign = 4096;
@@ -36,6 +36,7 @@ constexpr uint64_t kMaxGridWorkItems = (uint64_t(1) << 31);   // x extent of a l
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
+constexpr int64_t kLineBytes = 128;             // cache line: LDS tiles align their A spans to it
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5 };

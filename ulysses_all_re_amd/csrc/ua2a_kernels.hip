@@ -108,7 +108,8 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_kernel(LdsGeom g)
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
         const LdsTile d = lds_tile(g, t);
-        lds_fill<StreamMem, G, MODE1, kLdsBlock, kLdsUnroll>(g, d, threadIdx.x, lds);
+        // two loads in flight per lane pay off only with 16-byte pieces (measured)
+        lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, d, threadIdx.x, lds);
         __syncthreads();
         lds_drain<StreamMem, G, MODE1, kLdsBlock>(g, d, threadIdx.x, lds);
         __syncthreads();   // the next tile overwrites the LDS image
