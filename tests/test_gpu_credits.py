@@ -136,3 +136,36 @@ def test_publish_argument_checks():
     with pytest.raises(ValueError):
         ua.wait_credits(credits, 2, 3, 0, torch.zeros(1, dtype=torch.int32, device=DEV))
     plan.close()
+
+
+def test_publishing_exchange_in_a_hip_graph():
+    """Capture a publishing exchange once; every replay (new input copied in,
+    eager work and syncs between replays) gives the oracle's bytes and adds
+    one more credit per receiver."""
+    c = CONFIGS["mid"]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    credits = torch.zeros(w, dtype=torch.int32, device=DEV)
+    x_static = torch.zeros((w, B, S, H, D), dtype=torch.bfloat16, device=DEV)
+    y_static = torch.empty(plan.out_shape(0), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                 # warm up outside the capture
+        plan.exchange_publish(x_static, 0, credits, out=y_static, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note("graph capture of a publishing exchange")
+    with torch.cuda.graph(graph):
+        plan.exchange_publish(x_static, 0, credits, out=y_static)
+    for i in range(4):
+        x = make_tensor((w, B, S, H, D), "bf16", "bytes", 300 + i)
+        x_static.copy_(x.to(DEV))
+        bits(y_static).fill_(-1)
+        torch.cuda.synchronize()
+        note(f"publishing graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y_static.cpu()), oracle_bits(x, 0, w)), f"replay {i}"
+        assert bool((credits.cpu() == i + 2).all()), (i, credits.tolist())
+    plan.close()

@@ -226,3 +226,38 @@ def test_ranks_argument_checks_on_device_tensors():
     plan.exchange_ranks([xs[0], None], 0, outs=outs, first=0, count=1)
     torch.cuda.synchronize()
     plan.close()
+
+
+def test_per_rank_exchange_in_a_hip_graph():
+    """Capture one sender's per-rank exchange and the whole one; replays with
+    new inputs copied in between give the oracle's bytes each time."""
+    c = CONFIGS["mid"]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    ish, osh = stacked_shapes(w, B, S, H, D, 0)
+    xs = [torch.zeros(ish[1:], dtype=torch.bfloat16, device=DEV) for _ in range(w)]
+    outs = [torch.empty(osh[1:], dtype=torch.bfloat16, device=DEV) for _ in range(w)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.exchange_ranks(xs, 0, outs=outs, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note("graph capture of per-rank exchanges")
+    with torch.cuda.graph(graph):
+        plan.exchange_ranks(xs, 0, outs=outs, first=w - 1, count=1)
+        plan.exchange_ranks(xs, 0, outs=outs, first=0, count=w - 1)
+    for i in range(3):
+        x = make_tensor(ish, "bf16", "bytes", 400 + i)
+        for k in range(w):
+            xs[k].copy_(x[k].to(DEV))
+            bits(outs[k]).fill_(-1)
+        torch.cuda.synchronize()
+        note(f"per-rank graph replay {i}")
+        graph.replay()
+        torch.cuda.synchronize()
+        want = oracle.exchange(bits(x).numpy(), 0, w)
+        for k in range(w):
+            assert torch.equal(bits(outs[k].cpu()), torch.from_numpy(want[k])), (i, k)
+    plan.close()
