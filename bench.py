@@ -124,22 +124,38 @@ def run(args):
     stream = torch.cuda.current_stream(dev)
     bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[e]
 
-    def round_trip_bits():
+    def round_trips_ok():
         if args.ranks is None:
-            return z.view(bits)
-        return torch.stack([t.view(bits) for t in zs])
+            return all(torch.equal(zk.view(bits), xk.view(bits)) for xk, _, zk in sets)
+        return torch.equal(torch.stack([t.view(bits) for t in zs]), x.view(bits))
 
+    # Buffer sets the exchanges rotate through: enough that a cycle moves
+    # about 1 GiB, so that tensors smaller than the 256 MB Infinity Cache are
+    # timed against HBM too (at most 64 sets; one for the video-DiT tensors).
+    rotate = args.rotate if args.rotate > 0 else \
+        max(1, min(64, -(-(1 << 30) // (2 * lay["tensor_bytes"]))))
+    if args.ranks is not None or args.graph:
+        rotate = 1
     if args.ranks is None:
-        y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
-        z = torch.empty(plan.out_shape(1), dtype=dt, device=dev)
+        sets = []
+        for k in range(rotate):
+            xk = x if k == 0 else x.clone()
+            sets.append((xk, torch.empty(plan.out_shape(0), dtype=dt, device=dev),
+                         torch.empty(plan.out_shape(1), dtype=dt, device=dev)))
+        x, y, z = sets[0]
         info0 = plan.describe(x, 0, chunked, out=y)
         info1 = plan.describe(y, 1, chunked, out=z)
+        turn = [0, 0]
 
         def ex0():
-            plan.exchange(x, 0, chunked, out=y, stream=stream)
+            xk, yk, _ = sets[turn[0]]
+            turn[0] = (turn[0] + 1) % rotate
+            plan.exchange(xk, 0, chunked, out=yk, stream=stream)
 
         def ex1():
-            plan.exchange(y, 1, chunked, out=z, stream=stream)
+            _, yk, zk = sets[turn[1]]
+            turn[1] = (turn[1] + 1) % rotate
+            plan.exchange(yk, 1, chunked, out=zk, stream=stream)
     else:
         # per-rank allocations: every rank's tensors are allocations of their own
         if chunked:
@@ -164,11 +180,11 @@ def run(args):
     log(f"mode 0 launch {info0}")
     log(f"mode 1 launch {info1}")
 
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, rotate)):
         ex0()
         ex1()
     torch.cuda.synchronize(dev)
-    if not torch.equal(round_trip_bits(), x.view(bits)):
+    if not round_trips_ok():
         raise SystemExit("round trip did not return the input; refusing to report a number")
     log(f"warmup done ({args.warmup} steps), round trip bit-exact")
 
@@ -219,10 +235,18 @@ def run(args):
     # per-exchange averages for the roofline: each mode K times back to back
     avg0 = timed(ex0, K) / K
     avg1 = timed(ex1, K) / K
-    # device-to-device copy of the same byte count, timed the same way
-    cp = torch.empty_like(x)
-    timed(lambda: cp.copy_(x), 3)
-    avgc = timed(lambda: cp.copy_(x), K) / K
+    # device-to-device copy of the same byte count, timed the same way (over
+    # the same rotation of buffer sets)
+    cps = [torch.empty_like(x) for _ in range(rotate)]
+    cturn = [0]
+
+    def copy_leg():
+        k = cturn[0]
+        cturn[0] = (k + 1) % rotate
+        cps[k].copy_(sets[k][0] if args.ranks is None else x)
+
+    timed(copy_leg, 3)
+    avgc = timed(copy_leg, K) / K
     log(f"per exchange: mode 0 {avg0 * 1e3:.1f} us, mode 1 {avg1 * 1e3:.1f} us, "
         f"copy {avgc * 1e3:.1f} us")
 
@@ -280,7 +304,8 @@ def run(args):
                    "ranks": args.ranks,
                    "step": "mode 0 then mode 1",
                    "bytes_per_step": 2 * moved,
-                   "cache_resident": lay["tensor_bytes"] * 2 <= 256 * 2 ** 20},
+                   "buffer_sets": rotate,
+                   "cache_resident": rotate * lay["tensor_bytes"] * 2 <= 256 * 2 ** 20},
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "mode0": mode_entry(avg0, info0, 0),
         "mode1": mode_entry(avg1, info1, 1),
@@ -531,6 +556,9 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="time mode 0 + a per-rank consumer GEMM, serial vs pipelined on "
                          "readiness credits (its own JSON line)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="buffer sets to rotate through (0 = enough for about 1 GiB per cycle, "
+                         "at most 64; 1 for the video-DiT tensors)")
     ap.add_argument("--path", choices=("auto", "direct", "lds"), default="auto",
                     help="force a kernel family (default: the library's choice)")
     ap.add_argument("--cpu-steps", type=int, default=12,
