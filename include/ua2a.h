@@ -25,8 +25,9 @@
  * Conventions for every function below:
  *   - return 0 (UA2A_OK) or a negative UA2A_ERR_* code; nothing throws;
  *   - no function synchronises the host with the device;
- *   - ua2a_exchange and ua2a_exchange_ranks allocate nothing and launch
- *     only on the given stream;
+ *   - no function allocates device memory; the ones that launch work
+ *     (ua2a_exchange, ua2a_exchange_ranks, ua2a_exchange_publish,
+ *     ua2a_wait_credits) launch only on the given stream;
  *   - pointers named in/out/window are device pointers on the plan's
  *     device, owned by the caller, and are only borrowed by the library.
  */
@@ -44,7 +45,7 @@ extern "C" {
 #define UA2A_ERR_INVALID_ARG  (-1) /* null pointer, mode/chunked not 0/1, bad elem_bytes, bad path */
 #define UA2A_ERR_SHAPE        (-2) /* a dimension < 1, H % w != 0, or a size beyond the limits below */
 #define UA2A_ERR_ALIGN        (-3) /* a tensor or window pointer not aligned to elem_bytes */
-#define UA2A_ERR_ALIAS        (-4) /* byte ranges of in, out and window overlap */
+#define UA2A_ERR_ALIAS        (-4) /* byte ranges of inputs, outputs, window or counters overlap */
 #define UA2A_ERR_CAPACITY     (-5) /* chunked call with no window or one smaller than one plane */
 #define UA2A_ERR_DEVICE       (-6) /* the calling thread's current device is not the plan's */
 #define UA2A_ERR_HIP          (-7) /* a HIP runtime or launch call failed: the plan is now disabled */
@@ -183,12 +184,12 @@ int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
 /*
  * A consumer of the exchange (attention on a rank's gathered sequence, a
  * projection on a rank's restored tokens) can start on the receiving ranks
- * whose output is complete while the rest is still moving: the
- * publish-then-consume pipelining of the pypto-lib pull request "Perf:
- * pipeline HCA AllToAll into O-A" (its summary: readiness published by the
- * exchange, consumers launched from the window, credits released), here with
- * one credit counter per RECEIVING rank (mode 0: rank r's [B, S_local*w,
- * H/w, D]; mode 1: rank j's [B, S_local, H, D]).
+ * whose output is complete while the rest is still moving.  This is the
+ * pipelining of the pypto-lib pull request "Perf: pipeline HCA AllToAll into
+ * O-A" (its summary: the exchange marks parts ready, the consumer starts on
+ * them, and readiness is handed back when consumed), with one counter per
+ * RECEIVING rank (mode 0: rank r's [B, S_local*w, H/w, D]; mode 1: rank j's
+ * [B, S_local, H, D]).
  *
  * Credits are a caller-owned device array of w uint32_t, zeroed by the
  * caller once before first use; the library only ever adds to them.  Each
@@ -215,9 +216,9 @@ int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* 
 /*
  * ua2a_wait_credits: enqueue on `stream` one small kernel that returns once
  * credits[first .. first+count) have all reached `target` (modulo 2^32), so
- * that work enqueued after it on that stream sees those receivers' bytes.  Run it
- * on a stream other than the exchange's, enqueued after the exchange.  It
- * polls each counter at most spin_limit times (with a short sleep between
+ * that work enqueued after it on that stream sees those receivers' bytes.
+ * Run it on a stream other than the exchange's, enqueued after the exchange.
+ * It polls each counter at most spin_limit times (with a short sleep between
  * polls); if one never gets there it stores 1 into *status (a caller-owned,
  * caller-zeroed device int32) and returns anyway, so it always ends: check
  * *status after synchronising before trusting what followed it.  No plan is
