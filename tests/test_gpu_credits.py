@@ -169,3 +169,36 @@ def test_publishing_exchange_in_a_hip_graph():
         assert torch.equal(bits(y_static.cpu()), oracle_bits(x, 0, w)), f"replay {i}"
         assert bool((credits.cpu() == i + 2).all()), (i, credits.tolist())
     plan.close()
+
+
+@pytest.mark.parametrize("blocks", [7, 1000])
+def test_publish_with_a_capped_grid(blocks):
+    """A `blocks` cap puts the parts on the flat grid-stride kernel, whose
+    first workgroup adds the previous part's credits."""
+    c = CONFIGS["chunked"]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    plan = ua.Plan(w, B, S, H, D, torch.float16, blocks=blocks)
+    for mode in (0, 1):
+        credits = torch.zeros(w, dtype=torch.int32, device=DEV)
+        x = make_tensor(in_shape(w, B, S, H, D, mode), "fp16", "bytes", 500 + mode)
+        note(f"publish blocks={blocks} mode{mode}")
+        assert plan.describe(x.to(DEV), mode)["grid_dims"] == 1
+        out = plan.exchange_publish(x.to(DEV), mode, credits, parts=w)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out.cpu()), oracle_bits(x, mode, w)), (blocks, mode)
+        assert bool((credits.cpu() == 1).all()), (blocks, mode, credits.tolist())
+    plan.close()
+
+
+def test_wait_over_more_counters_than_lanes():
+    """130 counters: each lane of the wait kernel's wave polls several."""
+    credits = torch.full((130,), 5, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    note("wait over 130 counters")
+    ua.wait_credits(credits, 0, 130, 5, status, spin_limit=1000)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    credits[129] = 4                              # one short counter, last lane's second pass
+    ua.wait_credits(credits, 0, 130, 5, status, spin_limit=1000)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1

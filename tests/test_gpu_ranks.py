@@ -261,3 +261,18 @@ def test_per_rank_exchange_in_a_hip_graph():
         for k in range(w):
             assert torch.equal(bits(outs[k].cpu()), torch.from_numpy(want[k])), (i, k)
     plan.close()
+
+
+@pytest.mark.parametrize("blocks", [5, 3000])
+def test_ranks_with_a_capped_grid(blocks):
+    """A `blocks` cap shrinks the per-rank grid; the kernel's loops cover the rest."""
+    w, B, S, H, D = 4, 2, 300, 8, 64
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16, blocks=blocks)
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        x = make_tensor(ish, "bf16", "bytes", 600 + mode)
+        for first, count in ((0, w), (1, 2)):
+            note(f"ranks blocks={blocks} mode{mode} senders=[{first},{first + count})")
+            got, want = run_case(plan, x, mode, first, count)
+            assert_ranks_equal(got, want, f"blocks {blocks} mode {mode} [{first}, {first + count})")
+    plan.close()
