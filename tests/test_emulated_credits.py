@@ -169,3 +169,61 @@ def test_credit_argument_errors(emu):
     assert wc(c, 0, 4, 1, c + 8) == ua.UA2A_ERR_ALIAS              # status among the counters
     lib.ua2a_emu_fail_next_launch(96)
     assert wc(c, 0, 4, 1, s) == ua.UA2A_ERR_HIP
+
+
+# ----------------------------------------------------------- sanitizer build
+
+ASAN_PUBLISH_DRIVER = r"""
+import ctypes, sys
+import numpy as np
+sys.path.insert(0, {root!r})
+import oracle, ulysses_all_re_amd as ua
+lib = ua.declare_signatures(ctypes.CDLL({lib!r}))
+DT = {{1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}}
+for (w, B, S, H, D, e, mode, parts, blocks) in {cases!r}:
+    lay = ua.ua2a_layout_t()
+    assert lib.ua2a_layout(w, B, S, H, D, e, ctypes.byref(lay)) == 0
+    n = lay.tensor_bytes
+    xin = (ctypes.c_uint8 * n)()          # exact-size heap blocks
+    xout = (ctypes.c_uint8 * n)()
+    credits = (ctypes.c_uint32 * w)()
+    src = np.frombuffer(xin, dtype=np.uint8)
+    src[:] = np.random.default_rng(w * 7 + S).integers(0, 256, n, dtype=np.uint8)
+    h = ctypes.c_void_p()
+    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, blocks, None, 0, 0) == 0
+    rc = lib.ua2a_exchange_publish(h, mode, ctypes.addressof(xin), ctypes.addressof(xout),
+                                   ctypes.addressof(credits), parts, None)
+    assert rc == 0, rc
+    lib.ua2a_destroy(h)
+    ishape = (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+    want = oracle.exchange(src.view(DT[e]).reshape(ishape), mode, w).view(np.uint8).ravel()
+    assert np.array_equal(np.frombuffer(xout, dtype=np.uint8), want), (w, B, S, H, D, e, mode, parts, blocks)
+    assert list(credits) == [1] * w, list(credits)
+print("asan-ok")
+"""
+
+
+@pytest.mark.slow
+def test_publish_under_asan(tmp_path):
+    import os
+    import subprocess
+    import sys
+
+    from tests.emu import build as emu_build
+    lib = emu_build.build(sanitize=True)
+    cases = []
+    for shape in SHAPES:
+        for mode in (0, 1):
+            for parts in _parts(shape[0]):
+                for blocks in (0, 3):
+                    cases.append((*shape, mode, parts, blocks))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "asan_publish_driver.py"
+    script.write_text(ASAN_PUBLISH_DRIVER.format(root=root, lib=lib, cases=cases))
+    env = dict(os.environ, LD_PRELOAD=emu_build.asan_runtime(),
+               ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    res = subprocess.run([sys.executable, str(script)], env=env, capture_output=True, text=True,
+                         timeout=600)
+    assert res.returncode == 0, res.stdout[-3000:] + res.stderr[-6000:]
+    assert "asan-ok" in res.stdout
