@@ -20,7 +20,7 @@ namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[6] = {0, 0, 0, 0, 0, 0};
+int g_kernel_counts[7] = {0, 0, 0, 0, 0, 0, 0};
 uint32_t g_last_grid = 0;
 long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
 bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
@@ -77,19 +77,19 @@ void run_wait(const WaitGeom& g)
         }
 }
 
-template <int G, bool M1>
-void run_lds(const LdsGeom& g)
+template <int G, bool M1, class Bases>
+void run_lds(const LdsGeom& g, const Bases& bases)
 {
     // exactly lds_bytes, so any access past the reserved LDS is a heap
     // overflow that AddressSanitizer reports
     std::vector<uint8_t> lds(g.lds_bytes);
     for (uint32_t t = 0; t < g.num_tiles; ++t) {
         memset(lds.data(), 0xA5, lds.size());
-        const LdsTile d = lds_tile(g, t);
+        const LdsTile d = lds_tile(g, bases, t);
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-            lds_fill<PlainMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, d, tid, lds.data());
+            lds_fill<PlainMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-            lds_drain<PlainMem, G, M1, kLdsBlock>(g, d, tid, lds.data());
+            lds_drain<PlainMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
     }
 }
 
@@ -145,15 +145,15 @@ int dispatch_direct(const Launch& L, int vb)
     }
 }
 
-template <bool M1>
-int dispatch_lds(const LdsGeom& g, int gw)
+template <bool M1, class Bases>
+int dispatch_lds(const LdsGeom& g, const Bases& bases, int gw)
 {
     switch (gw) {
-    case 16: run_lds<16, M1>(g); return 0;
-    case 8: run_lds<8, M1>(g); return 0;
-    case 4: run_lds<4, M1>(g); return 0;
-    case 2: run_lds<2, M1>(g); return 0;
-    case 1: run_lds<1, M1>(g); return 0;
+    case 16: run_lds<16, M1>(g, bases); return 0;
+    case 8: run_lds<8, M1>(g, bases); return 0;
+    case 4: run_lds<4, M1>(g, bases); return 0;
+    case 2: run_lds<2, M1>(g, bases); return 0;
+    case 1: run_lds<1, M1>(g, bases); return 0;
     default: return 1;
     }
 }
@@ -191,7 +191,7 @@ int backend_launch(const Launch& L, void*)
     if (g_stalled) return 0;       // queued behind an unfinished launch
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
-    const uint32_t want_block = L.kernel == Kernel::Lds ? kLdsBlock
+    const uint32_t want_block = (L.kernel == Kernel::Lds || L.kernel == Kernel::LdsRanks) ? kLdsBlock
                               : L.kernel == Kernel::Copy ? kCopyBlock
                               : (L.kernel == Kernel::Wait || L.kernel == Kernel::Signal) ? kWaitBlock
                               : kDirectBlock;
@@ -215,7 +215,15 @@ int backend_launch(const Launch& L, void*)
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
             L.lds.lrow != L.lds.row + L.lds.pad || (L.lds.pad && L.width != 16))
             return 3;
-        return L.mode ? dispatch_lds<true>(L.lds, L.width) : dispatch_lds<false>(L.lds, L.width);
+        return L.mode ? dispatch_lds<true>(L.lds, StackedBases{L.lds}, L.width)
+                      : dispatch_lds<false>(L.lds, StackedBases{L.lds}, L.width);
+    case Kernel::LdsRanks:
+        if (L.grid_y != 1 || L.grid_z != 1) return 7;
+        if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
+            L.lds.p_rank != 0 || L.lds.a_rank != 0)
+            return 3;
+        return L.mode ? dispatch_lds<true>(L.lds, TableBases{L.lds_tab}, L.width)
+                      : dispatch_lds<false>(L.lds, TableBases{L.lds_tab}, L.width);
     case Kernel::Copy:
         return dispatch_copy(L.copy, L.width);
     case Kernel::Wait:

@@ -65,7 +65,9 @@ def emu_ranks(lib, shape, mode, first, count, in_mis=None, out_mis=None, seed=0,
         rc = lib.ua2a_exchange_ranks(h, mode, _tab(in_ptrs), _tab([b.ptr for b in xout]),
                                      first, count, None)
         assert rc == 0, (rc, lib.ua2a_plan_last_error(h))
-        assert lib.ua2a_emu_launches() == 1 and lib.ua2a_emu_kernel_count(3) == 1
+        # one launch: the per-rank direct kernel (3) or the per-rank LDS kernel (6)
+        want_kernel = 6 if info.path == ua.UA2A_PATH_LDS else 3
+        assert lib.ua2a_emu_launches() == 1 and lib.ua2a_emu_kernel_count(want_kernel) == 1
     finally:
         lib.ua2a_destroy(h)
     return ([b.view.copy() for b in xin], [b.view.copy() for b in xout], info, xin + xout)
@@ -312,3 +314,68 @@ def test_emulated_ranks_random_cases_match_oracle(emu, case):
     want = oracle_ranks(xs, shape, mode, first, count)
     assert all(np.array_equal(ys[k], want[k]) for k in range(shape[0])), (case, info.vector_bytes)
     assert all(b.guards_intact() for b in bufs), case
+
+
+def test_per_rank_path_choice(emu):
+    """Short runs take the LDS kernel in mode 0 (any senders) and in mode 1
+    when every rank sends; a partial mode-1 sender range and whole-line runs
+    take the direct kernel; a forced path is honoured where it applies."""
+    lib = emu
+    # 64 B runs with w = 8 (a mode-1 tile would read 128 B per head block) and 1 KiB runs
+    short, long_ = (8, 1, 40, 8, 32, 2), (4, 1, 40, 8, 256, 2)
+
+    def path(shape, mode, first, count, force=ua.UA2A_PATH_AUTO):
+        w, B, S, H, D, e = shape
+        n = _layout(lib, shape).tensor_bytes // w
+        big = Buf(2 * w * n)
+        ins = [big.ptr + k * n for k in range(w)]
+        outs = [big.ptr + (w + k) * n for k in range(w)]
+        h = ctypes.c_void_p()
+        assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, 0, None, 0, 0) == 0
+        try:
+            assert lib.ua2a_plan_set_path(h, force) == 0
+            info = ua.ua2a_launch_info_t()
+            assert lib.ua2a_describe_ranks(h, mode, _tab(ins), _tab(outs), first, count,
+                                           ctypes.byref(info)) == 0
+            return info.path, info.lds_rows
+        finally:
+            lib.ua2a_destroy(h)
+
+    L, Dp = ua.UA2A_PATH_LDS, ua.UA2A_PATH_DIRECT
+    assert path(short, 0, 0, 8)[0] == L and path(short, 0, 2, 1)[0] == L
+    assert path(short, 1, 0, 8)[0] == L and path(short, 1, 1, 2)[0] == Dp
+    assert path(long_, 0, 0, 4)[0] == Dp and path(long_, 1, 0, 4)[0] == Dp
+    assert path(long_, 0, 0, 4, L)[0] == L and path(long_, 1, 1, 2, L)[0] == Dp
+    assert path(short, 0, 0, 8, Dp) == (Dp, 0)
+    assert path(short, 0, 1, 3)[1] > 0
+    for shape in (short, long_):
+        w = shape[0]
+        for mode, first, count in ((0, 0, w), (0, 1, 2), (1, 0, w)):
+            for force in (ua.UA2A_PATH_AUTO, L, Dp):
+                xs, ys, info, bufs = _forced(lib, shape, mode, first, count, force)
+                want = oracle_ranks(xs, shape, mode, first, count)
+                assert all(np.array_equal(ys[k], want[k]) for k in range(w)), (shape, mode, force)
+                assert all(b.guards_intact() for b in bufs)
+
+
+def _forced(lib, shape, mode, first, count, force):
+    """emu_ranks with a forced path (set on the plan before the call)."""
+    w, B, S, H, D, e = shape
+    n = _layout(lib, shape).tensor_bytes // w
+    xin = [Buf(n) for _ in range(w)]
+    for k, b in enumerate(xin):
+        b.view[:] = rand_bytes(n, 50 + k)
+    xout = [Buf(n) for _ in range(w)]
+    for b in xout:
+        b.view[:] = FILL
+    h = ctypes.c_void_p()
+    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, 0, None, 0, 0) == 0
+    try:
+        assert lib.ua2a_plan_set_path(h, force) == 0
+        info = ua.ua2a_launch_info_t()
+        tin, tout = _tab([b.ptr for b in xin]), _tab([b.ptr for b in xout])
+        assert lib.ua2a_describe_ranks(h, mode, tin, tout, first, count, ctypes.byref(info)) == 0
+        assert lib.ua2a_exchange_ranks(h, mode, tin, tout, first, count, None) == 0
+    finally:
+        lib.ua2a_destroy(h)
+    return [b.view.copy() for b in xin], [b.view.copy() for b in xout], info, xin + xout

@@ -67,14 +67,15 @@ UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t ti
 //   mode 0: the P span itself (contiguous 16-byte chunks);
 //   mode 1: the w A spans, each read as contiguous chunks and scattered
 //           into its runs' places in the image in G-byte pieces.
-template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U>
-UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t* lds)
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases>
+UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, uint32_t tid,
+                      uint8_t* lds)
 {
     if (!MODE1) {
-        const uint8_t* pchunk0 = g.p_ptr + d.p_start - d.head;   // 16-aligned
+        const uint8_t* pchunk0 = d.p_span - d.head;   // 16-aligned
         const uint32_t pch = span_chunks(d.head, d.p_len);
         for (uint32_t c0 = tid; c0 < pch; c0 += BS * U) {
-            u32x4 v[U];
+            u32x4 v[U] = {};
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k) {
                 const uint32_t c = c0 + k * BS;
@@ -106,7 +107,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
                 if (i >= total) continue;
                 const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t c = i - r * stride;
-                const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
+                const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
                 if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
                     v[k] = Mem::ld(reinterpret_cast<const u32x4*>(aspan - ahead + c * 16));
@@ -117,7 +118,7 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
                 if (i >= total) continue;
                 const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t c = i - r * stride;
-                const uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
+                const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
                 if (c >= span_chunks(ahead, d.a_len)) continue;
                 if (chunk_full(c * 16, ahead, d.a_len))
@@ -133,8 +134,9 @@ UA2A_HD void lds_fill(const LdsGeom& g, const LdsTile& d, uint32_t tid, uint8_t*
 //   mode 0: each of the w A spans, gathered from the image, written as
 //           contiguous 16-byte chunks;
 //   mode 1: the P span, copied out of the image as contiguous chunks.
-template <class Mem, int G, bool MODE1, uint32_t BS>
-UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const uint8_t* lds)
+template <class Mem, int G, bool MODE1, uint32_t BS, class Bases>
+UA2A_HD void lds_drain(const LdsGeom& g, const Bases& bases, const LdsTile& d, uint32_t tid,
+                       const uint8_t* lds)
 {
     if (!MODE1) {
         // the w spans' chunks as one flat index space (see lds_fill)
@@ -143,7 +145,7 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
         for (uint32_t i = tid; i < total; i += BS) {
             const uint32_t r = fdiv(i, d.d_stride);
             const uint32_t c = i - r * stride;
-            uint8_t* aspan = g.a_ptr + d.a_start0 + static_cast<int64_t>(r) * g.a_rank;
+            uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
             const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
             if (c >= span_chunks(ahead, d.a_len)) continue;
             const uint32_t lo = c * 16;
@@ -153,7 +155,7 @@ UA2A_HD void lds_drain(const LdsGeom& g, const LdsTile& d, uint32_t tid, const u
                 a_partial_from_lds<G>(g, d, r, lo, ahead, lds, aspan - ahead);
         }
     } else {
-        uint8_t* pchunk0 = g.p_ptr + d.p_start - d.head;
+        uint8_t* pchunk0 = d.p_span - d.head;
         const uint32_t pch = span_chunks(d.head, d.p_len);
         for (uint32_t c = tid; c < pch; c += BS) {
             const uint32_t lo = c * 16;

@@ -344,6 +344,7 @@ struct LdsGeom {
     uint32_t tiles_per_plane;  // ceil(s_local / rows_per_tile)
     uint32_t num_tiles;        // w * nb * tiles_per_plane
     uint32_t w, nb;
+    uint32_t j0;               // first P-side rank the tiles cover (per-rank form: first sender)
     uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * lrow)
     uint32_t stride_full;      // 16-byte chunk slots per A span: tile of rows_per_tile rows
     uint32_t stride_last;      // ... and the plane's last tile
@@ -351,8 +352,9 @@ struct LdsGeom {
 };
 
 struct LdsTile {
-    int64_t p_start;   // byte offset of the P span (from p_ptr)
-    int64_t a_start0;  // byte offset of the A span of head block r = 0 (from a_ptr)
+    int64_t p_start;   // byte offset of the P span from its rank's base
+    int64_t a_start0;  // byte offset of each A span from its head block's base
+    uint8_t* p_span;   // the P span's first byte
     uint32_t p_len;    // rows * row
     uint32_t a_len;    // rows * run (each of the w A spans)
     uint32_t head;     // (p_ptr + p_start) mod 16: LDS position of the span's first byte
@@ -360,22 +362,55 @@ struct LdsTile {
     Div32 d_stride;
 };
 
-UA2A_HD LdsTile lds_tile(const LdsGeom& g, uint32_t t)
+// Where a tile's spans live.  Rank-stacked tensors: bases plus rank strides.
+struct StackedBases {
+    const LdsGeom& g;
+    UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return g.p_ptr + static_cast<int64_t>(j) * g.p_rank; }
+    UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return g.a_ptr + static_cast<int64_t>(r) * g.a_rank; }
+};
+
+// Per-rank allocations: one base pointer per rank and side (the rank strides
+// of the geometry are 0).  The P table is indexed by the tile's rank (one per
+// workgroup), the A table by each lane's head block.
+struct LdsTables {
+    uint8_t* p[kMaxRankTable];
+    uint8_t* a[kMaxRankTable];
+};
+
+struct TableBases {
+    const LdsTables& t;
+    UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return t.p[j]; }
+    UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return t.a[r]; }
+};
+
+// The same with the A table copied to a workgroup-local array first, so the
+// per-lane lookups of the (span, chunk) loops read LDS, not the kernel
+// argument in memory.
+struct StagedTableBases {
+    const LdsTables& t;
+    uint8_t* const* a;
+    UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return t.p[j]; }
+    UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return a[r]; }
+};
+
+template <class Bases>
+UA2A_HD LdsTile lds_tile(const LdsGeom& g, const Bases& bases, uint32_t t)
 {
     const uint32_t jb = fdiv(t, g.d_tpp);
     const uint32_t tt = t - jb * g.tiles_per_plane;
-    const uint32_t j = fdiv(jb, g.d_nb);
-    const uint32_t b = jb - j * g.nb;
+    const uint32_t jr = fdiv(jb, g.d_nb);
+    const uint32_t b = jb - jr * g.nb;
+    const uint32_t j = g.j0 + jr;
     const uint32_t s0 = tt * g.rows_per_tile;
     const uint32_t rows = umin32(g.rows_per_tile, g.s_local - s0);
     LdsTile d;
-    d.p_start = static_cast<int64_t>(j) * g.p_rank + static_cast<int64_t>(b) * g.p_plane +
-                static_cast<int64_t>(s0) * g.row;
+    d.p_start = static_cast<int64_t>(b) * g.p_plane + static_cast<int64_t>(s0) * g.row;
     d.a_start0 = static_cast<int64_t>(b) * g.a_plane +
                  (static_cast<int64_t>(j) * g.s_local + s0) * g.run;
     d.p_len = rows * g.row;
     d.a_len = rows * g.run;
-    d.head = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g.p_ptr + d.p_start) & 15u);
+    d.p_span = bases.p_rank_base(j) + d.p_start;
+    d.head = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(d.p_span) & 15u);
     const bool full = rows == g.rows_per_tile;
     d.stride = full ? g.stride_full : g.stride_last;
     d.d_stride = full ? g.d_stride_full : g.d_stride_last;

@@ -433,6 +433,41 @@ void prepare_ranks(const ua2a_plan_s* p, int32_t mode, const void* const* in, vo
     for (int32_t k = 0; k < p->w; ++k)
         vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out[k])));
 
+    // The LDS kernel moves whole P rows, so it serves mode 0 (every sender's
+    // rows are its own) and mode 1 only when every rank sends (each written
+    // row is then complete); the choice between the two follows ua2a_exchange.
+    const uint32_t rows = (mode == 0 || count == p->w) ? lds_rows(p, mode, vb) : 0;
+    bool use_lds;
+    if (p->path == UA2A_PATH_DIRECT || rows == 0)
+        use_lds = false;
+    else if (p->path == UA2A_PATH_LDS)
+        use_lds = true;
+    else
+        use_lds = !(vb == 16 && direct_reads_whole_lines(mode, p->w, run));
+    if (use_lds) {
+        L->kernel = Kernel::LdsRanks;
+        L->block = kLdsBlock;
+        L->width = static_cast<int32_t>(vb);
+        L->mode = mode;
+        L->grid_y = L->grid_z = 1;
+        // bases come from the tables: rank strides 0, plane strides within a rank
+        L->lds = make_lds(p, mode, vb, nullptr, nullptr, 0, plane, 0, plane,
+                          static_cast<uint32_t>(p->B));
+        L->lds.j0 = mode == 0 ? static_cast<uint32_t>(first) : 0u;
+        const uint32_t nj = mode == 0 ? static_cast<uint32_t>(count) : static_cast<uint32_t>(p->w);
+        L->lds.num_tiles = nj * L->lds.nb * L->lds.tiles_per_plane;
+        L->lds_bytes = L->lds.lds_bytes;
+        for (int32_t k = 0; k < p->w; ++k) {
+            uint8_t* inb = const_cast<uint8_t*>(static_cast<const uint8_t*>(
+                (k >= first && k < last) ? in[k] : nullptr));
+            uint8_t* outb = static_cast<uint8_t*>(out[k]);
+            L->lds_tab.p[k] = mode == 0 ? inb : outb;
+            L->lds_tab.a[k] = mode == 0 ? outb : inb;
+        }
+        L->grid = grid_for(L->lds.num_tiles, p->blocks, kLdsBlock);
+        return;
+    }
+
     RanksGeom& g = L->ranks;
     for (int32_t k = 0; k < p->w; ++k) {
         g.dst[k] = static_cast<uint8_t*>(out[k]);
@@ -768,14 +803,16 @@ int ua2a_describe_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
     Launch L;
     prepare_ranks(plan, mode, in_ptrs, out_ptrs, first, count, &L);
     memset(info, 0, sizeof *info);
-    info->path = UA2A_PATH_DIRECT;
+    const bool lds = L.kernel == Kernel::LdsRanks;
+    info->path = lds ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
     info->vector_bytes = L.width;
     info->grid = static_cast<int32_t>(static_cast<uint64_t>(L.grid) * L.grid_y * L.grid_z);
     info->block = static_cast<int32_t>(L.block);
-    info->tiles = static_cast<int64_t>(L.ranks.tiles_per_slab) * L.ranks.ny * L.ranks.nz;
+    info->tiles = lds ? static_cast<int64_t>(L.lds.num_tiles)
+                      : static_cast<int64_t>(L.ranks.tiles_per_slab) * L.ranks.ny * L.ranks.nz;
     info->launches = 1;
-    info->lds_rows = 0;
-    info->grid_dims = 3;
+    info->lds_rows = lds ? static_cast<int32_t>(L.lds.rows_per_tile) : 0;
+    info->grid_dims = lds ? 1 : 3;
     return UA2A_OK;
 }
 

@@ -39,7 +39,8 @@ constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row
 constexpr int64_t kLineBytes = 128;             // cache line: LDS tiles align their A spans to it
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
-enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5 };
+enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5,
+                              LdsRanks = 6 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -56,6 +57,7 @@ struct Launch {
     LdsGeom lds;
     CopyGeom copy;
     RanksGeom ranks;
+    LdsTables lds_tab;   // LdsRanks: the per-rank bases of `lds`
     WaitGeom wait;
     SignalGeom signal;
 };

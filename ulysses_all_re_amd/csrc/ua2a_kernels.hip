@@ -18,7 +18,8 @@
 //  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
 //    to move the one-plane window into the output.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
-//    allocations (pointer tables) and a range of sending ranks.
+//    allocations (pointer tables) and a range of sending ranks;
+//    ua2a_lds_ranks_kernel -- the LDS kernel over them.
 //  * ua2a_signal_kernel  -- adds the readiness credits of a publishing
 //    exchange's last part (earlier parts' credits are added by the next
 //    part's first workgroup); ua2a_wait_kernel -- one wave that waits for
@@ -101,19 +102,36 @@ __global__ __launch_bounds__(kWaitBlock) void ua2a_wait_kernel(WaitGeom g)
     if (!ok) __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, bool MODE1>
-__global__ __launch_bounds__(kLdsBlock) void ua2a_lds_kernel(LdsGeom g)
+template <int G, bool MODE1, class Bases>
+__device__ __forceinline__ void lds_tiles(const LdsGeom& g, const Bases& bases)
 {
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
     for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
-        const LdsTile d = lds_tile(g, t);
+        const LdsTile d = lds_tile(g, bases, t);
         // two loads in flight per lane pay off only with 16-byte pieces (measured)
-        lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, d, threadIdx.x, lds);
+        lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
         __syncthreads();
-        lds_drain<StreamMem, G, MODE1, kLdsBlock>(g, d, threadIdx.x, lds);
+        lds_drain<StreamMem, G, MODE1, kLdsBlock>(g, bases, d, threadIdx.x, lds);
         __syncthreads();   // the next tile overwrites the LDS image
     }
+}
+
+template <int G, bool MODE1>
+__global__ __launch_bounds__(kLdsBlock) void ua2a_lds_kernel(LdsGeom g)
+{
+    lds_tiles<G, MODE1>(g, StackedBases{g});
+}
+
+// The same over per-rank allocations (pointer tables); the A table, read
+// per lane, is staged in LDS once per workgroup.
+template <int G, bool MODE1>
+__global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, LdsTables tab)
+{
+    __shared__ uint8_t* a_tab[kMaxRankTable];
+    for (uint32_t i = threadIdx.x; i < g.w; i += kLdsBlock) a_tab[i] = tab.a[i];
+    __syncthreads();
+    lds_tiles<G, MODE1>(g, StagedTableBases{tab, a_tab});
 }
 
 // Per-rank allocations (pointer tables, sender range): one tile per
@@ -183,6 +201,19 @@ const void* lds_fn(int g)
     }
 }
 
+template <bool MODE1>
+const void* lds_ranks_fn(int g)
+{
+    switch (g) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_lds_ranks_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_lds_ranks_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_lds_ranks_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_lds_ranks_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_lds_ranks_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
 template <bool MODE1, bool TWO>
 const void* ranks_fn(int vb)
 {
@@ -225,6 +256,7 @@ int backend_launch(const Launch& L, void* stream)
 {
     const void* fn = nullptr;
     void* arg = nullptr;
+    void* arg2 = nullptr;      // the second kernel argument, if any
     DirectGeom dg = L.direct;
     LdsGeom lg = L.lds;
     CopyGeom cg = L.copy;
@@ -237,6 +269,12 @@ int backend_launch(const Launch& L, void* stream)
     case Kernel::Lds:
         fn = L.mode ? lds_fn<true>(L.width) : lds_fn<false>(L.width);
         arg = &lg;
+        shmem = L.lds_bytes;
+        break;
+    case Kernel::LdsRanks:
+        fn = L.mode ? lds_ranks_fn<true>(L.width) : lds_ranks_fn<false>(L.width);
+        arg = &lg;
+        arg2 = const_cast<LdsTables*>(&L.lds_tab);
         shmem = L.lds_bytes;
         break;
     case Kernel::Copy:
@@ -260,7 +298,7 @@ int backend_launch(const Launch& L, void* stream)
         break;
     }
     if (fn == nullptr) return static_cast<int>(hipErrorInvalidValue);
-    void* args[] = {arg};
+    void* args[] = {arg, arg2};
     const hipError_t e = hipLaunchKernel(fn, dim3(L.grid, L.grid_y, L.grid_z), dim3(L.block), args, shmem,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? 0 : static_cast<int>(e);
