@@ -170,9 +170,11 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked,
  * The tables are read during the call only (copied into the launch); the
  * tensors are borrowed as in ua2a_exchange.  Each used pointer must be
  * elem_bytes-aligned; outputs may overlap neither each other nor a used
- * input.  One launch of the direct kernel scheme (never the LDS path; the
- * plan's window and chunked mode do not apply).  w <= 64 (the tables travel
- * in the kernel argument).
+ * input.  One launch: the kernel family is chosen as for ua2a_exchange (and
+ * ua2a_plan_set_path applies), except that mode 1 with part of the senders
+ * always takes the direct family, whose writes need not cover whole rows.
+ * The plan's window and chunked mode do not apply.  w <= 64 (the tables
+ * travel in the kernel argument).
  * Errors: INVALID_ARG (NULL table or used entry, mode, first/count out of
  * range), SHAPE (w > 64), ALIGN, ALIAS, DEVICE (no state change); HIP
  * (the plan becomes disabled); DISABLED.
