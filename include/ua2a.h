@@ -81,10 +81,10 @@ typedef struct ua2a_layout_s {
 typedef struct ua2a_launch_info_s {
     int32_t path;          /* UA2A_PATH_DIRECT or UA2A_PATH_LDS */
     int32_t vector_bytes;  /* bytes per lane access of the permutation kernel (1..16) */
-    int32_t grid;          /* workgroups of the permutation kernel per launch (all dimensions) */
     int32_t block;         /* threads per workgroup */
-    int64_t tiles;         /* work tiles per launch */
     int32_t launches;      /* kernel launches per exchange (2*B when chunked: B permutes + B copies) */
+    int64_t grid;          /* workgroups of the permutation kernel per launch (all dimensions) */
+    int64_t tiles;         /* work tiles per launch */
     int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
     int32_t grid_dims;     /* 3: a 3-D grid (direct path by default, every per-rank launch); else 1 */
 } ua2a_launch_info_t;

@@ -84,9 +84,9 @@ static int run_case(int k, int32_t w, int64_t B, int64_t S, int64_t H, int64_t D
     if (ua2a_plan_last_error(plan)[0] != '\0') return 1;
     UA_OK(ua2a_exchange(plan, 0, 1, in, out, stream));
     HIP_OK(hipStreamSynchronize(stream));
-    printf("case %d: w=%d B=%lld S=%lld H=%lld D=%lld path=%d vector=%d grid=%d -> ok\n", k, w,
+    printf("case %d: w=%d B=%lld S=%lld H=%lld D=%lld path=%d vector=%d grid=%lld -> ok\n", k, w,
            (long long)B, (long long)S, (long long)H, (long long)D, info.path, info.vector_bytes,
-           info.grid);
+           (long long)info.grid);
     UA_OK(ua2a_destroy(plan));
     HIP_OK(hipStreamDestroy(stream));
     HIP_OK(hipFree(in));

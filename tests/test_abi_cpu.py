@@ -118,6 +118,31 @@ def test_huge_launches_stay_within_a_dispatch(lib, shape, mode, path, blocks):
         ua.ua2a_destroy(h)
 
 
+@pytest.mark.parametrize("shape,blocks,dims", [
+    ((16, 2 ** 21 + 1, 1, 16, 128, 2), 0, 1),    # 4 KiB rows: padding to whole groups would pass 2^32 tiles
+    ((65535, 1, 1, 65535, 1, 1), 0, 3),          # 1-byte runs: a 3-D grid of 65535^2 workgroups
+    ((65535, 1, 1, 65535, 1, 1), 2 ** 25, 1),    # ... or a flat grid looping over them
+])
+def test_tile_counts_near_2_32_are_exact(lib, shape, blocks, dims):
+    """Mode 0 needs one tile per KiB of each (r, b, j) slab: the launch counts
+    every one of them, in a grid the report does not truncate."""
+    w, B, S, H, D, e = shape
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    h = ua.ua2a_plan(w, B, S, H, D, e, blocks)
+    try:
+        base = 1 << 44
+        info = ua.ua2a_describe(h, 0, 0, base, base + lay["tensor_bytes"])
+        slab = S * lay["run_bytes"]
+        assert info["path"] == ua.UA2A_PATH_DIRECT and info["grid_dims"] == dims
+        assert info["tiles"] == w * w * B * -(-slab // 1024)
+        if dims == 3:
+            assert info["grid"] == info["tiles"] > 2 ** 31
+        else:
+            assert info["grid"] * info["block"] <= 2 ** 31
+    finally:
+        ua.ua2a_destroy(h)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ua, "_lib", None)
     monkeypatch.setattr(ua, "LIBRARY", str(tmp_path / "libua2a.so"))

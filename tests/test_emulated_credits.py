@@ -164,6 +164,8 @@ def test_credit_argument_errors(emu):
     assert wc(c, -1, 4, 1, s) == ua.UA2A_ERR_INVALID_ARG
     assert wc(c, 0, 4, 0, s) == ua.UA2A_ERR_INVALID_ARG           # spin_limit 0
     assert wc(c, 2 ** 32 - 2, 4, 1, s) == ua.UA2A_ERR_INVALID_ARG
+    assert wc(c, 2 ** 63 - 1, 4, 1, s) == ua.UA2A_ERR_INVALID_ARG     # first + count overflows
+    assert wc(c, 0, 2 ** 32, 1, s) == ua.UA2A_ERR_INVALID_ARG
     assert wc(c + 1, 0, 4, 1, s) == ua.UA2A_ERR_ALIGN
     assert wc(c, 0, 4, 1, s + 2) == ua.UA2A_ERR_ALIGN
     assert wc(c, 0, 4, 1, c + 8) == ua.UA2A_ERR_ALIAS              # status among the counters

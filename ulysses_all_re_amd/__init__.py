@@ -61,8 +61,8 @@ class ua2a_layout_t(ctypes.Structure):
 
 class ua2a_launch_info_t(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("tiles", ctypes.c_int64), ("launches", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("launches", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("lds_rows", ctypes.c_int32), ("grid_dims", ctypes.c_int32)]
 
 

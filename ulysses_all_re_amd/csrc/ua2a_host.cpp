@@ -102,15 +102,19 @@ DirectGeom make_direct(const ua2a_plan_s* p, uint32_t vb, uint8_t* p_ptr, uint8_
     // mode 0 reads one head-block column of P rows per slab: when the row
     // stride is a multiple of 4 KiB, cycle head blocks fastest (measured:
     // slab after slab is up to 20 % slower there)
+    // (the grouped order pads each slab to whole groups; it is skipped when
+    // the padded tile count would not fit the kernel's 32-bit tile index)
     const int64_t row_bytes = run * p->w;
-    g.group = (allow_group && mode == 0 && p->w > 1 && row_bytes % kDirectGroupRowAlign == 0)
-                  ? kDirectGroup : 0;
-    if (g.group) {
-        g.groups = (g.tiles_per_slab + g.group - 1) / g.group;
-        g.num_tiles = static_cast<uint32_t>(static_cast<uint64_t>(g.groups) * g.group * slabs);
-    } else {
-        g.num_tiles = static_cast<uint32_t>(slabs * g.tiles_per_slab);   // bounded by the tensor limit
+    if (allow_group && mode == 0 && p->w > 1 && row_bytes % kDirectGroupRowAlign == 0) {
+        const uint64_t groups = (g.tiles_per_slab + kDirectGroup - 1) / kDirectGroup;
+        if (groups * kDirectGroup * slabs <= UINT32_MAX) {
+            g.group = kDirectGroup;
+            g.groups = static_cast<uint32_t>(groups);
+            g.num_tiles = static_cast<uint32_t>(groups * kDirectGroup * slabs);
+        }
     }
+    if (!g.group)   // < 2^32: one tile per slab needs slabs < 2^32 runs, more needs >= 1 KiB per slab
+        g.num_tiles = static_cast<uint32_t>(slabs * g.tiles_per_slab);
     g.d_vr = make_div32(g.vr);
     g.d_prow = make_div32(g.p_row);
     g.d_tps = make_div32(g.tiles_per_slab);
@@ -712,7 +716,8 @@ int ua2a_wait_credits(const uint32_t* credits, int64_t first, int64_t count, uin
                       uint32_t spin_limit, int32_t* status, void* stream)
 {
     if (credits == nullptr || status == nullptr) return UA2A_ERR_INVALID_ARG;
-    if (first < 0 || count < 1 || first + count > int64_t(UINT32_MAX) || spin_limit < 1)
+    if (first < 0 || count < 1 || count > int64_t(UINT32_MAX) ||
+        first > int64_t(UINT32_MAX) - count || spin_limit < 1)
         return UA2A_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(credits) % sizeof(uint32_t) ||
         reinterpret_cast<uintptr_t>(status) % sizeof(int32_t))
@@ -783,7 +788,7 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     memset(info, 0, sizeof *info);
     info->path = pr.path;
     info->vector_bytes = pr.perm.width;
-    info->grid = static_cast<int32_t>(static_cast<uint64_t>(pr.perm.grid) * pr.perm.grid_y *
+    info->grid = static_cast<int64_t>(static_cast<uint64_t>(pr.perm.grid) * pr.perm.grid_y *
                                       pr.perm.grid_z);
     info->block = static_cast<int32_t>(pr.perm.block);
     info->tiles = pr.perm.kernel == Kernel::Direct ? pr.perm.direct.num_tiles : pr.perm.lds.num_tiles;
@@ -806,7 +811,7 @@ int ua2a_describe_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
     const bool lds = L.kernel == Kernel::LdsRanks;
     info->path = lds ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
     info->vector_bytes = L.width;
-    info->grid = static_cast<int32_t>(static_cast<uint64_t>(L.grid) * L.grid_y * L.grid_z);
+    info->grid = static_cast<int64_t>(static_cast<uint64_t>(L.grid) * L.grid_y * L.grid_z);
     info->block = static_cast<int32_t>(L.block);
     info->tiles = lds ? static_cast<int64_t>(L.lds.num_tiles)
                       : static_cast<int64_t>(L.ranks.tiles_per_slab) * L.ranks.ny * L.ranks.nz;

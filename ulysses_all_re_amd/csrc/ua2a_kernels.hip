@@ -60,9 +60,10 @@ template <int VB, bool MODE1, bool SIG>
 __global__ __launch_bounds__(kDirectBlock) void ua2a_direct_kernel(DirectGeom g)
 {
     if (SIG && blockIdx.x == 0) add_credits(g.sig_credits, g.sig_first, g.sig_count);
-    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
+    // 64-bit tile counter: t + gridDim.x may pass 2^32 when num_tiles is near it
+    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
         direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
-            g, direct_tile<MODE1>(g, t), threadIdx.x);
+            g, direct_tile<MODE1>(g, static_cast<uint32_t>(t)), threadIdx.x);
 }
 
 // One tile per workgroup on a 3-D grid (see direct_tile_3d).
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kWaitBlock) void ua2a_signal_kernel(SignalGeom g)
 __global__ __launch_bounds__(kWaitBlock) void ua2a_wait_kernel(WaitGeom g)
 {
     bool ok = true;
-    for (uint32_t i = threadIdx.x; i < g.count && ok; i += kWaitBlock) {
+    for (uint64_t i = threadIdx.x; i < g.count && ok; i += kWaitBlock) {
         const uint32_t* c = g.credits + g.first + i;
         uint32_t polls = 1;
         while (!credit_reached(__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT),
@@ -107,8 +108,8 @@ __device__ __forceinline__ void lds_tiles(const LdsGeom& g, const Bases& bases)
 {
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
-    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
-        const LdsTile d = lds_tile(g, bases, t);
+    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
+        const LdsTile d = lds_tile(g, bases, static_cast<uint32_t>(t));
         // two loads in flight per lane pay off only with 16-byte pieces (measured)
         lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
         __syncthreads();
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_ranks_kernel(RanksGeom g)
 template <int VB>
 __global__ __launch_bounds__(kCopyBlock) void ua2a_copy_kernel(CopyGeom g)
 {
-    for (uint32_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
-        copy_tile_body<StreamMem, VB, kCopyBlock, kDirectUnroll>(g, t, threadIdx.x);
+    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
+        copy_tile_body<StreamMem, VB, kCopyBlock, kDirectUnroll>(g, static_cast<uint32_t>(t), threadIdx.x);
 }
 
 namespace {
