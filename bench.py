@@ -25,7 +25,7 @@ workload.  A device-to-device copy of the same byte count is timed beside it
 
 reads the counter CSVs of two rocprofv3 --pmc runs (FETCH_SIZE, then
 WRITE_SIZE) under DIR and writes profiles/traffic_direct_video_dit.json, which
-later runs report as roofline.traffic while the kernel sources are unchanged.
+later runs report as roofline.traffic while the built library is unchanged.
 """
 from __future__ import annotations
 

@@ -5,9 +5,10 @@ kernels in libua2a.so.  PyTorch is used for device memory and streams.
 
 The functions mirror the C ABI of include/ua2a.h one to one
 (``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``, ``ua2a_exchange_ranks``,
-``ua2a_destroy``, ``ua2a_status_string``, ``ua2a_plan_last_error``,
-``ua2a_plan_set_path``, ``ua2a_describe``, ``ua2a_describe_ranks``) and raise
-:class:`UA2AError` on a non-zero status.
+``ua2a_exchange_publish``, ``ua2a_wait_credits``, ``ua2a_destroy``,
+``ua2a_status_string``, ``ua2a_plan_last_error``, ``ua2a_plan_set_path``,
+``ua2a_describe``, ``ua2a_describe_ranks``) and raise :class:`UA2AError` on a
+non-zero status.
 :class:`Plan` wraps them for torch tensors laid out rank-stacked:
 
     mode 0 input  [w, B, S_local, H, D]        -> output [w, B, S_local*w, H//w, D]
@@ -207,12 +208,15 @@ def wait_credits(credits, first: int, count: int, target: int, status, spin_limi
         raise TypeError("credits and status must be 4-byte integer tensors")
     if not (credits.is_contiguous() and credits.is_cuda and status.is_cuda):
         raise ValueError("credits and status must be contiguous device tensors")
+    if status.device != credits.device:
+        raise ValueError(f"status is on {status.device}, credits are on {credits.device}")
     if first < 0 or count < 1 or first + count > credits.numel():
         raise ValueError(f"slab range [{first}, {first + count}) is outside the {credits.numel()} counters")
     if stream is None:
         stream = torch.cuda.current_stream(credits.device)
-    ua2a_wait_credits(credits.data_ptr(), first, count, target, spin_limit, status.data_ptr(),
-                      stream.cuda_stream)
+    with torch.cuda.device(credits.device):     # launch on the counters' device
+        ua2a_wait_credits(credits.data_ptr(), first, count, target, spin_limit, status.data_ptr(),
+                          stream.cuda_stream)
 
 
 def ua2a_destroy(plan: int) -> None:
@@ -250,8 +254,11 @@ class Plan:
         self.w, self.B, self.S_local, self.H, self.D = w, B, S_local, H, D
         self.dtype = dtype
         self.elem_bytes = torch.empty((), dtype=dtype).element_size()
-        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
-                                   else torch.device(device).index or 0)
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError(f"a plan lives on a GPU, not on {dev}")
+        self.device = torch.device("cuda", torch.cuda.current_device() if dev.index is None
+                                   else dev.index)
         self.layout = ua2a_layout(w, B, S_local, H, D, self.elem_bytes)
         self.window = window
         wptr, wbytes = 0, 0
