@@ -331,7 +331,10 @@ def run_overlap(args):
     Serial: exchange, then the w GEMMs, one stream.  Pipelined: the publishing
     exchange (one part per receiving rank) on the main stream; on a second
     stream, for each r, a wait for r's credit, then r's GEMM.  Prints one JSON
-    line."""
+    line.  `--publish-blocks` caps the grid of the publishing exchange (its
+    parts then loop over their tiles): beside the GEMMs, 8192 single-wave
+    workgroups measured best, ahead of the uncapped one-tile-per-workgroup
+    grid (also timed, as `pipelined_uncapped`) and of smaller caps."""
     import torch
 
     import ulysses_all_re_amd as ua
@@ -344,6 +347,7 @@ def run_overlap(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     plan = ua.Plan(w, B, S, H, D, dt, device=dev)
+    pub = ua.Plan(w, B, S, H, D, dt, blocks=args.publish_blocks, device=dev)
     x = make_tensor((w, B, S, H, D), c["dtype"], "normal", c["seed0"]).to(dev)
     y = torch.empty(plan.out_shape(0), dtype=dt, device=dev)
     k = (H // w) * D
@@ -364,9 +368,9 @@ def run_overlap(args):
         for r in range(w):
             consume(r)
 
-    def pipelined():
+    def pipelined(p=pub):
         main.wait_stream(side)               # the previous step's consumers are done with y
-        plan.exchange_publish(x, 0, credits, out=y, stream=main)
+        p.exchange_publish(x, 0, credits, out=y, stream=main)
         epoch[0] += 1
         for r in range(w):
             ua.wait_credits(credits, r, 1, epoch[0], status, stream=side)
@@ -387,21 +391,23 @@ def run_overlap(args):
     for _ in range(args.warmup):
         serial()
         pipelined()
+        pipelined(plan)
     torch.cuda.synchronize(dev)
     serial()
     ref = z.clone()
-    z.zero_()
-    pipelined()
-    torch.cuda.synchronize(dev)
-    if int(status.item()) != 0:
-        raise SystemExit("a credit wait timed out; refusing to report a number")
-    if not torch.equal(z, ref):
-        raise SystemExit("pipelined consumers saw different data than serial ones")
+    for p in (pub, plan):
+        z.zero_()
+        pipelined(p)
+        torch.cuda.synchronize(dev)
+        if int(status.item()) != 0:
+            raise SystemExit("a credit wait timed out; refusing to report a number")
+        if not torch.equal(z, ref):
+            raise SystemExit("pipelined consumers saw different data than serial ones")
     K = args.steps
     t_exchange = timed(lambda: plan.exchange(x, 0, out=y, stream=main), K)
 
     def publish_only():
-        plan.exchange_publish(x, 0, credits, out=y, stream=main)
+        pub.exchange_publish(x, 0, credits, out=y, stream=main)
         epoch[0] += 1
 
     t_publish = timed(publish_only, K)
@@ -413,6 +419,7 @@ def run_overlap(args):
     t_consume = timed(consume_all, K)
     t_serial = timed(serial, K)
     t_pipe = timed(pipelined, K)
+    t_pipe_uncapped = timed(lambda: pipelined(plan), K)
     if int(status.item()) != 0:
         raise SystemExit("a credit wait timed out; refusing to report a number")
     flops = 2.0 * rows * k * k * w
@@ -423,14 +430,15 @@ def run_overlap(args):
         "dtype": c["dtype"], "data": "synthetic",
         "config": {"workload": name, "w": w, "B": B, "S_local": S, "H": H, "D": D,
                    "consumer": f"per rank: [{rows}, {k}] @ [{k}, {k}] {c['dtype']} GEMM (torch.matmul)",
-                   "parts": w},
+                   "parts": w, "publish_blocks": args.publish_blocks},
         "ms": {"exchange": round(t_exchange, 4), "exchange_publish": round(t_publish, 4),
                "consumers": round(t_consume, 4), "serial": round(t_serial, 4),
-               "pipelined": round(t_pipe, 4)},
+               "pipelined": round(t_pipe, 4), "pipelined_uncapped": round(t_pipe_uncapped, 4)},
         "publish_overhead": round(t_publish / t_exchange - 1, 4),
         "consumer_TFLOPs": round(flops / (t_consume * 1e-3) / 1e12, 1),
     }
     plan.close()
+    pub.close()
     print(json.dumps(result), flush=True)
 
 
@@ -556,6 +564,8 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="time mode 0 + a per-rank consumer GEMM, serial vs pipelined on "
                          "readiness credits (its own JSON line)")
+    ap.add_argument("--publish-blocks", type=int, default=8192,
+                    help="--overlap: grid cap of the publishing exchange (0 = one tile per workgroup)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="buffer sets to rotate through (0 = enough for about 1 GiB per cycle, "
                          "at most 64; 1 for the video-DiT tensors)")
