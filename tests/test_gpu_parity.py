@@ -360,6 +360,37 @@ def test_back_to_back_on_one_stream_and_side_stream():
     plan.close()
 
 
+def test_independent_plans_on_concurrent_streams():
+    """Four plans, two of them chunked with windows of their own, each running
+    three round trips on its own stream with no host sync in between: the
+    plans share no device state, so every stream ends with the oracle's bytes."""
+    cases = [((4, 1, 1024, 24, 128), "bf16", False), ((3, 2, 33, 12, 80), "fp32", True),
+             ((2, 3, 37, 2, 1024), "bf16", True), ((8, 1, 13, 40, 128), "fp16", False)]
+    dts = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    jobs = []
+    for k, ((w, B, S, H, D), dt, chunked) in enumerate(cases):
+        x = make_tensor((w, B, S, H, D), dt, "bytes", 40 + k)
+        e = x.element_size()
+        lay = ua.ua2a_layout(w, B, S, H, D, e)
+        window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV) if chunked else None
+        plan = ua.Plan(w, B, S, H, D, dts[dt], window=window)
+        y = poisoned(plan.out_shape(0), dts[dt])
+        z = poisoned(plan.in_shape(0), dts[dt])
+        jobs.append((plan, x, x.to(DEV), y, z, chunked, torch.cuda.Stream(), oracle_out(x, 0, w)))
+    torch.cuda.synchronize()
+    note("4 plans on 4 concurrent streams, 3 round trips each")
+    for _ in range(3):
+        for plan, _, xd, y, z, chunked, st, _ in jobs:
+            with torch.cuda.stream(st):
+                plan.exchange(xd, 0, chunked, out=y)
+                plan.exchange(y, 1, chunked, out=z)
+    torch.cuda.synchronize()
+    for k, (plan, x, _, y, z, chunked, _, want) in enumerate(jobs):
+        assert_same_bits(y, want, f"stream {k} mode 0")
+        assert_same_bits(z, bits(x), f"stream {k} round trip")
+        plan.close()
+
+
 def test_window_is_reused_and_left_alone_outside_its_size():
     """Chunked planes share one window; bytes past the one-plane size stay untouched."""
     w, B, S, H, D = 4, 3, 100, 8, 32
