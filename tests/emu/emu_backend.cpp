@@ -7,6 +7,8 @@
 // before its drain phase (what the workgroup barrier guarantees on the GPU).
 // Buffers are ordinary host memory, so the same C ABI can be exercised on a
 // machine with no GPU, under AddressSanitizer, and compared with the oracle.
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -83,7 +85,14 @@ void run_lds(const LdsGeom& g, const Bases& bases)
     // exactly lds_bytes, so any access past the reserved LDS is a heap
     // overflow that AddressSanitizer reports
     std::vector<uint8_t> lds(g.lds_bytes);
-    for (uint32_t t = 0; t < g.num_tiles; ++t) {
+    std::vector<uint8_t> seen(g.num_tiles, 0);
+    for (uint32_t slot = 0; slot < g.num_slots; ++slot) {
+        const uint32_t t = lds_slot_tile(g, slot);
+        if (t >= g.num_tiles) continue;
+        if (seen[t]++) {                 // the slot order must visit each tile once
+            fprintf(stderr, "emu: LDS tile %u visited twice\n", t);
+            abort();
+        }
         memset(lds.data(), 0xA5, lds.size());
         const LdsTile d = lds_tile(g, bases, t);
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
@@ -91,6 +100,11 @@ void run_lds(const LdsGeom& g, const Bases& bases)
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
             lds_drain<PlainMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
     }
+    for (uint32_t t = 0; t < g.num_tiles; ++t)
+        if (!seen[t]) {                  // ... and miss none
+            fprintf(stderr, "emu: LDS tile %u never visited\n", t);
+            abort();
+        }
 }
 
 template <int VB>
@@ -213,14 +227,18 @@ int backend_launch(const Launch& L, void*)
     case Kernel::Lds:
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
-            L.lds.lrow != L.lds.row + L.lds.pad || (L.lds.pad && L.width != 16))
+            L.lds.lrow != L.lds.row + L.lds.pad || (L.lds.pad && L.width != 16) ||
+            L.lds.num_slots < L.lds.num_tiles || (L.lds.xlog && L.lds.num_slots % (kXcds << L.lds.xlog) != 0) ||
+            L.grid > L.lds.num_slots)
             return 3;
         return L.mode ? dispatch_lds<true>(L.lds, StackedBases{L.lds}, L.width)
                       : dispatch_lds<false>(L.lds, StackedBases{L.lds}, L.width);
     case Kernel::LdsRanks:
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
-            L.lds.p_rank != 0 || L.lds.a_rank != 0)
+            L.lds.p_rank != 0 || L.lds.a_rank != 0 ||
+            L.lds.num_slots < L.lds.num_tiles || (L.lds.xlog && L.lds.num_slots % (kXcds << L.lds.xlog) != 0) ||
+            L.grid > L.lds.num_slots)
             return 3;
         return L.mode ? dispatch_lds<true>(L.lds, TableBases{L.lds_tab}, L.width)
                       : dispatch_lds<false>(L.lds, TableBases{L.lds_tab}, L.width);

@@ -20,7 +20,56 @@ struct PlainMem {
     UA2A_HD static T ld(const T* p) { return *p; }
     template <class T>
     UA2A_HD static void st(T* p, T v) { *p = v; }
+    // Bytes [lo, hi) of the aligned 16-byte chunk at p, the others zero: the
+    // emulation reads nothing outside a span.  (The kernels read such a chunk
+    // whole; see StreamMem.)
+    UA2A_HD static u32x4 ld_part(const u32x4* p, uint32_t lo, uint32_t hi)
+    {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        uint8_t* to = reinterpret_cast<uint8_t*>(&v);
+        const uint8_t* from = reinterpret_cast<const uint8_t*>(p);
+        for (uint32_t x = lo; x < hi; ++x) to[x] = from[x];
+        return v;
+    }
 };
+
+// The G-byte piece at byte `off` (a multiple of G) of a chunk held in
+// registers; bytes are little-endian within each 32-bit lane of the vector.
+template <int G> struct PieceOf;
+template <> struct PieceOf<16> {
+    UA2A_HD static u32x4 get(u32x4 v, uint32_t) { return v; }
+};
+template <> struct PieceOf<8> {
+    UA2A_HD static uint64_t get(u32x4 v, uint32_t off)
+    {
+        return off == 0 ? (static_cast<uint64_t>(v[1]) << 32) | v[0]
+                        : (static_cast<uint64_t>(v[3]) << 32) | v[2];
+    }
+};
+UA2A_HD uint32_t dword_of(u32x4 v, uint32_t off)
+{
+    const uint32_t d = off >> 2;
+    return d == 0 ? v[0] : d == 1 ? v[1] : d == 2 ? v[2] : v[3];
+}
+template <> struct PieceOf<4> {
+    UA2A_HD static uint32_t get(u32x4 v, uint32_t off) { return dword_of(v, off); }
+};
+template <> struct PieceOf<2> {
+    UA2A_HD static uint16_t get(u32x4 v, uint32_t off)
+    {
+        return static_cast<uint16_t>(dword_of(v, off) >> ((off & 2u) * 8u));
+    }
+};
+template <> struct PieceOf<1> {
+    UA2A_HD static uint8_t get(u32x4 v, uint32_t off)
+    {
+        return static_cast<uint8_t>(dword_of(v, off) >> ((off & 3u) * 8u));
+    }
+};
+
+// The in-chunk byte range of the span [head, head + len) in the chunk at lo.
+UA2A_HD uint32_t part_lo(uint32_t lo, uint32_t head) { return umax32(lo, head) - lo; }
+UA2A_HD uint32_t part_hi(uint32_t lo, uint32_t head, uint32_t len) { return umin32(lo + 16, head + len) - lo; }
 
 // Direct path: the BS lanes move whole VB-byte vectors of the tile; U
 // vectors per lane are loaded before any is stored.
@@ -63,10 +112,65 @@ UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t ti
     }
 }
 
+// A chunk that an A span covers only in part: its first or last chunk when
+// the span starts or ends inside an aligned 16-byte chunk.  Mode 1's fill
+// numbers them as slots, slot = 2 * r + end (end 0: first chunk, 1: last).
+struct PartChunk {
+    const u32x4* src;    // the aligned chunk in global memory
+    uint32_t lo, hi;     // its in-span bytes
+    uint32_t at;         // A-span byte of the chunk's first byte
+    uint32_t r;          // head block
+    bool valid;
+};
+
+template <class Bases>
+UA2A_HD PartChunk a_part_chunk(const LdsGeom& g, const Bases& bases, const LdsTile& d, uint32_t slot)
+{
+    PartChunk pc;
+    pc.valid = false;
+    pc.src = nullptr;
+    pc.lo = pc.hi = pc.at = pc.r = 0;
+    const uint32_t r = slot >> 1, end = slot & 1u;
+    if (r >= g.w) return pc;
+    const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
+    const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+    const uint32_t n = span_chunks(ahead, d.a_len);
+    if (n == 0 || (end == 1 && n == 1)) return pc;       // no chunk, or the first is also the last
+    const uint32_t c = end ? n - 1 : 0;
+    if (chunk_full(c * 16, ahead, d.a_len)) return pc;
+    pc.valid = true;
+    pc.src = reinterpret_cast<const u32x4*>(aspan - ahead + c * 16);
+    pc.lo = part_lo(c * 16, ahead);
+    pc.hi = part_hi(c * 16, ahead, d.a_len);
+    pc.at = c * 16 - ahead;
+    pc.r = r;
+    return pc;
+}
+
+// Place the in-span pieces of a partial A-span chunk, held in registers, in LDS.
+template <int G>
+UA2A_HD void place_a_part_chunk(const LdsGeom& g, const LdsTile& d, const PartChunk& pc, u32x4 v,
+                                uint8_t* lds)
+{
+    typedef typename Piece<G>::T T;
+    for (uint32_t o = pc.lo; o < pc.hi; o += G)
+        *reinterpret_cast<T*>(lds + lds_pos_of_a(g, d, pc.r, pc.at + o)) = PieceOf<G>::get(v, o);
+}
+
 // LDS path, first phase: global -> LDS image of the tile's P rows.
 //   mode 0: the P span itself (contiguous 16-byte chunks);
 //   mode 1: the w A spans, each read as contiguous chunks and scattered
 //           into its runs' places in the image in G-byte pieces.
+// Mode 1 reads its A spans' partial first and last chunks whole as well
+// (one load each, not a chain of piece-sized loads, which stalled the wave
+// at every tile of a span misaligned to 16 bytes): each lane loads the
+// partial chunk of slot tid before the loop, so that load is in flight with
+// the others, and places its pieces after it; slots beyond the workgroup
+// (w > BS / 2) follow in a loop of their own.  The loop itself moves whole
+// chunks only (a heavier loop body measured slower).  Mode 0 moves the P
+// span's partial chunks piece by piece in its loop: a P span starts and ends
+// on a row, so they occur only with a misaligned base, and every other form
+// measured slower on aligned spans.
 template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases>
 UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, uint32_t tid,
                       uint8_t* lds)
@@ -93,6 +197,10 @@ UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, ui
             }
         }
     } else {
+        // with G = 16 every A span is 16-aligned and has no partial chunk
+        const PartChunk pc = G < 16 ? a_part_chunk(g, bases, d, tid) : PartChunk{};
+        u32x4 pv = {0u, 0u, 0u, 0u};
+        if (G < 16 && pc.valid) pv = Mem::ld_part(pc.src, pc.lo, pc.hi);
         // the w spans' chunks as one flat index space, so every lane has work
         // even when one span is shorter than the workgroup; neighbouring lanes
         // take neighbouring chunks of one span (measured faster than putting
@@ -120,12 +228,15 @@ UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, ui
                 const uint32_t c = i - r * stride;
                 const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-                if (c >= span_chunks(ahead, d.a_len)) continue;
-                if (chunk_full(c * 16, ahead, d.a_len))
+                if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
                     scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k], lds);
-                else
-                    a_partial_to_lds<G>(g, d, r, c * 16, ahead, aspan - ahead, lds);
             }
+        }
+        if (G < 16 && pc.valid) place_a_part_chunk<G>(g, d, pc, pv, lds);
+        for (uint32_t slot = tid + BS; G < 16 && slot < 2 * g.w; slot += BS) {
+            const PartChunk more = a_part_chunk(g, bases, d, slot);
+            if (more.valid)
+                place_a_part_chunk<G>(g, d, more, Mem::ld_part(more.src, more.lo, more.hi), lds);
         }
     }
 }

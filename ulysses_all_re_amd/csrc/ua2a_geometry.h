@@ -330,6 +330,17 @@ UA2A_HD void ranks_vector(const RanksGeom& g, const RanksTile& d, uint32_t u, co
 // stride (a multiple of the bank period for power-of-two rows) made them
 // collide.  All units here are bytes.
 //     t = (j * nb + b) * tiles_per_plane + tt      (P-side memory order)
+// Tiles of one plane share a cache line wherever an A span's boundary is not
+// a line boundary (rows * run or the span start not a multiple of 128 bytes,
+// e.g. an odd S_local * run).  Workgroups are dealt round-robin to the
+// chip's XCDs, each with its own L2, so the halves of such a line would be
+// written (or read) through two L2s.  Launch slot L therefore takes tile
+//     t = L - L % (kXcds * K) + (L % kXcds) * K + (L / kXcds) % K,
+// K = 2^xlog: every XCD gets K consecutive tiles in a row, so K - 1 of every
+// K boundaries stay inside one L2, while the kXcds * K tiles in flight at one
+// time still cover one contiguous region.  Slots past num_tiles are empty.
+constexpr uint32_t kXcds = 8;             // XCDs per MI355X, workgroups dealt round-robin
+
 struct LdsGeom {
     uint8_t* p_ptr;            // base of the P-side tensor (read in mode 0, written in mode 1)
     uint8_t* a_ptr;            // base of the A-side tensor (written in mode 0, read in mode 1)
@@ -343,6 +354,8 @@ struct LdsGeom {
     uint32_t rows_per_tile;
     uint32_t tiles_per_plane;  // ceil(s_local / rows_per_tile)
     uint32_t num_tiles;        // w * nb * tiles_per_plane
+    uint32_t num_slots;        // launch slots: num_tiles rounded up to kXcds << xlog
+    uint32_t xlog;             // log2 of the consecutive tiles per XCD turn (0: plain order)
     uint32_t w, nb;
     uint32_t j0;               // first P-side rank the tiles cover (per-rank form: first sender)
     uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * lrow)
@@ -392,6 +405,14 @@ struct StagedTableBases {
     UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return t.p[j]; }
     UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return a[r]; }
 };
+
+// The tile that launch slot L runs (see LdsGeom); >= num_tiles: none.
+UA2A_HD uint32_t lds_slot_tile(const LdsGeom& g, uint32_t L)
+{
+    const uint32_t k = g.xlog;
+    const uint32_t span = kXcds << k;
+    return (L - L % span) + ((L % kXcds) << k) + ((L / kXcds) & ((1u << k) - 1u));
+}
 
 template <class Bases>
 UA2A_HD LdsTile lds_tile(const LdsGeom& g, const Bases& bases, uint32_t t)
@@ -534,17 +555,6 @@ UA2A_HD void a_partial_from_lds(const LdsGeom& g, const LdsTile& d, uint32_t r, 
     for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
         *reinterpret_cast<T*>(achunk0 + x) =
             *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead));
-}
-
-template <int G>
-UA2A_HD void a_partial_to_lds(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t lo,
-                              uint32_t ahead, const uint8_t* achunk0, uint8_t* lds)
-{
-    typedef typename Piece<G>::T T;
-    const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
-    for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
-        *reinterpret_cast<T*>(lds + lds_pos_of_a(g, d, r, x - ahead)) =
-            *reinterpret_cast<const T*>(achunk0 + x);
 }
 
 // ------------------------------------------------------------------------

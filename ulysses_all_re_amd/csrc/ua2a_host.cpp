@@ -180,6 +180,21 @@ uint32_t lds_rows(const ua2a_plan_s* p, int mode, uint32_t G)
     return static_cast<uint32_t>(rows);
 }
 
+// Launch slots of an LDS launch: num_tiles rounded up to whole XCD turns of
+// consecutive tiles (plain order if that would not fit 32 bits).
+void set_lds_slots(LdsGeom* g)
+{
+    g->xlog = kLdsXcdLog;
+    const uint64_t span = uint64_t(kXcds) << g->xlog;
+    const uint64_t slots = (uint64_t(g->num_tiles) + span - 1) / span * span;
+    if (slots > UINT32_MAX) {
+        g->xlog = 0;
+        g->num_slots = g->num_tiles;
+    } else {
+        g->num_slots = static_cast<uint32_t>(slots);
+    }
+}
+
 LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uint8_t* a_ptr,
                  int64_t p_rank, int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
 {
@@ -201,6 +216,7 @@ LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uin
     g.w = static_cast<uint32_t>(p->w);
     g.nb = nb;
     g.num_tiles = g.w * nb * g.tiles_per_plane;
+    set_lds_slots(&g);
     g.lds_bytes = (16 + g.rows_per_tile * g.lrow + 15) & ~15u;
     // chunk slots per A span: exactly its chunks when spans are 16-aligned,
     // else room for an unaligned start (the longest a span can touch)
@@ -353,7 +369,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.width = static_cast<int32_t>(g);
         L.lds = make_lds(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb);
         L.lds_bytes = L.lds.lds_bytes;
-        L.grid = grid_for(L.lds.num_tiles, p->blocks, kLdsBlock);
+        L.grid = grid_for(L.lds.num_slots, p->blocks, kLdsBlock);
     }
     pr->launches = 1;
     if (chunked) {
@@ -460,6 +476,7 @@ void prepare_ranks(const ua2a_plan_s* p, int32_t mode, const void* const* in, vo
         L->lds.j0 = mode == 0 ? static_cast<uint32_t>(first) : 0u;
         const uint32_t nj = mode == 0 ? static_cast<uint32_t>(count) : static_cast<uint32_t>(p->w);
         L->lds.num_tiles = nj * L->lds.nb * L->lds.tiles_per_plane;
+        set_lds_slots(&L->lds);
         L->lds_bytes = L->lds.lds_bytes;
         for (int32_t k = 0; k < p->w; ++k) {
             uint8_t* inb = const_cast<uint8_t*>(static_cast<const uint8_t*>(
@@ -468,7 +485,7 @@ void prepare_ranks(const ua2a_plan_s* p, int32_t mode, const void* const* in, vo
             L->lds_tab.p[k] = mode == 0 ? inb : outb;
             L->lds_tab.a[k] = mode == 0 ? outb : inb;
         }
-        L->grid = grid_for(L->lds.num_tiles, p->blocks, kLdsBlock);
+        L->grid = grid_for(L->lds.num_slots, p->blocks, kLdsBlock);
         return;
     }
 

@@ -37,6 +37,7 @@ constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgrou
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
 constexpr int64_t kLineBytes = 128;             // cache line: LDS tiles align their A spans to it
+constexpr uint32_t kLdsXcdLog = 2;              // LDS tiles: 2^kLdsXcdLog consecutive tiles per XCD turn
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5,

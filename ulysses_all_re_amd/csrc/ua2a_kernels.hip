@@ -41,6 +41,13 @@ struct StreamMem {
     __device__ static T ld(const T* p) { return __builtin_nontemporal_load(p); }
     template <class T>
     __device__ static void st(T* p, T v) { __builtin_nontemporal_store(v, p); }
+    // The first or last chunk of a span that starts or ends inside an aligned
+    // 16-byte chunk is read whole, in one load like the span's other chunks
+    // (reading its in-span pieces one by one stalled the wave on a chain of
+    // small loads).  An aligned 16-byte chunk lies within one page, so the
+    // bytes outside the span are mapped; they are never used, and only an
+    // exchange's input, which nothing writes meanwhile, is read this way.
+    __device__ static u32x4 ld_part(const u32x4* p, uint32_t, uint32_t) { return __builtin_nontemporal_load(p); }
 };
 
 // Readiness credits of a publishing exchange.  A launch that follows a part
@@ -108,8 +115,10 @@ __device__ __forceinline__ void lds_tiles(const LdsGeom& g, const Bases& bases)
 {
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
-    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
-        const LdsTile d = lds_tile(g, bases, static_cast<uint32_t>(t));
+    for (uint64_t slot = blockIdx.x; slot < g.num_slots; slot += gridDim.x) {
+        const uint32_t t = lds_slot_tile(g, static_cast<uint32_t>(slot));
+        if (t >= g.num_tiles) continue;      // the same for the whole workgroup
+        const LdsTile d = lds_tile(g, bases, t);
         // two loads in flight per lane pay off only with 16-byte pieces (measured)
         lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
         __syncthreads();
