@@ -156,6 +156,22 @@ def test_emulated_misaligned_bases(emu, shape, mis):
                     assert info.vector_bytes < 16
 
 
+@pytest.mark.parametrize("shape,mis", [((130, 1, 3, 130, 7, 2), 0), ((130, 2, 5, 260, 3, 2), 2),
+                                       ((4, 1, 61, 4, 7, 2), 6)],
+                         ids=["w130", "w130-B2-misaligned", "w4-odd-S"])
+def test_emulated_lds_partial_chunks(emu, shape, mis):
+    """A spans that start or end inside a 16-byte chunk (odd S_local * run, offset
+    bases): mode 1 reads those chunks whole and places their in-span pieces; with
+    w = 130 its 2w partial-chunk slots outnumber the 256 lanes of a workgroup, so
+    lanes take a second slot."""
+    for mode in (0, 1):
+        x, y, info, bufs = emu_exchange(emu, shape, mode, path=ua.UA2A_PATH_LDS, in_mis=mis,
+                                        out_mis=mis, seed=11 + mode)
+        assert info.path == ua.UA2A_PATH_LDS and info.vector_bytes < 16
+        assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
+        assert all(b.guards_intact() for b in bufs), mode
+
+
 @pytest.mark.parametrize("blocks", [1, 3, 7, 64, 100000])
 def test_emulated_blocks_hint_does_not_change_bytes(emu, blocks):
     shape = (4, 1, 40, 8, 128, 2)
@@ -405,6 +421,8 @@ def test_emulated_kernels_under_asan(tmp_path):
         for mode in (0, 1):
             for path in (ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS):
                 cases.append((*shape, mode, 1, path, 2))
+    for mode in (0, 1):      # more partial-chunk slots than lanes
+        cases.append((130, 2, 5, 260, 3, 2, mode, 0, ua.UA2A_PATH_LDS, 2))
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     script = tmp_path / "asan_driver.py"
     script.write_text(ASAN_DRIVER.format(root=root, lib=lib, cases=cases))

@@ -360,6 +360,37 @@ def test_back_to_back_on_one_stream_and_side_stream():
     plan.close()
 
 
+@pytest.mark.parametrize("shape", [(4, 1, 60001, 4, 7), (130, 1, 37, 130, 7), (8, 2, 1001, 8, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_lds_spans_misaligned_to_16_bytes(shape):
+    """Odd S_local with runs that are not a multiple of 16 B: the LDS path's A spans
+    start and end inside 16-byte chunks, which mode 1 reads whole (w = 130: more
+    such chunks per tile than lanes).  Stacked and, for w <= 64, per-rank calls,
+    both modes, against the oracle."""
+    w, B, S, H, D = shape
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    plan.set_path(ua.UA2A_PATH_LDS)
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), "bf16", "bytes", 60 + mode)
+        want = oracle_out(x, mode, w)
+        xd = x.to(DEV)
+        out = poisoned(plan.out_shape(mode), torch.bfloat16)
+        info = plan.describe(xd, mode, out=out)
+        assert info["path"] == ua.UA2A_PATH_LDS and info["vector_bytes"] < 16
+        note(f"misaligned LDS spans {shape} mode {mode}")
+        plan.exchange(xd, mode, out=out)
+        torch.cuda.synchronize()
+        assert_same_bits(out, want, f"stacked mode {mode}")
+        if w <= ua.MAX_RANK_TABLE:
+            xs = [xd[k].clone() for k in range(w)]
+            outs = [poisoned(plan.out_shape(mode)[1:], torch.bfloat16) for _ in range(w)]
+            assert plan.describe_ranks(xs, outs, mode)["path"] == ua.UA2A_PATH_LDS
+            plan.exchange_ranks(xs, mode, outs=outs)
+            torch.cuda.synchronize()
+            assert_same_bits(torch.stack(outs), want, f"per-rank mode {mode}")
+    plan.close()
+
+
 def test_independent_plans_on_concurrent_streams():
     """Four plans, two of them chunked with windows of their own, each running
     three round trips on its own stream with no host sync in between: the
