@@ -442,6 +442,126 @@ def run_overlap(args):
     print(json.dumps(result), flush=True)
 
 
+# ------------------------------------------------- per-configuration records
+
+RECORD_WORKLOADS = ("tiny", "mid", "video_dit", "chunked", "awkward")
+
+
+def run_records(args):
+    """One JSON line per (workload, mode, chunked) over the five workloads: the
+    chunked form only where the workload asks for it.  Each record holds the
+    per-launch time from HIP events recorded around every one of `--steps`
+    launches on the launch stream (median, min; the launches rotate through
+    buffer sets as in the main bench, so small tensors are timed against HBM),
+    the average of the same number of back-to-back launches, the runtime's
+    device-to-device copy of the same bytes timed per launch the same way, the
+    oracle's single-thread time on the same input, whether the output equals
+    the oracle's byte for byte, and the SHA-256 of the input bytes.  Mode-0
+    inputs use the workload's first seed, mode-1 inputs an independent tensor
+    of the mode-1 shape from its second seed."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import oracle
+    import ulysses_all_re_amd as ua
+    from workloads import BITS_VIEW, CONFIGS, DTYPES, make_tensor
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    K = args.steps
+    names = (args.records_workload,) if args.records_workload else RECORD_WORKLOADS
+    for name in names:
+        c = CONFIGS[name]
+        w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+        dt = DTYPES[c["dtype"]]
+        e = torch.empty((), dtype=dt).element_size()
+        lay = ua.ua2a_layout(w, B, S, H, D, e)
+        moved = lay["moved_bytes"]
+        rotate = max(1, min(64, -(-(1 << 30) // (2 * lay["tensor_bytes"]))))
+        window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=dev) if c["chunked"] else None
+        plan = ua.Plan(w, B, S, H, D, dt, window=window, device=dev)
+        for mode in (0, 1):
+            shape = (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+            seed = c["seed0"] if mode == 0 else c["seed1"]
+            x_cpu = make_tensor(shape, c["dtype"], c["dist"], seed)
+            xb = x_cpu.view(BITS_VIEW[e]).numpy()
+            sha = hashlib.sha256(xb.tobytes()).hexdigest()
+            for chunked in ((False, True) if c["chunked"] else (False,)):
+                log(f"records: {name} mode {mode} chunked={chunked}")
+                xs = [x_cpu.to(dev)] + [None] * (rotate - 1)
+                for k in range(1, rotate):
+                    xs[k] = xs[0].clone()
+                outs = [torch.empty(plan.out_shape(mode), dtype=dt, device=dev) for _ in range(rotate)]
+                info = plan.describe(xs[0], mode, chunked, out=outs[0])
+                t0 = time.perf_counter()
+                want = oracle.exchange(xb, mode, w, chunked=chunked)
+                oracle_s = time.perf_counter() - t0
+                plan.exchange(xs[0], mode, chunked, out=outs[0], stream=stream)
+                torch.cuda.synchronize(dev)
+                exact = bool(np.array_equal(outs[0].cpu().view(BITS_VIEW[e]).numpy(), want))
+                del want
+
+                def launch(i):
+                    plan.exchange(xs[i % rotate], mode, chunked, out=outs[i % rotate], stream=stream)
+
+                def copy(i):
+                    outs[i % rotate].view(-1).view(torch.uint8).copy_(xs[i % rotate].view(-1).view(torch.uint8))
+
+                def per_launch(fn):
+                    for i in range(2 * rotate):          # warm-up, every buffer set once or twice
+                        fn(i)
+                    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(K)]
+                    torch.cuda.synchronize(dev)
+                    for i, (a, b) in enumerate(ev):
+                        a.record(stream)
+                        fn(i)
+                        b.record(stream)
+                    torch.cuda.synchronize(dev)
+                    return [a.elapsed_time(b) * 1e3 for a, b in ev]      # us
+
+                def back_to_back(fn):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    torch.cuda.synchronize(dev)
+                    a.record(stream)
+                    for i in range(K):
+                        fn(i)
+                    b.record(stream)
+                    torch.cuda.synchronize(dev)
+                    return a.elapsed_time(b) * 1e3 / K
+
+                ts = per_launch(launch)
+                t_avg = back_to_back(launch)
+                tc = per_launch(copy)
+                med = statistics.median(ts)
+                rec = {
+                    "record": "exchange", "workload": name, "w": w, "B": B, "S_local": S, "H": H,
+                    "D": D, "dtype": c["dtype"], "mode": mode, "chunked": chunked,
+                    "path": {ua.UA2A_PATH_DIRECT: "direct", ua.UA2A_PATH_LDS: "lds"}[info["path"]],
+                    "bytes": moved,
+                    "launches_timed": K, "buffer_sets": rotate,
+                    "t_median_us": round(med, 3), "t_min_us": round(min(ts), 3),
+                    "t_avg_back_to_back_us": round(t_avg, 3),
+                    "GBps": round(moved / (med * 1e-6) / 1e9, 1),
+                    "pct_peak": round(100 * moved / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
+                    "memcpy_GBps": round(moved / (statistics.median(tc) * 1e-6) / 1e9, 1),
+                    "oracle_1core_s": round(oracle_s, 4),
+                    "oracle_ncore_s": None,
+                    "ncores": 1,
+                    "bit_exact": exact,
+                    "input_sha256": sha,
+                }
+                if chunked:
+                    rec["window_path_bytes"] = 2 * moved
+                print(json.dumps(rec), flush=True)
+                del xs, outs
+                torch.cuda.empty_cache()
+        plan.close()
+
+
 # ----------------------------------------------------- counter post-processing
 
 def _read_counter_rows(d):
@@ -575,6 +695,12 @@ def main():
                     help="oracle round trips timed for cpu_baseline (about 1 s each on the "
                          "video-DiT workload, so about 12 s in all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--records", action="store_true",
+                    help="one JSON line per (workload, mode, chunked) over the five workloads: "
+                         "median and min per-launch time, copy baseline, oracle time, "
+                         "bit-exactness, input SHA-256")
+    ap.add_argument("--records-workload", default=None, choices=RECORD_WORKLOADS,
+                    help="--records for this workload only")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE CSVs under DIR into traffic bytes")
     ap.add_argument("--summarize-trace", metavar="DIR", default=None,
@@ -597,6 +723,9 @@ def main():
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     if args.overlap:
         run_overlap(args)
+        return
+    if args.records:
+        run_records(args)
         return
     run(args)
 
