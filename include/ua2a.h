@@ -29,7 +29,12 @@
  *     (ua2a_exchange, ua2a_exchange_ranks, ua2a_exchange_publish,
  *     ua2a_wait_credits) launch only on the given stream;
  *   - pointers named in/out/window are device pointers on the plan's
- *     device, owned by the caller, and are only borrowed by the library.
+ *     device, owned by the caller, and are only borrowed by the library;
+ *   - kernels write only the bytes of out (and of the window and counters
+ *     where a call names them); they may read an input's first or last
+ *     aligned 16-byte chunk whole when the input starts or ends inside it,
+ *     and never use the bytes outside the input (an aligned 16-byte chunk
+ *     lies within one page, so such a read cannot fault).
  */
 #ifndef UA2A_H
 #define UA2A_H
