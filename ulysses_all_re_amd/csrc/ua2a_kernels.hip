@@ -4,7 +4,7 @@
 // The exchange is pure data movement (FastVideo "ulysses_a2a" API page,
 // method run_armed: mode 0 [B,S_local,H,D] -> [B,S_local*w,H/w,D] per rank,
 // mode 1 the inverse), so it is bound by HBM bandwidth: no MFMA, every byte
-// read once and written once.  Three kernels:
+// read once and written once.  The kernels:
 //
 //  * ua2a_direct_kernel  -- each lane moves one whole vector (16 bytes when
 //    the run and both bases allow) per pass; a workgroup covers one tile of
@@ -14,7 +14,8 @@
 //    cache lines.
 //  * ua2a_lds_kernel     -- for short or unaligned runs: a workgroup stages
 //    a contiguous span of P-side rows in LDS and moves both sides as 16-byte
-//    aligned chunks, re-ordering runs inside LDS in G-byte pieces.
+//    aligned chunks, re-ordering runs inside LDS in G-byte pieces; tiles go
+//    to the XCDs in runs of consecutive tiles (see LdsGeom).
 //  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
 //    to move the one-plane window into the output.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
