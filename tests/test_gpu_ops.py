@@ -75,6 +75,40 @@ def test_backward_is_the_inverse_exchange(shape):
     assert torch.equal(bits(u.grad.cpu()), oracle_bits(h, 0, w))
 
 
+def test_chunked_operator_grows_its_window():
+    """chunked=True: one window per device and stream, grown when a larger shape
+    arrives (the plans that borrowed the old one are rebuilt) and never shrunk;
+    every result, forward and backward, equals the unchunked one and the oracle."""
+    side = torch.cuda.Stream()
+    shapes = [(2, 2, 8, 4, 16), (4, 3, 100, 8, 64), (2, 2, 8, 4, 16), (3, 2, 33, 12, 80)]
+    sizes = []
+    with torch.cuda.stream(side):
+        for k, (w, B, S, H, D) in enumerate(shapes):
+            x = make_tensor((w, B, S, H, D), "bf16", "bytes", 70 + k)
+            xd = x.to(DEV).requires_grad_(False)
+            note(f"chunked op {(w, B, S, H, D)}")
+            y = ops.all_to_all_4D(xd, 2, 1, w, chunked=True)
+            z = ops.all_to_all_4D(y, 1, 2, w, chunked=True)
+            side.synchronize()
+            assert torch.equal(bits(y.cpu()), oracle_bits(x, 0, w)), k
+            assert torch.equal(bits(z.cpu()), bits(x)), k
+            sizes.append(ops._windows[(torch.device(DEV), side.stream_id)].numel())
+    e = 2
+    need = [w * S * H * D * e for (w, B, S, H, D) in shapes]
+    assert sizes == [max(need[:i + 1]) for i in range(len(shapes))]     # grows, never shrinks
+    # a chunked plan borrows the current window; the one built on the first window is gone
+    win = ops._windows[(torch.device(DEV), side.stream_id)]
+    chunked_plans = [p for key, p in ops._plans.items() if len(key) == 8 and key[-1] == side.stream_id]
+    assert chunked_plans and all(p.window is win for p in chunked_plans)
+    # backward of a chunked mode 0 is the chunked mode 1
+    w, B, S, H, D = 3, 2, 33, 12, 80
+    x = make_tensor((w, B, S, H, D), "fp32", "normal", 79).to(DEV).requires_grad_(True)
+    y = ops.all_to_all_4D(x, 2, 1, w, chunked=True)
+    g = make_tensor(tuple(y.shape), "fp32", "normal", 80)
+    y.backward(g.to(DEV))
+    assert torch.equal(bits(x.grad.cpu()), oracle_bits(g, 1, w))
+
+
 def test_torch_compile_traces_the_operator():
     w, B, S, H, D = 4, 2, 64, 8, 32
     x = make_tensor((w, B, S, H, D), "fp16", "uniform", 8).to(DEV)

@@ -15,6 +15,7 @@ def test_fake_shapes_follow_the_page(w, B, S, H, D):
     assert y.shape == (w, B, S * w, H // w, D) and y.dtype == x.dtype
     z = ops.all_to_all_4D(y, 1, 2, w)                    # the inverse
     assert z.shape == x.shape
+    assert ops.all_to_all_4D(x, 2, 1, w, chunked=True).shape == y.shape
 
 
 def test_traces_under_fake_tensor_mode():

@@ -269,6 +269,11 @@ class Plan:
         self.handle = ua2a_plan(w, B, S_local, H, D, self.elem_bytes, blocks, wptr, wbytes,
                                 self.device.index)
 
+    @staticmethod
+    def window_bytes(w: int, B: int, S_local: int, H: int, D: int, elem_bytes: int) -> int:
+        """Bytes a chunked exchange of this shape needs in its window (one plane of every rank)."""
+        return ua2a_layout(w, B, S_local, H, D, elem_bytes)["window_bytes"]
+
     def in_shape(self, mode: int):
         w, B, S, H, D = self.w, self.B, self.S_local, self.H, self.D
         return (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)

@@ -16,6 +16,14 @@ has a shape-only fake implementation, so ``torch.compile`` traces it as one
 opaque call (where the page has to decline inside compiled regions, this
 operator needs no decline).  Every call runs the HIP library; there is no
 other implementation.
+
+``chunked=True`` runs the page's chunked form: one batch plane at a time
+through a window sized for one plane of every rank.  As the page's
+communicator keeps one registered window and rebuilds it larger when a call
+needs more, the operator keeps one window per device and stream, grows it
+(never shrinks it) when a larger shape arrives, and rebuilds the chunked
+plans that borrowed the old one.  Calls on one stream share its window in
+stream order; other streams get windows of their own.
 """
 from __future__ import annotations
 
@@ -26,16 +34,42 @@ import torch
 from . import Plan
 
 _plans: dict = {}
+_windows: dict = {}       # (device, stream) -> the uint8 window of chunked exchanges there
 _lock = threading.Lock()
 
 
-def _plan_for(w: int, B: int, S_local: int, H: int, D: int, dtype, device) -> Plan:
-    """One cached plan per shape, dtype and device (plans are small host objects)."""
-    key = (w, B, S_local, H, D, dtype, device)
+def _window_for(device, stream, nbytes: int):
+    """The stream's window, grown to at least nbytes; growing closes the plans
+    that borrowed the old one (caller holds _lock)."""
+    key = (device, stream.stream_id)
+    win = _windows.get(key)
+    if win is not None and win.numel() >= nbytes:
+        return win
+    if win is not None:
+        for k in [k for k, p in _plans.items() if p.window is win]:
+            _plans.pop(k).close()
+    # the old window is released to torch's allocator in this stream's order
+    win = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _windows[key] = win
+    return win
+
+
+def _plan_for(w: int, B: int, S_local: int, H: int, D: int, dtype, device,
+              chunked: bool = False) -> Plan:
+    """One cached plan per shape, dtype and device (plans are small host
+    objects); chunked plans per stream too, each borrowing its stream's window."""
     with _lock:
+        window = None
+        key = (w, B, S_local, H, D, dtype, device)
+        if chunked:
+            stream = torch.cuda.current_stream(device)
+            e = torch.empty((), dtype=dtype).element_size()
+            need = Plan.window_bytes(w, B, S_local, H, D, e)
+            window = _window_for(device, stream, need)
+            key += (stream.stream_id,)
         plan = _plans.get(key)
         if plan is None:
-            plan = Plan(w, B, S_local, H, D, dtype, device=device)
+            plan = Plan(w, B, S_local, H, D, dtype, window=window, device=device)
             _plans[key] = plan
         return plan
 
@@ -60,7 +94,7 @@ def _out_shape(shape, w: int, mode: int):
 
 
 @torch.library.custom_op("ua2a::exchange", mutates_args=())
-def exchange(x: torch.Tensor, w: int, mode: int) -> torch.Tensor:
+def exchange(x: torch.Tensor, w: int, mode: int, chunked: bool = False) -> torch.Tensor:
     """Rank-stacked Ulysses exchange on the GPU (mode 0 or 1); returns a new tensor."""
     if mode not in (0, 1):
         raise ValueError("mode must be 0 or 1")
@@ -68,35 +102,38 @@ def exchange(x: torch.Tensor, w: int, mode: int) -> torch.Tensor:
         raise RuntimeError(f"the exchange runs on the GPU only (got a {x.device.type} tensor)")
     B, S, H, D = _local_shape(x.shape, w, mode)
     x = x.contiguous()
-    plan = _plan_for(w, B, S, H, D, x.dtype, x.device)
-    return plan.exchange(x, mode)
+    plan = _plan_for(w, B, S, H, D, x.dtype, x.device, chunked)
+    return plan.exchange(x, mode, chunked)
 
 
 @exchange.register_fake
-def _exchange_fake(x: torch.Tensor, w: int, mode: int) -> torch.Tensor:
+def _exchange_fake(x: torch.Tensor, w: int, mode: int, chunked: bool = False) -> torch.Tensor:
     return x.new_empty(_out_shape(x.shape, w, mode))
 
 
 def _setup_context(ctx, inputs, output):
-    _, w, mode = inputs
+    _, w, mode, chunked = inputs
     ctx.w = w
     ctx.mode = mode
+    ctx.chunked = chunked
 
 
 def _backward(ctx, grad):
     # d(out)/d(in) is a permutation matrix; its transpose is the inverse exchange
-    return exchange(grad.contiguous(), ctx.w, 1 - ctx.mode), None, None
+    return exchange(grad.contiguous(), ctx.w, 1 - ctx.mode, ctx.chunked), None, None, None
 
 
 exchange.register_autograd(_backward, setup_context=_setup_context)
 
 
-def all_to_all_4D(x: torch.Tensor, scatter_dim: int, gather_dim: int, w: int) -> torch.Tensor:
+def all_to_all_4D(x: torch.Tensor, scatter_dim: int, gather_dim: int, w: int,
+                  chunked: bool = False) -> torch.Tensor:
     """The page's 4-D all-to-all on rank-stacked tensors ``[w, B, S, H, D]``.
 
     ``scatter_dim`` / ``gather_dim`` index one rank's ``[B, S, H, D]``: (2, 1)
     scatters heads and gathers the sequence (mode 0), (1, 2) is the inverse
     (mode 1).  Other pairs are not an exchange this operator implements.
+    ``chunked`` moves one batch plane at a time through the stream's window.
     """
     if (scatter_dim, gather_dim) == (2, 1):
         mode = 0
@@ -105,4 +142,4 @@ def all_to_all_4D(x: torch.Tensor, scatter_dim: int, gather_dim: int, w: int) ->
     else:
         raise ValueError(f"unsupported (scatter_dim, gather_dim) = ({scatter_dim}, {gather_dim}); "
                          "use (2, 1) for heads -> sequence or (1, 2) for the inverse")
-    return exchange(x, w, mode)
+    return exchange(x, w, mode, chunked)
