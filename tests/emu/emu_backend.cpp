@@ -286,6 +286,17 @@ int ua2a_emu_launches(void) { return ua2a::g_launches; }
 int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
 unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 
+/* The LDS kernels' launch-slot order for num_slots slots with 2^xlog
+ * consecutive tiles per XCD turn: out[L] = the tile slot L runs. */
+void ua2a_emu_lds_slot_tiles(uint32_t num_slots, uint32_t xlog, uint32_t* out)
+{
+    ua2a::LdsGeom g;
+    memset(&g, 0, sizeof g);
+    g.num_slots = num_slots;
+    g.xlog = xlog;
+    for (uint32_t L = 0; L < num_slots; ++L) out[L] = ua2a::lds_slot_tile(g, L);
+}
+
 /* The kernels' magic-number division, for checking against exact division. */
 void ua2a_emu_fdiv(uint32_t d, const uint32_t* n, uint32_t* q, int count)
 {

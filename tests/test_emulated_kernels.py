@@ -233,6 +233,29 @@ def _plan(lib, shape=(2, 2, 4, 4, 8, 2), window=None, wbytes=0, device=0):
     return rc, h
 
 
+def test_lds_slot_order_visits_every_tile_once(emu):
+    """The LDS kernels deal tiles to the XCDs in runs of 2^xlog consecutive tiles:
+    launch slot L -> tile.  Over num_slots = num_tiles rounded up to 8 * 2^xlog
+    slots (as the host launches them) every tile runs exactly once, the rest of
+    the slots are empty, and the 8 slots of one XCD turn hold consecutive runs."""
+    fn = emu.ua2a_emu_lds_slot_tiles
+    fn.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    for xlog in range(5):
+        span = 8 << xlog
+        for num_tiles in list(range(1, 70)) + [255, 256, 257, 1000, 4681 * 4, 65537]:
+            slots = -(-num_tiles // span) * span
+            out = np.zeros(slots, dtype=np.uint32)
+            fn(slots, xlog, out.ctypes.data)
+            used = np.sort(out[out < num_tiles])
+            assert np.array_equal(used, np.arange(num_tiles)), (xlog, num_tiles)
+            assert np.array_equal(np.sort(out), np.arange(slots)), (xlog, num_tiles)
+            # slots L and L + 8 run on the same XCD: consecutive tiles within a run
+            run = 1 << xlog
+            for L in range(0, min(slots, 4 * span)):
+                if (L // 8) % run != run - 1:
+                    assert out[L + 8] == out[L] + 1, (xlog, num_tiles, L)
+
+
 def test_layout_and_plan_errors(emu):
     lay = ua.ua2a_layout_t()
     assert emu.ua2a_layout(2, 1, 8, 4, 16, 2, None) == ua.UA2A_ERR_INVALID_ARG
