@@ -18,6 +18,20 @@
 
 namespace ua2a {
 
+// PlainMem, with every tile store checked against the tile's written range
+// (the kernels store through a buffer resource over exactly that range).
+struct CheckedMem : PlainMem {
+    template <class T>
+    static void st_tile(uint8_t* base, uint32_t nbytes, uint32_t off, T v)
+    {
+        if (off % sizeof(T) != 0 || static_cast<uint64_t>(off) + sizeof(T) > nbytes) {
+            fprintf(stderr, "emu: tile store at %u (+%zu) outside its %u bytes\n", off, sizeof(T), nbytes);
+            abort();
+        }
+        *reinterpret_cast<T*>(base + off) = v;
+    }
+};
+
 namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
@@ -55,7 +69,7 @@ void run_direct(const Launch& L)
                     if (!take_tile()) return;
                     const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
                     for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-                        direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+                        direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
                 }
         return;
     }
@@ -64,7 +78,7 @@ void run_direct(const Launch& L)
         if (!take_tile()) return;
         const DirectTile d = direct_tile<M1>(g, t);
         for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-            direct_tile_body<PlainMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+            direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
     }
 }
 
@@ -96,9 +110,9 @@ void run_lds(const LdsGeom& g, const Bases& bases)
         memset(lds.data(), 0xA5, lds.size());
         const LdsTile d = lds_tile(g, bases, t);
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-            lds_fill<PlainMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
+            lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
         for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-            lds_drain<PlainMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
+            lds_drain<CheckedMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
     }
     for (uint32_t t = 0; t < g.num_tiles; ++t)
         if (!seen[t]) {                  // ... and miss none
@@ -112,7 +126,7 @@ void run_copy(const CopyGeom& g)
 {
     for (uint32_t t = 0; t < g.num_tiles; ++t)
         for (uint32_t tid = 0; tid < kCopyBlock; ++tid)
-            copy_tile_body<PlainMem, VB, kCopyBlock, kDirectUnroll>(g, t, tid);
+            copy_tile_body<CheckedMem, VB, kCopyBlock, kDirectUnroll>(g, t, tid);
 }
 
 // Every workgroup of the launch's grid runs the kernel's loops over the
@@ -129,7 +143,7 @@ void run_ranks(const Launch& L)
                         for (uint32_t x = bx; x < g.tiles_per_slab; x += L.grid) {
                             const RanksTile d = ranks_tile<M1, TWO>(g, x, y, z);
                             for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-                                ranks_tile_body<PlainMem, VB, M1, TWO, kDirectBlock>(g, d, tid);
+                                ranks_tile_body<CheckedMem, VB, M1, TWO, kDirectBlock>(g, d, tid);
                         }
 }
 

@@ -14,12 +14,18 @@ namespace ua2a {
 
 // Global-memory access policy of the bodies.  The kernels use one that
 // marks accesses non-temporal (streamed once, not worth keeping in cache);
-// the host emulation uses PlainMem.
+// the host emulation uses PlainMem (with bounds checks of its own).
 struct PlainMem {
     template <class T>
     UA2A_HD static T ld(const T* p) { return *p; }
     template <class T>
     UA2A_HD static void st(T* p, T v) { *p = v; }
+    // A store at byte `off` of a tile's written range [base, base + nbytes).
+    template <class T>
+    UA2A_HD static void st_tile(uint8_t* base, uint32_t, uint32_t off, T v)
+    {
+        *reinterpret_cast<T*>(base + off) = v;
+    }
     // Bytes [lo, hi) of the aligned 16-byte chunk at p, the others zero: the
     // emulation reads nothing outside a span.  (The kernels read such a chunk
     // whole; see StreamMem.)
@@ -78,7 +84,11 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
 {
     typedef typename Piece<VB>::T T;
     const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
-    T* __restrict__ dst = reinterpret_cast<T*>(g.dst);
+    // the tile writes one contiguous range of the written side: its nvec
+    // vectors from d.dst_slab + d.u0 on
+    const int64_t first = d.dst_slab + d.u0;
+    uint8_t* const tile = g.dst + first * VB;
+    const uint32_t tile_bytes = d.nvec * VB;
     for (uint32_t base = tid; base < d.nvec; base += BS * U) {
         T v[U];
         int64_t to[U];
@@ -93,7 +103,8 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
         }
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k)
-            if (base + k * BS < d.nvec) Mem::st(dst + to[k], v[k]);
+            if (base + k * BS < d.nvec)
+                Mem::st_tile(tile, tile_bytes, static_cast<uint32_t>((to[k] - first) * VB), v[k]);
     }
 }
 
@@ -104,11 +115,21 @@ UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t ti
 {
     typedef typename Piece<VB>::T T;
     T* dst = reinterpret_cast<T*>(d.dst);
+    // mode 0, and mode 1 when every rank sends, write one contiguous range
+    // per tile (from its first vector on); part of the senders in mode 1 write
+    // pieces of several rows
+    const bool one_range = !MODE1 || g.count == g.w;
+    const int64_t first = d.dst_off + d.u0;
+    uint8_t* const tile = d.dst + first * VB;
     for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
         const uint8_t* sp;
         int64_t from, to;
         ranks_vector<MODE1, TWO>(g, d, d.u0 + delta, sp, from, to);
-        Mem::st(dst + to, Mem::ld(reinterpret_cast<const T*>(sp) + from));
+        const T v = Mem::ld(reinterpret_cast<const T*>(sp) + from);
+        if (one_range)
+            Mem::st_tile(tile, d.nvec * VB, static_cast<uint32_t>((to - first) * VB), v);
+        else
+            Mem::st(dst + to, v);
     }
 }
 
@@ -270,9 +291,8 @@ UA2A_HD void lds_drain(const LdsGeom& g, const Bases& bases, const LdsTile& d, u
         const uint32_t pch = span_chunks(d.head, d.p_len);
         for (uint32_t c = tid; c < pch; c += BS) {
             const uint32_t lo = c * 16;
-            if (chunk_full(lo, d.head, d.p_len))
-                Mem::st(reinterpret_cast<u32x4*>(pchunk0 + lo),
-                        *reinterpret_cast<const u32x4*>(lds + lds_pos_of_p(g, lo)));
+            if (chunk_full(lo, d.head, d.p_len))     // the P span: one contiguous range per tile
+                Mem::st_tile(pchunk0, pch * 16, lo, *reinterpret_cast<const u32x4*>(lds + lds_pos_of_p(g, lo)));
             else
                 copy_partial_chunk<G>(lds, pchunk0, lo, d.head, d.p_len);
         }
@@ -285,8 +305,8 @@ UA2A_HD void copy_tile_body(const CopyGeom& g, uint32_t t, uint32_t tid)
 {
     typedef typename Piece<VB>::T T;
     const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
-    T* __restrict__ dst = reinterpret_cast<T*>(g.dst);
     const CopyTile c = copy_tile(g, t);
+    uint8_t* const tile = g.dst + c.dst_base * VB;      // the tile's contiguous written range
     for (uint32_t base = tid; base < c.nvec; base += BS * U) {
         T v[U];
 #pragma unroll
@@ -294,7 +314,7 @@ UA2A_HD void copy_tile_body(const CopyGeom& g, uint32_t t, uint32_t tid)
             if (base + k * BS < c.nvec) v[k] = Mem::ld(src + c.src_base + base + k * BS);
 #pragma unroll
         for (uint32_t k = 0; k < U; ++k)
-            if (base + k * BS < c.nvec) Mem::st(dst + c.dst_base + base + k * BS, v[k]);
+            if (base + k * BS < c.nvec) Mem::st_tile(tile, c.nvec * VB, (base + k * BS) * VB, v[k]);
     }
 }
 
