@@ -131,7 +131,7 @@ void run_copy(const CopyGeom& g)
 
 // Every workgroup of the launch's grid runs the kernel's loops over the
 // slab grid exactly as on the device.
-template <int VB, bool M1, bool TWO>
+template <int VB, bool M1, bool TWO, bool PART>
 void run_ranks(const Launch& L)
 {
     const RanksGeom& g = L.ranks;
@@ -143,19 +143,19 @@ void run_ranks(const Launch& L)
                         for (uint32_t x = bx; x < g.tiles_per_slab; x += L.grid) {
                             const RanksTile d = ranks_tile<M1, TWO>(g, x, y, z);
                             for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-                                ranks_tile_body<CheckedMem, VB, M1, TWO, kDirectBlock>(g, d, tid);
+                                ranks_tile_body<CheckedMem, VB, M1, TWO, PART, kDirectBlock>(g, d, tid);
                         }
 }
 
-template <bool M1, bool TWO>
+template <bool M1, bool TWO, bool PART>
 int dispatch_ranks(const Launch& L, int vb)
 {
     switch (vb) {
-    case 16: run_ranks<16, M1, TWO>(L); return 0;
-    case 8: run_ranks<8, M1, TWO>(L); return 0;
-    case 4: run_ranks<4, M1, TWO>(L); return 0;
-    case 2: run_ranks<2, M1, TWO>(L); return 0;
-    case 1: run_ranks<1, M1, TWO>(L); return 0;
+    case 16: run_ranks<16, M1, TWO, PART>(L); return 0;
+    case 8: run_ranks<8, M1, TWO, PART>(L); return 0;
+    case 4: run_ranks<4, M1, TWO, PART>(L); return 0;
+    case 2: run_ranks<2, M1, TWO, PART>(L); return 0;
+    case 1: run_ranks<1, M1, TWO, PART>(L); return 0;
     default: return 1;
     }
 }
@@ -271,9 +271,12 @@ int backend_launch(const Launch& L, void*)
         if (L.grid_y < 1 || L.grid_z < 1 || L.grid_y > 65535 || L.grid_z > 65535 ||
             static_cast<uint64_t>(L.grid) * L.block > (uint64_t(1) << 31))
             return 8;
-        if (!L.mode) return dispatch_ranks<false, false>(L, L.width);
-        return L.ranks.two_runs ? dispatch_ranks<true, true>(L, L.width)
-                                : dispatch_ranks<true, false>(L, L.width);
+        if (!L.mode) return dispatch_ranks<false, false, false>(L, L.width);
+        if (L.ranks.count == L.ranks.w)
+            return L.ranks.two_runs ? dispatch_ranks<true, true, false>(L, L.width)
+                                    : dispatch_ranks<true, false, false>(L, L.width);
+        return L.ranks.two_runs ? dispatch_ranks<true, true, true>(L, L.width)
+                                : dispatch_ranks<true, false, true>(L, L.width);
     }
     return 4;
 }

@@ -110,26 +110,45 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
 
 // Per-rank allocations: as direct_tile_body, the tensors taken from the
 // geometry's pointer tables (per tile, or per vector in mode 1).
-template <class Mem, int VB, bool MODE1, bool TWO, uint32_t BS>
+// PART: mode 1 with part of the senders (a kernel instance of its own, so the
+// others keep the plain contiguous-range stores).
+template <class Mem, int VB, bool MODE1, bool TWO, bool PART, uint32_t BS>
 UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t tid)
 {
     typedef typename Piece<VB>::T T;
-    T* dst = reinterpret_cast<T*>(d.dst);
-    // mode 0, and mode 1 when every rank sends, write one contiguous range
-    // per tile (from its first vector on); part of the senders in mode 1 write
-    // pieces of several rows
-    const bool one_range = !MODE1 || g.count == g.w;
-    const int64_t first = d.dst_off + d.u0;
-    uint8_t* const tile = d.dst + first * VB;
-    for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
-        const uint8_t* sp;
-        int64_t from, to;
-        ranks_vector<MODE1, TWO>(g, d, d.u0 + delta, sp, from, to);
-        const T v = Mem::ld(reinterpret_cast<const T*>(sp) + from);
-        if (one_range)
+    if (!PART) {
+        // mode 0, and mode 1 when every rank sends: the tile writes one
+        // contiguous range, from its first vector on
+        const int64_t first = d.dst_off + d.u0;
+        uint8_t* const tile = d.dst + first * VB;
+        for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
+            const uint8_t* sp;
+            int64_t from, to;
+            ranks_vector<MODE1, TWO>(g, d, d.u0 + delta, sp, from, to);
+            const T v = Mem::ld(reinterpret_cast<const T*>(sp) + from);
             Mem::st_tile(tile, d.nvec * VB, static_cast<uint32_t>((to - first) * VB), v);
-        else
-            Mem::st(dst + to, v);
+        }
+    } else {
+        // mode 1 with part of the senders: pieces of consecutive rows, stored
+        // through the range from the tile's first written vector to its last
+        // while that spans less than 4 GiB, else plainly
+        T* dst = reinterpret_cast<T*>(d.dst);
+        const uint8_t* sp;
+        int64_t from, first, last;
+        ranks_vector<MODE1, TWO>(g, d, d.u0, sp, from, first);
+        ranks_vector<MODE1, TWO>(g, d, d.u0 + d.nvec - 1, sp, from, last);
+        const int64_t span = last - first + 1;
+        const bool ranged = span * VB <= static_cast<int64_t>(UINT32_MAX);
+        uint8_t* const tile = d.dst + first * VB;
+        for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
+            int64_t to;
+            ranks_vector<MODE1, TWO>(g, d, d.u0 + delta, sp, from, to);
+            const T v = Mem::ld(reinterpret_cast<const T*>(sp) + from);
+            if (ranged)
+                Mem::st_tile(tile, static_cast<uint32_t>(span * VB), static_cast<uint32_t>((to - first) * VB), v);
+            else
+                Mem::st(dst + to, v);
+        }
     }
 }
 

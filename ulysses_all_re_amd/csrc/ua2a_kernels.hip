@@ -176,13 +176,13 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, Ld
 
 // Per-rank allocations (pointer tables, sender range): one tile per
 // workgroup when the grid covers the slab grid, else each dimension loops.
-template <int VB, bool MODE1, bool TWO>
+template <int VB, bool MODE1, bool TWO, bool PART>
 __global__ __launch_bounds__(kDirectBlock) void ua2a_ranks_kernel(RanksGeom g)
 {
     for (uint32_t z = blockIdx.z; z < g.nz; z += gridDim.z)
         for (uint32_t y = blockIdx.y; y < g.ny; y += gridDim.y)
             for (uint32_t x = blockIdx.x; x < g.tiles_per_slab; x += gridDim.x)
-                ranks_tile_body<StreamMem, VB, MODE1, TWO, kDirectBlock>(
+                ranks_tile_body<StreamMem, VB, MODE1, TWO, PART, kDirectBlock>(
                     g, ranks_tile<MODE1, TWO>(g, x, y, z), threadIdx.x);
 }
 
@@ -254,15 +254,15 @@ const void* lds_ranks_fn(int g)
     }
 }
 
-template <bool MODE1, bool TWO>
+template <bool MODE1, bool TWO, bool PART>
 const void* ranks_fn(int vb)
 {
     switch (vb) {
-    case 16: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<16, MODE1, TWO>);
-    case 8: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<8, MODE1, TWO>);
-    case 4: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<4, MODE1, TWO>);
-    case 2: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<2, MODE1, TWO>);
-    case 1: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<1, MODE1, TWO>);
+    case 16: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<16, MODE1, TWO, PART>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<8, MODE1, TWO, PART>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<4, MODE1, TWO, PART>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<2, MODE1, TWO, PART>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_ranks_kernel<1, MODE1, TWO, PART>);
     default: return nullptr;
     }
 }
@@ -331,9 +331,11 @@ int backend_launch(const Launch& L, void* stream)
         break;
     case Kernel::Ranks:
         if (!L.mode)
-            fn = ranks_fn<false, false>(L.width);
+            fn = ranks_fn<false, false, false>(L.width);
+        else if (L.ranks.count == L.ranks.w)
+            fn = L.ranks.two_runs ? ranks_fn<true, true, false>(L.width) : ranks_fn<true, false, false>(L.width);
         else
-            fn = L.ranks.two_runs ? ranks_fn<true, true>(L.width) : ranks_fn<true, false>(L.width);
+            fn = L.ranks.two_runs ? ranks_fn<true, true, true>(L.width) : ranks_fn<true, false, true>(L.width);
         arg = const_cast<RanksGeom*>(&L.ranks);
         break;
     }
