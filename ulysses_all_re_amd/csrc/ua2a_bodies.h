@@ -293,17 +293,40 @@ UA2A_HD void lds_drain(const LdsGeom& g, const Bases& bases, const LdsTile& d, u
         // the w spans' chunks as one flat index space (see lds_fill)
         const uint32_t stride = d.stride;
         const uint32_t total = g.w * stride;
-        for (uint32_t i = tid; i < total; i += BS) {
-            const uint32_t r = fdiv(i, d.d_stride);
-            const uint32_t c = i - r * stride;
-            uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
-            const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-            if (c >= span_chunks(ahead, d.a_len)) continue;
-            const uint32_t lo = c * 16;
-            if (chunk_full(lo, ahead, d.a_len))
-                Mem::st(reinterpret_cast<u32x4*>(aspan - ahead + lo), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
-            else
-                a_partial_from_lds<G>(g, d, r, lo, ahead, lds, aspan - ahead);
+        if constexpr (Bases::kStacked && G == 16) {
+            // rank-stacked tensors with 16-byte pieces: with a_window, one range
+            // from head block 0's span holds all w spans of the tile, and the
+            // chunks are stored through it.  (Per-rank tables keep plain
+            // stores, and so do narrower pieces: their spans' partial chunks are
+            // written plainly, and lines written both ways by neighbouring
+            // chunks measured 9-52 % slower.)
+            uint8_t* const win = g.a_ptr + d.a_start0;      // 16-aligned with G = 16
+            const uint32_t win_bytes = g.a_window
+                ? static_cast<uint32_t>(static_cast<int64_t>(g.w - 1) * g.a_rank + d.a_len + 32) : 0u;
+            for (uint32_t i = tid; i < total; i += BS) {
+                const uint32_t r = fdiv(i, d.d_stride);
+                const uint32_t c = i - r * stride;
+                uint8_t* const p = bases.a_rank_base(r) + d.a_start0 + c * 16;
+                if (c * 16 >= d.a_len) continue;
+                const u32x4 v = gather_a_chunk<G>(g, d, r, c * 16, lds);
+                if (g.a_window)
+                    Mem::st_tile(win, win_bytes, static_cast<uint32_t>(p - win), v);
+                else
+                    Mem::st(reinterpret_cast<u32x4*>(p), v);
+            }
+        } else {
+            for (uint32_t i = tid; i < total; i += BS) {
+                const uint32_t r = fdiv(i, d.d_stride);
+                const uint32_t c = i - r * stride;
+                uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
+                const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+                if (c >= span_chunks(ahead, d.a_len)) continue;
+                const uint32_t lo = c * 16;
+                if (chunk_full(lo, ahead, d.a_len))
+                    Mem::st(reinterpret_cast<u32x4*>(aspan - ahead + lo), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
+                else
+                    a_partial_from_lds<G>(g, d, r, lo, ahead, lds, aspan - ahead);
+            }
         }
     } else {
         uint8_t* pchunk0 = d.p_span - d.head;

@@ -358,6 +358,9 @@ struct LdsGeom {
     uint32_t xlog;             // log2 of the consecutive tiles per XCD turn (0: plain order)
     uint32_t w, nb;
     uint32_t j0;               // first P-side rank the tiles cover (per-rank form: first sender)
+    uint32_t a_window;         // 1: rank-stacked A side of under 4 GiB, so a tile's w A spans
+                               //    lie within 4 GiB past head block 0's (mode 0 stores through
+                               //    that range); 0: per-rank tables or larger tensors
     uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * lrow)
     uint32_t stride_full;      // 16-byte chunk slots per A span: tile of rows_per_tile rows
     uint32_t stride_last;      // ... and the plane's last tile
@@ -377,6 +380,7 @@ struct LdsTile {
 
 // Where a tile's spans live.  Rank-stacked tensors: bases plus rank strides.
 struct StackedBases {
+    static constexpr bool kStacked = true;
     const LdsGeom& g;
     UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return g.p_ptr + static_cast<int64_t>(j) * g.p_rank; }
     UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return g.a_ptr + static_cast<int64_t>(r) * g.a_rank; }
@@ -391,6 +395,7 @@ struct LdsTables {
 };
 
 struct TableBases {
+    static constexpr bool kStacked = false;
     const LdsTables& t;
     UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return t.p[j]; }
     UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return t.a[r]; }
@@ -400,6 +405,7 @@ struct TableBases {
 // per-lane lookups of the (span, chunk) loops read LDS, not the kernel
 // argument in memory.
 struct StagedTableBases {
+    static constexpr bool kStacked = false;
     const LdsTables& t;
     uint8_t* const* a;
     UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return t.p[j]; }

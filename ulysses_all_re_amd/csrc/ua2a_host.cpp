@@ -218,6 +218,9 @@ LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uin
     g.num_tiles = g.w * nb * g.tiles_per_plane;
     set_lds_slots(&g);
     g.lds_bytes = (16 + g.rows_per_tile * g.lrow + 15) & ~15u;
+    // every A span of a stacked tensor lies in [a_ptr, a_ptr + w * a_rank)
+    g.a_window = (a_ptr != nullptr && static_cast<uint64_t>(g.w) * static_cast<uint64_t>(a_rank) + 64 <=
+                  UINT32_MAX) ? 1u : 0u;
     // chunk slots per A span: exactly its chunks when spans are 16-aligned,
     // else room for an unaligned start (the longest a span can touch)
     const uint32_t rows_last = g.s_local - (g.tiles_per_plane - 1) * g.rows_per_tile;
