@@ -228,6 +228,42 @@ def test_large_tensor_sampled():
     plan.close()
 
 
+@pytest.mark.parametrize("B", [1, 3], ids=["2GiB", "6GiB"])
+def test_lds_path_sampled_around_4_gib(B):
+    """32-byte runs (the LDS path, 16-byte pieces) on rank-stacked tensors of 2 GiB
+    (mode 0 stores each tile's spans through one range) and 6 GiB (too large for
+    one range: plain stores): sampled outputs against the element oracle, both
+    modes, chunked and not, and a full round trip."""
+    w, S, H, D = 8, 2 ** 20, 8, 4
+    n = w * B * S * H * D
+    lay = ua.ua2a_layout(w, B, S, H, D, 8)
+    window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, torch.int64, window=window)
+    plan.set_path(ua.UA2A_PATH_LDS)
+    x = torch.arange(n, dtype=torch.int64, device=DEV).view(w, B, S, H, D)
+    gen = torch.Generator("cpu").manual_seed(13 + B)
+    idx = torch.cat([torch.arange(4096), torch.randint(0, n, (200000,), generator=gen),
+                     torch.arange(n - 4096, n)])
+    for mode in (0, 1):
+        for chunked in (False, True):
+            info = plan.describe(x, mode, chunked)
+            assert info["path"] == ua.UA2A_PATH_LDS and info["vector_bytes"] == 16
+            note(f"LDS sampled B={B} mode={mode} chunked={chunked} {info}")
+            src = x if mode == 0 else x.view(plan.in_shape(1))
+            y = plan.exchange(src, mode, chunked)
+            torch.cuda.synchronize()
+            got = y.view(-1)[idx.to(DEV)].cpu().numpy()
+            want = oracle.source_indices(mode, w, B, S, H, D, idx.numpy())
+            assert np.array_equal(got, want), (mode, chunked)
+            del y
+    note(f"LDS round trip B={B}")
+    y = plan.exchange(x, 0)
+    z = plan.exchange(y, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(z, x)
+    plan.close()
+
+
 def test_capped_grid_at_64_gib():
     """64 GiB per tensor with 4 KiB token rows: mode 0 runs the flat grouped
     order with 2^26 tiles, more than one dispatch can count in lanes, so the
