@@ -633,9 +633,11 @@ def traffic_from(d):
     print(json.dumps(out, indent=2))
 
 
-def summarize_trace(d, workload, ranks=None):
+def summarize_trace(d, workload, ranks=None, chunked=False):
     """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run
-    (with ranks == "one", each exchange launch moves one sender's share, 1/w)."""
+    (with ranks == "one", each exchange launch moves one sender's share, 1/w;
+    with chunked, each launch moves one plane, 1/B, and a launch that also
+    carries the previous plane's copy moves two)."""
     paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -646,9 +648,10 @@ def summarize_trace(d, workload, ranks=None):
     c = {**CONFIGS, **MEASURE}[workload]
     e = torch.empty((), dtype=DTYPES[c["dtype"]]).element_size()
     moved = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], e)["moved_bytes"]
-    share = moved // c["w"] if ranks == "one" else moved
+    share = moved // c["w"] if ranks == "one" else moved // c["B"] if chunked else moved
     print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {share // 2} B"
-          + (", one sender" if ranks == "one" else "") + ") |")
+          + (", one sender" if ranks == "one" else ", one plane" if chunked else "")
+          + ("; 4 x for the carry kernel" if chunked else "") + ") |")
     print("|---|---|---|---|---|---|")
     with open(paths[0], newline="") as f:
         for r in csv.DictReader(f):
@@ -658,7 +661,8 @@ def summarize_trace(d, workload, ranks=None):
             avg = float(r["AverageNs"])
             rate = ""
             if "ua2a_" in r["Name"]:
-                rate = f"{share / (avg * 1e-9) / 1e9:.1f}"
+                k = 2 if chunked and "carry" in r["Name"] else 1
+                rate = f"{k * share / (avg * 1e-9) / 1e9:.1f}"
             elif COPY_KERNEL_HINT in r["Name"] and ranks is None:   # per-rank runs also clone ranks
                 rate = f"{moved / (avg * 1e-9) / 1e9:.1f}"
             print(f"| `{name}` | {r['Calls']} | {avg / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
@@ -710,7 +714,7 @@ def main():
         traffic_from(args.traffic_from)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload, args.ranks)
+        summarize_trace(args.summarize_trace, args.workload, args.ranks, args.chunked)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -87,7 +87,8 @@ typedef struct ua2a_launch_info_s {
     int32_t path;          /* UA2A_PATH_DIRECT or UA2A_PATH_LDS */
     int32_t vector_bytes;  /* bytes per lane access of the permutation kernel (1..16) */
     int32_t block;         /* threads per workgroup */
-    int32_t launches;      /* kernel launches per exchange (2*B when chunked: B permutes + B copies) */
+    int32_t launches;      /* kernel launches per exchange; chunked: B permutes + B copies (2*B),
+                              or B + 1 when the copies ride in the next plane's permute */
     int64_t grid;          /* workgroups of the permutation kernel per launch (all dimensions) */
     int64_t tiles;         /* work tiles per launch */
     int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
@@ -136,8 +137,14 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *   chunked  0: one permutation launch over all B planes;
  *            1: per plane p, a permutation of plane p of every rank into the
  *               window, then a copy of the window into plane p of `out`;
- *               plane p+1 reuses the window only after plane p's copy, by
- *               stream order.  Needs window_bytes >= layout.window_bytes.
+ *               plane p+1 overwrites a window byte only after plane p's copy
+ *               has read it.  On the direct path with its default 3-D grid,
+ *               plane p's copy runs inside plane p+1's launch (each tile
+ *               copies its window range out, then overwrites it) and only
+ *               the last plane's copy is a launch of its own: B + 1 launches
+ *               instead of 2*B, same bytes moved.  After the call the window
+ *               holds plane B-1 of every rank, in `out`'s layout.
+ *               Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]
  *   out      the other layout; must not overlap `in` or the window.
  * Both tensors must be elem_bytes-aligned; 16-byte alignment (and run_bytes

@@ -37,6 +37,7 @@ int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
 int g_kernel_counts[7] = {0, 0, 0, 0, 0, 0, 0};
+int g_carry_launches = 0;     // direct launches that also copied a chunked plane out
 uint32_t g_last_grid = 0;
 long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
 bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
@@ -68,11 +69,20 @@ void run_direct(const Launch& L)
                 for (uint32_t x = 0; x < L.grid; ++x) {
                     if (!take_tile()) return;
                     const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
+                    if (L.carry.dst != nullptr) {
+                        // a chunked plane after the first: the previous plane's
+                        // window range goes out first, tile by tile
+                        uint8_t* ct = L.carry.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(z) * L.carry.step) * VB;
+                        for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+                            direct_carry_tile_body<CheckedMem, VB, M1, kDirectBlock>(g, d, tid, ct);
+                        continue;
+                    }
                     for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
                         direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
                 }
         return;
     }
+    if (L.carry.dst != nullptr) abort();   // the carry launch exists on the 3-D grid only
     // a capped grid loops grid-stride; every tile is visited exactly once either way
     for (uint32_t t = 0; t < g.num_tiles; ++t) {
         if (!take_tile()) return;
@@ -216,6 +226,7 @@ int backend_launch(const Launch& L, void*)
     }
     ++g_launches;
     ++g_kernel_counts[static_cast<int>(L.kernel)];
+    if (L.kernel == Kernel::Direct && L.carry.dst != nullptr) ++g_carry_launches;
     if (g_stalled) return 0;       // queued behind an unfinished launch
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
@@ -234,7 +245,9 @@ int backend_launch(const Launch& L, void*)
                 slabs * L.direct.tiles_per_slab != L.direct.num_tiles ||
                 L.grid_y != (L.mode ? L.direct.nb : L.direct.w) || L.grid_z % (L.mode ? 1u : L.direct.nb))
                 return 6;
-        } else if (L.grid_y != 1 || L.grid_z != 1) {
+            // a carry launch covers one plane (z is then the window block)
+            if (L.carry.dst != nullptr && (L.direct.nb != 1 || L.direct.sig_count != 0)) return 8;
+        } else if (L.grid_y != 1 || L.grid_z != 1 || L.carry.dst != nullptr) {
             return 7;
         }
         return L.mode ? dispatch_direct<true>(L, L.width) : dispatch_direct<false>(L, L.width);
@@ -297,10 +310,12 @@ void ua2a_emu_reset_counts(void)
 {
     ua2a::g_launches = 0;
     for (int& c : ua2a::g_kernel_counts) c = 0;
+    ua2a::g_carry_launches = 0;
 }
 
 int ua2a_emu_launches(void) { return ua2a::g_launches; }
 int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
+int ua2a_emu_carry_launches(void) { return ua2a::g_carry_launches; }
 unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 
 /* The LDS kernels' launch-slot order for num_slots slots with 2^xlog

@@ -187,8 +187,11 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
     shape = (4, 4, 32, 16, 64, 2)
     w, B, S, H, D, e = shape
     x, y, info, _ = emu_exchange(emu, shape, 0, chunked=True, seed=7)
-    assert info.launches == 2 * B
-    assert emu.ua2a_emu_kernel_count(2) == B                 # B window -> output copies
+    # B permutes, planes 1..B-1 each also copying the previous plane out of
+    # the window, and one copy launch for the last plane
+    assert info.launches == B + 1
+    assert emu.ua2a_emu_kernel_count(0) == B and emu.ua2a_emu_carry_launches() == B - 1
+    assert emu.ua2a_emu_kernel_count(2) == 1
     assert np.array_equal(y, oracle_bytes(x, shape, 0))
     # feed mode 0's output back through mode 1
     lay = ua2a_layout(emu, *shape)
@@ -202,6 +205,30 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
 
 
 # ------------------------------------------------------ magic-number division
+
+@pytest.mark.parametrize("shape", [(4, 4, 32, 16, 64, 2), (3, 3, 5, 6, 4, 4), (2, 5, 9, 4, 64, 2),
+                                   (5, 2, 4, 10, 2, 1), (4, 3, 7, 8, 3, 8), (2, 3, 37, 2, 1024, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_emulated_chunked_carry(emu, shape):
+    """Chunked exchanges on the direct path's 3-D grid copy each plane but the
+    last out of the window inside the next plane's launch; a blocks hint (flat
+    grid), the grouped tile order and the LDS path keep one copy launch per
+    plane.  Every form matches the oracle, leaves the guard bands alone and
+    ends with the last plane in the window."""
+    w, B, S, H, D, e = shape
+    for mode in (0, 1):
+        for path, blocks in ((ua.UA2A_PATH_DIRECT, 0), (ua.UA2A_PATH_DIRECT, 5), (ua.UA2A_PATH_LDS, 0)):
+            x, y, info, bufs = emu_exchange(emu, shape, mode, True, path, blocks=blocks, seed=11 + mode)
+            assert np.array_equal(y, oracle_bytes(x, shape, mode)), (mode, path, blocks)
+            assert all(b.guards_intact() for b in bufs), (mode, path, blocks)
+            carry = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3 and B > 1
+            assert info.launches == (B + 1 if carry else 2 * B), (mode, path, blocks)
+            assert emu.ua2a_emu_carry_launches() == (B - 1 if carry else 0)
+            assert emu.ua2a_emu_kernel_count(2) == (1 if carry else B)
+            # the window holds the last plane of every rank, in the output's layout
+            out = y.reshape(w, B, -1)
+            assert np.array_equal(bufs[2].view.reshape(w, -1), out[:, B - 1]), (mode, path, blocks)
+
 
 def test_fdiv_matches_exact_division(emu):
     """The kernels' multiply-high division against exact integer division."""

@@ -26,6 +26,10 @@ struct PlainMem {
     {
         *reinterpret_cast<T*>(base + off) = v;
     }
+    // Order point: later accesses wait until v has been read (the host runs
+    // each thread in program order, so nothing to do here).
+    template <class T>
+    UA2A_HD static void held(const T&) {}
     // Bytes [lo, hi) of the aligned 16-byte chunk at p, the others zero: the
     // emulation reads nothing outside a span.  (The kernels read such a chunk
     // whole; see StreamMem.)
@@ -105,6 +109,32 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
         for (uint32_t k = 0; k < U; ++k)
             if (base + k * BS < d.nvec)
                 Mem::st_tile(tile, tile_bytes, static_cast<uint32_t>((to[k] - first) * VB), v[k]);
+    }
+}
+
+// direct_tile_body for a chunked plane after the first: each lane first
+// moves the window vector it is about to overwrite (the previous plane's) to
+// `carry_tile`, the tile's range in the output, then writes the new vector
+// there.  Mem::held(old) keeps every later memory access after the point
+// where the old vector is in registers, so the overwrite cannot pass the
+// read of the same address.
+template <class Mem, int VB, bool MODE1, uint32_t BS>
+UA2A_HD void direct_carry_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t tid,
+                                    uint8_t* carry_tile)
+{
+    typedef typename Piece<VB>::T T;
+    const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
+    const int64_t first = d.dst_slab + d.u0;
+    uint8_t* const tile = g.dst + first * VB;
+    const uint32_t tile_bytes = d.nvec * VB;
+    for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
+        int64_t from, to;
+        direct_vector<MODE1>(g, d, d.u0 + delta, from, to);
+        const T old = Mem::ld(reinterpret_cast<const T*>(tile) + delta);
+        const T v = Mem::ld(src + from);
+        Mem::st_tile(carry_tile, tile_bytes, delta * VB, old);
+        Mem::held(old);
+        Mem::st_tile(tile, tile_bytes, static_cast<uint32_t>((to - first) * VB), v);
     }
 }
 

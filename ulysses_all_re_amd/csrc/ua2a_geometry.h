@@ -111,6 +111,19 @@ struct DirectTile {
     uint32_t nvec;      // vectors in this tile
 };
 
+// Chunked exchange, planes after the first: the window still holds the
+// previous plane, and each tile copies its window range out to that plane of
+// the output just before overwriting it (the same workgroup owns both, so the
+// copy needs no launch of its own).  The window is [w][one plane]; its block
+// k goes to out[k][previous plane], so window vector x lands at
+// dst + x + k * step (vectors), with dst the previous plane of rank 0 and
+// step = rank stride - plane.  dst == nullptr: no copy.  On the 3-D grid of
+// a one-plane launch the block k is the z coordinate in both modes.
+struct DirectCarry {
+    uint8_t* dst;
+    int64_t step;
+};
+
 template <bool MODE1>
 UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
 {

@@ -63,6 +63,9 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
 
 // Everything one exchange launches.  For a chunked exchange, perm and copy
 // describe plane 0; plane p adds p * plane_bytes to the pointers named below.
+// With `carry`, planes after the first copy the previous plane out of the
+// window inside their own permute launch, and only the last plane's copy is
+// a launch of its own.
 struct Prepared {
     int32_t path;            // UA2A_PATH_DIRECT or UA2A_PATH_LDS
     int32_t chunked;
@@ -70,6 +73,9 @@ struct Prepared {
     Launch copy;
     int64_t plane_bytes;     // S_local * H * D * elem_bytes
     int32_t launches;
+    int32_t carry;
+    uint8_t* out;            // the exchange's output (plane 0 of rank 0)
+    int64_t carry_step;      // (rank stride - plane) in the permute's vectors
 };
 
 // `recv` receiving ranks from the ones at the given bases (w for a whole
@@ -388,11 +394,17 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
         C.grid = grid_for(C.copy.num_tiles, 0, kCopyBlock);
-        pr->launches = static_cast<int32_t>(2 * p->B);
+        // the copy rides in the next plane's permute when that is a direct
+        // launch with one workgroup per tile on the 3-D grid (z = window block)
+        pr->carry = p->B > 1 && L.kernel == Kernel::Direct && L.grid3d;
+        pr->out = outb;
+        pr->carry_step = (rank_bytes - plane) / L.width;
+        pr->launches = static_cast<int32_t>(pr->carry ? p->B + 1 : 2 * p->B);
     }
 }
 
-// Shift plane-0 launches of a chunked exchange to plane `pl`.
+// Shift plane-0 launches of a chunked exchange to plane `pl`; with carry,
+// the permute of a later plane also copies plane pl - 1 out of the window.
 void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch* copy)
 {
     *perm = pr.perm;
@@ -406,6 +418,10 @@ void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch
     else
         perm->lds.a_ptr += off;
     copy->copy.dst += off;
+    if (pr.carry && pl > 0) {
+        perm->carry.dst = pr.out + (pl - 1) * pr.plane_bytes;
+        perm->carry.step = pr.carry_step;
+    }
 }
 
 // Per-rank tables: only the entries a call uses are looked at -- the inputs
@@ -629,12 +645,14 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     }
     // Chunked: per plane, permute into the window, then copy the window out.
     // Stream order makes plane p's copy finish before plane p+1 overwrites
-    // the window.
+    // the window.  With carry, plane p's copy is part of plane p+1's launch
+    // (each tile copies its window range out before overwriting it), and
+    // only the last plane's copy is launched on its own.
     for (int64_t pl = 0; pl < plan->B; ++pl) {
         Launch perm, copy;
         to_plane(pr, mode, pl, &perm, &copy);
         err = backend_launch(perm, stream);
-        if (err == 0) err = backend_launch(copy, stream);
+        if (err == 0 && (!pr.carry || pl == plan->B - 1)) err = backend_launch(copy, stream);
         if (err != 0) {
             disable(plan, "launching a chunked-plane kernel", err);
             return UA2A_ERR_HIP;

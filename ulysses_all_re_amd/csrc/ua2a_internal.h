@@ -55,6 +55,7 @@ struct Launch {
     uint32_t grid;       // workgroups along x
     uint32_t lds_bytes;  // dynamic LDS (Lds kernel only)
     DirectGeom direct;
+    DirectCarry carry;   // Direct on the 3-D grid: copy the previous chunked plane out (dst null: no)
     LdsGeom lds;
     CopyGeom copy;
     RanksGeom ranks;

@@ -17,7 +17,9 @@
 //    aligned chunks, re-ordering runs inside LDS in G-byte pieces; tiles go
 //    to the XCDs in runs of consecutive tiles (see LdsGeom).
 //  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
-//    to move the one-plane window into the output.
+//    to move the one-plane window into the output (after the last plane;
+//    on the direct path each earlier plane's copy rides in the next plane's
+//    launch, ua2a_direct3d_carry_kernel).
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
@@ -78,6 +80,19 @@ struct StreamMem {
     // bytes outside the span are mapped; they are never used, and only an
     // exchange's input, which nothing writes meanwhile, is read this way.
     __device__ static u32x4 ld_part(const u32x4* p, uint32_t, uint32_t) { return __builtin_nontemporal_load(p); }
+    // Order point: v's registers are an input (so the wave waits for v's load
+    // to return before going on) and memory is clobbered (so the compiler
+    // moves no access across it).
+    template <class T>
+    __device__ static void held(const T& v)
+    {
+        if constexpr (sizeof(T) == 16)
+            asm volatile("" ::"v"(__builtin_bit_cast(v4i32, v)) : "memory");
+        else if constexpr (sizeof(T) == 8)
+            asm volatile("" ::"v"(__builtin_bit_cast(v2i32, v)) : "memory");
+        else
+            asm volatile("" ::"v"(static_cast<uint32_t>(v)) : "memory");
+    }
 };
 
 // Readiness credits of a publishing exchange.  A launch that follows a part
@@ -111,6 +126,16 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom 
         add_credits(g.sig_credits, g.sig_first, g.sig_count);
     direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
         g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
+}
+
+// A chunked plane after the first (3-D grid, one plane): the tile copies the
+// previous plane's window range out to `c` before overwriting it.
+template <int VB, bool MODE1>
+__global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_carry_kernel(DirectGeom g, DirectCarry c)
+{
+    const DirectTile d = direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z);
+    uint8_t* const carry_tile = c.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(blockIdx.z) * c.step) * VB;
+    direct_carry_tile_body<StreamMem, VB, MODE1, kDirectBlock>(g, d, threadIdx.x, carry_tile);
 }
 
 // The credits of a publishing exchange's last part.
@@ -221,6 +246,19 @@ const void* direct3d_fn(int vb)
     }
 }
 
+template <bool MODE1>
+const void* carry3d_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
 template <bool SIG>
 const void* direct_any(const Launch& L)
 {
@@ -303,7 +341,13 @@ int backend_launch(const Launch& L, void* stream)
     size_t shmem = 0;
     switch (L.kernel) {
     case Kernel::Direct:
-        fn = L.direct.sig_count ? direct_any<true>(L) : direct_any<false>(L);
+        if (L.carry.dst != nullptr) {
+            if (!L.grid3d || L.direct.sig_count) return static_cast<int>(hipErrorInvalidValue);
+            fn = L.mode ? carry3d_fn<true>(L.width) : carry3d_fn<false>(L.width);
+            arg2 = const_cast<DirectCarry*>(&L.carry);
+        } else {
+            fn = L.direct.sig_count ? direct_any<true>(L) : direct_any<false>(L);
+        }
         arg = &dg;
         break;
     case Kernel::Lds:
