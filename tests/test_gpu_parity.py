@@ -473,6 +473,38 @@ def test_window_is_reused_and_left_alone_outside_its_size():
     plan.close()
 
 
+@pytest.mark.parametrize("shape", [(4, 5, 96, 8, 64, "bf16"), (3, 2, 50, 6, 5, "fp32"),
+                                   (2, 4, 33, 4, 3, "bf16"), (4, 3, 40, 4, 3, "bf16"),
+                                   (3, 3, 41, 3, 5, "u8"), (8, 6, 17, 40, 128, "bf16")],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_chunked_copies_carried_by_the_next_plane(shape):
+    """Chunked exchanges on the direct path (16/8/4/2/1-byte vectors, 2-6 planes): planes
+    after the first copy the previous plane out of the window inside their own
+    launch (B + 1 launches).  The output matches the oracle, and the window ends
+    holding the last plane of every rank in the output's layout."""
+    w, B, S, H, D, dtype = shape
+    dt = {"bf16": torch.bfloat16, "fp32": torch.float32, "u8": torch.uint8}[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    win = torch.full((lay["window_bytes"],), 0x5A, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=win)
+    plan.set_path(ua.UA2A_PATH_DIRECT)
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 21 + mode)
+        want = oracle_out(x, mode, w)
+        xd = x.to(DEV)
+        info = plan.describe(xd, mode, True)
+        assert info["path"] == ua.UA2A_PATH_DIRECT and info["grid_dims"] == 3
+        assert info["launches"] == B + 1
+        note(f"carry {shape} mode={mode} {info}")
+        y = plan.exchange(xd, mode, True, out=poisoned(plan.out_shape(mode), dt))
+        torch.cuda.synchronize()
+        assert_same_bits(y, want, f"carry {shape} mode {mode}")
+        last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+        assert torch.equal(win.cpu().reshape(w, -1), last), f"window after {shape} mode {mode}"
+    plan.close()
+
+
 # ------------------------------------------------------------- argument checks
 
 def test_argument_checks_on_device_tensors():
