@@ -445,6 +445,44 @@ def run_overlap(args):
 # ------------------------------------------------- per-configuration records
 
 RECORD_WORKLOADS = ("tiny", "mid", "video_dit", "chunked", "awkward")
+HOST_CPU_SHARE = 16      # host threads a GPU job may use on the MI355X hosts
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_on_threads(xb, mode, w):
+    """The oracle over every sender, the senders split into contiguous ranges
+    run by as many threads as there are senders (at most the host share): each
+    range is one per-rank oracle call, which writes only the runs its senders
+    send, so the ranges write disjoint bytes of the same output.  Returns
+    (output, seconds, threads)."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle
+
+    B, S_local, H, D = oracle.local_shape(xb.shape, mode, w)
+    out = np.empty((w, B, S_local * w, H // w, D) if mode == 0 else (w, B, S_local, H, D),
+                   dtype=xb.dtype)
+    threads = max(1, min(w, HOST_CPU_SHARE, os.cpu_count() or 1))
+    cuts = [w * t // threads for t in range(threads + 1)]
+    xs, outs = [xb[k] for k in range(w)], [out[k] for k in range(w)]
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(threads) as pool:     # the calls release the GIL
+        for f in [pool.submit(oracle.exchange_ranks, xs, outs, mode, cuts[t], cuts[t + 1] - cuts[t])
+                  for t in range(threads)]:
+            f.result()
+    return out, time.perf_counter() - t0, threads
 
 
 def run_records(args):
@@ -455,8 +493,10 @@ def run_records(args):
     buffer sets as in the main bench, so small tensors are timed against HBM),
     the average of the same number of back-to-back launches, the runtime's
     device-to-device copy of the same bytes timed per launch the same way, the
-    oracle's single-thread time on the same input, whether the output equals
-    the oracle's byte for byte, and the SHA-256 of the input bytes.  Mode-0
+    oracle's single-thread time on the same input (and, unchunked, its time
+    with the senders split over threads, one per sender up to the host share,
+    checked equal to the single-thread result), whether the output equals the
+    oracle's byte for byte, and the SHA-256 of the input bytes.  Mode-0
     inputs use the workload's first seed, mode-1 inputs an independent tensor
     of the mode-1 shape from its second seed."""
     import statistics
@@ -502,6 +542,11 @@ def run_records(args):
                 plan.exchange(xs[0], mode, chunked, out=outs[0], stream=stream)
                 torch.cuda.synchronize(dev)
                 exact = bool(np.array_equal(outs[0].cpu().view(BITS_VIEW[e]).numpy(), want))
+                if not chunked:
+                    got_n, oracle_n_s, n_threads = oracle_on_threads(xb, mode, w)
+                    if not np.array_equal(got_n, want):
+                        raise SystemExit(f"records: the threaded oracle differs on {name} mode {mode}")
+                    del got_n
                 del want
 
                 def launch(i):
@@ -549,8 +594,10 @@ def run_records(args):
                     "pct_peak": round(100 * moved / (med * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2),
                     "memcpy_GBps": round(moved / (statistics.median(tc) * 1e-6) / 1e9, 1),
                     "oracle_1core_s": round(oracle_s, 4),
-                    "oracle_ncore_s": None,
-                    "ncores": 1,
+                    "oracle_ncore_s": None if chunked else round(oracle_n_s, 4),
+                    "ncores": None if chunked else n_threads,
+                    "oracle_ncore_form": None if chunked else "sender ranges on threads",
+                    "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
                     "bit_exact": exact,
                     "input_sha256": sha,
                 }

@@ -1,5 +1,5 @@
-"""bench.py's host-side logic, on the CPU: the one-GPU refusal and the parsing of
-kernel names in rocprofv3 output."""
+"""bench.py's host-side logic, on the CPU: the one-GPU refusal, the parsing of
+kernel names in rocprofv3 output and the records' threaded oracle timing."""
 from __future__ import annotations
 
 import os
@@ -25,3 +25,20 @@ def test_mode_of_a_kernel_name():
     assert not bench._is_mode1("_ZN4ua2a20ua2a_direct3d_kernelILi16ELb0ELb1EEEvNS_10DirectGeomE")
     assert bench._is_mode1("_ZN4ua2a20ua2a_direct3d_kernelILi16ELb1ELb0EEEvNS_10DirectGeomE")
     assert not bench._is_mode1("__amd_rocclr_copyBuffer")
+
+
+def test_threaded_oracle_equals_the_single_thread_oracle():
+    """The records' multi-thread oracle timing splits the senders over threads;
+    its output must be the single-thread oracle's, byte for byte."""
+    import numpy as np
+
+    import oracle
+    rng = np.random.default_rng(3)
+    for (w, B, S, H, D, dt) in [(1, 2, 3, 4, 5, np.uint16), (3, 2, 5, 6, 4, np.uint32),
+                                (8, 1, 7, 16, 3, np.uint8), (5, 2, 4, 10, 2, np.uint64)]:
+        for mode in (0, 1):
+            shape = (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+            x = rng.integers(0, np.iinfo(dt).max, size=shape, dtype=dt)
+            got, secs, threads = bench.oracle_on_threads(x, mode, w)
+            assert threads == min(w, bench.HOST_CPU_SHARE, os.cpu_count() or 1) and secs >= 0
+            assert np.array_equal(got, oracle.exchange(x, mode, w)), (w, mode)

@@ -47,4 +47,5 @@ def test_records_are_bit_exact():
     assert [(r["mode"], r["chunked"]) for r in recs] == [(0, False), (1, False)]
     for r in recs:
         assert r["bit_exact"] is True and r["launches_timed"] == 5
+        assert r["ncores"] == 2 and r["oracle_ncore_s"] is not None    # tiny: w = 2 senders
         assert r["t_min_us"] <= r["t_median_us"] and len(r["input_sha256"]) == 64
