@@ -351,6 +351,49 @@ def test_random_cases(case):
     plan.close()
 
 
+def _random_carry_cases(n, seed):
+    """Seeded chunked exchanges of 2-9 planes on the direct path (each later
+    plane's launch carries the previous plane's copy), misaligned bases included."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in _random_cases(n, seed):
+        c.update(B=int(rng.integers(2, 10)), chunked=True, path="direct")
+        c["S"] = max(1, min(c["S"], (32 << 20) // (c["w"] * c["B"] * c["H"] * c["D"] * c["e"])))
+        cases.append(c)
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_carry_cases(24, 4242), ids=lambda c: (
+    f"w{c['w']}B{c['B']}S{c['S']}H{c['H']}D{c['D']}{c['name']}m{c['mode']}{c['mis_in']}{c['mis_out']}"))
+def test_random_carried_chunks(case):
+    w, B, S, H, D, dt = case["w"], case["B"], case["S"], case["H"], case["D"], case["dt"]
+    n = w * B * S * H * D
+    mode = case["mode"]
+    lay = ua.ua2a_layout(w, B, S, H, D, case["e"])
+    window = torch.full((lay["window_bytes"] + 256,), 0x3C, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=window[:lay["window_bytes"]])
+    plan.set_path(ua.UA2A_PATH_DIRECT)
+    x = make_tensor(in_shape(w, B, S, H, D, mode), case["name"], "bytes", n % 7919)
+    want = oracle_out(x, mode, w)
+    xin = torch.zeros(n + 8, dtype=dt, device=DEV)
+    xin[case["mis_in"]:case["mis_in"] + n] = x.reshape(-1).to(DEV)
+    outbuf = poisoned((n + 8,), dt)
+    xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
+    yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
+    info = plan.describe(xi, mode, True, out=yo)
+    note(f"random carry {case} {info}")
+    plan.exchange(xi, mode, True, out=yo)
+    torch.cuda.synchronize()
+    assert_same_bits(yo, want, f"random carry case {case}")
+    guard = bits(outbuf.cpu())
+    full = 255 if guard.dtype == torch.uint8 else POISON
+    assert (guard[:case["mis_out"]] == full).all() and (guard[case["mis_out"] + n:] == full).all()
+    assert (window[lay["window_bytes"]:].cpu() == 0x3C).all()
+    if info["grid_dims"] == 3:
+        assert info["launches"] == B + 1
+    plan.close()
+
+
 # ------------------------------------------------------ launch-shape freedom
 
 @pytest.mark.parametrize("blocks", [1, 7, 64, 0])
