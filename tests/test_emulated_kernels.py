@@ -230,6 +230,19 @@ def test_emulated_chunked_carry(emu, shape):
             assert np.array_equal(bufs[2].view.reshape(w, -1), out[:, B - 1]), (mode, path, blocks)
 
 
+def test_emulated_chunked_carry_many_planes(emu):
+    """Forty planes through one window: 41 launches, every plane but the last
+    copied out by the next plane's launch, the result the oracle's."""
+    shape = (3, 40, 5, 6, 8, 2)
+    w, B, S, H, D, e = shape
+    for mode in (0, 1):
+        x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_DIRECT, seed=17 + mode)
+        assert info.launches == B + 1 and emu.ua2a_emu_carry_launches() == B - 1
+        assert emu.ua2a_emu_kernel_count(2) == 1
+        assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
+        assert all(b.guards_intact() for b in bufs), mode
+
+
 def test_fdiv_matches_exact_division(emu):
     """The kernels' multiply-high division against exact integer division."""
     fn = emu.ua2a_emu_fdiv
