@@ -70,11 +70,16 @@ void run_direct(const Launch& L)
                     if (!take_tile()) return;
                     const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
                     if (L.carry.dst != nullptr) {
-                        // a chunked plane after the first: the previous plane's
-                        // window range goes out first, tile by tile
+                        // a chunked plane after the first: every lane of both
+                        // waves loads, then (the barrier) every lane stores
                         uint8_t* ct = L.carry.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(z) * L.carry.step) * VB;
-                        for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-                            direct_carry_tile_body<CheckedMem, VB, M1, kDirectBlock>(g, d, tid, ct);
+                        std::vector<CarryVectors<VB>> v(kCarryBlock);
+                        for (uint32_t tid = 0; tid < kCarryBlock; ++tid)
+                            v[tid] = direct_carry_load<CheckedMem, VB, M1, kDirectBlock>(
+                                g, d, tid / kDirectBlock, tid % kDirectBlock);
+                        for (uint32_t tid = 0; tid < kCarryBlock; ++tid)
+                            direct_carry_store<CheckedMem, VB, M1, kDirectBlock>(
+                                g, d, tid / kDirectBlock, tid % kDirectBlock, ct, v[tid]);
                         continue;
                     }
                     for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
@@ -233,6 +238,7 @@ int backend_launch(const Launch& L, void*)
     const uint32_t want_block = (L.kernel == Kernel::Lds || L.kernel == Kernel::LdsRanks) ? kLdsBlock
                               : L.kernel == Kernel::Copy ? kCopyBlock
                               : (L.kernel == Kernel::Wait || L.kernel == Kernel::Signal) ? kWaitBlock
+                              : (L.kernel == Kernel::Direct && L.carry.dst != nullptr) ? kCarryBlock
                               : kDirectBlock;
     if (L.block != want_block) return 5;
     switch (L.kernel) {

@@ -26,10 +26,6 @@ struct PlainMem {
     {
         *reinterpret_cast<T*>(base + off) = v;
     }
-    // Order point: later accesses wait until v has been read (the host runs
-    // each thread in program order, so nothing to do here).
-    template <class T>
-    UA2A_HD static void held(const T&) {}
     // Bytes [lo, hi) of the aligned 16-byte chunk at p, the others zero: the
     // emulation reads nothing outside a span.  (The kernels read such a chunk
     // whole; see StreamMem.)
@@ -112,29 +108,54 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
     }
 }
 
-// direct_tile_body for a chunked plane after the first: each lane first
-// moves the window vector it is about to overwrite (the previous plane's) to
-// `carry_tile`, the tile's range in the output, then writes the new vector
-// there.  Mem::held(old) keeps every later memory access after the point
-// where the old vector is in registers, so the overwrite cannot pass the
-// read of the same address.
+// A chunked plane after the first, on two waves of BS lanes: wave 0 moves
+// the tile's window range (the previous plane) out to `carry_tile`, its range
+// in the output; wave 1 writes the new plane into the window.  Each lane
+// loads its vectors (direct_carry_load), the workgroup waits at a barrier
+// until every load has returned, then each lane stores (direct_carry_store):
+// no new vector can reach the window before the old one has been read.  A
+// tile is 16 * BS bytes, so a lane holds 16 / VB vectors: lane + k * BS.
+// `wave` is uniform across a wave, so each wave takes one side only.
+template <int VB>
+struct CarryVectors {
+    static constexpr uint32_t kPerLane = 16 / VB;
+    typename Piece<VB>::T v[kPerLane];
+};
+
 template <class Mem, int VB, bool MODE1, uint32_t BS>
-UA2A_HD void direct_carry_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t tid,
-                                    uint8_t* carry_tile)
+UA2A_HD CarryVectors<VB> direct_carry_load(const DirectGeom& g, const DirectTile& d, uint32_t wave,
+                                           uint32_t lane)
 {
     typedef typename Piece<VB>::T T;
-    const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
-    const int64_t first = d.dst_slab + d.u0;
-    uint8_t* const tile = g.dst + first * VB;
-    const uint32_t tile_bytes = d.nvec * VB;
-    for (uint32_t delta = tid; delta < d.nvec; delta += BS) {
-        int64_t from, to;
-        direct_vector<MODE1>(g, d, d.u0 + delta, from, to);
-        const T old = Mem::ld(reinterpret_cast<const T*>(tile) + delta);
-        const T v = Mem::ld(src + from);
-        Mem::st_tile(carry_tile, tile_bytes, delta * VB, old);
-        Mem::held(old);
-        Mem::st_tile(tile, tile_bytes, static_cast<uint32_t>((to - first) * VB), v);
+    CarryVectors<VB> c;
+#pragma unroll
+    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k) {
+        const uint32_t delta = lane + k * BS;
+        c.v[k] = T{};
+        if (delta < d.nvec) {
+            if (wave == 0) {
+                c.v[k] = Mem::ld(reinterpret_cast<const T*>(g.dst) + d.dst_slab + d.u0 + delta);
+            } else {
+                int64_t from, to;
+                direct_vector<MODE1>(g, d, d.u0 + delta, from, to);
+                c.v[k] = Mem::ld(reinterpret_cast<const T*>(g.src) + from);
+            }
+        }
+    }
+    return c;
+}
+
+template <class Mem, int VB, bool MODE1, uint32_t BS>
+UA2A_HD void direct_carry_store(const DirectGeom& g, const DirectTile& d, uint32_t wave, uint32_t lane,
+                                uint8_t* carry_tile, const CarryVectors<VB>& c)
+{
+    // each wave's stores go through one range: the tile's place in the output
+    // (wave 0) or in the window (wave 1), written in order of its vectors
+    uint8_t* const base = wave == 0 ? carry_tile : g.dst + (d.dst_slab + d.u0) * VB;
+#pragma unroll
+    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k) {
+        const uint32_t delta = lane + k * BS;
+        if (delta < d.nvec) Mem::st_tile(base, d.nvec * VB, delta * VB, c.v[k]);
     }
 }
 

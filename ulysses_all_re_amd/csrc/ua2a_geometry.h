@@ -31,6 +31,7 @@ namespace ua2a {
 // workgroup (measured fastest on MI355X for these streams); LDS kernel: four
 // waves sharing one LDS tile.
 constexpr uint32_t kDirectBlock = 64;
+constexpr uint32_t kCarryBlock = 2 * kDirectBlock;   // carry kernel: one wave copies out, one permutes
 constexpr uint32_t kCopyBlock = 64;
 constexpr uint32_t kLdsBlock = 256;
 

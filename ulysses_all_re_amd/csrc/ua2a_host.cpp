@@ -421,6 +421,7 @@ void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch
     if (pr.carry && pl > 0) {
         perm->carry.dst = pr.out + (pl - 1) * pr.plane_bytes;
         perm->carry.step = pr.carry_step;
+        perm->block = kCarryBlock;
     }
 }
 

@@ -186,16 +186,24 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom 
         g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
 }
 
-// A chunked plane after the first (3-D grid, one plane): the tile copies the
-// previous plane's window range out to `c` before overwriting it.
+// A chunked plane after the first (3-D grid, one plane, two waves): the tile
+// copies the previous plane's window range out to `c` before overwriting it.
 template <int VB, bool MODE1>
-__global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_carry_kernel(DirectGeom g, DirectCarry c)
+__global__ __launch_bounds__(kCarryBlock) void ua2a_direct3d_carry_kernel(DirectGeom g, DirectCarry c)
 {
     args_up_front(g);
     asm volatile("" ::"s"(c.dst), "s"(c.step));
     const DirectTile d = direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z);
     uint8_t* const carry_tile = c.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(blockIdx.z) * c.step) * VB;
-    direct_carry_tile_body<StreamMem, VB, MODE1, kDirectBlock>(g, d, threadIdx.x, carry_tile);
+    static_assert(kTileBytes == 16 * kDirectBlock, "a carry tile is 16 bytes per lane of a wave");
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kDirectBlock);
+    const uint32_t lane = threadIdx.x % kDirectBlock;
+    const CarryVectors<VB> v = direct_carry_load<StreamMem, VB, MODE1, kDirectBlock>(g, d, wave, lane);
+#pragma unroll
+    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k)
+        StreamMem::held(v.v[k]);   // this lane's loads have returned ...
+    __syncthreads();               // ... and so have every other lane's
+    direct_carry_store<StreamMem, VB, MODE1, kDirectBlock>(g, d, wave, lane, carry_tile, v);
 }
 
 // The credits of a publishing exchange's last part.
