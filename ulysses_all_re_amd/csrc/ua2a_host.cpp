@@ -419,6 +419,8 @@ void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch
         perm->lds.a_ptr += off;
     copy->copy.dst += off;
     if (pr.carry && pl > 0) {
+        // two waves per tile; x stays far inside a dispatch's 2^31 lanes, as a
+        // slab lies within one plane (< 2^32 bytes, so < 2^22 tiles)
         perm->carry.dst = pr.out + (pl - 1) * pr.plane_bytes;
         perm->carry.step = pr.carry_step;
         perm->block = kCarryBlock;
