@@ -683,8 +683,8 @@ def traffic_from(d):
 def summarize_trace(d, workload, ranks=None, chunked=False):
     """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run
     (with ranks == "one", each exchange launch moves one sender's share, 1/w;
-    with chunked, each launch moves one plane, 1/B, and a launch that also
-    carries the previous plane's copy moves two)."""
+    with chunked, a per-plane launch moves one plane, 1/B, and the one-launch
+    chunked kernel the whole exchange)."""
     paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -698,7 +698,7 @@ def summarize_trace(d, workload, ranks=None, chunked=False):
     share = moved // c["w"] if ranks == "one" else moved // c["B"] if chunked else moved
     print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {share // 2} B"
           + (", one sender" if ranks == "one" else ", one plane" if chunked else "")
-          + ("; 4 x for the carry kernel" if chunked else "") + ") |")
+          + ("; B x for the one-launch chunked kernel" if chunked else "") + ") |")
     print("|---|---|---|---|---|---|")
     with open(paths[0], newline="") as f:
         for r in csv.DictReader(f):
@@ -708,7 +708,7 @@ def summarize_trace(d, workload, ranks=None, chunked=False):
             avg = float(r["AverageNs"])
             rate = ""
             if "ua2a_" in r["Name"]:
-                k = 2 if chunked and "carry" in r["Name"] else 1
+                k = c["B"] if chunked and "chunked_kernel" in r["Name"] else 1
                 rate = f"{k * share / (avg * 1e-9) / 1e9:.1f}"
             elif COPY_KERNEL_HINT in r["Name"] and ranks is None:   # per-rank runs also clone ranks
                 rate = f"{moved / (avg * 1e-9) / 1e9:.1f}"

@@ -18,9 +18,49 @@
 
 namespace ua2a {
 
+// The window of a one-launch chunked exchange: which lane (of which tile)
+// last stored each byte.  A lane may read back only window bytes that it
+// stored itself, so no lane depends on another's window accesses, and the
+// order in which the emulation runs lanes (one lane's planes after another's)
+// cannot hide a race that the device could hit.
+namespace {
+const uint8_t* g_win = nullptr;
+size_t g_win_bytes = 0;
+std::vector<int64_t> g_win_owner;     // -1: never stored
+int64_t g_lane_id = 0;                // tile * 64 + lane of the running body
+}  // namespace
+
 // PlainMem, with every tile store checked against the tile's written range
 // (the kernels store through a buffer resource over exactly that range).
 struct CheckedMem : PlainMem {
+    template <class T>
+    static size_t win_index(const T* p)
+    {
+        const uint8_t* b = reinterpret_cast<const uint8_t*>(p);
+        if (g_win == nullptr || b < g_win || b + sizeof(T) > g_win + g_win_bytes) {
+            fprintf(stderr, "emu: window access outside the window\n");
+            abort();
+        }
+        return static_cast<size_t>(b - g_win);
+    }
+    template <class T>
+    static void st_win(T* p, T v)
+    {
+        const size_t i = win_index(p);
+        for (size_t k = 0; k < sizeof(T); ++k) g_win_owner[i + k] = g_lane_id;
+        *p = v;
+    }
+    template <class T>
+    static T ld_win(const T* p)
+    {
+        const size_t i = win_index(p);
+        for (size_t k = 0; k < sizeof(T); ++k)
+            if (g_win_owner[i + k] != g_lane_id) {
+                fprintf(stderr, "emu: window byte %zu read by a lane that did not store it\n", i + k);
+                abort();
+            }
+        return *p;
+    }
     template <class T>
     static void st_tile(uint8_t* base, uint32_t nbytes, uint32_t off, T v)
     {
@@ -36,8 +76,7 @@ namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[7] = {0, 0, 0, 0, 0, 0, 0};
-int g_carry_launches = 0;     // direct launches that also copied a chunked plane out
+int g_kernel_counts[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 uint32_t g_last_grid = 0;
 long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
 bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
@@ -69,25 +108,11 @@ void run_direct(const Launch& L)
                 for (uint32_t x = 0; x < L.grid; ++x) {
                     if (!take_tile()) return;
                     const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
-                    if (L.carry.dst != nullptr) {
-                        // a chunked plane after the first: every lane of both
-                        // waves loads, then (the barrier) every lane stores
-                        uint8_t* ct = L.carry.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(z) * L.carry.step) * VB;
-                        std::vector<CarryVectors<VB>> v(kCarryBlock);
-                        for (uint32_t tid = 0; tid < kCarryBlock; ++tid)
-                            v[tid] = direct_carry_load<CheckedMem, VB, M1, kDirectBlock>(
-                                g, d, tid / kDirectBlock, tid % kDirectBlock);
-                        for (uint32_t tid = 0; tid < kCarryBlock; ++tid)
-                            direct_carry_store<CheckedMem, VB, M1, kDirectBlock>(
-                                g, d, tid / kDirectBlock, tid % kDirectBlock, ct, v[tid]);
-                        continue;
-                    }
                     for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
                         direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
                 }
         return;
     }
-    if (L.carry.dst != nullptr) abort();   // the carry launch exists on the 3-D grid only
     // a capped grid loops grid-stride; every tile is visited exactly once either way
     for (uint32_t t = 0; t < g.num_tiles; ++t) {
         if (!take_tile()) return;
@@ -95,6 +120,39 @@ void run_direct(const Launch& L)
         for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
             direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
     }
+}
+
+// The one-launch chunked exchange: every workgroup of the 3-D grid, every
+// lane, with the window's byte owners tracked (see CheckedMem).
+template <int VB, bool M1>
+void run_chunked(const Launch& L)
+{
+    const DirectGeom& g = L.direct;
+    g_win = g.dst;
+    g_win_bytes = static_cast<size_t>(g.w) * static_cast<size_t>(L.chunk.plane) * VB;
+    g_win_owner.assign(g_win_bytes, -1);
+    int64_t tile = 0;
+    for (uint32_t z = 0; z < L.grid_z; ++z)
+        for (uint32_t y = 0; y < L.grid_y; ++y)
+            for (uint32_t x = 0; x < L.grid; ++x, ++tile) {
+                const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
+                const bool full = d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock;
+                for (uint32_t tid = 0; tid < kDirectBlock; ++tid) {
+                    g_lane_id = tile * kDirectBlock + tid;
+                    if (full)
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, true>(g, d, L.chunk, z, tid);
+                    else
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, false>(g, d, L.chunk, z, tid);
+                }
+            }
+    // every window byte belongs to exactly one lane and was written
+    for (size_t i = 0; i < g_win_bytes; ++i)
+        if (g_win_owner[i] < 0) {
+            fprintf(stderr, "emu: window byte %zu never written\n", i);
+            abort();
+        }
+    g_win = nullptr;
+    g_win_bytes = 0;
 }
 
 // The wait kernel with nothing running beside it: a counter short of its
@@ -188,6 +246,19 @@ int dispatch_direct(const Launch& L, int vb)
     }
 }
 
+template <bool M1>
+int dispatch_chunked(const Launch& L, int vb)
+{
+    switch (vb) {
+    case 16: run_chunked<16, M1>(L); return 0;
+    case 8: run_chunked<8, M1>(L); return 0;
+    case 4: run_chunked<4, M1>(L); return 0;
+    case 2: run_chunked<2, M1>(L); return 0;
+    case 1: run_chunked<1, M1>(L); return 0;
+    default: return 1;
+    }
+}
+
 template <bool M1, class Bases>
 int dispatch_lds(const LdsGeom& g, const Bases& bases, int gw)
 {
@@ -231,14 +302,12 @@ int backend_launch(const Launch& L, void*)
     }
     ++g_launches;
     ++g_kernel_counts[static_cast<int>(L.kernel)];
-    if (L.kernel == Kernel::Direct && L.carry.dst != nullptr) ++g_carry_launches;
     if (g_stalled) return 0;       // queued behind an unfinished launch
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
     const uint32_t want_block = (L.kernel == Kernel::Lds || L.kernel == Kernel::LdsRanks) ? kLdsBlock
                               : L.kernel == Kernel::Copy ? kCopyBlock
                               : (L.kernel == Kernel::Wait || L.kernel == Kernel::Signal) ? kWaitBlock
-                              : (L.kernel == Kernel::Direct && L.carry.dst != nullptr) ? kCarryBlock
                               : kDirectBlock;
     if (L.block != want_block) return 5;
     switch (L.kernel) {
@@ -251,12 +320,20 @@ int backend_launch(const Launch& L, void*)
                 slabs * L.direct.tiles_per_slab != L.direct.num_tiles ||
                 L.grid_y != (L.mode ? L.direct.nb : L.direct.w) || L.grid_z % (L.mode ? 1u : L.direct.nb))
                 return 6;
-            // a carry launch covers one plane (z is then the window block)
-            if (L.carry.dst != nullptr && (L.direct.nb != 1 || L.direct.sig_count != 0)) return 8;
-        } else if (L.grid_y != 1 || L.grid_z != 1 || L.carry.dst != nullptr) {
+        } else if (L.grid_y != 1 || L.grid_z != 1) {
             return 7;
         }
         return L.mode ? dispatch_direct<true>(L, L.width) : dispatch_direct<false>(L, L.width);
+    case Kernel::Chunked: {
+        // the 3-D grid of one plane's tiles of every rank, z = window block
+        const DirectGeom& g = L.direct;
+        if (!L.grid3d || g.nb != 1 || g.sig_count != 0 || g.group != 0 || L.grid != g.tiles_per_slab ||
+            static_cast<uint64_t>(L.grid_y) * L.grid_z * g.tiles_per_slab != g.num_tiles ||
+            L.grid_y != (L.mode ? 1u : g.w) || L.grid_z != g.w || L.chunk.planes < 1 ||
+            L.chunk.plane != (L.mode ? g.p_rank : g.a_rank))
+            return 6;
+        return L.mode ? dispatch_chunked<true>(L, L.width) : dispatch_chunked<false>(L, L.width);
+    }
     case Kernel::Lds:
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||
@@ -316,12 +393,10 @@ void ua2a_emu_reset_counts(void)
 {
     ua2a::g_launches = 0;
     for (int& c : ua2a::g_kernel_counts) c = 0;
-    ua2a::g_carry_launches = 0;
 }
 
 int ua2a_emu_launches(void) { return ua2a::g_launches; }
 int ua2a_emu_kernel_count(int kernel) { return ua2a::g_kernel_counts[kernel]; }
-int ua2a_emu_carry_launches(void) { return ua2a::g_carry_launches; }
 unsigned ua2a_emu_last_grid(void) { return ua2a::g_last_grid; }
 
 /* The LDS kernels' launch-slot order for num_slots slots with 2^xlog

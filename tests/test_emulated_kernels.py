@@ -187,11 +187,9 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
     shape = (4, 4, 32, 16, 64, 2)
     w, B, S, H, D, e = shape
     x, y, info, _ = emu_exchange(emu, shape, 0, chunked=True, seed=7)
-    # B permutes, planes 1..B-1 each also copying the previous plane out of
-    # the window, and one copy launch for the last plane
-    assert info.launches == B + 1
-    assert emu.ua2a_emu_kernel_count(0) == B and emu.ua2a_emu_carry_launches() == B - 1
-    assert emu.ua2a_emu_kernel_count(2) == 1
+    # the whole chunked exchange is one launch of the chunked kernel
+    assert info.launches == 1 and info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH
+    assert emu.ua2a_emu_kernel_count(7) == 1 and emu.ua2a_emu_launches() == 1
     assert np.array_equal(y, oracle_bytes(x, shape, 0))
     # feed mode 0's output back through mode 1
     lay = ua2a_layout(emu, *shape)
@@ -209,36 +207,54 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
 @pytest.mark.parametrize("shape", [(4, 4, 32, 16, 64, 2), (3, 3, 5, 6, 4, 4), (2, 5, 9, 4, 64, 2),
                                    (5, 2, 4, 10, 2, 1), (4, 3, 7, 8, 3, 8), (2, 3, 37, 2, 1024, 2)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_emulated_chunked_carry(emu, shape):
-    """Chunked exchanges on the direct path's 3-D grid copy each plane but the
-    last out of the window inside the next plane's launch; a blocks hint (flat
-    grid), the grouped tile order and the LDS path keep one copy launch per
-    plane.  Every form matches the oracle, leaves the guard bands alone and
-    ends with the last plane in the window."""
+def test_emulated_chunked_forms(emu, shape):
+    """Chunked exchanges on the direct path's 3-D grid are one launch of the
+    chunked kernel, in which every lane reads back only window bytes it
+    stored itself (the emulation tracks each window byte's last writer); a
+    blocks hint (flat grid), the grouped tile order and the LDS path run a
+    permute and a copy launch per plane.  Every form matches the oracle,
+    leaves the guard bands alone and ends with the last plane in the window."""
     w, B, S, H, D, e = shape
     for mode in (0, 1):
         for path, blocks in ((ua.UA2A_PATH_DIRECT, 0), (ua.UA2A_PATH_DIRECT, 5), (ua.UA2A_PATH_LDS, 0)):
             x, y, info, bufs = emu_exchange(emu, shape, mode, True, path, blocks=blocks, seed=11 + mode)
             assert np.array_equal(y, oracle_bytes(x, shape, mode)), (mode, path, blocks)
             assert all(b.guards_intact() for b in bufs), (mode, path, blocks)
-            carry = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3 and B > 1
-            assert info.launches == (B + 1 if carry else 2 * B), (mode, path, blocks)
-            assert emu.ua2a_emu_carry_launches() == (B - 1 if carry else 0)
-            assert emu.ua2a_emu_kernel_count(2) == (1 if carry else B)
+            fused = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3
+            assert info.chunked_form == (ua.UA2A_CHUNKED_ONE_LAUNCH if fused else ua.UA2A_CHUNKED_PER_PLANE)
+            assert info.launches == (1 if fused else 2 * B), (mode, path, blocks)
+            assert emu.ua2a_emu_kernel_count(7) == (1 if fused else 0)
+            assert emu.ua2a_emu_kernel_count(2) == (0 if fused else B)
             # the window holds the last plane of every rank, in the output's layout
             out = y.reshape(w, B, -1)
             assert np.array_equal(bufs[2].view.reshape(w, -1), out[:, B - 1]), (mode, path, blocks)
 
 
-def test_emulated_chunked_carry_many_planes(emu):
-    """Forty planes through one window: 41 launches, every plane but the last
-    copied out by the next plane's launch, the result the oracle's."""
+@pytest.mark.parametrize("mis", [0, 8, 4, 2], ids=lambda m: f"mis{m}")
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 7, 9])
+def test_emulated_chunked_one_launch_planes(emu, B, mis):
+    """The one-launch chunked kernel over 1-9 planes with 16-, 8-, 4- and
+    2-byte vectors (bases misaligned to match), so every count of planes in
+    flight per lane meets a remainder; output, guards and window checked."""
+    shape = (4, B, 6, 8, 32, 2)      # run 128 B, slabs of 768 B: partial tiles
+    w = shape[0]
+    for mode in (0, 1):
+        x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_DIRECT, mis, mis, mis,
+                                        seed=31 + B + mode)
+        assert info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH and info.launches == 1
+        assert info.vector_bytes == (16 if mis == 0 else mis)
+        assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
+        assert all(b.guards_intact() for b in bufs), mode
+        assert np.array_equal(bufs[2].view.reshape(w, -1), y.reshape(w, B, -1)[:, B - 1]), mode
+
+
+def test_emulated_chunked_many_planes(emu):
+    """Forty planes through one window, in one launch; the result the oracle's."""
     shape = (3, 40, 5, 6, 8, 2)
     w, B, S, H, D, e = shape
     for mode in (0, 1):
         x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_DIRECT, seed=17 + mode)
-        assert info.launches == B + 1 and emu.ua2a_emu_carry_launches() == B - 1
-        assert emu.ua2a_emu_kernel_count(2) == 1
+        assert info.launches == 1 and emu.ua2a_emu_kernel_count(7) == 1
         assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
         assert all(b.guards_intact() for b in bufs), mode
 

@@ -109,6 +109,29 @@ def test_chunked_operator_grows_its_window():
     assert torch.equal(bits(x.grad.cpu()), oracle_bits(g, 1, w))
 
 
+def test_chunked_operator_caches_are_bounded_and_growth_is_logged(monkeypatch, caplog):
+    """Chunked calls on more streams than MAX_WINDOWS keep at most that many
+    windows (and at most MAX_PLANS plans); each window's creation and growth
+    is logged; every result matches the oracle."""
+    monkeypatch.setattr(ops, "MAX_WINDOWS", 2)
+    monkeypatch.setattr(ops, "MAX_PLANS", 3)
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    shapes = [(2, 2, 8, 4, 16), (2, 2, 16, 4, 16)]          # the second needs a larger window
+    caplog.set_level("INFO", logger=ops.__name__)
+    for k, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            for j, (w, B, S, H, D) in enumerate(shapes):
+                x = make_tensor((w, B, S, H, D), "bf16", "bytes", 90 + 2 * k + j)
+                note(f"bounded caches stream {k} shape {(w, B, S, H, D)}")
+                y = ops.all_to_all_4D(x.to(DEV), 2, 1, w, chunked=True)
+                st.synchronize()
+                assert torch.equal(bits(y.cpu()), oracle_bits(x, 0, w)), (k, j)
+        assert len(ops._windows) <= 2 and len(ops._plans) <= 3
+    grown = [r for r in caplog.records if "grown from" in r.getMessage()]
+    created = [r for r in caplog.records if "created with" in r.getMessage()]
+    assert len(grown) >= len(streams) and len(created) >= len(streams)
+
+
 def test_torch_compile_traces_the_operator():
     w, B, S, H, D = 4, 2, 64, 8, 32
     x = make_tensor((w, B, S, H, D), "fp16", "uniform", 8).to(DEV)

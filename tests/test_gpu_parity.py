@@ -351,9 +351,9 @@ def test_random_cases(case):
     plan.close()
 
 
-def _random_carry_cases(n, seed):
-    """Seeded chunked exchanges of 2-9 planes on the direct path (each later
-    plane's launch carries the previous plane's copy), misaligned bases included."""
+def _random_chunked_cases(n, seed):
+    """Seeded chunked exchanges of 2-9 planes on the direct path (one launch of
+    the chunked kernel), misaligned bases included."""
     rng = np.random.default_rng(seed)
     cases = []
     for c in _random_cases(n, seed):
@@ -363,9 +363,9 @@ def _random_carry_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_carry_cases(24, 4242), ids=lambda c: (
+@pytest.mark.parametrize("case", _random_chunked_cases(24, 4242), ids=lambda c: (
     f"w{c['w']}B{c['B']}S{c['S']}H{c['H']}D{c['D']}{c['name']}m{c['mode']}{c['mis_in']}{c['mis_out']}"))
-def test_random_carried_chunks(case):
+def test_random_chunked_one_launch(case):
     w, B, S, H, D, dt = case["w"], case["B"], case["S"], case["H"], case["D"], case["dt"]
     n = w * B * S * H * D
     mode = case["mode"]
@@ -381,16 +381,18 @@ def test_random_carried_chunks(case):
     xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
     yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
     info = plan.describe(xi, mode, True, out=yo)
-    note(f"random carry {case} {info}")
+    note(f"random chunked {case} {info}")
     plan.exchange(xi, mode, True, out=yo)
     torch.cuda.synchronize()
-    assert_same_bits(yo, want, f"random carry case {case}")
+    assert_same_bits(yo, want, f"random chunked case {case}")
     guard = bits(outbuf.cpu())
     full = 255 if guard.dtype == torch.uint8 else POISON
     assert (guard[:case["mis_out"]] == full).all() and (guard[case["mis_out"] + n:] == full).all()
     assert (window[lay["window_bytes"]:].cpu() == 0x3C).all()
+    last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+    assert torch.equal(window[:lay["window_bytes"]].cpu().reshape(w, -1), last), f"window after {case}"
     if info["grid_dims"] == 3:
-        assert info["launches"] == B + 1
+        assert info["launches"] == 1 and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
     plan.close()
 
 
@@ -520,11 +522,12 @@ def test_window_is_reused_and_left_alone_outside_its_size():
                                    (2, 4, 33, 4, 3, "bf16"), (4, 3, 40, 4, 3, "bf16"),
                                    (3, 3, 41, 3, 5, "u8"), (8, 6, 17, 40, 128, "bf16")],
                          ids=lambda s: "x".join(map(str, s)))
-def test_chunked_copies_carried_by_the_next_plane(shape):
-    """Chunked exchanges on the direct path (16/8/4/2/1-byte vectors, 2-6 planes): planes
-    after the first copy the previous plane out of the window inside their own
-    launch (B + 1 launches).  The output matches the oracle, and the window ends
-    holding the last plane of every rank in the output's layout."""
+def test_chunked_exchange_in_one_launch(shape):
+    """Chunked exchanges on the direct path (16/8/4/2/1-byte vectors, 2-6 planes) run as
+    one launch of the chunked kernel: each workgroup moves its window tile through
+    every plane, reading each plane back from the window before storing it to the
+    output.  The output matches the oracle, and the window ends holding the last
+    plane of every rank in the output's layout."""
     w, B, S, H, D, dtype = shape
     dt = {"bf16": torch.bfloat16, "fp32": torch.float32, "u8": torch.uint8}[dtype]
     e = torch.empty((), dtype=dt).element_size()
@@ -538,11 +541,11 @@ def test_chunked_copies_carried_by_the_next_plane(shape):
         xd = x.to(DEV)
         info = plan.describe(xd, mode, True)
         assert info["path"] == ua.UA2A_PATH_DIRECT and info["grid_dims"] == 3
-        assert info["launches"] == B + 1
-        note(f"carry {shape} mode={mode} {info}")
+        assert info["launches"] == 1 and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
+        note(f"chunked one launch {shape} mode={mode} {info}")
         y = plan.exchange(xd, mode, True, out=poisoned(plan.out_shape(mode), dt))
         torch.cuda.synchronize()
-        assert_same_bits(y, want, f"carry {shape} mode {mode}")
+        assert_same_bits(y, want, f"chunked one launch {shape} mode {mode}")
         last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
         assert torch.equal(win.cpu().reshape(w, -1), last), f"window after {shape} mode {mode}"
     plan.close()

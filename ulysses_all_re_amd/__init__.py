@@ -44,6 +44,9 @@ UA2A_PATH_AUTO = 0
 UA2A_PATH_DIRECT = 1
 UA2A_PATH_LDS = 2
 
+UA2A_CHUNKED_ONE_LAUNCH = 1
+UA2A_CHUNKED_PER_PLANE = 2
+
 # every symbol include/ua2a.h declares
 EXPORTED = (
     "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_ranks", "ua2a_destroy",
@@ -64,7 +67,8 @@ class ua2a_launch_info_t(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("vector_bytes", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("tiles", ctypes.c_int64),
-                ("lds_rows", ctypes.c_int32), ("grid_dims", ctypes.c_int32)]
+                ("lds_rows", ctypes.c_int32), ("grid_dims", ctypes.c_int32),
+                ("chunked_form", ctypes.c_int32)]
 
 
 class UA2AError(RuntimeError):
@@ -353,7 +357,8 @@ class Plan:
         no-argument function that issues it on the current device -- the same
         tensors, senders and stream every time -- for loops where per-call
         checks would cost more than the launch.  The function keeps the
-        tensors alive."""
+        tensors and this plan alive, reads the plan's handle at every call,
+        and raises UA2AError (invalid argument) once the plan is closed."""
         import torch
         count = self.w - first if count is None else count
         self._check_ranks(xs, outs, mode, first, count)
@@ -363,14 +368,19 @@ class Plan:
         lib = load_library()
         in_tab = _table([None if x is None else x.data_ptr() for x in xs])
         out_tab = _table([o.data_ptr() for o in outs])
-        handle, sptr = self.handle, stream.cuda_stream
+        sptr = stream.cuda_stream
+        plan = self
 
         def call():
+            handle = plan.handle
+            if not handle:
+                raise UA2AError(UA2A_ERR_INVALID_ARG, "ua2a_exchange_ranks", "the plan is closed")
             rc = lib.ua2a_exchange_ranks(handle, mode, in_tab, out_tab, first, count, sptr)
             if rc != UA2A_OK:
                 raise UA2AError(rc, "ua2a_exchange_ranks", ua2a_plan_last_error(handle))
 
         call.tensors = (list(xs), list(outs))
+        call.plan = plan
         return call
 
     def exchange_publish(self, x, mode: int, credits, out=None, parts=None, stream=None):

@@ -20,6 +20,13 @@ struct PlainMem {
     UA2A_HD static T ld(const T* p) { return *p; }
     template <class T>
     UA2A_HD static void st(T* p, T v) { *p = v; }
+    // Window accesses of the one-launch chunked exchange, and the order point
+    // between a window store and the load that reads it back.
+    template <class T>
+    UA2A_HD static T ld_win(const T* p) { return *p; }
+    template <class T>
+    UA2A_HD static void st_win(T* p, T v) { *p = v; }
+    UA2A_HD static void win_order() {}
     // A store at byte `off` of a tile's written range [base, base + nbytes).
     template <class T>
     UA2A_HD static void st_tile(uint8_t* base, uint32_t, uint32_t off, T v)
@@ -108,54 +115,80 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
     }
 }
 
-// A chunked plane after the first, on two waves of BS lanes: wave 0 moves
-// the tile's window range (the previous plane) out to `carry_tile`, its range
-// in the output; wave 1 writes the new plane into the window.  Each lane
-// loads its vectors (direct_carry_load), the workgroup waits at a barrier
-// until every load has returned, then each lane stores (direct_carry_store):
-// no new vector can reach the window before the old one has been read.  A
-// tile is 16 * BS bytes, so a lane holds 16 / VB vectors: lane + k * BS.
-// `wave` is uniform across a wave, so each wave takes one side only.
+// Chunked exchange in one launch (see ChunkedGeom): the tile's window range
+// is written and read back plane after plane by the lanes that own it.  A
+// tile is 16 * BS bytes, so a lane owns K = 16 / VB window vectors,
+// lane + k * BS, and moves them for U planes at a time: it loads the U
+// planes' input vectors, then for each plane in order stores its vectors
+// into the window and loads them back, then stores what it read to that
+// plane of the output.  The window vectors a lane touches are its own for
+// the whole launch, so the only ordering the window needs is that of one
+// lane's accesses to one address, which the hardware keeps in program order
+// (a later plane's store cannot overtake an earlier plane's load of the same
+// vector, and a load sees the same lane's earlier store).  Mem::win_order()
+// keeps the compiler from forwarding a stored vector to the load that reads
+// it back, so every output byte really is read from the window.  Window
+// accesses go through Mem::ld_win / st_win (cached: the window is re-read
+// within the launch); input and output stay streamed.
 template <int VB>
-struct CarryVectors {
-    static constexpr uint32_t kPerLane = 16 / VB;
-    typename Piece<VB>::T v[kPerLane];
+struct ChunkedLane {
+    static constexpr uint32_t kVecs = 16 / VB;                  // window vectors per lane
+    static constexpr uint32_t kPlanes = kVecs >= 4 ? 1 : 4 / kVecs;   // planes in flight per lane
 };
 
-template <class Mem, int VB, bool MODE1, uint32_t BS>
-UA2A_HD CarryVectors<VB> direct_carry_load(const DirectGeom& g, const DirectTile& d, uint32_t wave,
-                                           uint32_t lane)
+// FULL: the tile holds K vectors for every lane (all but a slab's last
+// tile), so no lane needs a bounds test -- per-lane tests split the body
+// into masked blocks, across which the compiler waits for every load in
+// flight before each store.
+template <class Mem, int VB, bool MODE1, uint32_t BS, bool FULL>
+UA2A_HD void chunked_tile_body(const DirectGeom& g, const DirectTile& d, const ChunkedGeom& c, uint32_t z,
+                               uint32_t lane)
 {
     typedef typename Piece<VB>::T T;
-    CarryVectors<VB> c;
+    constexpr uint32_t K = ChunkedLane<VB>::kVecs;
+    constexpr uint32_t U = ChunkedLane<VB>::kPlanes;
+    const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
+    T* const win = reinterpret_cast<T*>(g.dst) + d.dst_slab + d.u0;     // the tile's window range
+    const int64_t out0 = d.dst_slab + d.u0 + static_cast<int64_t>(z) * c.step;   // its range in out[z][0]
+    const uint32_t tile_bytes = d.nvec * VB;
+    int64_t from[K];
+    bool ok[K];
 #pragma unroll
-    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k) {
-        const uint32_t delta = lane + k * BS;
-        c.v[k] = T{};
-        if (delta < d.nvec) {
-            if (wave == 0) {
-                c.v[k] = Mem::ld(reinterpret_cast<const T*>(g.dst) + d.dst_slab + d.u0 + delta);
-            } else {
-                int64_t from, to;
-                direct_vector<MODE1>(g, d, d.u0 + delta, from, to);
-                c.v[k] = Mem::ld(reinterpret_cast<const T*>(g.src) + from);
-            }
+    for (uint32_t k = 0; k < K; ++k) {
+        from[k] = 0;
+        ok[k] = FULL || lane + k * BS < d.nvec;
+        if (ok[k]) {
+            int64_t to;
+            direct_vector<MODE1>(g, d, d.u0 + lane + k * BS, from[k], to);
         }
     }
-    return c;
-}
-
-template <class Mem, int VB, bool MODE1, uint32_t BS>
-UA2A_HD void direct_carry_store(const DirectGeom& g, const DirectTile& d, uint32_t wave, uint32_t lane,
-                                uint8_t* carry_tile, const CarryVectors<VB>& c)
-{
-    // each wave's stores go through one range: the tile's place in the output
-    // (wave 0) or in the window (wave 1), written in order of its vectors
-    uint8_t* const base = wave == 0 ? carry_tile : g.dst + (d.dst_slab + d.u0) * VB;
+    for (uint32_t p0 = 0; p0 < c.planes; p0 += U) {
+        const uint32_t n = umin32(U, c.planes - p0);     // planes this turn
+        T v[U][K];
 #pragma unroll
-    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k) {
-        const uint32_t delta = lane + k * BS;
-        if (delta < d.nvec) Mem::st_tile(base, d.nvec * VB, delta * VB, c.v[k]);
+        for (uint32_t i = 0; i < U; ++i)
+#pragma unroll
+            for (uint32_t k = 0; k < K; ++k)
+                if (i < n && ok[k]) v[i][k] = Mem::ld(src + (p0 + i) * c.plane + from[k]);
+#pragma unroll
+        for (uint32_t i = 0; i < U; ++i) {
+            if (i >= n) break;
+#pragma unroll
+            for (uint32_t k = 0; k < K; ++k)
+                if (ok[k]) Mem::st_win(win + lane + k * BS, v[i][k]);
+            Mem::win_order();
+#pragma unroll
+            for (uint32_t k = 0; k < K; ++k)
+                if (ok[k]) v[i][k] = Mem::ld_win(win + lane + k * BS);
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < U; ++i) {
+            if (i >= n) break;
+            uint8_t* const tile = c.out + (out0 + (p0 + i) * c.plane) * VB;
+#pragma unroll
+            for (uint32_t k = 0; k < K; ++k)
+                if (ok[k]) Mem::st_tile(tile, tile_bytes, (lane + k * BS) * VB, v[i][k]);
+        }
     }
 }
 

@@ -31,7 +31,6 @@ namespace ua2a {
 // workgroup (measured fastest on MI355X for these streams); LDS kernel: four
 // waves sharing one LDS tile.
 constexpr uint32_t kDirectBlock = 64;
-constexpr uint32_t kCarryBlock = 2 * kDirectBlock;   // carry kernel: one wave copies out, one permutes
 constexpr uint32_t kCopyBlock = 64;
 constexpr uint32_t kLdsBlock = 256;
 
@@ -112,17 +111,21 @@ struct DirectTile {
     uint32_t nvec;      // vectors in this tile
 };
 
-// Chunked exchange, planes after the first: the window still holds the
-// previous plane, and each tile copies its window range out to that plane of
-// the output just before overwriting it (the same workgroup owns both, so the
-// copy needs no launch of its own).  The window is [w][one plane]; its block
-// k goes to out[k][previous plane], so window vector x lands at
-// dst + x + k * step (vectors), with dst the previous plane of rank 0 and
-// step = rank stride - plane.  dst == nullptr: no copy.  On the 3-D grid of
-// a one-plane launch the block k is the z coordinate in both modes.
-struct DirectCarry {
-    uint8_t* dst;
-    int64_t step;
+// Chunked exchange in one launch (direct path, 3-D grid of one plane's
+// tiles; DirectGeom then describes plane 0 of every rank into the window).
+// The window is [w][one plane] in the layout of the output side, and its
+// block k is the z coordinate of the grid in both modes.  Each tile's window
+// range belongs to one workgroup for the whole launch, and within it each
+// window vector to one lane: for every plane p that lane stores plane p's
+// vector into the window, reads it back, and stores it to out[k][p], so
+// window vector x of block k lands at out + x + k * step + p * plane
+// (vectors; out = plane 0 of rank 0, step = rank stride - plane).  The input
+// of plane p is the plane-0 input moved by p * plane.
+struct ChunkedGeom {
+    uint8_t* out;
+    int64_t step;       // rank stride minus one plane, in vectors
+    int64_t plane;      // one plane of one rank, in vectors
+    uint32_t planes;    // B
 };
 
 template <bool MODE1>

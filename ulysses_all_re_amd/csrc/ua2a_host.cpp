@@ -61,21 +61,19 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
     return static_cast<uint32_t>(g);
 }
 
-// Everything one exchange launches.  For a chunked exchange, perm and copy
-// describe plane 0; plane p adds p * plane_bytes to the pointers named below.
-// With `carry`, planes after the first copy the previous plane out of the
-// window inside their own permute launch, and only the last plane's copy is
-// a launch of its own.
+// Everything one exchange launches.  A chunked exchange on the direct path
+// with its 3-D grid is one launch of the chunked kernel (`fused`: perm is
+// that launch).  Otherwise perm and copy describe plane 0 of a chunked
+// exchange, and plane p adds p * plane_bytes to the pointers named in
+// to_plane: B permutes into the window, each followed by a copy out.
 struct Prepared {
     int32_t path;            // UA2A_PATH_DIRECT or UA2A_PATH_LDS
     int32_t chunked;
+    int32_t fused;           // chunked exchange in one launch
     Launch perm;
     Launch copy;
     int64_t plane_bytes;     // S_local * H * D * elem_bytes
     int32_t launches;
-    int32_t carry;
-    uint8_t* out;            // the exchange's output (plane 0 of rank 0)
-    int64_t carry_step;      // (rank stride - plane) in the permute's vectors
 };
 
 // `recv` receiving ranks from the ones at the given bases (w for a whole
@@ -382,6 +380,17 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     }
     pr->launches = 1;
     if (chunked) {
+        if (L.kernel == Kernel::Direct && L.grid3d) {
+            // one launch: every tile of the one-plane window moves through
+            // all B planes (the 3-D grid's z coordinate is the window block)
+            pr->fused = 1;
+            L.kernel = Kernel::Chunked;
+            L.chunk.out = outb;
+            L.chunk.step = (rank_bytes - plane) / L.width;
+            L.chunk.plane = plane / L.width;
+            L.chunk.planes = static_cast<uint32_t>(p->B);
+            return;
+        }
         // window -> plane 0 of every rank of `out`: w blocks of one plane
         uint32_t vb = pow2_align(static_cast<uint64_t>(plane));
         vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
@@ -394,17 +403,11 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
         C.grid = grid_for(C.copy.num_tiles, 0, kCopyBlock);
-        // the copy rides in the next plane's permute when that is a direct
-        // launch with one workgroup per tile on the 3-D grid (z = window block)
-        pr->carry = p->B > 1 && L.kernel == Kernel::Direct && L.grid3d;
-        pr->out = outb;
-        pr->carry_step = (rank_bytes - plane) / L.width;
-        pr->launches = static_cast<int32_t>(pr->carry ? p->B + 1 : 2 * p->B);
+        pr->launches = static_cast<int32_t>(2 * p->B);
     }
 }
 
-// Shift plane-0 launches of a chunked exchange to plane `pl`; with carry,
-// the permute of a later plane also copies plane pl - 1 out of the window.
+// Shift plane-0 launches of a per-plane chunked exchange to plane `pl`.
 void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch* copy)
 {
     *perm = pr.perm;
@@ -418,13 +421,6 @@ void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch
     else
         perm->lds.a_ptr += off;
     copy->copy.dst += off;
-    if (pr.carry && pl > 0) {
-        // two waves per tile; x stays far inside a dispatch's 2^31 lanes, as a
-        // slab lies within one plane (< 2^32 bytes, so < 2^22 tiles)
-        perm->carry.dst = pr.out + (pl - 1) * pr.plane_bytes;
-        perm->carry.step = pr.carry_step;
-        perm->block = kCarryBlock;
-    }
 }
 
 // Per-rank tables: only the entries a call uses are looked at -- the inputs
@@ -646,16 +642,23 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
         }
         return UA2A_OK;
     }
-    // Chunked: per plane, permute into the window, then copy the window out.
+    // Chunked: one launch on the direct path's 3-D grid; otherwise per
+    // plane a permute into the window, then a copy of the window out.
     // Stream order makes plane p's copy finish before plane p+1 overwrites
-    // the window.  With carry, plane p's copy is part of plane p+1's launch
-    // (each tile copies its window range out before overwriting it), and
-    // only the last plane's copy is launched on its own.
+    // the window.
+    if (pr.fused) {
+        err = backend_launch(pr.perm, stream);
+        if (err != 0) {
+            disable(plan, "launching the chunked exchange kernel", err);
+            return UA2A_ERR_HIP;
+        }
+        return UA2A_OK;
+    }
     for (int64_t pl = 0; pl < plan->B; ++pl) {
         Launch perm, copy;
         to_plane(pr, mode, pl, &perm, &copy);
         err = backend_launch(perm, stream);
-        if (err == 0 && (!pr.carry || pl == plan->B - 1)) err = backend_launch(copy, stream);
+        if (err == 0) err = backend_launch(copy, stream);
         if (err != 0) {
             disable(plan, "launching a chunked-plane kernel", err);
             return UA2A_ERR_HIP;
@@ -832,10 +835,11 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     info->grid = static_cast<int64_t>(static_cast<uint64_t>(pr.perm.grid) * pr.perm.grid_y *
                                       pr.perm.grid_z);
     info->block = static_cast<int32_t>(pr.perm.block);
-    info->tiles = pr.perm.kernel == Kernel::Direct ? pr.perm.direct.num_tiles : pr.perm.lds.num_tiles;
+    info->tiles = pr.perm.kernel == Kernel::Lds ? pr.perm.lds.num_tiles : pr.perm.direct.num_tiles;
     info->launches = pr.launches;
     info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
     info->grid_dims = pr.perm.grid3d ? 3 : 1;
+    info->chunked_form = !chunked ? 0 : pr.fused ? UA2A_CHUNKED_ONE_LAUNCH : UA2A_CHUNKED_PER_PLANE;
     return UA2A_OK;
 }
 

@@ -41,7 +41,7 @@ constexpr uint32_t kLdsXcdLog = 2;              // LDS tiles: 2^kLdsXcdLog conse
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5,
-                              LdsRanks = 6 };
+                              LdsRanks = 6, Chunked = 7 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -49,13 +49,13 @@ struct Launch {
     uint32_t block;      // threads per workgroup
     uint32_t grid_y;     // 3-D grid of the direct kernel (1 otherwise)
     uint32_t grid_z;
-    int32_t grid3d;      // direct kernel: one tile per workgroup on (grid, grid_y, grid_z)
+    int32_t grid3d;      // direct/chunked kernel: one tile per workgroup on (grid, grid_y, grid_z)
     int32_t width;       // Direct/Copy/Ranks: bytes per lane vector; Lds: LDS piece bytes G
     int32_t mode;        // Direct/Lds/Ranks: 0 or 1
     uint32_t grid;       // workgroups along x
     uint32_t lds_bytes;  // dynamic LDS (Lds kernel only)
-    DirectGeom direct;
-    DirectCarry carry;   // Direct on the 3-D grid: copy the previous chunked plane out (dst null: no)
+    DirectGeom direct;   // Direct; Chunked: plane 0 of every rank into the window
+    ChunkedGeom chunk;   // Chunked: output, plane strides and plane count
     LdsGeom lds;
     CopyGeom copy;
     RanksGeom ranks;

@@ -16,10 +16,13 @@
 //    a contiguous span of P-side rows in LDS and moves both sides as 16-byte
 //    aligned chunks, re-ordering runs inside LDS in G-byte pieces; tiles go
 //    to the XCDs in runs of consecutive tiles (see LdsGeom).
+//  * ua2a_chunked_kernel -- a whole chunked exchange in one launch on the
+//    direct path: each workgroup owns one tile of the one-plane window and
+//    moves it through every batch plane (permute into the window, read back,
+//    store to the output).
 //  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
-//    to move the one-plane window into the output (after the last plane;
-//    on the direct path each earlier plane's copy rides in the next plane's
-//    launch, ua2a_direct3d_carry_kernel).
+//    on the LDS path (and with a capped grid) to move the one-plane window
+//    into the output after each plane's permutation launch.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
@@ -55,6 +58,14 @@ struct StreamMem {
     __device__ static T ld(const T* p) { return __builtin_nontemporal_load(p); }
     template <class T>
     __device__ static void st(T* p, T v) { __builtin_nontemporal_store(v, p); }
+    // The window of a one-launch chunked exchange is read back right after
+    // it is written, so its accesses keep the default cache policy (the
+    // lines stay in the XCD's L2 between the store and the load).
+    template <class T>
+    __device__ static T ld_win(const T* p) { return *p; }
+    template <class T>
+    __device__ static void st_win(T* p, T v) { *p = v; }
+    __device__ static void win_order() { asm volatile("" ::: "memory"); }
     // A store at byte `off` of a tile's written range [base, base + nbytes),
     // through a buffer resource over that range (a store outside it would be
     // dropped by the hardware rather than land elsewhere).
@@ -80,19 +91,6 @@ struct StreamMem {
     // bytes outside the span are mapped; they are never used, and only an
     // exchange's input, which nothing writes meanwhile, is read this way.
     __device__ static u32x4 ld_part(const u32x4* p, uint32_t, uint32_t) { return __builtin_nontemporal_load(p); }
-    // Order point: v's registers are an input (so the wave waits for v's load
-    // to return before going on) and memory is clobbered (so the compiler
-    // moves no access across it).
-    template <class T>
-    __device__ static void held(const T& v)
-    {
-        if constexpr (sizeof(T) == 16)
-            asm volatile("" ::"v"(__builtin_bit_cast(v4i32, v)) : "memory");
-        else if constexpr (sizeof(T) == 8)
-            asm volatile("" ::"v"(__builtin_bit_cast(v2i32, v)) : "memory");
-        else
-            asm volatile("" ::"v"(static_cast<uint32_t>(v)) : "memory");
-    }
 };
 
 // Kernel arguments up front.  A direct, copy or per-rank workgroup moves one
@@ -186,24 +184,19 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_direct3d_kernel(DirectGeom 
         g, direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z), threadIdx.x);
 }
 
-// A chunked plane after the first (3-D grid, one plane, two waves): the tile
-// copies the previous plane's window range out to `c` before overwriting it.
+// A whole chunked exchange in one launch (3-D grid of one plane's tiles,
+// see ChunkedGeom): every workgroup moves its window tile through all B
+// planes.
 template <int VB, bool MODE1>
-__global__ __launch_bounds__(kCarryBlock) void ua2a_direct3d_carry_kernel(DirectGeom g, DirectCarry c)
+__global__ __launch_bounds__(kDirectBlock) void ua2a_chunked_kernel(DirectGeom g, ChunkedGeom c)
 {
     args_up_front(g);
-    asm volatile("" ::"s"(c.dst), "s"(c.step));
+    asm volatile("" ::"s"(c.out), "s"(c.step), "s"(c.plane), "s"(c.planes));
     const DirectTile d = direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z);
-    uint8_t* const carry_tile = c.dst + (d.dst_slab + d.u0 + static_cast<int64_t>(blockIdx.z) * c.step) * VB;
-    static_assert(kTileBytes == 16 * kDirectBlock, "a carry tile is 16 bytes per lane of a wave");
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kDirectBlock);
-    const uint32_t lane = threadIdx.x % kDirectBlock;
-    const CarryVectors<VB> v = direct_carry_load<StreamMem, VB, MODE1, kDirectBlock>(g, d, wave, lane);
-#pragma unroll
-    for (uint32_t k = 0; k < CarryVectors<VB>::kPerLane; ++k)
-        StreamMem::held(v.v[k]);   // this lane's loads have returned ...
-    __syncthreads();               // ... and so have every other lane's
-    direct_carry_store<StreamMem, VB, MODE1, kDirectBlock>(g, d, wave, lane, carry_tile, v);
+    if (d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock)      // the same for the whole workgroup
+        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, true>(g, d, c, blockIdx.z, threadIdx.x);
+    else
+        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, false>(g, d, c, blockIdx.z, threadIdx.x);
 }
 
 // The credits of a publishing exchange's last part.
@@ -318,14 +311,14 @@ const void* direct3d_fn(int vb)
 }
 
 template <bool MODE1>
-const void* carry3d_fn(int vb)
+const void* chunked_fn(int vb)
 {
     switch (vb) {
-    case 16: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<16, MODE1>);
-    case 8: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<8, MODE1>);
-    case 4: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<4, MODE1>);
-    case 2: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<2, MODE1>);
-    case 1: return reinterpret_cast<const void*>(&ua2a_direct3d_carry_kernel<1, MODE1>);
+    case 16: return reinterpret_cast<const void*>(&ua2a_chunked_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_chunked_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_chunked_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_chunked_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_chunked_kernel<1, MODE1>);
     default: return nullptr;
     }
 }
@@ -412,14 +405,14 @@ int backend_launch(const Launch& L, void* stream)
     size_t shmem = 0;
     switch (L.kernel) {
     case Kernel::Direct:
-        if (L.carry.dst != nullptr) {
-            if (!L.grid3d || L.direct.sig_count) return static_cast<int>(hipErrorInvalidValue);
-            fn = L.mode ? carry3d_fn<true>(L.width) : carry3d_fn<false>(L.width);
-            arg2 = const_cast<DirectCarry*>(&L.carry);
-        } else {
-            fn = L.direct.sig_count ? direct_any<true>(L) : direct_any<false>(L);
-        }
+        fn = L.direct.sig_count ? direct_any<true>(L) : direct_any<false>(L);
         arg = &dg;
+        break;
+    case Kernel::Chunked:
+        if (!L.grid3d || L.direct.sig_count) return static_cast<int>(hipErrorInvalidValue);
+        fn = L.mode ? chunked_fn<true>(L.width) : chunked_fn<false>(L.width);
+        arg = &dg;
+        arg2 = const_cast<ChunkedGeom*>(&L.chunk);
         break;
     case Kernel::Lds:
         fn = L.mode ? lds_fn<true>(L.width) : lds_fn<false>(L.width);

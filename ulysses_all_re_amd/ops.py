@@ -20,22 +20,41 @@ other implementation.
 ``chunked=True`` runs the page's chunked form: one batch plane at a time
 through a window sized for one plane of every rank.  As the page's
 communicator keeps one registered window and rebuilds it larger when a call
-needs more, the operator keeps one window per device and stream, grows it
-(never shrinks it) when a larger shape arrives, and rebuilds the chunked
-plans that borrowed the old one.  Calls on one stream share its window in
-stream order; other streams get windows of their own.
+needs more (and says so in its log), the operator keeps one window per device
+and stream, grows it (never shrinks it) when a larger shape arrives, logs the
+growth, and rebuilds the chunked plans that borrowed the old one.  Calls on
+one stream share its window in stream order; other streams get windows of
+their own.
+
+Both caches are bounded: at most ``MAX_PLANS`` plans and ``MAX_WINDOWS``
+windows are kept, the least recently used going first (a window's plans go
+with it).  A dropped window returns to torch's allocator in its own stream's
+order, after the work already queued there.  One lock covers the lookup and
+the enqueue of each call, so a plan is never closed while another thread is
+between finding it and launching on it.
 """
 from __future__ import annotations
 
+import logging
 import threading
+from collections import OrderedDict
 
 import torch
 
 from . import Plan
 
-_plans: dict = {}
-_windows: dict = {}       # (device, stream) -> the uint8 window of chunked exchanges there
+MAX_PLANS = 64
+MAX_WINDOWS = 8
+
+_log = logging.getLogger(__name__)
+_plans: "OrderedDict" = OrderedDict()     # key -> Plan, least recently used first
+_windows: "OrderedDict" = OrderedDict()   # (device, stream id) -> uint8 window of chunked exchanges
 _lock = threading.Lock()
+
+
+def _drop_plans_of(win) -> None:
+    for k in [k for k, p in _plans.items() if p.window is win]:
+        _plans.pop(k).close()
 
 
 def _window_for(device, stream, nbytes: int):
@@ -44,34 +63,47 @@ def _window_for(device, stream, nbytes: int):
     key = (device, stream.stream_id)
     win = _windows.get(key)
     if win is not None and win.numel() >= nbytes:
+        _windows.move_to_end(key)
         return win
     if win is not None:
-        for k in [k for k, p in _plans.items() if p.window is win]:
-            _plans.pop(k).close()
+        _drop_plans_of(win)
+        _log.info("ua2a: chunked window of %s stream %d grown from %d to %d bytes",
+                  device, stream.stream_id, win.numel(), nbytes)
+    else:
+        _log.info("ua2a: chunked window of %s stream %d created with %d bytes",
+                  device, stream.stream_id, nbytes)
     # the old window is released to torch's allocator in this stream's order
     win = torch.empty(nbytes, dtype=torch.uint8, device=device)
     _windows[key] = win
+    _windows.move_to_end(key)
+    while len(_windows) > MAX_WINDOWS:
+        _, old = _windows.popitem(last=False)
+        _drop_plans_of(old)
     return win
 
 
 def _plan_for(w: int, B: int, S_local: int, H: int, D: int, dtype, device,
               chunked: bool = False) -> Plan:
     """One cached plan per shape, dtype and device (plans are small host
-    objects); chunked plans per stream too, each borrowing its stream's window."""
-    with _lock:
-        window = None
-        key = (w, B, S_local, H, D, dtype, device)
-        if chunked:
-            stream = torch.cuda.current_stream(device)
-            e = torch.empty((), dtype=dtype).element_size()
-            need = Plan.window_bytes(w, B, S_local, H, D, e)
-            window = _window_for(device, stream, need)
-            key += (stream.stream_id,)
-        plan = _plans.get(key)
-        if plan is None:
-            plan = Plan(w, B, S_local, H, D, dtype, window=window, device=device)
-            _plans[key] = plan
-        return plan
+    objects); chunked plans per stream too, each borrowing its stream's
+    window (caller holds _lock)."""
+    window = None
+    key = (w, B, S_local, H, D, dtype, device)
+    if chunked:
+        stream = torch.cuda.current_stream(device)
+        e = torch.empty((), dtype=dtype).element_size()
+        need = Plan.window_bytes(w, B, S_local, H, D, e)
+        window = _window_for(device, stream, need)
+        key += (stream.stream_id,)
+    plan = _plans.get(key)
+    if plan is None:
+        plan = Plan(w, B, S_local, H, D, dtype, window=window, device=device)
+        _plans[key] = plan
+        while len(_plans) > MAX_PLANS:
+            _plans.popitem(last=False)[1].close()
+    else:
+        _plans.move_to_end(key)
+    return plan
 
 
 def _local_shape(shape, w: int, mode: int):
@@ -102,8 +134,9 @@ def exchange(x: torch.Tensor, w: int, mode: int, chunked: bool = False) -> torch
         raise RuntimeError(f"the exchange runs on the GPU only (got a {x.device.type} tensor)")
     B, S, H, D = _local_shape(x.shape, w, mode)
     x = x.contiguous()
-    plan = _plan_for(w, B, S, H, D, x.dtype, x.device, chunked)
-    return plan.exchange(x, mode, chunked)
+    with _lock:
+        plan = _plan_for(w, B, S, H, D, x.dtype, x.device, chunked)
+        return plan.exchange(x, mode, chunked)
 
 
 @exchange.register_fake
