@@ -26,8 +26,9 @@
  *   - return 0 (UA2A_OK) or a negative UA2A_ERR_* code; nothing throws;
  *   - no function synchronises the host with the device;
  *   - no function allocates device memory; the ones that launch work
- *     (ua2a_exchange, ua2a_exchange_ranks, ua2a_exchange_publish,
- *     ua2a_wait_credits) launch only on the given stream;
+ *     (ua2a_exchange, ua2a_exchange_chunked_noalloc, ua2a_exchange_ranks,
+ *     ua2a_exchange_publish, ua2a_wait_credits) launch only on the given
+ *     stream;
  *   - pointers named in/out/window are device pointers on the plan's
  *     device, owned by the caller, and are only borrowed by the library;
  *   - kernels write only the bytes of out (and of the window and counters
@@ -164,6 +165,31 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  */
 int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked,
                   const void* in, void* out, void* stream);
+
+/* Bytes of the library's own window (64 MiB), the largest one-plane window
+ * (layout.window_bytes) that ua2a_exchange_chunked_noalloc accepts. */
+#define UA2A_NOALLOC_WINDOW_BYTES (64 * 1024 * 1024)
+
+/*
+ * ua2a_exchange_chunked_noalloc: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It is ua2a_exchange(plan, mode, 1, in, out, stream)
+ * with the library's own window in place of the plan's, so the plan needs no
+ * window (one it has is not used).  That window is a static device array of
+ * UA2A_NOALLOC_WINDOW_BYTES that every device the library runs on holds for
+ * the life of the process; the first call on a device looks up its address
+ * there, and no call allocates or frees anything.
+ *   All calls on one device share its window, which keeps the last call's
+ *   contents (plane B-1 of every rank, as ua2a_exchange leaves its window).
+ *   Calls that can overlap on one device -- on different streams, or from
+ *   different threads without ordering -- race on the window: order them on
+ *   one stream, or with events between streams.
+ * Errors: those of ua2a_exchange with chunked = 1, with CAPACITY meaning
+ * layout.window_bytes > UA2A_NOALLOC_WINDOW_BYTES; HIP also when the window's
+ * address cannot be looked up (the plan becomes disabled).
+ */
+int ua2a_exchange_chunked_noalloc(ua2a_plan_t plan, int32_t mode, const void* in, void* out,
+                                  void* stream);
 
 /*
  * ua2a_exchange_ranks: the same exchange when each rank's tensors are

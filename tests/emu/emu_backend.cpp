@@ -291,6 +291,19 @@ int backend_current_device(int32_t* device)
     return 0;
 }
 
+// The library's own window of the no-allocation entry point: host memory of
+// the same size per emulated device, 256-byte aligned like the device array.
+int backend_scratch_window(int32_t device, uint8_t** window)
+{
+    static std::vector<std::vector<uint8_t>> per_device(64);
+    if (device < 0 || device >= 64) return 10;
+    std::vector<uint8_t>& buf = per_device[device];
+    if (buf.empty()) buf.resize(UA2A_NOALLOC_WINDOW_BYTES + 256);
+    uintptr_t p = reinterpret_cast<uintptr_t>(buf.data());
+    *window = buf.data() + ((256 - p % 256) % 256);
+    return 0;
+}
+
 const char* backend_error_name(int) { return "emulated launch failure"; }
 
 int backend_launch(const Launch& L, void*)

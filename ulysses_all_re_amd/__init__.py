@@ -4,7 +4,8 @@ Argument marshalling only: every byte of the exchange is moved by the HIP
 kernels in libua2a.so.  PyTorch is used for device memory and streams.
 
 The functions mirror the C ABI of include/ua2a.h one to one
-(``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``, ``ua2a_exchange_ranks``,
+(``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``,
+``ua2a_exchange_chunked_noalloc``, ``ua2a_exchange_ranks``,
 ``ua2a_exchange_publish``, ``ua2a_wait_credits``, ``ua2a_destroy``,
 ``ua2a_status_string``, ``ua2a_plan_last_error``, ``ua2a_plan_set_path``,
 ``ua2a_describe``, ``ua2a_describe_ranks``) and raise :class:`UA2AError` on a
@@ -47,9 +48,12 @@ UA2A_PATH_LDS = 2
 UA2A_CHUNKED_ONE_LAUNCH = 1
 UA2A_CHUNKED_PER_PLANE = 2
 
+UA2A_NOALLOC_WINDOW_BYTES = 64 * 1024 * 1024   # the library's own window (no-allocation entry point)
+
 # every symbol include/ua2a.h declares
 EXPORTED = (
-    "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_ranks", "ua2a_destroy",
+    "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_chunked_noalloc",
+    "ua2a_exchange_ranks", "ua2a_destroy",
     "ua2a_status_string", "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
     "ua2a_describe_ranks", "ua2a_exchange_publish", "ua2a_wait_credits",
 )
@@ -105,6 +109,7 @@ def declare_signatures(lib: ctypes.CDLL) -> ctypes.CDLL:
         "ua2a_layout": ([i32, i64, i64, i64, i64, i32, ctypes.POINTER(ua2a_layout_t)], ctypes.c_int),
         "ua2a_plan": ([ctypes.POINTER(vp), i32, i64, i64, i64, i64, i32, i32, vp, i64, i32], ctypes.c_int),
         "ua2a_exchange": ([vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        "ua2a_exchange_chunked_noalloc": ([vp, i32, vp, vp, vp], ctypes.c_int),
         "ua2a_destroy": ([vp], ctypes.c_int),
         "ua2a_status_string": ([i32], ctypes.c_char_p),
         "ua2a_plan_last_error": ([vp], ctypes.c_char_p),
@@ -157,6 +162,13 @@ def ua2a_exchange(plan: int, mode: int, chunked: int, inp: int, out: int, stream
     rc = load_library().ua2a_exchange(plan, mode, chunked, inp or None, out or None, stream or None)
     if rc != UA2A_OK:
         raise UA2AError(rc, "ua2a_exchange", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_exchange_chunked_noalloc(plan: int, mode: int, inp: int, out: int, stream: int = 0) -> None:
+    """Enqueue one chunked exchange through the library's own window (no allocation)."""
+    rc = load_library().ua2a_exchange_chunked_noalloc(plan, mode, inp or None, out or None, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_exchange_chunked_noalloc", ua2a_plan_last_error(plan) if plan else "")
 
 
 def _table(ptrs):
@@ -314,6 +326,20 @@ class Plan:
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         self._on_device(ua2a_exchange, self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
+                        stream.cuda_stream)
+        return out
+
+    def exchange_noalloc(self, x, mode: int, out, stream=None):
+        """Chunked exchange through the library's own window
+        (ua2a_exchange_chunked_noalloc): nothing is allocated, so the caller
+        passes `out`; calls that can overlap on one device race on the
+        shared window.  Returns out."""
+        import torch
+        self._check(x, self.in_shape(mode), "input")
+        self._check(out, self.out_shape(mode), "output")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._on_device(ua2a_exchange_chunked_noalloc, self.handle, mode, x.data_ptr(), out.data_ptr(),
                         stream.cuda_stream)
         return out
 

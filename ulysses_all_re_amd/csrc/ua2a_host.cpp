@@ -287,8 +287,10 @@ void direct_launch(const ua2a_plan_s* p, int mode, uint32_t vb, uint8_t* p_ptr, 
     }
 }
 
-int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in,
-               const void* out)
+// Checks of one exchange call against a window of window_bytes at `window`
+// (the plan's, or the library's own for the no-allocation entry point).
+int check_call_window(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in,
+                      const void* out, const void* window, int64_t window_bytes)
 {
     if (p == nullptr) return UA2A_ERR_INVALID_ARG;
     if (p->disabled) return UA2A_ERR_DISABLED;
@@ -300,18 +302,26 @@ int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* 
     const int64_t n = p->layout.tensor_bytes;
     if (overlaps(in, n, out, n)) return UA2A_ERR_ALIAS;
     if (chunked) {
-        if (p->window == nullptr || p->window_bytes < p->layout.window_bytes)
-            return UA2A_ERR_CAPACITY;
+        if (window == nullptr || window_bytes < p->layout.window_bytes) return UA2A_ERR_CAPACITY;
         const int64_t wn = p->layout.window_bytes;
-        if (overlaps(p->window, wn, in, n) || overlaps(p->window, wn, out, n))
-            return UA2A_ERR_ALIAS;
+        if (overlaps(window, wn, in, n) || overlaps(window, wn, out, n)) return UA2A_ERR_ALIAS;
     }
     return UA2A_OK;
 }
 
-void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in, void* out,
-             Prepared* pr, int32_t force_path = UA2A_PATH_AUTO)
+int check_call(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in,
+               const void* out)
 {
+    if (p == nullptr) return UA2A_ERR_INVALID_ARG;
+    return check_call_window(p, mode, chunked, in, out, p->window, p->window_bytes);
+}
+
+// The launches of one exchange; a chunked one goes through `window` (the
+// plan's own unless given).
+void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in, void* out,
+             Prepared* pr, int32_t force_path = UA2A_PATH_AUTO, uint8_t* window = nullptr)
+{
+    if (window == nullptr) window = p->window;
     memset(pr, 0, sizeof *pr);
     const int64_t run = p->layout.run_bytes;
     const int64_t plane = p->S_local * p->H * p->D * p->elem_bytes;   // one plane of one rank
@@ -322,7 +332,7 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     uint32_t g = pow2_align(static_cast<uint64_t>(run));
     g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(in)));
     g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(out)));
-    if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
+    if (chunked) g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(window)));
 
     const uint32_t rows = lds_rows(p, mode, g);
     const int32_t want = force_path != UA2A_PATH_AUTO ? force_path : p->path;
@@ -353,10 +363,10 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         nb = 1;
         if (mode == 0) {
             p_ptr = inb;       p_rank = rank_bytes;
-            a_ptr = p->window; a_rank = plane;
+            a_ptr = window;    a_rank = plane;
         } else {
             a_ptr = inb;       a_rank = rank_bytes;
-            p_ptr = p->window; p_rank = plane;
+            p_ptr = window;    p_rank = plane;
         }
         p_plane = a_plane = 0;
     }
@@ -393,14 +403,14 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         }
         // window -> plane 0 of every rank of `out`: w blocks of one plane
         uint32_t vb = pow2_align(static_cast<uint64_t>(plane));
-        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(p->window)));
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(window)));
         vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out)));
         Launch& C = pr->copy;
         C.kernel = Kernel::Copy;
         C.block = kCopyBlock;
         C.grid_y = C.grid_z = 1;
         C.width = static_cast<int32_t>(vb);
-        C.copy = make_copy(vb, p->window, outb, plane, rank_bytes, plane,
+        C.copy = make_copy(vb, window, outb, plane, rank_bytes, plane,
                            static_cast<uint32_t>(p->w));
         C.grid = grid_for(C.copy.num_tiles, 0, kCopyBlock);
         pr->launches = static_cast<int32_t>(2 * p->B);
@@ -556,6 +566,59 @@ void disable(ua2a_plan_s* p, const char* what, int err)
     snprintf(p->reason, sizeof p->reason, "%s failed: %s (%d)", what, backend_error_name(err), err);
 }
 
+// Enqueue one validated exchange (the current device is the plan's).
+int launch_exchange(ua2a_plan_s* plan, int32_t mode, int32_t chunked, const void* in, void* out,
+                    uint8_t* window, void* stream)
+{
+    Prepared pr;
+    prepare(plan, mode, chunked, in, out, &pr, UA2A_PATH_AUTO, window);
+    int err;
+    if (!chunked) {
+        err = backend_launch(pr.perm, stream);
+        if (err != 0) {
+            disable(plan, "launching the exchange kernel", err);
+            return UA2A_ERR_HIP;
+        }
+        return UA2A_OK;
+    }
+    // Chunked: one launch on the direct path's 3-D grid; otherwise per
+    // plane a permute into the window, then a copy of the window out.
+    // Stream order makes plane p's copy finish before plane p+1 overwrites
+    // the window.
+    if (pr.fused) {
+        err = backend_launch(pr.perm, stream);
+        if (err != 0) {
+            disable(plan, "launching the chunked exchange kernel", err);
+            return UA2A_ERR_HIP;
+        }
+        return UA2A_OK;
+    }
+    for (int64_t pl = 0; pl < plan->B; ++pl) {
+        Launch perm, copy;
+        to_plane(pr, mode, pl, &perm, &copy);
+        err = backend_launch(perm, stream);
+        if (err == 0) err = backend_launch(copy, stream);
+        if (err != 0) {
+            disable(plan, "launching a chunked-plane kernel", err);
+            return UA2A_ERR_HIP;
+        }
+    }
+    return UA2A_OK;
+}
+
+// The calling thread's current device is the plan's (UA2A_OK), is another
+// (UA2A_ERR_DEVICE), or cannot be queried (UA2A_ERR_HIP, plan disabled).
+int check_device(ua2a_plan_s* plan)
+{
+    int32_t dev = -1;
+    const int err = backend_current_device(&dev);
+    if (err != 0) {
+        disable(plan, "querying the current device", err);
+        return UA2A_ERR_HIP;
+    }
+    return dev == plan->device ? UA2A_OK : UA2A_ERR_DEVICE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -624,47 +687,30 @@ int ua2a_exchange(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
                   void* stream)
 {
     int rc = check_call(plan, mode, chunked, in, out);
+    if (rc == UA2A_OK) rc = check_device(plan);
     if (rc != UA2A_OK) return rc;
-    int32_t dev = -1;
-    int err = backend_current_device(&dev);
+    return launch_exchange(plan, mode, chunked, in, out, plan->window, stream);
+}
+
+int ua2a_exchange_chunked_noalloc(ua2a_plan_t plan, int32_t mode, const void* in, void* out,
+                                  void* stream)
+{
+    // everything but the window first, as for ua2a_exchange: the window's
+    // address is known only once the device is
+    int rc = check_call_window(plan, mode, 0, in, out, nullptr, 0);
+    if (rc != UA2A_OK) return rc;
+    if (plan->layout.window_bytes > UA2A_NOALLOC_WINDOW_BYTES) return UA2A_ERR_CAPACITY;
+    rc = check_device(plan);
+    if (rc != UA2A_OK) return rc;
+    uint8_t* window = nullptr;
+    const int err = backend_scratch_window(plan->device, &window);
     if (err != 0) {
-        disable(plan, "querying the current device", err);
+        disable(plan, "looking up the library's window", err);
         return UA2A_ERR_HIP;
     }
-    if (dev != plan->device) return UA2A_ERR_DEVICE;
-    Prepared pr;
-    prepare(plan, mode, chunked, in, out, &pr);
-    if (!chunked) {
-        err = backend_launch(pr.perm, stream);
-        if (err != 0) {
-            disable(plan, "launching the exchange kernel", err);
-            return UA2A_ERR_HIP;
-        }
-        return UA2A_OK;
-    }
-    // Chunked: one launch on the direct path's 3-D grid; otherwise per
-    // plane a permute into the window, then a copy of the window out.
-    // Stream order makes plane p's copy finish before plane p+1 overwrites
-    // the window.
-    if (pr.fused) {
-        err = backend_launch(pr.perm, stream);
-        if (err != 0) {
-            disable(plan, "launching the chunked exchange kernel", err);
-            return UA2A_ERR_HIP;
-        }
-        return UA2A_OK;
-    }
-    for (int64_t pl = 0; pl < plan->B; ++pl) {
-        Launch perm, copy;
-        to_plane(pr, mode, pl, &perm, &copy);
-        err = backend_launch(perm, stream);
-        if (err == 0) err = backend_launch(copy, stream);
-        if (err != 0) {
-            disable(plan, "launching a chunked-plane kernel", err);
-            return UA2A_ERR_HIP;
-        }
-    }
-    return UA2A_OK;
+    rc = check_call_window(plan, mode, 1, in, out, window, UA2A_NOALLOC_WINDOW_BYTES);
+    if (rc != UA2A_OK) return rc;
+    return launch_exchange(plan, mode, 1, in, out, window, stream);
 }
 
 int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,

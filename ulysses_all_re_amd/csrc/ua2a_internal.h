@@ -70,5 +70,8 @@ struct Launch {
 int backend_current_device(int32_t* device);
 int backend_launch(const Launch& launch, void* stream);
 const char* backend_error_name(int err);
+// The device address of the library's own UA2A_NOALLOC_WINDOW_BYTES window on
+// `device` (the calling thread's current device).
+int backend_scratch_window(int32_t device, uint8_t** window);
 
 }  // namespace ua2a

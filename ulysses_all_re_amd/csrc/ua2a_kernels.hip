@@ -35,6 +35,8 @@
 // (ua2a_geometry.h) are shared with a host emulation used by the tests.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "ua2a_bodies.h"
 #include "ua2a_internal.h"
 
@@ -382,6 +384,34 @@ const void* copy_fn(int vb)
 }
 
 }  // namespace
+
+// The window of ua2a_exchange_chunked_noalloc, for callers that cannot
+// allocate: every device the library runs on holds its own copy for the life
+// of the process.  In host code `scratch` names a host-side stand-in, not
+// device memory, so the host passes kernels only the address that
+// hipGetSymbolAddress reports for the current device, looked up once per
+// device and kept.
+static __device__ __align__(256) uint8_t scratch[UA2A_NOALLOC_WINDOW_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+int backend_scratch_window(int32_t device, uint8_t** window)
+{
+    if (device < 0 || device >= kMaxScratchDevices) return static_cast<int>(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return static_cast<int>(e);
+        g_scratch_ptr[device] = static_cast<uint8_t*>(ptr);
+    }
+    *window = g_scratch_ptr[device];
+    return 0;
+}
 
 int backend_current_device(int32_t* device)
 {
