@@ -16,10 +16,13 @@ timed steps (algorithmic bytes: every element read once and written once per
 exchange, 2 * 774 144 000 B per exchange, two exchanges per step); the timed region holds the K steps and
 nothing else.  The `roofline` object is for the slower of the two
 permutation kernels, its average launch duration taken from K back-to-back
-launches between HIP events recorded on the stream the kernel is launched on.  `cpu_baseline` times the
-plain CPU oracle on the host (single thread) on a bounded sample of the same
-workload.  A device-to-device copy of the same byte count is timed beside it
-(`memcpy_GBps`).
+launches between HIP events recorded on the stream the kernel is launched on.
+`per_config` gives every workload's rate in both modes (and the four-plane
+workload chunked), each output checked against the oracle outside the timed
+launches.  `cpu_baseline` times the plain CPU oracle on the host on a bounded
+sample of the same workload, on one thread and with the senders split over
+threads (`all_cores`, with the CPU count and model).  A device-to-device copy
+of the same byte count is timed beside it (`memcpy_GBps`).
 
     python bench.py --traffic-from DIR
 
@@ -76,24 +79,142 @@ def load_traffic():
 
 
 def cpu_baseline(x_cpu, w, steps, moved_bytes, workload):
-    """The oracle as it stands, single-threaded, on `steps` full round trips."""
+    """The oracle as it stands on `steps` full round trips: on one thread, and
+    with each exchange's senders split over threads (one per sender, up to the
+    host share of cores; each thread makes one per-rank oracle call, and the
+    result must equal the single-thread one)."""
+    import numpy as np
+
     import oracle
     from workloads import BITS_VIEW
     xb = x_cpu.view(BITS_VIEW[x_cpu.element_size()]).numpy()
     t0 = time.perf_counter()
     for _ in range(steps):
         y = oracle.exchange(xb, 0, w)
-        oracle.exchange(y, 1, w)
+        z = oracle.exchange(y, 1, w)
     dt = time.perf_counter() - t0
+    threads, dt_n = 1, 0.0
+    for k in range(steps):
+        yn, s0, threads = oracle_on_threads(xb, 0, w)
+        zn, s1, _ = oracle_on_threads(yn, 1, w)
+        dt_n += s0 + s1
+        if k == 0 and not (np.array_equal(yn, y) and np.array_equal(zn, z)):
+            raise SystemExit("the threaded oracle differs from the single-thread oracle")
+        del yn, zn
+    algorithmic = 2 * moved_bytes * steps
     return {
-        "value": round(2 * moved_bytes * steps / dt / 1e9, 3),
+        "value": round(algorithmic / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{steps} full {workload} round trips (mode 0 then mode 1, "
-                  f"{2 * moved_bytes * steps} algorithmic bytes) through the C nested-loop "
-                  f"oracle, one thread, {dt:.2f} s",
+        "sample": f"{steps} full {workload} round trips (mode 0 then mode 1, {algorithmic} "
+                  f"algorithmic bytes) through the C nested-loop oracle, one thread, {dt:.2f} s",
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "all_cores": {
+            "value": round(algorithmic / dt_n / 1e9, 3),
+            "unit": "GB/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": f"the same {steps} round trips with each exchange's {w} senders split over "
+                      f"{threads} threads (one per-rank oracle call per thread; host share "
+                      f"{HOST_CPU_SHARE} of {os.cpu_count()} CPUs), {dt_n:.2f} s",
+        },
     }
+
+
+def rotation(tensor_bytes: int) -> int:
+    """Buffer sets to rotate through so that a cycle moves about 1 GiB: small
+    tensors are then timed against HBM, not the 256 MB on-package cache (at
+    most 64 sets; one for tensors of 512 MiB and more)."""
+    return max(1, min(64, -(-(1 << 30) // (2 * tensor_bytes))))
+
+
+PER_CONFIG = (("tiny", False), ("mid", False), ("video_dit", False), ("chunked", False),
+              ("chunked", True), ("awkward", False))
+
+
+def per_config(dev, stream, K, main=None):
+    """The five workloads, both modes (the chunked workload also chunked):
+    back-to-back microseconds per exchange over K launches rotating through
+    buffer sets, GB/s and fraction of 8 TB/s on the algorithmic bytes, and
+    whether the output equals the oracle's byte for byte (checked outside
+    the timed launches).  Mode-0 inputs come from the workload's first seed,
+    mode-1 inputs are an independent tensor of the mode-1 shape from its
+    second seed.  `main` = (x, y, z, avg0_ms, avg1_ms) of the bench's own
+    video-DiT run, whose timings and outputs are reused (z = mode 1 of y)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import ulysses_all_re_amd as ua
+    from workloads import BITS_VIEW, CONFIGS, DTYPES, make_tensor
+
+    out = {}
+    for name, chunked in PER_CONFIG:
+        c = CONFIGS[name]
+        w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+        dt = DTYPES[c["dtype"]]
+        e = torch.empty((), dtype=dt).element_size()
+        lay = ua.ua2a_layout(w, B, S, H, D, e)
+        moved = lay["moved_bytes"]
+        key = f"{name}_chunked" if chunked else name
+        entry = {}
+        if name == "video_dit" and not chunked and main is not None:
+            x, y, z, avg0, avg1 = main
+            bits = BITS_VIEW[e]
+            xb = x.cpu().view(bits).numpy()
+            yb = y.cpu().view(bits).numpy()
+            exact0 = bool(np.array_equal(yb, oracle.exchange(xb, 0, w)))
+            exact1 = bool(np.array_equal(z.cpu().view(bits).numpy(), oracle.exchange(yb, 1, w)))
+            for m, avg, exact in ((0, avg0, exact0), (1, avg1, exact1)):
+                gb = moved / (avg * 1e-3) / 1e9
+                entry[f"mode{m}"] = {"us": round(avg * 1e3, 2), "GBps": round(gb, 1),
+                                     "frac": round(gb / PEAK_HBM_GBPS, 4), "bit_exact": exact,
+                                     "input": "seed 0" if m == 0 else "mode 0's output"}
+            entry["buffer_sets"] = 1
+            out[key] = entry
+            continue
+        window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=dev) if chunked else None
+        plan = ua.Plan(w, B, S, H, D, dt, window=window, device=dev)
+        rot = rotation(lay["tensor_bytes"])
+        for mode in (0, 1):
+            shape = (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
+            x_cpu = make_tensor(shape, c["dtype"], c["dist"], c["seed0"] if mode == 0 else c["seed1"])
+            xs = [x_cpu.to(dev)]
+            xs += [xs[0].clone() for _ in range(rot - 1)]
+            ys = [torch.empty(plan.out_shape(mode), dtype=dt, device=dev) for _ in range(rot)]
+            plan.exchange(xs[0], mode, chunked, out=ys[0], stream=stream)
+            torch.cuda.synchronize(dev)
+            want = oracle.exchange(x_cpu.view(BITS_VIEW[e]).numpy(), mode, w, chunked=chunked)
+            exact = bool(np.array_equal(ys[0].cpu().view(BITS_VIEW[e]).numpy(), want))
+            del want
+            for i in range(2 * rot):                       # warm-up, every set at least twice
+                plan.exchange(xs[i % rot], mode, chunked, out=ys[i % rot], stream=stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            a.record(stream)
+            for i in range(K):
+                plan.exchange(xs[i % rot], mode, chunked, out=ys[i % rot], stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            us = a.elapsed_time(b) * 1e3 / K
+            gb = moved / (us * 1e-6) / 1e9
+            info = plan.describe(xs[0], mode, chunked, out=ys[0])
+            entry[f"mode{mode}"] = {"us": round(us, 2), "GBps": round(gb, 1),
+                                    "frac": round(gb / PEAK_HBM_GBPS, 4), "bit_exact": exact,
+                                    "launches": info["launches"],
+                                    "path": {ua.UA2A_PATH_DIRECT: "direct", ua.UA2A_PATH_LDS: "lds"}[info["path"]],
+                                    "input": f"seed {c['seed0'] if mode == 0 else c['seed1']}"
+                                             if c["dist"] != "index" else "flat index"}
+            del xs, ys
+        entry["buffer_sets"] = rot
+        entry["bytes_per_exchange"] = moved
+        out[key] = entry
+        plan.close()
+        del window
+        torch.cuda.empty_cache()
+    return out
 
 
 def run(args):
@@ -132,8 +253,7 @@ def run(args):
     # Buffer sets the exchanges rotate through: enough that a cycle moves
     # about 1 GiB, so that tensors smaller than the 256 MB Infinity Cache are
     # timed against HBM too (at most 64 sets; one for the video-DiT tensors).
-    rotate = args.rotate if args.rotate > 0 else \
-        max(1, min(64, -(-(1 << 30) // (2 * lay["tensor_bytes"]))))
+    rotate = args.rotate if args.rotate > 0 else rotation(lay["tensor_bytes"])
     if args.ranks is not None or args.graph:
         rotate = 1
     if args.ranks is None:
@@ -316,8 +436,13 @@ def run(args):
     if chunked:
         # what the window path actually moves: permute into the window + copy out of it
         result["window_path_bytes_per_exchange"] = 2 * moved
+    if not args.no_per_config and args.ranks is None and not args.graph:
+        log("per-configuration rates and oracle checks")
+        main = (x, y, z, avg0, avg1) if (name == WORKLOAD and not chunked and args.path == "auto"
+                                         and rotate == 1) else None
+        result["per_config"] = per_config(dev, stream, max(K, 20), main)
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: {args.cpu_steps} oracle round trips")
+        log(f"cpu baseline: {args.cpu_steps} oracle round trips, one thread and threaded")
         result["cpu_baseline"] = cpu_baseline(x_cpu, w, args.cpu_steps, moved, name)
     plan.close()
     print(json.dumps(result), flush=True)
@@ -520,7 +645,7 @@ def run_records(args):
         e = torch.empty((), dtype=dt).element_size()
         lay = ua.ua2a_layout(w, B, S, H, D, e)
         moved = lay["moved_bytes"]
-        rotate = max(1, min(64, -(-(1 << 30) // (2 * lay["tensor_bytes"]))))
+        rotate = rotation(lay["tensor_bytes"])
         window = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=dev) if c["chunked"] else None
         plan = ua.Plan(w, B, S, H, D, dt, window=window, device=dev)
         for mode in (0, 1):
@@ -746,6 +871,8 @@ def main():
                     help="oracle round trips timed for cpu_baseline (about 1 s each on the "
                          "video-DiT workload, so about 12 s in all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="leave out the per_config object (rates and oracle checks of all five workloads)")
     ap.add_argument("--records", action="store_true",
                     help="one JSON line per (workload, mode, chunked) over the five workloads: "
                          "median and min per-launch time, copy baseline, oracle time, "

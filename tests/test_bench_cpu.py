@@ -42,3 +42,18 @@ def test_threaded_oracle_equals_the_single_thread_oracle():
             got, secs, threads = bench.oracle_on_threads(x, mode, w)
             assert threads == min(w, bench.HOST_CPU_SHARE, os.cpu_count() or 1) and secs >= 0
             assert np.array_equal(got, oracle.exchange(x, mode, w)), (w, mode)
+
+
+def test_cpu_baseline_reports_one_thread_and_all_cores():
+    import torch
+
+    from workloads import make_tensor
+    x = make_tensor((4, 1, 64, 8, 16), "bf16", "normal", 0)
+    moved = 2 * x.numel() * 2
+    cb = bench.cpu_baseline(x, 4, 2, moved, "small")
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    assert cb["nproc"] == os.cpu_count() and cb["cpu_model"]
+    allc = cb["all_cores"]
+    assert allc["kind"] == "oracle" and allc["value"] > 0
+    assert allc["cores"] == min(4, bench.HOST_CPU_SHARE, os.cpu_count() or 1)
+    assert isinstance(x, torch.Tensor)

@@ -30,7 +30,8 @@ def run_bench(*args):
 
 
 def test_bench_line_contract():
-    (line,) = run_bench("--workload", "tiny", "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    (line,) = run_bench("--workload", "tiny", "--steps", "3", "--warmup", "1", "--no-cpu-baseline",
+                        "--no-per-config")
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
@@ -49,3 +50,16 @@ def test_records_are_bit_exact():
         assert r["bit_exact"] is True and r["launches_timed"] == 5
         assert r["ncores"] == 2 and r["oracle_ncore_s"] is not None    # tiny: w = 2 senders
         assert r["t_min_us"] <= r["t_median_us"] and len(r["input_sha256"]) == 64
+
+
+def test_per_config_covers_the_five_workloads():
+    """The default line's per_config: every workload in both modes (and the
+    four-plane one chunked), each bit-exact against the oracle."""
+    (line,) = run_bench("--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    pc = line["per_config"]
+    assert sorted(pc) == sorted(["tiny", "mid", "video_dit", "chunked", "chunked_chunked", "awkward"])
+    for name, entry in pc.items():
+        for m in ("mode0", "mode1"):
+            assert entry[m]["bit_exact"] is True, (name, m)
+            assert entry[m]["us"] > 0 and 0 <= entry[m]["frac"] < 1, (name, m)
+    assert pc["chunked_chunked"]["mode0"]["launches"] == 1

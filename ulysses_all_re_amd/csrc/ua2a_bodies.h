@@ -136,10 +136,45 @@ struct ChunkedLane {
     static constexpr uint32_t kPlanes = kVecs >= 4 ? 1 : 4 / kVecs;   // planes in flight per lane
 };
 
+// N consecutive planes from p0 on, for the lane's K window vectors: the N
+// planes' input loads first, then per plane its window store and read-back,
+// then the output stores.  ok[k]: vector k lies in the tile.
+template <class Mem, int VB, uint32_t BS, uint32_t K, uint32_t N>
+UA2A_HD void chunked_planes(const ChunkedGeom& c, const typename Piece<VB>::T* src, const int64_t* from,
+                            const bool* ok, typename Piece<VB>::T* win, int64_t out0, uint32_t tile_bytes,
+                            uint32_t lane, uint32_t p0)
+{
+    typedef typename Piece<VB>::T T;
+    T v[N][K];
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i)
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k)
+            if (ok[k]) v[i][k] = Mem::ld(src + (p0 + i) * c.plane + from[k]);
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i) {
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k)
+            if (ok[k]) Mem::st_win(win + lane + k * BS, v[i][k]);
+        Mem::win_order();
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k)
+            if (ok[k]) v[i][k] = Mem::ld_win(win + lane + k * BS);
+    }
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i) {
+        uint8_t* const tile = c.out + (out0 + (p0 + i) * c.plane) * VB;
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k)
+            if (ok[k]) Mem::st_tile(tile, tile_bytes, (lane + k * BS) * VB, v[i][k]);
+    }
+}
+
 // FULL: the tile holds K vectors for every lane (all but a slab's last
-// tile), so no lane needs a bounds test -- per-lane tests split the body
-// into masked blocks, across which the compiler waits for every load in
-// flight before each store.
+// tile), so no lane needs a bounds test, and the planes go U at a time (the
+// rest one by one).  A partial tile moves one plane at a time: per-lane
+// tests split the body into masked blocks, across which the compiler keeps
+// fewer values in flight anyway.
 template <class Mem, int VB, bool MODE1, uint32_t BS, bool FULL>
 UA2A_HD void chunked_tile_body(const DirectGeom& g, const DirectTile& d, const ChunkedGeom& c, uint32_t z,
                                uint32_t lane)
@@ -162,34 +197,12 @@ UA2A_HD void chunked_tile_body(const DirectGeom& g, const DirectTile& d, const C
             direct_vector<MODE1>(g, d, d.u0 + lane + k * BS, from[k], to);
         }
     }
-    for (uint32_t p0 = 0; p0 < c.planes; p0 += U) {
-        const uint32_t n = umin32(U, c.planes - p0);     // planes this turn
-        T v[U][K];
-#pragma unroll
-        for (uint32_t i = 0; i < U; ++i)
-#pragma unroll
-            for (uint32_t k = 0; k < K; ++k)
-                if (i < n && ok[k]) v[i][k] = Mem::ld(src + (p0 + i) * c.plane + from[k]);
-#pragma unroll
-        for (uint32_t i = 0; i < U; ++i) {
-            if (i >= n) break;
-#pragma unroll
-            for (uint32_t k = 0; k < K; ++k)
-                if (ok[k]) Mem::st_win(win + lane + k * BS, v[i][k]);
-            Mem::win_order();
-#pragma unroll
-            for (uint32_t k = 0; k < K; ++k)
-                if (ok[k]) v[i][k] = Mem::ld_win(win + lane + k * BS);
-        }
-#pragma unroll
-        for (uint32_t i = 0; i < U; ++i) {
-            if (i >= n) break;
-            uint8_t* const tile = c.out + (out0 + (p0 + i) * c.plane) * VB;
-#pragma unroll
-            for (uint32_t k = 0; k < K; ++k)
-                if (ok[k]) Mem::st_tile(tile, tile_bytes, (lane + k * BS) * VB, v[i][k]);
-        }
-    }
+    uint32_t p0 = 0;
+    if (FULL)
+        for (; p0 + U <= c.planes; p0 += U)
+            chunked_planes<Mem, VB, BS, K, U>(c, src, from, ok, win, out0, tile_bytes, lane, p0);
+    for (; p0 < c.planes; ++p0)
+        chunked_planes<Mem, VB, BS, K, 1>(c, src, from, ok, win, out0, tile_bytes, lane, p0);
 }
 
 // Per-rank allocations: as direct_tile_body, the tensors taken from the
