@@ -567,6 +567,71 @@ def run_overlap(args):
     print(json.dumps(result), flush=True)
 
 
+# ------------------------------------------------------------ size sweep
+
+SWEEP_S_LOCAL = (50, 100, 200, 305, 400, 600, 800, 1200, 1600, 2400, 3200, 4800, 6400)
+
+
+def fit_line(xs, ys):
+    """Least-squares y = a + b x."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    return my - b * mx, b
+
+
+def run_sweep(args):
+    """The exchange's launch time against its size: the video-DiT head layout
+    (w = 8, H = 40, D = 128, bf16, 1280-byte runs) at S_local from 50 to 6400
+    tokens per rank (4 to 524 MB per tensor), both modes, K back-to-back
+    launches rotating through buffer sets (about 1 GiB per cycle).  One JSON
+    line per (mode, size), then per mode the fit t = t0 + moved / BW over the
+    sizes of 64 MB and up, and each size's excess over that line."""
+    import torch
+
+    import ulysses_all_re_amd as ua
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    K = args.steps
+    w, B, H, D = 8, 1, 40, 128
+    pts = {0: [], 1: []}
+    for S in SWEEP_S_LOCAL:
+        plan = ua.Plan(w, B, S, H, D, torch.bfloat16, device=dev)
+        n = plan.layout["tensor_bytes"]
+        sets = rotation(n)
+        for mode in (0, 1):
+            xs = [torch.ones(plan.in_shape(mode), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+            ys = [torch.empty(plan.out_shape(mode), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+            for i in range(2 * sets):
+                plan.exchange(xs[i % sets], mode, out=ys[i % sets], stream=stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            a.record(stream)
+            for i in range(K):
+                plan.exchange(xs[i % sets], mode, out=ys[i % sets], stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize(dev)
+            us = a.elapsed_time(b) * 1e3 / K
+            moved = 2 * n
+            pts[mode].append((moved, us))
+            print(json.dumps({"record": "sweep", "mode": mode, "S_local": S, "bytes_moved": moved,
+                              "buffer_sets": sets, "us": round(us, 3),
+                              "GBps": round(moved / (us * 1e-6) / 1e9, 1)}), flush=True)
+            del xs, ys
+        plan.close()
+        torch.cuda.empty_cache()
+    for mode, p in pts.items():
+        big = [(m, t) for m, t in p if m >= 128 << 20]
+        t0, slope = fit_line([m for m, _ in big], [t for _, t in big])
+        bw = 1e-3 / slope            # bytes per us -> GB/s
+        excess = {str(m): round(t - (t0 + m * slope), 2) for m, t in p}
+        print(json.dumps({"record": "sweep_fit", "mode": mode, "t0_us": round(t0, 3),
+                          "BW_GBps": round(bw, 1), "fit_from_bytes_moved": 128 << 20,
+                          "excess_us_by_bytes_moved": excess}), flush=True)
+
+
 # ------------------------------------------------- per-configuration records
 
 RECORD_WORKLOADS = ("tiny", "mid", "video_dit", "chunked", "awkward")
@@ -877,6 +942,8 @@ def main():
                     help="one JSON line per (workload, mode, chunked) over the five workloads: "
                          "median and min per-launch time, copy baseline, oracle time, "
                          "bit-exactness, input SHA-256")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the exchange at 13 sizes (4-524 MB per tensor) and fit t = t0 + bytes/BW")
     ap.add_argument("--records-workload", default=None, choices=RECORD_WORKLOADS,
                     help="--records for this workload only")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
@@ -904,6 +971,9 @@ def main():
         return
     if args.records:
         run_records(args)
+        return
+    if args.sweep:
+        run_sweep(args)
         return
     run(args)
 
