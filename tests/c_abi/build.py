@@ -1,4 +1,5 @@
-"""Build tests/c_abi/ua2a_consumer with gcc against include/ua2a.h and libua2a.so."""
+"""Build the C-ABI test programs (tests/c_abi/ua2a_consumer, tests/c_abi/ua2a_graph)
+with gcc against include/ua2a.h and libua2a.so."""
 from __future__ import annotations
 
 import os
@@ -8,18 +9,21 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
 PKG = os.path.join(ROOT, "ulysses_all_re_amd")
 BINARY = os.path.join(HERE, "ua2a_consumer")
+GRAPH_BINARY = os.path.join(HERE, "ua2a_graph")
 
 
-def build() -> str:
+def build(name: str = "ua2a_consumer") -> str:
+    binary = os.path.join(HERE, name)
     cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
            f"-I{os.path.join(ROOT, 'include')}", "-I/opt/rocm/include",
-           os.path.join(HERE, "ua2a_consumer.c"), "-o", BINARY + ".tmp",
+           os.path.join(HERE, name + ".c"), "-o", binary + ".tmp",
            f"-L{PKG}", "-lua2a", f"-Wl,-rpath,{PKG}", "-L/opt/rocm/lib", "-lamdhip64",
            "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.check_call(cmd)
-    os.replace(BINARY + ".tmp", BINARY)
-    return BINARY
+    os.replace(binary + ".tmp", binary)
+    return binary
 
 
 if __name__ == "__main__":
     print(build())
+    print(build("ua2a_graph"))
