@@ -17,7 +17,9 @@ and elements are moved as raw bit patterns (any numpy dtype of 1, 2, 4 or 8
 bytes; bf16 travels as uint16/int16).
 
 ``exchange_ranks`` runs the exchange between separate per-rank arrays,
-restricted to a range of sending ranks.
+restricted to a range of sending ranks; ``pack_ranks`` and ``unpack_ranks``
+run it in two steps through one receive window per receiving rank (see
+``ua2a_oracle.c``).
 
 ``source_indices`` gives, for chosen output positions, the input position
 each one comes from (the same definitions, one element at a time), for
@@ -29,7 +31,9 @@ agreement with an all-to-all over torch.distributed's gloo backend in w
 processes, agreement with numpy reshape/transpose, hand-derived worked
 examples under tests/golden/, bijection of the element multiset; for the
 per-rank form, the numpy permutation masked by the source rank of every
-element, and the union of single-sender calls.
+element, and the union of single-sender calls; for pack and unpack, numpy
+slices and transposes of each window, and pack followed by unpack equal to
+the numpy exchange.
 """
 from __future__ import annotations
 
@@ -69,8 +73,10 @@ def _load():
         fn.restype = ctypes.c_int
     lib.ua2a_oracle_chunked.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp]
     lib.ua2a_oracle_chunked.restype = ctypes.c_int
-    lib.ua2a_oracle_ranks.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp, i32, i32]
-    lib.ua2a_oracle_ranks.restype = ctypes.c_int
+    for name in ("ua2a_oracle_ranks", "ua2a_oracle_pack_ranks", "ua2a_oracle_unpack_ranks"):
+        fn = getattr(lib, name)
+        fn.argtypes = [i32, i32, i64, i64, i64, i64, i32, vp, vp, i32, i32]
+        fn.restype = ctypes.c_int
     lib.ua2a_oracle_source_index.argtypes = [i32, i32, i64, i64, i64, i64, i64]
     lib.ua2a_oracle_source_index.restype = i64
     lib.ua2a_oracle_source_indices.argtypes = [i32, i32, i64, i64, i64, i64, vp, i64, vp]
@@ -156,6 +162,70 @@ def exchange_ranks(xs, outs, mode: int, first: int = 0, count=None) -> None:
     out_tab = (vp * w)(*[o.ctypes.data for o in outs])
     rc = _load().ua2a_oracle_ranks(mode, w, B, S_local, H, D, ref.dtype.itemsize,
                                    ctypes.cast(in_tab, vp), ctypes.cast(out_tab, vp), first, count)
+    if rc != 0:
+        raise OracleError(rc)
+
+
+def _window_shape(B, S_local, H, D, w):
+    return (B, S_local * w, H // w, D)
+
+
+def pack_ranks(xs, wins, mode: int, first: int = 0, count=None) -> None:
+    """Pack, in place into `wins`: wins[q] is receiver q's window
+    [B, S_local*w, H//w, D]; token block k of each plane receives what sender
+    k (in [first, first + count)) sends q.  xs as for exchange_ranks."""
+    w = len(wins)
+    count = w - first if count is None else count
+    if len(xs) != w:
+        raise ValueError("xs and wins must both hold one entry per rank")
+    senders = [xs[k] for k in range(first, first + count)]
+    if not senders or any(x is None for x in senders):
+        raise OracleError(-1)
+    ref = senders[0]
+    if any(x.shape != ref.shape or x.dtype != ref.dtype or not x.flags.c_contiguous for x in senders):
+        raise ValueError("sender inputs must share one shape and dtype and be C-contiguous")
+    B, S_local, H, D = local_shape((w, *ref.shape), mode, w)
+    if H % w:
+        raise OracleError(-2)
+    for wn in wins:
+        if wn.shape != _window_shape(B, S_local, H, D, w) or wn.dtype != ref.dtype or not wn.flags.c_contiguous:
+            raise ValueError("every window must be a C-contiguous [B, S_local*w, H//w, D] array")
+    vp = ctypes.c_void_p
+    in_tab = (vp * w)(*[None if x is None else x.ctypes.data for x in xs])
+    win_tab = (vp * w)(*[x.ctypes.data for x in wins])
+    rc = _load().ua2a_oracle_pack_ranks(mode, w, B, S_local, H, D, ref.dtype.itemsize,
+                                        ctypes.cast(in_tab, vp), ctypes.cast(win_tab, vp), first, count)
+    if rc != 0:
+        raise OracleError(rc)
+
+
+def unpack_ranks(wins, outs, mode: int, first: int = 0, count=None) -> None:
+    """Unpack receivers [first, first + count), in place into `outs`: outs[q]
+    (mode 0: [B, S_local*w, H//w, D]; mode 1: [B, S_local, H, D]) from window
+    wins[q]; other entries are not touched (and may be None)."""
+    w = len(wins)
+    count = w - first if count is None else count
+    if len(outs) != w:
+        raise ValueError("wins and outs must both hold one entry per rank")
+    used = [(wins[q], outs[q]) for q in range(first, first + count)]
+    if not used or any(a is None or b is None for a, b in used):
+        raise OracleError(-1)
+    ref = used[0][0]
+    B, S_g, Hl, D = ref.shape
+    if S_g % w:
+        raise ValueError("a window holds w token blocks")
+    S_local, H = S_g // w, Hl * w
+    out_shape = _window_shape(B, S_local, H, D, w) if mode == 0 else (B, S_local, H, D)
+    for a, b in used:
+        if a.shape != ref.shape or a.dtype != ref.dtype or not a.flags.c_contiguous:
+            raise ValueError("windows must share one shape and dtype and be C-contiguous")
+        if b.shape != out_shape or b.dtype != ref.dtype or not b.flags.c_contiguous:
+            raise ValueError(f"every used output must be a C-contiguous {out_shape} array")
+    vp = ctypes.c_void_p
+    win_tab = (vp * w)(*[None if x is None else x.ctypes.data for x in wins])
+    out_tab = (vp * w)(*[None if x is None else x.ctypes.data for x in outs])
+    rc = _load().ua2a_oracle_unpack_ranks(mode, w, B, S_local, H, D, ref.dtype.itemsize,
+                                          ctypes.cast(win_tab, vp), ctypes.cast(out_tab, vp), first, count)
     if rc != 0:
         raise OracleError(rc)
 

@@ -193,6 +193,91 @@ int ua2a_oracle_ranks(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64
     return 0;
 }
 
+/* The exchange between per-rank allocations in two steps, pack then unpack,
+ * through one receive window per receiving rank.  In a multi-device exchange
+ * each sender pushes its share into every receiver's registered window and
+ * each receiver then moves its window into its own output, which never
+ * aliases the window (same page, method run_armed: saved activations never
+ * alias the reusable window).  Reading: the window of receiver q has the
+ * layout of one rank's sequence-gathered tensor, [B][w*S_local][H/w][D], and
+ * its token block k of plane b, [k*S_local, (k+1)*S_local), holds what
+ * sender k sends q, so every sender's share is one contiguous block per
+ * plane.
+ *
+ * Pack, senders [first, first+count): win[q][b][k*S_local+s][h][d] =
+ *   mode 0: in[k][b][s][q*Hl+h][d]       (in[k]: [B][S_local][H][D])
+ *   mode 1: in[k][b][q*S_local+s][h][d]  (in[k]: [B][S_local*w][Hl][D])
+ * for every receiver q; other window elements are left untouched.
+ * Unpack, receivers [first, first+count): out[q] from win[q] =
+ *   mode 0: out[q][b][t][h][d] = win[q][b][t][h][d]  (out[q]: [B][S_local*w][Hl][D])
+ *   mode 1: out[q][b][s][k*Hl+h][d] = win[q][b][k*S_local+s][h][d]  (out[q]: [B][S_local][H][D])
+ * Pack by every sender followed by unpack of every receiver is the exchange
+ * of ua2a_oracle_ranks with every rank sending. */
+static int check_ranks_args(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64_t H, int64_t D,
+                            int32_t elem_bytes, const void* const* in, void* const* out,
+                            int32_t first, int32_t count)
+{
+    if (in == NULL || out == NULL) return -1;
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return -1;
+    if (mode != 0 && mode != 1) return -1;
+    if (w < 1 || B < 1 || S_local < 1 || H < 1 || D < 1 || H % w != 0) return -2;
+    if (first < 0 || count < 1 || first + count > w) return -1;
+    return 0;
+}
+
+int ua2a_oracle_pack_ranks(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64_t H,
+                           int64_t D, int32_t elem_bytes, const void* const* in, void* const* win,
+                           int32_t first, int32_t count)
+{
+    int rc = check_ranks_args(mode, w, B, S_local, H, D, elem_bytes, in, win, first, count);
+    if (rc != 0) return rc;
+    for (int32_t k = first; k < first + count; ++k)
+        if (in[k] == NULL) return -1;
+    for (int32_t q = 0; q < w; ++q)
+        if (win[q] == NULL) return -1;
+    const int64_t Hl = H / w;
+    const int64_t S_global = S_local * w;
+    const size_t e = (size_t)elem_bytes;
+    for (int64_t q = 0; q < w; ++q)                              /* receiving rank */
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t k = first; k < first + count; ++k)      /* sending rank */
+                for (int64_t s = 0; s < S_local; ++s)
+                    for (int64_t h = 0; h < Hl; ++h)
+                        for (int64_t d = 0; d < D; ++d) {
+                            int64_t si = mode == 0 ? ((b * S_local + s) * H + (q * Hl + h)) * D + d
+                                                   : ((b * S_global + (q * S_local + s)) * Hl + h) * D + d;
+                            int64_t wi = ((b * S_global + (k * S_local + s)) * Hl + h) * D + d;
+                            memcpy((unsigned char*)win[q] + (size_t)wi * e,
+                                   (const unsigned char*)in[k] + (size_t)si * e, e);
+                        }
+    return 0;
+}
+
+int ua2a_oracle_unpack_ranks(int32_t mode, int32_t w, int64_t B, int64_t S_local, int64_t H,
+                             int64_t D, int32_t elem_bytes, const void* const* win, void* const* out,
+                             int32_t first, int32_t count)
+{
+    int rc = check_ranks_args(mode, w, B, S_local, H, D, elem_bytes, win, out, first, count);
+    if (rc != 0) return rc;
+    for (int32_t q = first; q < first + count; ++q)
+        if (win[q] == NULL || out[q] == NULL) return -1;
+    const int64_t Hl = H / w;
+    const int64_t S_global = S_local * w;
+    const size_t e = (size_t)elem_bytes;
+    for (int64_t q = first; q < first + count; ++q)              /* receiving rank */
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t k = 0; k < w; ++k)                      /* sending rank */
+                for (int64_t s = 0; s < S_local; ++s)
+                    for (int64_t h = 0; h < Hl; ++h)
+                        for (int64_t d = 0; d < D; ++d) {
+                            int64_t wi = ((b * S_global + (k * S_local + s)) * Hl + h) * D + d;
+                            int64_t di = mode == 0 ? wi : ((b * S_local + s) * H + (k * Hl + h)) * D + d;
+                            memcpy((unsigned char*)out[q] + (size_t)di * e,
+                                   (const unsigned char*)win[q] + (size_t)wi * e, e);
+                        }
+    return 0;
+}
+
 /* Flat position in the rank-stacked input of the element that the exchange
  * (mode 0 or 1) writes at flat position out_index of the output: the
  * definitions above, for one element at a time (used to check outputs too

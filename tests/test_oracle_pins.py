@@ -400,3 +400,126 @@ def test_ranks_argument_errors():
     assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, ctypes.cast(nulls, vp), 0, 1) == -1   # output NULL
     assert oracle.raw_call(f, 0, 2, 1, 2, 3, 3, 2, i, q, 0, 2) == -2     # H % w
     assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, None, q, 0, 2) == -1  # no table
+
+
+# ------------------------------------------- pack and unpack through windows
+#
+# Receiver q's window is [B, S_local*w, H//w, D]; its token block k of each
+# plane holds what sender k sends q.  Each pin restates that with numpy
+# slicing and transposes of the rank tensors, independent of the loops.
+
+def numpy_window(x, w, mode, q):
+    """Receiver q's whole window from the rank-stacked input x."""
+    if mode == 0:                               # x [w, B, S, H, D]: head block q of every sender
+        _, B, S, H, D = x.shape
+        Hl = H // w
+        blk = x[:, :, :, q * Hl:(q + 1) * Hl, :]             # [k, B, S, Hl, D]
+    else:                                       # x [w, B, S*w, Hl, D]: token block q of every sender
+        _, B, Sg, Hl, D = x.shape
+        S = Sg // w
+        blk = x[:, :, q * S:(q + 1) * S, :, :]               # [k, B, S, Hl, D]
+    k, B, S, Hl, D = blk.shape
+    return blk.transpose(1, 0, 2, 3, 4).reshape(B, k * S, Hl, D)
+
+
+def numpy_unpack(win, w, mode):
+    if mode == 0:
+        return win.copy()
+    B, Sg, Hl, D = win.shape
+    S = Sg // w
+    return win.reshape(B, w, S, Hl, D).transpose(0, 2, 1, 3, 4).reshape(B, S, w * Hl, D)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_pack_sender_ranges_match_numpy_slices(shape, mode):
+    """Every sender range: the senders' token blocks of every window hold
+    numpy's slices of their tensors, every other block keeps its fill."""
+    w, B, S, H, D = shape
+    in_shape = shape if mode == 0 else mode1_shape(*shape)
+    x = rand_bits(in_shape, 4, 20 + mode)
+    wshape = (B, S * w, H // w, D)
+    for first in range(w):
+        for count in range(1, w - first + 1):
+            xs = [x[k].copy() if first <= k < first + count else None for k in range(w)]
+            wins = [np.full(wshape, 0xA5A5A5A5, np.uint32) for _ in range(w)]
+            oracle.pack_ranks(xs, wins, mode, first, count)
+            for q in range(w):
+                want = numpy_window(x, w, mode, q).reshape(B, w, S, H // w, D)
+                got = wins[q].reshape(B, w, S, H // w, D)
+                assert np.array_equal(got[:, first:first + count], want[:, first:first + count]), (q, first, count)
+                rest = np.concatenate([got[:, :first], got[:, first + count:]], axis=1)
+                assert (rest == 0xA5A5A5A5).all(), (q, first, count)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_unpack_receiver_ranges_match_numpy_transpose(shape, mode):
+    w, B, S, H, D = shape
+    wins = [rand_bits((B, S * w, H // w, D), 2, 30 + q) for q in range(w)]
+    out_shape = (B, S * w, H // w, D) if mode == 0 else (B, S, H, D)
+    for first in range(w):
+        for count in range(1, w - first + 1):
+            outs = [np.full(out_shape, 7, np.uint16) if first <= q < first + count else None for q in range(w)]
+            oracle.unpack_ranks(wins, outs, mode, first, count)
+            for q in range(first, first + count):
+                assert np.array_equal(outs[q], numpy_unpack(wins[q], w, mode)), (q, first, count)
+
+
+@pytest.mark.parametrize("itemsize", [1, 2, 4, 8])
+@pytest.mark.parametrize("shape", SHAPES + [s[:5] for s in TAIL_SHAPES])
+def test_pack_then_unpack_is_the_exchange(shape, itemsize):
+    """One pack per sender, then one unpack per receiver, gives numpy's
+    exchange (itself pinned to a real all-to-all above)."""
+    w, B, S, H, D = shape
+    for mode, in_shape in ((0, shape), (1, mode1_shape(*shape))):
+        x = rand_bits(in_shape, itemsize, 40 + mode)
+        full = numpy_mode0(x, w) if mode == 0 else numpy_mode1(x, w)
+        wins = [np.zeros((B, S * w, H // w, D), x.dtype) for _ in range(w)]
+        for k in range(w):
+            oracle.pack_ranks([x[j].copy() for j in range(w)], wins, mode, k, 1)
+        outs = [np.zeros(full.shape[1:], x.dtype) for _ in range(w)]
+        for q in range(w):
+            oracle.unpack_ranks(wins, outs, mode, q, 1)
+        assert np.array_equal(np.stack(outs), full), mode
+
+
+def test_pack_pins_reject_plausible_mistakes():
+    """A window built with the senders reversed, with the receiver's block of
+    the wrong side (heads where tokens are meant), or an unpack that keeps
+    [k][s] order, all disagree with the oracle on a generic shape."""
+    w, B, S, H, D = 3, 2, 5, 6, 4
+    x0 = rand_bits((w, B, S, H, D), 4, 50)
+    x1 = rand_bits(mode1_shape(w, B, S, H, D), 4, 51)
+    wins0 = [np.zeros((B, S * w, H // w, D), np.uint32) for _ in range(w)]
+    wins1 = [np.zeros((B, S * w, H // w, D), np.uint32) for _ in range(w)]
+    oracle.pack_ranks([x0[k].copy() for k in range(w)], wins0, 0)
+    oracle.pack_ranks([x1[k].copy() for k in range(w)], wins1, 1)
+    # senders reversed
+    assert not np.array_equal(wins0[1], numpy_window(x0[::-1].copy(), w, 0, 1))
+    # mode 1 taking the token block of the sender instead of the receiver
+    wrong = np.stack([x1[k][:, k * S:(k + 1) * S] for k in range(w)], 1).reshape(B, S * w, H // w, D)
+    assert not np.array_equal(wins1[1], wrong)
+    # unpack in [k][s] order instead of [s][k]
+    outs = [np.zeros((B, S, H, D), np.uint32) for _ in range(w)]
+    oracle.unpack_ranks(wins1, outs, 1)
+    assert not np.array_equal(outs[1], wins1[1].reshape(B, S, H, D))
+    assert np.array_equal(outs[1], numpy_unpack(wins1[1], w, 1))
+
+
+def test_pack_unpack_argument_errors():
+    w = 2
+    x = [np.zeros((1, 2, 4, 3), np.int16) for _ in range(w)]
+    wn = [np.zeros((1, 4, 2, 3), np.int16) for _ in range(w)]
+    vp = ctypes.c_void_p
+    i = ctypes.cast((vp * 2)(x[0].ctypes.data, x[1].ctypes.data), vp)
+    q = ctypes.cast((vp * 2)(wn[0].ctypes.data, wn[1].ctypes.data), vp)
+    nulls = ctypes.cast((vp * 2)(None, None), vp)
+    for f in ("ua2a_oracle_pack_ranks", "ua2a_oracle_unpack_ranks"):
+        assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, q, 0, 2) == 0
+        assert oracle.raw_call(f, 2, 2, 1, 2, 4, 3, 2, i, q, 0, 2) == -1     # mode
+        assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 3, i, q, 0, 2) == -1     # elem_bytes
+        assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, q, 1, 2) == -1     # first + count > w
+        assert oracle.raw_call(f, 0, 2, 1, 2, 3, 3, 2, i, q, 0, 2) == -2     # H % w
+        assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, nulls, q, 0, 1) == -1  # a used input NULL
+        assert oracle.raw_call(f, 0, 2, 1, 2, 4, 3, 2, i, nulls, 0, 1) == -1  # a used output NULL
