@@ -567,6 +567,96 @@ def run_overlap(args):
     print(json.dumps(result), flush=True)
 
 
+# ------------------------------------------------------------ pack / unpack
+
+def run_pack(args):
+    """The per-rank exchange in two steps through receive windows, as one
+    device of a multi-device exchange runs it: ua2a_pack_ranks with one
+    sender per launch (its push into every receiver's window), then
+    ua2a_unpack_ranks with one receiver per launch (window -> output).  Both
+    modes; next to it, the direct push of one sender per launch
+    (ua2a_exchange_ranks), which writes into the receivers' outputs.  Each
+    launch moves one rank's tensor in and one out (tensor / w each way); the
+    line gives microseconds and GB/s per launch, averaged over K rounds of w
+    launches.  The round trip (pack + unpack in mode 0, then in mode 1) is
+    checked to return the input before timing.  Prints one JSON line."""
+    import torch
+
+    import ulysses_all_re_amd as ua
+    from workloads import CONFIGS, DTYPES, MEASURE, make_tensor
+
+    name = args.workload
+    c = {**CONFIGS, **MEASURE}[name]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dt = DTYPES[c["dtype"]]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    plan = ua.Plan(w, B, S, H, D, dt, device=dev)
+    plan.set_path({"auto": ua.UA2A_PATH_AUTO, "direct": ua.UA2A_PATH_DIRECT,
+                   "lds": ua.UA2A_PATH_LDS}[args.path])
+    dist = "index_bits" if c["dist"] == "index" else c["dist"]
+    x = make_tensor((w, B, S, H, D), c["dtype"], dist, c["seed0"]).to(dev)
+    xs = [x[k].clone() for k in range(w)]
+    del x
+    wins = [torch.empty(plan.window_shape(), dtype=dt, device=dev) for _ in range(w)]
+    ys = [torch.empty(plan.out_shape(0)[1:], dtype=dt, device=dev) for _ in range(w)]
+    zs = [torch.empty(plan.out_shape(1)[1:], dtype=dt, device=dev) for _ in range(w)]
+    per_launch = 2 * plan.layout["tensor_bytes"] // w
+
+    def pack(mode, src):
+        for k in range(w):
+            plan.pack_ranks(src, mode, wins, first=k, count=1, stream=stream)
+
+    def unpack(mode, dst):
+        for q in range(w):
+            plan.unpack_ranks(wins, mode, dst, first=q, count=1, stream=stream)
+
+    pushes = {m: [plan.bind_ranks(src, m, dst, k, 1, stream) for k in range(w)]
+              for m, src, dst in ((0, xs, ys), (1, ys, zs))}
+    pack(0, xs)
+    unpack(0, ys)
+    pack(1, ys)
+    unpack(1, zs)
+    torch.cuda.synchronize(dev)
+    bits = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[xs[0].element_size()]
+    if not all(torch.equal(z.view(bits), x.view(bits)) for z, x in zip(zs, xs)):
+        raise SystemExit("pack + unpack round trip did not return the input; refusing to report a number")
+    K = args.steps
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        a.record(stream)
+        for _ in range(K):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize(dev)
+        us = a.elapsed_time(b) * 1e3 / (K * w)
+        return {"us_per_launch": round(us, 2), "GBps": round(per_launch / (us * 1e-6) / 1e9, 1)}
+
+    def push_all(m):
+        for call in pushes[m]:
+            call()
+
+    result = {
+        "metric": "per-launch time of one sender's pack and one receiver's unpack, 1 MI355X",
+        "unit": "us per launch", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": name, "w": w, "B": B, "S_local": S, "H": H, "D": D,
+                   "run_bytes": plan.layout["run_bytes"], "bytes_per_launch": per_launch,
+                   "path": args.path},
+        "mode0": {"pack": timed(lambda: pack(0, xs)), "unpack": timed(lambda: unpack(0, ys)),
+                  "direct_push": timed(lambda: push_all(0))},
+        "mode1": {"pack": timed(lambda: pack(1, ys)), "unpack": timed(lambda: unpack(1, zs)),
+                  "direct_push": timed(lambda: push_all(1))},
+    }
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
 # ------------------------------------------------------------ size sweep
 
 SWEEP_S_LOCAL = (50, 100, 200, 305, 400, 600, 800, 1200, 1600, 2400, 3200, 4800, 6400)
@@ -942,6 +1032,9 @@ def main():
                     help="one JSON line per (workload, mode, chunked) over the five workloads: "
                          "median and min per-launch time, copy baseline, oracle time, "
                          "bit-exactness, input SHA-256")
+    ap.add_argument("--pack", action="store_true",
+                    help="time one sender's pack (ua2a_pack_ranks) and one receiver's unpack "
+                         "(ua2a_unpack_ranks) per launch, next to the direct one-sender push")
     ap.add_argument("--sweep", action="store_true",
                     help="time the exchange at 13 sizes (4-524 MB per tensor) and fit t = t0 + bytes/BW")
     ap.add_argument("--records-workload", default=None, choices=RECORD_WORKLOADS,
@@ -974,6 +1067,9 @@ def main():
         return
     if args.sweep:
         run_sweep(args)
+        return
+    if args.pack:
+        run_pack(args)
         return
     run(args)
 

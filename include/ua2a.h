@@ -27,8 +27,8 @@
  *   - no function synchronises the host with the device;
  *   - no function allocates device memory; the ones that launch work
  *     (ua2a_exchange, ua2a_exchange_chunked_noalloc, ua2a_exchange_ranks,
- *     ua2a_exchange_publish, ua2a_wait_credits) launch only on the given
- *     stream;
+ *     ua2a_pack_ranks, ua2a_unpack_ranks, ua2a_exchange_publish,
+ *     ua2a_wait_credits) launch only on the given stream;
  *   - pointers named in/out/window are device pointers on the plan's
  *     device, owned by the caller, and are only borrowed by the library;
  *   - kernels write only the bytes of out (and of the window and counters
@@ -226,6 +226,44 @@ int ua2a_exchange_chunked_noalloc(ua2a_plan_t plan, int32_t mode, const void* in
  */
 int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
                         void* const* out_ptrs, int32_t first, int32_t count, void* stream);
+
+/*
+ * ua2a_pack_ranks / ua2a_unpack_ranks: the per-rank exchange in two steps
+ * through one receive window per receiving rank, as a multi-device exchange
+ * runs it: every sender pushes its share into each receiver's registered
+ * window, then each receiver moves its window into its own output, which never
+ * aliases the window (FastVideo "ulysses_a2a" API page, run_armed: saved
+ * activations never alias the reusable window).
+ *   Window of receiver q (win_ptrs[q]): one rank's sequence-gathered layout,
+ *   [B][S_local*w][H/w][D] (layout.tensor_bytes / w bytes); token block k of
+ *   plane b, [k*S_local, (k+1)*S_local), holds what sender k sends q:
+ *     mode 0: win_q[b][k*S_local+s][h][d] = x_k[b][s][q*(H/w)+h][d]
+ *     mode 1: win_q[b][k*S_local+s][h][d] = y_k[b][q*S_local+s][h][d]
+ *   so each sender's share is one contiguous block per plane and receiver
+ *   (in mode 1 a plain copy of S_local runs, whatever the run length).
+ * ua2a_pack_ranks: senders [first, first+count) write their blocks into
+ *   every window (in_ptrs as for ua2a_exchange_ranks; all w windows must
+ *   exist; other blocks are left as they were).  Mode 0 is exactly
+ *   ua2a_exchange_ranks with the windows as outputs.  One launch.
+ * ua2a_unpack_ranks: receivers [first, first+count) move their windows to
+ *   their outputs (out_ptrs[q] as ua2a_exchange_ranks' outputs):
+ *     mode 0: out_q = win_q (the same layout);
+ *     mode 1: out_q[b][s][k*(H/w)+h][d] = win_q[b][k*S_local+s][h][d].
+ *   One launch per receiver; entries outside the range are not read.
+ * Packing every sender and then unpacking every receiver gives
+ * ua2a_exchange_ranks(plan, mode, in, out, 0, w).  Tables are read during
+ * the call only; tensors and windows are borrowed.  Each used pointer must be
+ * elem_bytes-aligned.  Pack: windows may overlap neither each other nor a
+ * used input, and w <= 64 (the tables travel in the kernel argument).
+ * Unpack: a used output may overlap no other used output and no used window.
+ * Errors: INVALID_ARG (NULL table or used entry, mode, first/count out of
+ * range), SHAPE (pack with w > 64), ALIGN, ALIAS, DEVICE (no state change);
+ * HIP (the plan becomes disabled); DISABLED.
+ */
+int ua2a_pack_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs,
+                    void* const* win_ptrs, int32_t first, int32_t count, void* stream);
+int ua2a_unpack_ranks(ua2a_plan_t plan, int32_t mode, const void* const* win_ptrs,
+                      void* const* out_ptrs, int32_t first, int32_t count, void* stream);
 
 /* ------------------------------------------------------ readiness credits */
 /*

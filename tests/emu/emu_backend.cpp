@@ -76,7 +76,7 @@ namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+int g_kernel_counts[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
 uint32_t g_last_grid = 0;
 long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
 bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
@@ -218,6 +218,35 @@ void run_ranks(const Launch& L)
                             for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
                                 ranks_tile_body<CheckedMem, VB, M1, TWO, PART, kDirectBlock>(g, d, tid);
                         }
+}
+
+// Every workgroup of the pack launch's grid runs the kernel's loops.
+template <int VB>
+void run_pack(const Launch& L)
+{
+    const PackGeom& g = L.pack;
+    for (uint32_t bz = 0; bz < L.grid_z; ++bz)
+        for (uint32_t by = 0; by < L.grid_y; ++by)
+            for (uint32_t bx = 0; bx < L.grid; ++bx)
+                for (uint32_t z = bz; z < g.nz; z += L.grid_z)
+                    for (uint32_t y = by; y < g.ny; y += L.grid_y)
+                        for (uint32_t x = bx; x < g.tiles_per_block; x += L.grid) {
+                            const PackTile t = pack_tile<VB>(g, x, y, z);
+                            for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+                                pack_tile_body<CheckedMem, VB, kDirectBlock>(t, tid);
+                        }
+}
+
+int dispatch_pack(const Launch& L, int vb)
+{
+    switch (vb) {
+    case 16: run_pack<16>(L); return 0;
+    case 8: run_pack<8>(L); return 0;
+    case 4: run_pack<4>(L); return 0;
+    case 2: run_pack<2>(L); return 0;
+    case 1: run_pack<1>(L); return 0;
+    default: return 1;
+    }
 }
 
 template <bool M1, bool TWO, bool PART>
@@ -375,6 +404,11 @@ int backend_launch(const Launch& L, void*)
         if (L.grid != 1 || L.grid_y != 1 || L.grid_z != 1) return 9;
         for (uint32_t i = 0; i < L.signal.count; ++i) ++L.signal.credits[L.signal.first + i];
         return 0;
+    case Kernel::Pack:
+        if (L.grid_y < 1 || L.grid_z < 1 || L.grid_y > 65535 || L.grid_z > 65535 ||
+            static_cast<uint64_t>(L.grid) * L.block > (uint64_t(1) << 31))
+            return 8;
+        return dispatch_pack(L, L.width);
     case Kernel::Ranks:
         // the hardware's limits on a dispatch's extents
         if (L.grid_y < 1 || L.grid_z < 1 || L.grid_y > 65535 || L.grid_z > 65535 ||

@@ -379,3 +379,136 @@ def _forced(lib, shape, mode, first, count, force):
     finally:
         lib.ua2a_destroy(h)
     return [b.view.copy() for b in xin], [b.view.copy() for b in xout], info, xin + xout
+
+
+# -------------------------------------------------- pack and unpack (windows)
+
+def emu_pack_unpack(lib, shape, mode, first, count, mis=None, seed=0, path=ua.UA2A_PATH_AUTO, blocks=0):
+    """Pack senders [first, first+count) into every window, then unpack
+    receivers [first, first+count) (the same range, reused as receivers).
+    Returns (inputs, windows after pack, outputs after unpack) as byte arrays,
+    the launch counts, and every buffer."""
+    w, B, S, H, D, e = shape
+    n = _layout(lib, shape).tensor_bytes // w
+    m = mis or [0] * w
+    xin = [Buf(n, m[k]) for k in range(w)]
+    for k, b in enumerate(xin):
+        b.view[:] = rand_bytes(n, seed * 1000 + k)
+    wins = [Buf(n, m[(k + 1) % w]) for k in range(w)]
+    for b in wins:
+        b.view[:] = FILL
+    outs = [Buf(n, m[(k + 2) % w]) for k in range(w)]
+    for b in outs:
+        b.view[:] = FILL
+    used = [first <= k < first + count for k in range(w)]
+    h = ctypes.c_void_p()
+    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, blocks, None, 0, 0) == 0
+    try:
+        assert lib.ua2a_plan_set_path(h, path) == 0
+        lib.ua2a_emu_reset_counts()
+        rc = lib.ua2a_pack_ranks(h, mode, _tab([b.ptr if used[k] else None for k, b in enumerate(xin)]),
+                                 _tab([b.ptr for b in wins]), first, count, None)
+        assert rc == 0, (rc, lib.ua2a_plan_last_error(h))
+        packed = [b.view.copy() for b in wins]
+        launches_pack = lib.ua2a_emu_launches()
+        pack_kernel = lib.ua2a_emu_kernel_count(8)
+        lib.ua2a_emu_reset_counts()
+        rc = lib.ua2a_unpack_ranks(h, mode, _tab([b.ptr if used[k] else None for k, b in enumerate(wins)]),
+                                   _tab([b.ptr if used[k] else None for k, b in enumerate(outs)]),
+                                   first, count, None)
+        assert rc == 0, (rc, lib.ua2a_plan_last_error(h))
+        launches_unpack = lib.ua2a_emu_launches()
+    finally:
+        lib.ua2a_destroy(h)
+    return ([b.view.copy() for b in xin], packed, [b.view.copy() for b in outs],
+            (launches_pack, pack_kernel, launches_unpack), xin + wins + outs)
+
+
+def oracle_pack_unpack(inputs, shape, mode, first, count):
+    w, B, S, H, D, e = shape
+    dt = DT[e]
+    ishape = (B, S, H, D) if mode == 0 else (B, S * w, H // w, D)
+    wshape = (B, S * w, H // w, D)
+    oshape = wshape if mode == 0 else (B, S, H, D)
+    xs = [x.view(dt).reshape(ishape) for x in inputs]
+    wins = [np.full(wshape, FILL, np.uint8).view(dt) if e == 1 else
+            np.frombuffer(bytes([FILL]) * (int(np.prod(wshape)) * e), dtype=dt).reshape(wshape).copy()
+            for _ in range(w)]
+    oracle.pack_ranks([xs[k] if first <= k < first + count else None for k in range(w)], wins, mode,
+                      first, count)
+    outs = [np.frombuffer(bytes([FILL]) * (int(np.prod(oshape)) * e), dtype=dt).reshape(oshape).copy()
+            for _ in range(w)]
+    oracle.unpack_ranks(wins, outs, mode, first, count)
+    return ([wn.view(np.uint8).ravel() for wn in wins], [o.view(np.uint8).ravel() for o in outs])
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_emulated_pack_unpack_match_oracle(emu, shape):
+    """Pack of every sender range and unpack of the same range of receivers,
+    both modes, against the oracle's pack and unpack; windows and outputs
+    outside the ranges keep their fill; guards intact."""
+    w = shape[0]
+    ranges = [(0, w)] + [(k, 1) for k in range(w)] + ([(1, w - 1)] if w > 2 else [])
+    for mode in (0, 1):
+        for first, count in ranges:
+            x, packed, outs, (lp, pk, lu), bufs = emu_pack_unpack(emu, shape, mode, first, count, seed=mode + 5)
+            want_w, want_o = oracle_pack_unpack(x, shape, mode, first, count)
+            for q in range(w):
+                assert np.array_equal(packed[q], want_w[q]), (mode, first, count, q)
+                assert np.array_equal(outs[q], want_o[q]), (mode, first, count, q)
+            assert lp == 1 and lu == count
+            assert pk == (1 if mode == 1 else 0)      # mode 0 packs with the per-rank exchange
+            assert all(b.guards_intact() for b in bufs)
+
+
+@pytest.mark.parametrize("path", [ua.UA2A_PATH_AUTO, ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS],
+                         ids=["auto", "direct", "lds"])
+@pytest.mark.parametrize("shape", [(3, 2, 5, 3, 7, 2), (4, 1, 40, 8, 128, 2), (2, 2, 9, 4, 64, 2),
+                                   (5, 3, 37, 10, 3, 1), (3, 2, 11, 6, 5, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_emulated_pack_then_unpack_is_the_exchange(emu, shape, path):
+    """One pack per sender and one unpack of every receiver equal the
+    oracle's exchange, with misaligned bases too (narrower vectors)."""
+    w, B, S, H, D, e = shape
+    for mis in (None, [e * ((k % 3) + 1) for k in range(w)]):
+        for mode in (0, 1):
+            x, _, outs, _, bufs = emu_pack_unpack(emu, shape, mode, 0, w, mis=mis, seed=mode + 9, path=path)
+            xs = np.stack([a.view(DT[e]) for a in x]).reshape(
+                (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D))
+            want = oracle.exchange(xs, mode, w)
+            assert np.array_equal(np.stack(outs).view(DT[e]).reshape(want.shape), want), (mode, mis)
+            assert all(b.guards_intact() for b in bufs)
+
+
+@pytest.mark.parametrize("blocks", [1, 5, 1000])
+def test_emulated_pack_with_a_capped_grid(emu, blocks):
+    shape = (4, 3, 50, 8, 16, 2)
+    for mode in (0, 1):
+        x, packed, outs, _, _ = emu_pack_unpack(emu, shape, mode, 0, 4, seed=3, blocks=blocks)
+        want_w, want_o = oracle_pack_unpack(x, shape, mode, 0, 4)
+        assert all(np.array_equal(a, b) for a, b in zip(packed, want_w)), mode
+        assert all(np.array_equal(a, b) for a, b in zip(outs, want_o)), mode
+
+
+def test_emulated_pack_unpack_argument_errors(emu):
+    w, B, S, H, D, e = 2, 1, 4, 2, 8, 2
+    n = _layout(emu, (w, B, S, H, D, e)).tensor_bytes // w
+    bufs = [Buf(n) for _ in range(6)]
+    xs, wins, outs = [b.ptr for b in bufs[:2]], [b.ptr for b in bufs[2:4]], [b.ptr for b in bufs[4:]]
+    h = ctypes.c_void_p()
+    assert emu.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, 0, None, 0, 0) == 0
+    assert emu.ua2a_pack_ranks(h, 2, _tab(xs), _tab(wins), 0, 2, None) == ua.UA2A_ERR_INVALID_ARG
+    assert emu.ua2a_pack_ranks(h, 1, _tab(xs), _tab([wins[0], None]), 0, 1, None) == ua.UA2A_ERR_INVALID_ARG
+    assert emu.ua2a_pack_ranks(h, 1, _tab(xs), _tab([wins[0], wins[0]]), 0, 2, None) == ua.UA2A_ERR_ALIAS
+    assert emu.ua2a_pack_ranks(h, 1, _tab(xs), _tab([xs[1], wins[1]]), 0, 2, None) == ua.UA2A_ERR_ALIAS
+    assert emu.ua2a_pack_ranks(h, 1, _tab(xs), _tab([wins[0] + 1, wins[1]]), 0, 2, None) == ua.UA2A_ERR_ALIGN
+    assert emu.ua2a_unpack_ranks(h, 1, _tab(wins), _tab(outs), 1, 2, None) == ua.UA2A_ERR_INVALID_ARG
+    assert emu.ua2a_unpack_ranks(h, 1, _tab(wins), _tab([wins[1], outs[1]]), 0, 2, None) == ua.UA2A_ERR_ALIAS
+    assert emu.ua2a_unpack_ranks(h, 1, _tab(wins), _tab([outs[0], outs[0]]), 0, 2, None) == ua.UA2A_ERR_ALIAS
+    assert emu.ua2a_unpack_ranks(h, 1, _tab([None, wins[1]]), _tab([None, outs[1]]), 1, 1, None) == 0
+    emu.ua2a_emu_set_device(1)
+    assert emu.ua2a_pack_ranks(h, 1, _tab(xs), _tab(wins), 0, 2, None) == ua.UA2A_ERR_DEVICE
+    assert emu.ua2a_unpack_ranks(h, 1, _tab(wins), _tab(outs), 0, 2, None) == ua.UA2A_ERR_DEVICE
+    emu.ua2a_emu_set_device(0)
+    assert emu.ua2a_plan_last_error(h) == b""
+    emu.ua2a_destroy(h)

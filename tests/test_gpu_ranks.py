@@ -1,4 +1,6 @@
-"""GPU parity of the per-rank exchange (ua2a_exchange_ranks) against the CPU oracle.
+"""GPU parity of the per-rank exchange (ua2a_exchange_ranks) and of its two-step
+form through receive windows (ua2a_pack_ranks, ua2a_unpack_ranks) against
+the CPU oracle.
 
 Each rank's input and output is a tensor of its own (a separate device
 allocation); outputs start poisoned so that the runs of non-sending ranks
@@ -275,4 +277,95 @@ def test_ranks_with_a_capped_grid(blocks):
             note(f"ranks blocks={blocks} mode{mode} senders=[{first},{first + count})")
             got, want = run_case(plan, x, mode, first, count)
             assert_ranks_equal(got, want, f"blocks {blocks} mode {mode} [{first}, {first + count})")
+    plan.close()
+
+
+# ------------------------------------------------- pack and unpack (windows)
+
+def run_pack_unpack(plan, x_stacked, mode, senders, receivers, offsets=None):
+    """Pack the senders (one call each) into every receiver's window, then
+    unpack the receivers (one call each).  Windows and outputs start
+    poisoned; each rank's tensors may sit at an element offset inside a larger
+    allocation (offsets[k] = (input, window, output)).  Returns the device
+    windows and outputs and the oracle's, all as CPU bit arrays."""
+    w = plan.w
+    dt = x_stacked.dtype
+    ish, osh = stacked_shapes(plan.w, plan.B, plan.S_local, plan.H, plan.D, mode)
+    wsh = plan.window_shape()
+    pb = poison_bits(dt)
+    n = int(np.prod(ish[1:]))
+    offsets = offsets or [(0, 0, 0)] * w
+
+    def at(k, which, shape, fill=None, src=None):
+        off = offsets[k][which]
+        buf = torch.empty(n + off, dtype=dt, device=DEV)
+        if fill is not None:
+            bits(buf).fill_(fill)
+        if src is not None:
+            buf[off:].copy_(src.reshape(-1).to(DEV))
+        return buf[off:].view(shape)
+
+    used = sorted(set(senders))
+    xs = [at(k, 0, ish[1:], src=x_stacked[k]) if k in used else None for k in range(w)]
+    wins = [at(k, 1, wsh, fill=pb) for k in range(w)]
+    outs = [at(k, 2, osh[1:], fill=pb) for k in range(w)]
+    for k in senders:
+        plan.pack_ranks(xs, mode, wins, first=k, count=1)
+    for q in receivers:
+        plan.unpack_ranks(wins, mode, outs, first=q, count=1)
+    torch.cuda.synchronize()
+    xb = bits(x_stacked).numpy()
+    want_w = [np.full(wsh, pb, dtype=xb.dtype) for _ in range(w)]
+    for k in senders:
+        oracle.pack_ranks([xb[j] if j in used else None for j in range(w)], want_w, mode, k, 1)
+    want_o = [np.full(osh[1:], pb, dtype=xb.dtype) for _ in range(w)]
+    for q in receivers:
+        oracle.unpack_ranks(want_w, want_o, mode, q, 1)
+    return ([bits(t.cpu()) for t in wins], [torch.from_numpy(a) for a in want_w],
+            [bits(t.cpu()) for t in outs], [torch.from_numpy(a) for a in want_o])
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "video_dit", "chunked", "awkward"])
+def test_workload_pack_unpack_parity(name):
+    """Each workload, both modes: every sender packs on its own (what one
+    device of a multi-device exchange runs), every receiver unpacks on its
+    own; windows and outputs equal the oracle's, and the outputs equal the
+    oracle's exchange."""
+    c = CONFIGS[name]
+    w, B, S, H, D = c["w"], c["B"], c["S_local"], c["H"], c["D"]
+    dt = DTYPES[c["dtype"]]
+    plan = ua.Plan(w, B, S, H, D, dt)
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        dist = c["dist"] if (c["dist"] != "index" or mode == 0) else "index_bits"
+        x = make_tensor(ish, c["dtype"], dist, c["seed0"] if mode == 0 else c["seed1"])
+        note(f"pack/unpack {name} mode {mode}")
+        gw, ww, go, wo = run_pack_unpack(plan, x, mode, list(range(w)), list(range(w)))
+        assert_ranks_equal(gw, ww, f"{name} mode {mode} windows")
+        assert_ranks_equal(go, wo, f"{name} mode {mode} outputs")
+        full = oracle.exchange(bits(x).numpy(), mode, w)
+        assert torch.equal(torch.stack(go), torch.from_numpy(full)), f"{name} mode {mode} exchange"
+        del x, gw, ww, go, wo
+    plan.close()
+
+
+@pytest.mark.parametrize("shape", TAIL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_tail_pack_unpack_parity(shape):
+    """Runs that are short or not a multiple of 16 bytes, misaligned
+    per-rank bases, a partial sender range (the other windows' blocks keep
+    their poison) and a partial receiver range."""
+    w, B, S, H, D, dtype = shape
+    dt = DTYPES[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    plan = ua.Plan(w, B, S, H, D, dt)
+    offsets = [(k % 3, (k + 1) % 3, (k + 2) % 3) for k in range(w)] if e < 8 else None
+    for mode in (0, 1):
+        ish, _ = stacked_shapes(w, B, S, H, D, mode)
+        x = make_tensor(ish, dtype, "bytes", 60 + mode)
+        senders = list(range(w)) if w < 3 else [0, w - 1]
+        receivers = list(range(w)) if w < 3 else list(range(1, w))
+        note(f"pack/unpack tail {shape} mode {mode} senders {senders} receivers {receivers}")
+        gw, ww, go, wo = run_pack_unpack(plan, x, mode, senders, receivers, offsets)
+        assert_ranks_equal(gw, ww, f"{shape} mode {mode} windows")
+        assert_ranks_equal(go, wo, f"{shape} mode {mode} outputs")
     plan.close()

@@ -5,7 +5,8 @@ kernels in libua2a.so.  PyTorch is used for device memory and streams.
 
 The functions mirror the C ABI of include/ua2a.h one to one
 (``ua2a_layout``, ``ua2a_plan``, ``ua2a_exchange``,
-``ua2a_exchange_chunked_noalloc``, ``ua2a_exchange_ranks``,
+``ua2a_exchange_chunked_noalloc``, ``ua2a_exchange_ranks``, ``ua2a_pack_ranks``,
+``ua2a_unpack_ranks``,
 ``ua2a_exchange_publish``, ``ua2a_wait_credits``, ``ua2a_destroy``,
 ``ua2a_status_string``, ``ua2a_plan_last_error``, ``ua2a_plan_set_path``,
 ``ua2a_describe``, ``ua2a_describe_ranks``) and raise :class:`UA2AError` on a
@@ -53,7 +54,7 @@ UA2A_NOALLOC_WINDOW_BYTES = 64 * 1024 * 1024   # the library's own window (no-al
 # every symbol include/ua2a.h declares
 EXPORTED = (
     "ua2a_layout", "ua2a_plan", "ua2a_exchange", "ua2a_exchange_chunked_noalloc",
-    "ua2a_exchange_ranks", "ua2a_destroy",
+    "ua2a_exchange_ranks", "ua2a_pack_ranks", "ua2a_unpack_ranks", "ua2a_destroy",
     "ua2a_status_string", "ua2a_plan_last_error", "ua2a_plan_set_path", "ua2a_describe",
     "ua2a_describe_ranks", "ua2a_exchange_publish", "ua2a_wait_credits",
 )
@@ -116,6 +117,8 @@ def declare_signatures(lib: ctypes.CDLL) -> ctypes.CDLL:
         "ua2a_plan_set_path": ([vp, i32], ctypes.c_int),
         "ua2a_describe": ([vp, i32, i32, vp, vp, ctypes.POINTER(ua2a_launch_info_t)], ctypes.c_int),
         "ua2a_exchange_ranks": ([vp, i32, vp, vp, i32, i32, vp], ctypes.c_int),
+        "ua2a_pack_ranks": ([vp, i32, vp, vp, i32, i32, vp], ctypes.c_int),
+        "ua2a_unpack_ranks": ([vp, i32, vp, vp, i32, i32, vp], ctypes.c_int),
         "ua2a_describe_ranks": ([vp, i32, vp, vp, i32, i32, ctypes.POINTER(ua2a_launch_info_t)],
                                 ctypes.c_int),
         "ua2a_exchange_publish": ([vp, i32, vp, vp, vp, i32, vp], ctypes.c_int),
@@ -185,6 +188,26 @@ def ua2a_exchange_ranks(plan: int, mode: int, in_ptrs, out_ptrs, first: int, cou
                                             first, count, stream or None)
     if rc != UA2A_OK:
         raise UA2AError(rc, "ua2a_exchange_ranks", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_pack_ranks(plan: int, mode: int, in_ptrs, win_ptrs, first: int, count: int,
+                    stream: int = 0) -> None:
+    """Enqueue the pack of senders [first, first+count) into every receiver's window."""
+    rc = load_library().ua2a_pack_ranks(plan, mode, _table(in_ptrs) if in_ptrs is not None else None,
+                                        _table(win_ptrs) if win_ptrs is not None else None,
+                                        first, count, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_pack_ranks", ua2a_plan_last_error(plan) if plan else "")
+
+
+def ua2a_unpack_ranks(plan: int, mode: int, win_ptrs, out_ptrs, first: int, count: int,
+                      stream: int = 0) -> None:
+    """Enqueue the unpack of receivers [first, first+count) from their windows."""
+    rc = load_library().ua2a_unpack_ranks(plan, mode, _table(win_ptrs) if win_ptrs is not None else None,
+                                          _table(out_ptrs) if out_ptrs is not None else None,
+                                          first, count, stream or None)
+    if rc != UA2A_OK:
+        raise UA2AError(rc, "ua2a_unpack_ranks", ua2a_plan_last_error(plan) if plan else "")
 
 
 def ua2a_describe_ranks(plan: int, mode: int, in_ptrs, out_ptrs, first: int, count: int) -> dict:
@@ -376,6 +399,61 @@ class Plan:
             stream = torch.cuda.current_stream(self.device)
         self._on_device(ua2a_exchange_ranks, self.handle, mode, in_ptrs, out_ptrs, first, count,
                         stream.cuda_stream)
+        return outs
+
+    def window_shape(self):
+        """Shape of one receiver's window for pack_ranks / unpack_ranks: one
+        rank's sequence-gathered tensor, [B, S_local*w, H//w, D]."""
+        return (self.B, self.S_local * self.w, self.H // self.w, self.D)
+
+    def pack_ranks(self, xs, mode: int, wins=None, first: int = 0, count=None, stream=None):
+        """Senders [first, first+count) write their shares into every
+        receiver's window (token block k of each plane holds sender k's share);
+        xs as for exchange_ranks.  Returns wins (allocated when None)."""
+        import torch
+        count = self.w - first if count is None else count
+        if wins is None:
+            wins = [torch.empty(self.window_shape(), dtype=self.dtype, device=self.device)
+                    for _ in range(self.w)]
+        if len(wins) != self.w:
+            raise ValueError(f"wins needs one entry per rank ({self.w}), got {len(wins)}")
+        for q, wn in enumerate(wins):
+            self._check(wn, self.window_shape(), f"window of rank {q}")
+        if len(xs) != self.w:
+            raise ValueError(f"xs needs one entry per rank ({self.w}), got {len(xs)}")
+        if not (0 <= first and 1 <= count and first + count <= self.w):
+            raise ValueError(f"sender range [{first}, {first + count}) is not within [0, {self.w})")
+        for k in range(first, first + count):
+            if xs[k] is None:
+                raise ValueError(f"sending rank {k} has no input")
+            self._check(xs[k], self.in_shape(mode)[1:], f"input of rank {k}")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._on_device(ua2a_pack_ranks, self.handle, mode, [None if x is None else x.data_ptr() for x in xs],
+                        [wn.data_ptr() for wn in wins], first, count, stream.cuda_stream)
+        return wins
+
+    def unpack_ranks(self, wins, mode: int, outs=None, first: int = 0, count=None, stream=None):
+        """Receivers [first, first+count) move their windows into their outputs
+        (one launch each).  Returns outs (allocated when None; entries outside
+        the range may be None)."""
+        import torch
+        count = self.w - first if count is None else count
+        if not (0 <= first and 1 <= count and first + count <= self.w):
+            raise ValueError(f"receiver range [{first}, {first + count}) is not within [0, {self.w})")
+        if outs is None:
+            outs = [torch.empty(self.out_shape(mode)[1:], dtype=self.dtype, device=self.device)
+                    if first <= q < first + count else None for q in range(self.w)]
+        if len(wins) != self.w or len(outs) != self.w:
+            raise ValueError(f"wins and outs need one entry per rank ({self.w})")
+        for q in range(first, first + count):
+            self._check(wins[q], self.window_shape(), f"window of rank {q}")
+            self._check(outs[q], self.out_shape(mode)[1:], f"output of rank {q}")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._on_device(ua2a_unpack_ranks, self.handle, mode,
+                        [None if wn is None else wn.data_ptr() for wn in wins],
+                        [None if o is None else o.data_ptr() for o in outs], first, count, stream.cuda_stream)
         return outs
 
     def bind_ranks(self, xs, mode: int, outs, first: int = 0, count=None, stream=None):

@@ -249,6 +249,16 @@ UA2A_HD void ranks_tile_body(const RanksGeom& g, const RanksTile& d, uint32_t ti
     }
 }
 
+// Pack, mode 1: one tile of a contiguous block, one vector per lane per pass.
+template <class Mem, int VB, uint32_t BS>
+UA2A_HD void pack_tile_body(const PackTile& t, uint32_t tid)
+{
+    typedef typename Piece<VB>::T T;
+    const T* __restrict__ src = reinterpret_cast<const T*>(t.src) + t.u0;
+    uint8_t* const tile = t.dst + static_cast<int64_t>(t.u0) * VB;
+    for (uint32_t i = tid; i < t.nvec; i += BS) Mem::st_tile(tile, t.nvec * VB, i * VB, Mem::ld(src + i));
+}
+
 // A chunk that an A span covers only in part: its first or last chunk when
 // the span starts or ends inside an aligned 16-byte chunk.  Mode 1's fill
 // numbers them as slots, slot = 2 * r + end (end 0: first chunk, 1: last).

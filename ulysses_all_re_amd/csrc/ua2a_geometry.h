@@ -335,6 +335,44 @@ UA2A_HD void ranks_vector(const RanksGeom& g, const RanksTile& d, uint32_t u, co
 }
 
 // ------------------------------------------------------------------------
+// Pack, mode 1, over per-rank allocations: every sender k in [first,
+// first + count) copies, for every receiver q and plane b, its token block q
+// -- one contiguous block of s_local runs -- into block k of q's window
+// (receive windows laid out like one rank's sequence-gathered tensor,
+// [B][S_local * w][H/w][D]).  Slab grid: x = tile within the block, y = k -
+// first, z = q * nb + b (looped past the grid's extent).  Units: VB-byte
+// vectors; a block is block_vecs of them, contiguous on both sides.
+struct PackGeom {
+    const uint8_t* src[kMaxRankTable];   // per sender: its tensor [B][S_local * w][H/w][D]
+    uint8_t* dst[kMaxRankTable];         // per receiver: its window
+    int64_t src_b, src_q;                // sender side: plane, receiver's token block
+    int64_t dst_b, dst_k;                // window side: plane, sender's token block
+    uint32_t block_vecs, tile_vecs, tiles_per_block;
+    uint32_t first, ny, nz;              // ny = count, nz = w * nb
+    Div32 d_nb;
+};
+
+struct PackTile {
+    const uint8_t* src;   // the block's first byte in the sender's tensor
+    uint8_t* dst;         // ... and in the receiver's window
+    uint32_t u0, nvec;    // first vector of the tile within the block; vectors in it
+};
+
+template <int VB>
+UA2A_HD PackTile pack_tile(const PackGeom& g, uint32_t x, uint32_t y, uint32_t z)
+{
+    const uint32_t k = g.first + y;
+    const uint32_t q = fdiv(z, g.d_nb);
+    const uint32_t b = z - q * g.d_nb.d;
+    PackTile t;
+    t.u0 = x * g.tile_vecs;
+    t.nvec = umin32(g.tile_vecs, g.block_vecs - t.u0);
+    t.src = g.src[k] + (static_cast<int64_t>(b) * g.src_b + static_cast<int64_t>(q) * g.src_q) * VB;
+    t.dst = g.dst[q] + (static_cast<int64_t>(b) * g.dst_b + static_cast<int64_t>(k) * g.dst_k) * VB;
+    return t;
+}
+
+// ------------------------------------------------------------------------
 // LDS path: a workgroup stages rows [s0, s0 + rows) of one (j, b) -- a
 // contiguous span of rows * w * run bytes on the P side -- in LDS, laid out
 // as on the P side but shifted by `head` = the span's address mod 16 so that

@@ -568,6 +568,129 @@ void prepare_ranks(const ua2a_plan_s* p, int32_t mode, const void* const* in, vo
     if (L->grid_z > kMaxGridYZ) L->grid_z = kMaxGridYZ;
 }
 
+// Pack, mode 1: for every sender k in [first, first + count), receiver q and
+// plane b, the contiguous block of q's tokens (S_local runs) goes to block k
+// of plane b of q's window.  Every offset is a multiple of the block, so the
+// vector width follows the block and the bases, not the run: 14-byte runs
+// still move as 16-byte vectors when S_local * run allows.  (Mode 0's pack
+// is the per-rank exchange into the windows, prepare_ranks.)
+void prepare_pack1(const ua2a_plan_s* p, const void* const* in, void* const* win, int32_t first,
+                   int32_t count, Launch* L)
+{
+    memset(L, 0, sizeof *L);
+    const int64_t run = p->layout.run_bytes;
+    const int64_t block = p->S_local * run;                 // one token block of one plane
+    const int64_t plane = block * p->w;                     // one plane of a sequence-gathered tensor
+    uint32_t vb = pow2_align(static_cast<uint64_t>(block));
+    for (int32_t k = first; k < first + count; ++k)
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(in[k])));
+    for (int32_t q = 0; q < p->w; ++q) vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(win[q])));
+    PackGeom& g = L->pack;
+    for (int32_t k = 0; k < p->w; ++k) {
+        g.src[k] = (k >= first && k < first + count) ? static_cast<const uint8_t*>(in[k]) : nullptr;
+        g.dst[k] = static_cast<uint8_t*>(win[k]);
+    }
+    g.src_b = g.dst_b = plane / vb;
+    g.src_q = g.dst_k = block / vb;
+    g.block_vecs = static_cast<uint32_t>(block / vb);      // < 2^32 by the plane-size limit
+    g.tile_vecs = kTileBytes / vb;
+    g.tiles_per_block = (g.block_vecs + g.tile_vecs - 1) / g.tile_vecs;
+    g.first = static_cast<uint32_t>(first);
+    g.ny = static_cast<uint32_t>(count);
+    g.nz = static_cast<uint32_t>(p->w) * static_cast<uint32_t>(p->B);   // < 2^32 by the run-count limit
+    g.d_nb = make_div32(static_cast<uint32_t>(p->B));
+    L->kernel = Kernel::Pack;
+    L->block = kDirectBlock;
+    L->width = static_cast<int32_t>(vb);
+    L->mode = 1;
+    L->grid = grid_for(g.tiles_per_block, p->blocks, kDirectBlock);
+    uint64_t room = p->blocks > 0 ? static_cast<uint64_t>(p->blocks) / L->grid : kMaxGridYZ;
+    if (room < 1) room = 1;
+    L->grid_y = static_cast<uint32_t>(g.ny < room ? g.ny : room);
+    room = p->blocks > 0 ? room / L->grid_y : kMaxGridYZ;
+    if (room < 1) room = 1;
+    L->grid_z = static_cast<uint32_t>(g.nz < room ? g.nz : room);
+    if (L->grid_z > kMaxGridYZ) L->grid_z = kMaxGridYZ;
+}
+
+// Unpack of one receiver: mode 0's window already has the output's layout
+// (one copy); mode 1 is the mode-1 exchange restricted to this receiver's
+// rows, reading sender k's runs from token block k of the window (A-side
+// rank stride S_local * run, plane stride S_local * w * run), by the same
+// path choice as ua2a_exchange.
+void prepare_unpack(const ua2a_plan_s* p, int32_t mode, const void* win, void* out, Launch* L)
+{
+    memset(L, 0, sizeof *L);
+    uint8_t* winb = const_cast<uint8_t*>(static_cast<const uint8_t*>(win));
+    uint8_t* outb = static_cast<uint8_t*>(out);
+    const int64_t run = p->layout.run_bytes;
+    const int64_t rank_bytes = p->layout.tensor_bytes / p->w;
+    L->grid_y = L->grid_z = 1;
+    L->mode = mode;
+    if (mode == 0) {
+        uint32_t vb = pow2_align(static_cast<uint64_t>(rank_bytes));
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(win)));
+        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out)));
+        L->kernel = Kernel::Copy;
+        L->block = kCopyBlock;
+        L->width = static_cast<int32_t>(vb);
+        L->copy = make_copy(vb, winb, outb, 0, 0, rank_bytes, 1);
+        L->grid = grid_for(L->copy.num_tiles, 0, kCopyBlock);
+        return;
+    }
+    const int64_t block = p->S_local * run;
+    const int64_t a_plane = block * p->w;
+    const int64_t p_plane = p->S_local * p->H * p->D * p->elem_bytes;
+    uint32_t g = pow2_align(static_cast<uint64_t>(run));
+    g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(win)));
+    g = umin32(g, pow2_align(reinterpret_cast<uintptr_t>(out)));
+    const uint32_t rows = lds_rows(p, 1, g);
+    bool lds;
+    if (p->path == UA2A_PATH_DIRECT || rows == 0)
+        lds = false;
+    else if (p->path == UA2A_PATH_LDS)
+        lds = true;
+    else
+        lds = !(g == 16 && direct_reads_whole_lines(1, p->w, run));
+    if (!lds) {
+        direct_launch(p, 1, g, outb, winb, 0, p_plane, block, a_plane, static_cast<uint32_t>(p->B), 1, false, L);
+        return;
+    }
+    L->kernel = Kernel::Lds;
+    L->block = kLdsBlock;
+    L->width = static_cast<int32_t>(g);
+    L->lds = make_lds(p, 1, g, outb, winb, 0, p_plane, block, a_plane, static_cast<uint32_t>(p->B));
+    L->lds.num_tiles = L->lds.nb * L->lds.tiles_per_plane;     // the receiver's rows only
+    set_lds_slots(&L->lds);
+    L->lds_bytes = L->lds.lds_bytes;
+    L->grid = grid_for(L->lds.num_slots, p->blocks, kLdsBlock);
+}
+
+// Unpack arguments: receivers [first, first + count) need their windows and
+// outputs; an output may overlap no other used output and no used window.
+int check_unpack_call(const ua2a_plan_s* p, int32_t mode, const void* const* win, void* const* out,
+                      int32_t first, int32_t count)
+{
+    if (p == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (p->disabled) return UA2A_ERR_DISABLED;
+    if (mode != 0 && mode != 1) return UA2A_ERR_INVALID_ARG;
+    if (win == nullptr || out == nullptr) return UA2A_ERR_INVALID_ARG;
+    if (first < 0 || count < 1 || first > p->w - count) return UA2A_ERR_INVALID_ARG;
+    const int32_t last = first + count;
+    const uintptr_t e = static_cast<uintptr_t>(p->elem_bytes);
+    for (int32_t q = first; q < last; ++q) {
+        if (win[q] == nullptr || out[q] == nullptr) return UA2A_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(win[q]) % e || reinterpret_cast<uintptr_t>(out[q]) % e)
+            return UA2A_ERR_ALIGN;
+    }
+    const int64_t n = p->layout.tensor_bytes / p->w;       // one rank's tensor, and one window
+    for (int32_t q = first; q < last; ++q)
+        for (int32_t q2 = first; q2 < last; ++q2)
+            if ((q2 > q && overlaps(out[q], n, out[q2], n)) || overlaps(out[q], n, win[q2], n))
+                return UA2A_ERR_ALIAS;
+    return UA2A_OK;
+}
+
 void disable(ua2a_plan_s* p, const char* what, int err)
 {
     p->disabled = 1;
@@ -725,20 +848,52 @@ int ua2a_exchange_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
                         void* const* out_ptrs, int32_t first, int32_t count, void* stream)
 {
     int rc = check_ranks_call(plan, mode, in_ptrs, out_ptrs, first, count);
+    if (rc == UA2A_OK) rc = check_device(plan);
     if (rc != UA2A_OK) return rc;
-    int32_t dev = -1;
-    int err = backend_current_device(&dev);
-    if (err != 0) {
-        disable(plan, "querying the current device", err);
-        return UA2A_ERR_HIP;
-    }
-    if (dev != plan->device) return UA2A_ERR_DEVICE;
     Launch L;
     prepare_ranks(plan, mode, in_ptrs, out_ptrs, first, count, &L);
-    err = backend_launch(L, stream);
+    const int err = backend_launch(L, stream);
     if (err != 0) {
         disable(plan, "launching the per-rank exchange kernel", err);
         return UA2A_ERR_HIP;
+    }
+    return UA2A_OK;
+}
+
+int ua2a_pack_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_ptrs, void* const* win_ptrs,
+                    int32_t first, int32_t count, void* stream)
+{
+    // the windows are checked as the per-rank exchange checks its outputs
+    int rc = check_ranks_call(plan, mode, in_ptrs, win_ptrs, first, count);
+    if (rc == UA2A_OK) rc = check_device(plan);
+    if (rc != UA2A_OK) return rc;
+    Launch L;
+    if (mode == 0)
+        prepare_ranks(plan, 0, in_ptrs, win_ptrs, first, count, &L);
+    else
+        prepare_pack1(plan, in_ptrs, win_ptrs, first, count, &L);
+    const int err = backend_launch(L, stream);
+    if (err != 0) {
+        disable(plan, "launching the pack kernel", err);
+        return UA2A_ERR_HIP;
+    }
+    return UA2A_OK;
+}
+
+int ua2a_unpack_ranks(ua2a_plan_t plan, int32_t mode, const void* const* win_ptrs, void* const* out_ptrs,
+                      int32_t first, int32_t count, void* stream)
+{
+    int rc = check_unpack_call(plan, mode, win_ptrs, out_ptrs, first, count);
+    if (rc == UA2A_OK) rc = check_device(plan);
+    if (rc != UA2A_OK) return rc;
+    for (int32_t q = first; q < first + count; ++q) {
+        Launch L;
+        prepare_unpack(plan, mode, win_ptrs[q], out_ptrs[q], &L);
+        const int err = backend_launch(L, stream);
+        if (err != 0) {
+            disable(plan, "launching the unpack kernel", err);
+            return UA2A_ERR_HIP;
+        }
     }
     return UA2A_OK;
 }
@@ -753,13 +908,9 @@ int ua2a_exchange_publish(ua2a_plan_t plan, int32_t mode, const void* in, void* 
     const int64_t cbytes = int64_t(plan->w) * static_cast<int64_t>(sizeof(uint32_t));
     const int64_t n = plan->layout.tensor_bytes;
     if (overlaps(credits, cbytes, in, n) || overlaps(credits, cbytes, out, n)) return UA2A_ERR_ALIAS;
-    int32_t dev = -1;
-    int err = backend_current_device(&dev);
-    if (err != 0) {
-        disable(plan, "querying the current device", err);
-        return UA2A_ERR_HIP;
-    }
-    if (dev != plan->device) return UA2A_ERR_DEVICE;
+    rc = check_device(plan);
+    if (rc != UA2A_OK) return rc;
+    int err;
     // Part k covers receiving ranks [w*k/parts, w*(k+1)/parts): the direct
     // kernel on bases moved to its first receiver (mode 0: A rank r0 and head
     // block r0 of the P rows; mode 1: P rank j0 and token block j0 of the A

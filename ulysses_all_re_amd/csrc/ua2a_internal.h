@@ -41,7 +41,7 @@ constexpr uint32_t kLdsXcdLog = 2;              // LDS tiles: 2^kLdsXcdLog conse
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5,
-                              LdsRanks = 6, Chunked = 7 };
+                              LdsRanks = 6, Chunked = 7, Pack = 8 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -59,6 +59,7 @@ struct Launch {
     LdsGeom lds;
     CopyGeom copy;
     RanksGeom ranks;
+    PackGeom pack;       // Pack: blocks from the senders' tensors into the receivers' windows
     LdsTables lds_tab;   // LdsRanks: the per-rank bases of `lds`
     WaitGeom wait;
     SignalGeom signal;

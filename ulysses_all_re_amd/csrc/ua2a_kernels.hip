@@ -26,6 +26,8 @@
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
+//  * ua2a_pack_kernel    -- mode 1's pack into the receivers' windows:
+//    contiguous blocks from every sender to every receiver.
 //  * ua2a_signal_kernel  -- adds the readiness credits of a publishing
 //    exchange's last part (earlier parts' credits are added by the next
 //    part's first workgroup); ua2a_wait_kernel -- one wave that waits for
@@ -134,6 +136,13 @@ __device__ __forceinline__ void args_up_front(const RanksGeom& g)
                  "s"(g.tiles_per_slab), "s"(g.ny), "s"(g.nz), "s"(g.two_runs), "s"(g.d_vr.m), "s"(g.d_vr.s),
                  "s"(g.d_seg.m), "s"(g.d_seg.s), "s"(g.d_nb.m), "s"(g.d_nb.s), "s"(g.d_count.m),
                  "s"(g.d_count.s));
+}
+
+__device__ __forceinline__ void args_up_front(const PackGeom& g)
+{
+    asm volatile("" ::"s"(g.src_b), "s"(g.src_q), "s"(g.dst_b), "s"(g.dst_k), "s"(g.block_vecs),
+                 "s"(g.tile_vecs), "s"(g.tiles_per_block), "s"(g.first), "s"(g.ny), "s"(g.nz), "s"(g.d_nb.d),
+                 "s"(g.d_nb.m), "s"(g.d_nb.s));
 }
 
 // The LDS kernels already fetch their fields at the start, but in two rounds
@@ -276,6 +285,19 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_ranks_kernel(RanksGeom g)
                     g, ranks_tile<MODE1, TWO>(g, x, y, z), threadIdx.x);
 }
 
+// Pack, mode 1: contiguous blocks from the senders' tensors into the
+// receivers' windows, one tile per workgroup when the grid covers the slab
+// grid, else each dimension loops.
+template <int VB>
+__global__ __launch_bounds__(kDirectBlock) void ua2a_pack_kernel(PackGeom g)
+{
+    args_up_front(g);
+    for (uint32_t z = blockIdx.z; z < g.nz; z += gridDim.z)
+        for (uint32_t y = blockIdx.y; y < g.ny; y += gridDim.y)
+            for (uint32_t x = blockIdx.x; x < g.tiles_per_block; x += gridDim.x)
+                pack_tile_body<StreamMem, VB, kDirectBlock>(pack_tile<VB>(g, x, y, z), threadIdx.x);
+}
+
 template <int VB>
 __global__ __launch_bounds__(kCopyBlock) void ua2a_copy_kernel(CopyGeom g)
 {
@@ -371,6 +393,18 @@ const void* ranks_fn(int vb)
     }
 }
 
+const void* pack_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_pack_kernel<16>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_pack_kernel<8>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_pack_kernel<4>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_pack_kernel<2>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_pack_kernel<1>);
+    default: return nullptr;
+    }
+}
+
 const void* copy_fn(int vb)
 {
     switch (vb) {
@@ -458,6 +492,10 @@ int backend_launch(const Launch& L, void* stream)
     case Kernel::Copy:
         fn = copy_fn(L.width);
         arg = &cg;
+        break;
+    case Kernel::Pack:
+        fn = pack_fn(L.width);
+        arg = const_cast<PackGeom*>(&L.pack);
         break;
     case Kernel::Wait:
         fn = reinterpret_cast<const void*>(&ua2a_wait_kernel);
