@@ -113,13 +113,40 @@ void run_direct(const Launch& L)
                 }
         return;
     }
-    // a capped grid loops grid-stride; every tile is visited exactly once either way
-    for (uint32_t t = 0; t < g.num_tiles; ++t) {
-        if (!take_tile()) return;
-        const DirectTile d = direct_tile<M1>(g, t);
-        for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
-            direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+    // every workgroup runs the kernel's loop: with cap_tiles > 1, groups of
+    // kCapTiles grid-strided tiles (all loaded before any is stored when all
+    // are full), then the rest one at a time; each tile visited exactly once
+    std::vector<uint8_t> seen(g.num_tiles, 0);
+    const uint64_t step = L.grid;
+    for (uint32_t bx = 0; bx < L.grid; ++bx) {
+        uint64_t t = bx;
+        for (; g.cap_tiles > 1 && t + (kCapTiles - 1) * step < g.num_tiles; t += kCapTiles * step) {
+            DirectTile d[kCapTiles];
+            bool full = true;
+            for (uint32_t i = 0; i < kCapTiles; ++i) {
+                if (!take_tile()) return;
+                if (seen[t + i * step]++) abort();
+                d[i] = direct_tile<M1>(g, static_cast<uint32_t>(t + i * step));
+                full = full && d[i].nvec == g.tile_vecs;
+            }
+            for (uint32_t tid = 0; tid < kDirectBlock; ++tid) {
+                if (full)
+                    direct_full_tiles_body<CheckedMem, VB, M1, kDirectBlock, kCapTiles>(g, d, tid);
+                else
+                    for (uint32_t i = 0; i < kCapTiles; ++i)
+                        direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d[i], tid);
+            }
+        }
+        for (; t < g.num_tiles; t += step) {
+            if (!take_tile()) return;
+            if (seen[t]++) abort();
+            const DirectTile d = direct_tile<M1>(g, static_cast<uint32_t>(t));
+            for (uint32_t tid = 0; tid < kDirectBlock; ++tid)
+                direct_tile_body<CheckedMem, VB, M1, kDirectBlock, kDirectUnroll>(g, d, tid);
+        }
     }
+    for (uint32_t t = 0; t < g.num_tiles; ++t)
+        if (!seen[t]) abort();
 }
 
 // The one-launch chunked exchange: every workgroup of the 3-D grid, every

@@ -115,6 +115,37 @@ UA2A_HD void direct_tile_body(const DirectGeom& g, const DirectTile& d, uint32_t
     }
 }
 
+// N full tiles of a capped flat grid at once: every lane loads its vectors
+// of all N tiles before it stores any, so a workgroup that loops over several
+// tiles keeps N tiles' loads in flight instead of one.  A full tile (16 * BS
+// bytes) gives each lane exactly 16 / VB vectors, so no lane needs a bounds
+// test (per-lane tests would split the body into masked blocks, across which
+// the compiler waits for each load before going on).
+template <class Mem, int VB, bool MODE1, uint32_t BS, uint32_t N>
+UA2A_HD void direct_full_tiles_body(const DirectGeom& g, const DirectTile* d, uint32_t tid)
+{
+    typedef typename Piece<VB>::T T;
+    constexpr uint32_t K = 16 / VB;
+    const T* __restrict__ src = reinterpret_cast<const T*>(g.src);
+    T v[N][K];
+    int64_t to[N][K];
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i)
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k) {
+            int64_t from;
+            direct_vector<MODE1>(g, d[i], d[i].u0 + tid + k * BS, from, to[i][k]);
+            v[i][k] = Mem::ld(src + from);
+        }
+#pragma unroll
+    for (uint32_t i = 0; i < N; ++i) {
+        const int64_t first = d[i].dst_slab + d[i].u0;
+#pragma unroll
+        for (uint32_t k = 0; k < K; ++k)
+            Mem::st_tile(g.dst + first * VB, 16 * BS, static_cast<uint32_t>((to[i][k] - first) * VB), v[i][k]);
+    }
+}
+
 // Chunked exchange in one launch (see ChunkedGeom): the tile's window range
 // is written and read back plane after plane by the lanes that own it.  A
 // tile is 16 * BS bytes, so a lane owns K = 16 / VB window vectors,

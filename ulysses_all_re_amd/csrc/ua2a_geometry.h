@@ -101,6 +101,8 @@ struct DirectGeom {
     uint32_t num_tiles;        // slabs * tiles_per_slab (grouped: slabs * ceil(tps / F) * F)
     uint32_t group;            // 0: slab after slab; F > 0: groups of F tiles, r fastest
     uint32_t groups;           // ceil(tiles_per_slab / F)
+    uint32_t cap_tiles;        // flat grid: tiles a workgroup loads before storing (1, or more
+                               //   when a capped grid would keep too few tiles in flight)
     Div32 d_vr, d_prow, d_tps, d_w, d_nb, d_group, d_groups;
 };
 

@@ -26,6 +26,8 @@ namespace ua2a {
 // and non-temporal accesses move the most bytes per second; deeper per-lane
 // unrolling, bigger workgroups or persistent grids are slower there.
 constexpr uint32_t kDirectUnroll = 1;           // vectors per lane per pass (direct, copy)
+constexpr uint32_t kCapTiles = 4;               // tiles in flight per workgroup of a low-capped flat grid
+constexpr uint32_t kCapInFlight = 8192;         // ... used while grid * kCapTiles stays within this
 constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
 constexpr uint32_t kLdsUnroll = 2;              // 16-byte chunks per lane per pass (LDS fill, G = 16)
 constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least contiguous read per head block

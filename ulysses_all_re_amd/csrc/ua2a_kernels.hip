@@ -117,6 +117,7 @@ __device__ __forceinline__ void flat_args_up_front(const DirectGeom& g)
 {
     args_up_front(g);
     asm volatile("" ::"s"(g.num_tiles), "s"(g.tiles_per_slab), "s"(g.group), "s"(g.groups), "s"(g.w),
+                 "s"(g.cap_tiles),
                  "s"(g.d_tps.m), "s"(g.d_tps.s), "s"(g.d_w.m), "s"(g.d_w.s), "s"(g.d_group.m),
                  "s"(g.d_group.s), "s"(g.d_groups.m), "s"(g.d_groups.s));
 }
@@ -178,8 +179,31 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_direct_kernel(DirectGeom g)
 {
     flat_args_up_front(g);
     if (SIG && blockIdx.x == 0) add_credits(g.sig_credits, g.sig_first, g.sig_count);
-    // 64-bit tile counter: t + gridDim.x may pass 2^32 when num_tiles is near it
-    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x)
+    // 64-bit tile counters: t + gridDim.x may pass 2^32 when num_tiles is near it.
+    // With cap_tiles > 1 (a grid capped so low that one tile per workgroup
+    // would keep too few loads in flight) a workgroup takes its tiles
+    // kCapTiles at a time (t, t + grid, ...), all loaded before any is stored;
+    // a group holding a partial or padding tile, the rest, and every other
+    // grid go one tile at a time.
+    static_assert(kTileBytes == 16 * kDirectBlock, "a full tile is 16 bytes per lane");
+    const uint64_t step = gridDim.x;
+    uint64_t t = blockIdx.x;
+    for (; g.cap_tiles > 1 && t + (kCapTiles - 1) * step < g.num_tiles; t += kCapTiles * step) {
+        DirectTile d[kCapTiles];
+        bool full = true;
+#pragma unroll
+        for (uint32_t i = 0; i < kCapTiles; ++i) {
+            d[i] = direct_tile<MODE1>(g, static_cast<uint32_t>(t + i * step));
+            full = full && d[i].nvec == g.tile_vecs;
+        }
+        if (full) {
+            direct_full_tiles_body<StreamMem, VB, MODE1, kDirectBlock, kCapTiles>(g, d, threadIdx.x);
+        } else {
+            for (uint32_t i = 0; i < kCapTiles; ++i)
+                direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(g, d[i], threadIdx.x);
+        }
+    }
+    for (; t < g.num_tiles; t += step)
         direct_tile_body<StreamMem, VB, MODE1, kDirectBlock, kDirectUnroll>(
             g, direct_tile<MODE1>(g, static_cast<uint32_t>(t)), threadIdx.x);
 }
