@@ -1,6 +1,7 @@
 """The README's Python examples run as written (in order, one namespace) and
 give consistent results: the round trip returns the input, the operator and
-the per-rank calls agree with the plan's exchange, and the credit waits end
+the per-rank calls and the pack/unpack pair agree with the plan's exchange,
+and the credit waits end
 without a time-out."""
 from __future__ import annotations
 
@@ -29,5 +30,6 @@ def test_readme_python_examples():
     assert torch.equal(bits(z), bits(x))
     assert torch.equal(bits(ns["plan"].exchange(x, 0)), bits(y))
     assert all(torch.equal(bits(ns["outs"][k]), bits(y[k])) for k in range(w))
+    assert all(torch.equal(bits(ns["outs2"][k]), bits(y[k])) for k in range(w))
     assert int(ns["status"].item()) == 0
     assert bool((ns["credits"].cpu() == 1).all())

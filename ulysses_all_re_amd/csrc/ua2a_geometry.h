@@ -418,6 +418,8 @@ struct LdsGeom {
     uint32_t a_window;         // 1: rank-stacked A side of under 4 GiB, so a tile's w A spans
                                //    lie within 4 GiB past head block 0's (mode 0 stores through
                                //    that range); 0: per-rank tables or larger tensors
+    uint32_t a_whole16;        // 1: the A base and rank stride are 16-aligned (a tile whose
+                               //    start and span length are too has only whole chunks)
     uint32_t lds_bytes;        // LDS bytes the kernel reserves (>= 16 + rows_per_tile * lrow)
     uint32_t stride_full;      // 16-byte chunk slots per A span: tile of rows_per_tile rows
     uint32_t stride_last;      // ... and the plane's last tile

@@ -225,6 +225,7 @@ LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uin
     // every A span of a stacked tensor lies in [a_ptr, a_ptr + w * a_rank)
     g.a_window = (a_ptr != nullptr && static_cast<uint64_t>(g.w) * static_cast<uint64_t>(a_rank) + 64 <=
                   UINT32_MAX) ? 1u : 0u;
+    g.a_whole16 = (a_ptr != nullptr && reinterpret_cast<uintptr_t>(a_ptr) % 16 == 0 && a_rank % 16 == 0) ? 1u : 0u;
     // chunk slots per A span: its chunks when spans are 16-aligned, else room
     // for an unaligned start (the longest a span can touch), rounded up to
     // whole 128-byte lines.  Consecutive lanes take consecutive slots, so a

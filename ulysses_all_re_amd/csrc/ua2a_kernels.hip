@@ -155,7 +155,7 @@ __device__ __forceinline__ void args_up_front(const LdsGeom& g)
     asm volatile("" ::"s"(g.p_ptr), "s"(g.a_ptr), "s"(g.a_rank), "s"(g.a_plane), "s"(g.p_rank), "s"(g.p_plane),
                  "s"(g.run), "s"(g.row), "s"(g.pad), "s"(g.lrow), "s"(g.s_local), "s"(g.rows_per_tile),
                  "s"(g.tiles_per_plane), "s"(g.num_tiles), "s"(g.num_slots), "s"(g.xlog), "s"(g.w), "s"(g.nb),
-                 "s"(g.j0), "s"(g.a_window), "s"(g.stride_full), "s"(g.stride_last));
+                 "s"(g.j0), "s"(g.a_window), "s"(g.a_whole16), "s"(g.stride_full), "s"(g.stride_last));
     asm volatile("" ::"s"(g.d_tpp.m), "s"(g.d_tpp.s), "s"(g.d_nb.m), "s"(g.d_nb.s), "s"(g.d_run.m),
                  "s"(g.d_run.s), "s"(g.d_row.m), "s"(g.d_row.s), "s"(g.d_stride_full.m),
                  "s"(g.d_stride_full.s), "s"(g.d_stride_last.m), "s"(g.d_stride_last.s));

@@ -54,6 +54,9 @@ TAIL_SHAPES = [
     (3, 2, 11, 6, 5, "f64"),    # run 80 B, 8-byte elements
     (2, 1, 300, 4, 16, "bf16"),  # run 64 B, many rows
     (8, 2, 257, 8, 24, "bf16"),  # run 48 B
+    (4, 2, 192, 4, 7, "bf16"),   # run 14 B, tiles of whole 128-byte lines (16-byte chunks only)
+    (2, 2, 64, 6, 5, "fp32"),    # run 60 B, the same with 4-byte pieces
+    (2, 1, 80, 2, 12, "fp16"),   # run 24 B, the same with 8-byte pieces
 ]
 
 DTYPES = {
