@@ -460,7 +460,7 @@ sys.path.insert(0, {root!r})
 import oracle, ulysses_all_re_amd as ua
 lib = ua.declare_signatures(ctypes.CDLL({lib!r}))
 cases = {cases!r}
-for (w, B, S, H, D, e, mode, chunked, path, mis) in cases:
+for (w, B, S, H, D, e, mode, chunked, path, mis, blocks) in cases:
     lay = ua.ua2a_layout_t()
     assert lib.ua2a_layout(w, B, S, H, D, e, ctypes.byref(lay)) == 0
     n = lay.tensor_bytes
@@ -471,7 +471,7 @@ for (w, B, S, H, D, e, mode, chunked, path, mis) in cases:
     src = np.frombuffer(xin, dtype=np.uint8)[mis:]
     src[:] = np.random.default_rng(w * 131 + S).integers(0, 256, n, dtype=np.uint8)
     h = ctypes.c_void_p()
-    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, 0,
+    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, blocks,
                          (ctypes.addressof(win) + mis) if chunked else None,
                          lay.window_bytes if chunked else 0, 0) == 0
     assert lib.ua2a_plan_set_path(h, path) == 0
@@ -482,7 +482,7 @@ for (w, B, S, H, D, e, mode, chunked, path, mis) in cases:
     ishape = (w, B, S, H, D) if mode == 0 else (w, B, S * w, H // w, D)
     want = oracle.exchange(src.view(dt).reshape(ishape), mode, w).view(np.uint8).ravel()
     got = np.frombuffer(xout, dtype=np.uint8)[mis:]
-    assert np.array_equal(got, want), (w, B, S, H, D, e, mode, chunked, path, mis)
+    assert np.array_equal(got, want), (w, B, S, H, D, e, mode, chunked, path, mis, blocks)
 print("asan-ok", len(cases))
 """
 
@@ -495,13 +495,19 @@ def test_emulated_kernels_under_asan(tmp_path):
         for mode in (0, 1):
             for chunked in (0, 1):
                 for path in (ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS):
-                    cases.append((*shape, mode, chunked, path, 0))
+                    cases.append((*shape, mode, chunked, path, 0, 0))
     for shape in [(3, 1, 5, 3, 7, 2), (4, 1, 40, 8, 128, 2), (2, 2, 9, 4, 64, 2)]:
         for mode in (0, 1):
             for path in (ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS):
-                cases.append((*shape, mode, 1, path, 2))
+                cases.append((*shape, mode, 1, path, 2, 0))
     for mode in (0, 1):      # more partial-chunk slots than lanes
-        cases.append((130, 2, 5, 260, 3, 2, mode, 0, ua.UA2A_PATH_LDS, 2))
+        cases.append((130, 2, 5, 260, 3, 2, mode, 0, ua.UA2A_PATH_LDS, 2, 0))
+    # capped flat grids: groups of four tiles per workgroup, partial groups, remainders
+    for shape in [(4, 3, 50, 8, 16, 2), (3, 2, 33, 12, 80, 4), (2, 2, 37, 2, 1024, 2)]:
+        for mode in (0, 1):
+            for chunked in (0, 1):
+                for blocks in (3, 7):
+                    cases.append((*shape, mode, chunked, ua.UA2A_PATH_DIRECT, 0, blocks))
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     script = tmp_path / "asan_driver.py"
     script.write_text(ASAN_DRIVER.format(root=root, lib=lib, cases=cases))

@@ -255,6 +255,25 @@ for (w, B, S, H, D, e, mode, first, count, mis) in {cases!r}:
     for k in range(w):
         got = np.frombuffer(xout[k], dtype=np.uint8)[mis:]
         assert np.array_equal(got, outs[k].view(np.uint8).ravel()), (w, B, S, H, D, e, mode, first, count, mis, k)
+    # pack by the sender range into exact-size windows, unpack the same range of receivers
+    wins = [(ctypes.c_uint8 * (n + mis))() for _ in range(w)]
+    wp = [ctypes.addressof(b) + mis for b in wins]
+    h = ctypes.c_void_p()
+    assert lib.ua2a_plan(ctypes.byref(h), w, B, S, H, D, e, 0, None, 0, 0) == 0
+    assert lib.ua2a_pack_ranks(h, mode, tab(ip), tab(wp), first, count, None) == 0
+    assert lib.ua2a_unpack_ranks(h, mode, tab(wp), tab(op), first, count, None) == 0
+    lib.ua2a_destroy(h)
+    wshape = (B, S * w, H // w, D)
+    want_w = [np.zeros(wshape, DT[e]) for _ in range(w)]
+    oracle.pack_ranks(xs, want_w, mode, first, count)
+    for q in range(w):
+        got = np.frombuffer(wins[q], dtype=np.uint8)[mis:]
+        assert np.array_equal(got, want_w[q].view(np.uint8).ravel()), ("pack", w, mode, first, count, mis, q)
+    want_o = [np.zeros(oshape, DT[e]) for _ in range(w)]
+    oracle.unpack_ranks(want_w, want_o, mode, first, count)
+    for q in range(first, first + count):
+        got = np.frombuffer(xout[q], dtype=np.uint8)[mis:]
+        assert np.array_equal(got, want_o[q].view(np.uint8).ravel()), ("unpack", w, mode, first, count, mis, q)
 print("asan-ok")
 """
 
