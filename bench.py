@@ -383,7 +383,7 @@ def run(args):
     if args.ranks is not None:
         kname = "ua2a_ranks_kernel"
     elif chunked and not per_plane:
-        kname = "ua2a_chunked_kernel"
+        kname = "ua2a_chunked_kernel" if dom_info["path"] == ua.UA2A_PATH_DIRECT else "ua2a_lds_chunked_kernel"
     elif dom_info["path"] == ua.UA2A_PATH_DIRECT:
         kname = "ua2a_direct3d_kernel" if dom_info["grid_dims"] == 3 else "ua2a_direct_kernel"
     else:
@@ -1008,7 +1008,7 @@ def main():
     ap.add_argument("--blocks", type=int, default=0, help="grid-size cap (0 = library default)")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload to time (default: the video-DiT exchange the metric is quoted on)")
-    ap.add_argument("--chunked", action="store_true", help="time the chunked (per-plane window) path")
+    ap.add_argument("--chunked", action="store_true", help="time the chunked exchange (through a window of one batch plane)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step as a HIP graph and time its replays")
     ap.add_argument("--ranks", choices=("all", "one"), default=None,

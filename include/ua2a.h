@@ -84,7 +84,8 @@ typedef struct ua2a_layout_s {
 #define UA2A_PATH_LDS     2  /* rows staged through LDS, both sides moved as contiguous spans */
 
 /* How a chunked exchange is launched (ua2a_launch_info_t.chunked_form). */
-#define UA2A_CHUNKED_ONE_LAUNCH  1  /* direct path, 3-D grid: one launch of the chunked kernel */
+#define UA2A_CHUNKED_ONE_LAUNCH  1  /* one launch of the chunked kernel (direct path, 3-D grid)
+                                       or of the chunked LDS kernel (LDS path) */
 #define UA2A_CHUNKED_PER_PLANE   2  /* per plane: a permute into the window, then a copy out */
 
 /* What an exchange would launch (ua2a_describe). */
@@ -148,9 +149,16 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               window.  On the direct path with its default 3-D grid the
  *               whole exchange is ONE launch: each workgroup owns one tile of
  *               the window and, plane after plane, writes the tile, reads it
- *               back and stores it to `out` (UA2A_CHUNKED_ONE_LAUNCH).
- *               Otherwise (LDS path, or a `blocks` cap) each plane is a
- *               permute launch and a copy launch (UA2A_CHUNKED_PER_PLANE).
+ *               back and stores it to `out` (UA2A_CHUNKED_ONE_LAUNCH).  On
+ *               the LDS path it is one launch too when `out` and the window
+ *               lie at the same offset modulo 16 bytes and a plane of one
+ *               rank (S_local*H*D*elem_bytes) is a multiple of 16: each
+ *               workgroup stages its tile of every plane in LDS, writes it to
+ *               the window, and after a workgroup barrier copies it to `out`.
+ *               Otherwise (a `blocks` cap on the direct path, the grouped
+ *               tile order, or an LDS-path call that does not meet those
+ *               conditions) each plane is a permute launch and a copy launch
+ *               (UA2A_CHUNKED_PER_PLANE).
  *               After the call the window holds plane B-1 of every rank, in
  *               `out`'s layout.  Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]

@@ -72,11 +72,31 @@ struct CheckedMem : PlainMem {
     }
 };
 
+// Window stores of the LDS path's one-launch chunked kernel (its drain):
+// recorded like CheckedMem::st_win, with the id of the running workgroup and
+// plane.  That workgroup reads its window spans back after a barrier, so any
+// of its lanes may read what another stored, but only in the same plane.
+struct CheckedWinMem : CheckedMem {
+    template <class T>
+    static void st(T* p, T v) { CheckedMem::st_win(p, v); }
+    template <class T>
+    static void st_tile(uint8_t* base, uint32_t nbytes, uint32_t off, T v)
+    {
+        if (off % sizeof(T) != 0 || static_cast<uint64_t>(off) + sizeof(T) > nbytes) {
+            fprintf(stderr, "emu: window tile store at %u (+%zu) outside its %u bytes\n", off, sizeof(T), nbytes);
+            abort();
+        }
+        CheckedMem::st_win(reinterpret_cast<T*>(base + off), v);
+    }
+    template <class T>
+    static void st_piece(T* p, T v) { CheckedMem::st_win(p, v); }
+};
+
 namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
 int g_launches = 0;           // launches since the last reset
-int g_kernel_counts[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+int g_kernel_counts[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 uint32_t g_last_grid = 0;
 long long g_tile_budget = -1;  // test hook: direct tiles left to run (< 0: all)
 bool g_stalled = false;        // a launch was cut short: later launches on the stream wait
@@ -219,6 +239,68 @@ void run_lds(const LdsGeom& g, const Bases& bases)
             fprintf(stderr, "emu: LDS tile %u never visited\n", t);
             abort();
         }
+}
+
+// The LDS path's one-launch chunked exchange: every launch slot's tile
+// through all planes -- fill for all lanes, drain into the window for all
+// lanes, then the read-back for all lanes (the two workgroup barriers), with
+// the window bytes' writers tracked per (tile, plane).
+template <int G, bool M1>
+void run_lds_chunked(const Launch& L)
+{
+    const LdsGeom& g = L.lds;
+    const LdsChunkGeom& c = L.lds_chunk;
+    g_win = M1 ? g.p_ptr : g.a_ptr;
+    g_win_bytes = static_cast<size_t>(g.w) * static_cast<size_t>(c.plane);
+    g_win_owner.assign(g_win_bytes, -1);
+    std::vector<uint8_t> lds(g.lds_bytes);
+    std::vector<uint8_t> seen(g.num_tiles, 0);
+    for (uint32_t slot = 0; slot < g.num_slots; ++slot) {
+        const uint32_t t = lds_slot_tile(g, slot);
+        if (t >= g.num_tiles) continue;
+        if (seen[t]++) {
+            fprintf(stderr, "emu: LDS tile %u visited twice\n", t);
+            abort();
+        }
+        for (uint32_t p = 0; p < c.planes; ++p) {
+            const int64_t off = static_cast<int64_t>(p) * c.plane;
+            const PlaneBases bases{g, M1 ? 0 : off, M1 ? off : 0};
+            const LdsTile d = lds_tile(g, bases, t);
+            g_lane_id = static_cast<int64_t>(t) * c.planes + p;
+            memset(lds.data(), 0xA5, lds.size());
+            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+                lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
+            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+                lds_drain<CheckedWinMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
+            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+                lds_readback<CheckedMem, G, M1, kLdsBlock, kLdsReadback>(g, bases, d, c, p, tid);
+        }
+    }
+    for (uint32_t t = 0; t < g.num_tiles; ++t)
+        if (!seen[t]) {
+            fprintf(stderr, "emu: LDS tile %u never visited\n", t);
+            abort();
+        }
+    for (size_t i = 0; i < g_win_bytes; ++i)
+        if (g_win_owner[i] < 0) {
+            fprintf(stderr, "emu: window byte %zu never written\n", i);
+            abort();
+        }
+    g_win = nullptr;
+    g_win_bytes = 0;
+}
+
+template <bool M1>
+int dispatch_lds_chunked(const Launch& L)
+{
+    switch (L.width) {
+    case 16: run_lds_chunked<16, M1>(L); return 0;
+    case 8: run_lds_chunked<8, M1>(L); return 0;
+    case 4: run_lds_chunked<4, M1>(L); return 0;
+    case 2: run_lds_chunked<2, M1>(L); return 0;
+    case 1: run_lds_chunked<1, M1>(L); return 0;
+    default: return 1;
+    }
 }
 
 template <int VB>
@@ -374,7 +456,8 @@ int backend_launch(const Launch& L, void*)
     if (g_stalled) return 0;       // queued behind an unfinished launch
     g_last_grid = L.grid;
     if (L.grid < 1) return 2;
-    const uint32_t want_block = (L.kernel == Kernel::Lds || L.kernel == Kernel::LdsRanks) ? kLdsBlock
+    const uint32_t want_block = (L.kernel == Kernel::Lds || L.kernel == Kernel::LdsRanks ||
+                                 L.kernel == Kernel::LdsChunked) ? kLdsBlock
                               : L.kernel == Kernel::Copy ? kCopyBlock
                               : (L.kernel == Kernel::Wait || L.kernel == Kernel::Signal) ? kWaitBlock
                               : kDirectBlock;
@@ -412,6 +495,21 @@ int backend_launch(const Launch& L, void*)
             return 3;
         return L.mode ? dispatch_lds<true>(L.lds, StackedBases{L.lds}, L.width)
                       : dispatch_lds<false>(L.lds, StackedBases{L.lds}, L.width);
+    case Kernel::LdsChunked: {
+        // plane 0 of every rank <-> the window (one plane of every rank), the
+        // output sharing the window's 16-byte chunks
+        const LdsGeom& g = L.lds;
+        const LdsChunkGeom& c = L.lds_chunk;
+        if (L.grid_y != 1 || L.grid_z != 1) return 7;
+        if (L.lds_bytes != g.lds_bytes || g.lds_bytes < 16 + g.rows_per_tile * g.lrow || g.lrow != g.row + g.pad ||
+            (g.pad && L.width != 16) || g.num_slots < g.num_tiles ||
+            (g.xlog && g.num_slots % (kXcds << g.xlog) != 0) || L.grid > g.num_slots || g.nb != 1 ||
+            g.p_plane != 0 || g.a_plane != 0 || c.planes < 1 || c.plane % 16 != 0 ||
+            (L.mode ? g.p_rank : g.a_rank) != c.plane ||
+            (reinterpret_cast<uintptr_t>(c.out) - reinterpret_cast<uintptr_t>(L.mode ? g.p_ptr : g.a_ptr)) % 16)
+            return 3;
+        return L.mode ? dispatch_lds_chunked<true>(L) : dispatch_lds_chunked<false>(L);
+    }
     case Kernel::LdsRanks:
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != L.lds.lds_bytes || L.lds.lds_bytes < 16 + L.lds.rows_per_tile * L.lds.lrow ||

@@ -210,21 +210,31 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
 def test_emulated_chunked_forms(emu, shape):
     """Chunked exchanges on the direct path's 3-D grid are one launch of the
     chunked kernel, in which every lane reads back only window bytes it
-    stored itself (the emulation tracks each window byte's last writer); a
-    blocks hint (flat grid), the grouped tile order and the LDS path run a
-    permute and a copy launch per plane.  Every form matches the oracle,
-    leaves the guard bands alone and ends with the last plane in the window."""
+    stored itself (the emulation tracks each window byte's last writer); on
+    the LDS path (aligned buffers, planes of whole 16-byte chunks) one launch
+    of the chunked LDS kernel, whose workgroups read back only window bytes
+    they stored in the same plane; a blocks hint (flat grid) and the grouped
+    tile order run a permute and a copy launch per plane.  Every form matches
+    the oracle, leaves the guard bands alone and ends with the last plane in
+    the window."""
     w, B, S, H, D, e = shape
+    assert (S * H * D * e) % 16 == 0
     for mode in (0, 1):
-        for path, blocks in ((ua.UA2A_PATH_DIRECT, 0), (ua.UA2A_PATH_DIRECT, 5), (ua.UA2A_PATH_LDS, 0)):
+        for path, blocks in ((ua.UA2A_PATH_DIRECT, 0), (ua.UA2A_PATH_DIRECT, 5), (ua.UA2A_PATH_LDS, 0),
+                             (ua.UA2A_PATH_LDS, 3)):
             x, y, info, bufs = emu_exchange(emu, shape, mode, True, path, blocks=blocks, seed=11 + mode)
             assert np.array_equal(y, oracle_bytes(x, shape, mode)), (mode, path, blocks)
             assert all(b.guards_intact() for b in bufs), (mode, path, blocks)
-            fused = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3
+            direct = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3
+            lds = info.path == ua.UA2A_PATH_LDS
+            fused = direct or lds
             assert info.chunked_form == (ua.UA2A_CHUNKED_ONE_LAUNCH if fused else ua.UA2A_CHUNKED_PER_PLANE)
             assert info.launches == (1 if fused else 2 * B), (mode, path, blocks)
-            assert emu.ua2a_emu_kernel_count(7) == (1 if fused else 0)
+            assert emu.ua2a_emu_kernel_count(7) == (1 if direct else 0)
+            assert emu.ua2a_emu_kernel_count(9) == (1 if lds else 0)
             assert emu.ua2a_emu_kernel_count(2) == (0 if fused else B)
+            if lds and blocks:
+                assert info.grid == blocks
             # the window holds the last plane of every rank, in the output's layout
             out = y.reshape(w, B, -1)
             assert np.array_equal(bufs[2].view.reshape(w, -1), out[:, B - 1]), (mode, path, blocks)
@@ -243,6 +253,45 @@ def test_emulated_chunked_one_launch_planes(emu, B, mis):
                                         seed=31 + B + mode)
         assert info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH and info.launches == 1
         assert info.vector_bytes == (16 if mis == 0 else mis)
+        assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
+        assert all(b.guards_intact() for b in bufs), mode
+        assert np.array_equal(bufs[2].view.reshape(w, -1), y.reshape(w, B, -1)[:, B - 1]), mode
+
+
+@pytest.mark.parametrize("shape,mis", [
+    ((3, 4, 8, 3, 7, 2), (0, 0, 0)),          # run 14 B: 2-byte pieces
+    ((3, 4, 8, 3, 7, 2), (2, 2, 2)),          # ... spans off the 16-byte grid: partial chunks
+    ((4, 3, 64, 4, 7, 2), (6, 6, 6)),         # line-aligned tiles, bases 6 bytes off
+    ((2, 5, 4, 6, 5, 4), (4, 4, 4)),          # run 60 B, 4-byte pieces
+    ((2, 3, 80, 2, 12, 2), (0, 0, 0)),        # run 24 B, spans of whole chunks
+    ((8, 2, 257, 8, 24, 2), (8, 8, 8)),       # run 48 B, 8-byte pieces, odd S_local
+    ((2, 9, 300, 4, 16, 2), (0, 0, 0)),       # run 64 B, 16-byte pieces, nine planes
+    ((3, 2, 16, 3, 5, 1), (3, 3, 3)),         # run 5 B: 1-byte pieces
+    ((130, 2, 8, 260, 3, 2), (2, 2, 2)),      # 2w partial-chunk slots > 256 lanes
+    ((3, 2, 16, 3, 5, 1), (0, 5, 5)),         # input off by 5, output and window agree
+    ((3, 4, 8, 3, 7, 2), (0, 0, 2)),          # window 2 bytes off the output: per plane
+    ((3, 4, 8, 3, 7, 2), (0, 4, 0)),          # output 4 bytes off the window: per plane
+    ((3, 3, 7, 3, 7, 2), (0, 0, 0)),          # plane 294 B, not whole chunks: per plane
+    ((4, 3, 61, 4, 7, 2), (6, 6, 6)),         # plane 3416 B: per plane
+    ((5, 2, 37, 10, 3, 1), (3, 3, 3)),        # plane 1110 B: per plane
+], ids=lambda v: "x".join(map(str, v)))
+def test_emulated_chunked_lds_one_launch(emu, shape, mis):
+    """The LDS path's chunked exchange is one launch when the window and the
+    output share their 16-byte chunks (same offset modulo 16, planes of whole
+    chunks), else a permute and a copy per plane; both match the oracle,
+    keep the guard bands and end with the last plane in the window.  In the
+    one-launch form the emulation checks that each workgroup reads back only
+    window bytes that it stored in the same plane, and that every window byte
+    is written."""
+    w, B, S, H, D, e = shape
+    plane = S * H * D * e
+    fused_expected = plane % 16 == 0 and (mis[1] - mis[2]) % 16 == 0
+    for mode in (0, 1):
+        x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_LDS, *mis, seed=41 + B + mode)
+        assert info.path == ua.UA2A_PATH_LDS, mode
+        assert info.chunked_form == (ua.UA2A_CHUNKED_ONE_LAUNCH if fused_expected
+                                     else ua.UA2A_CHUNKED_PER_PLANE), mode
+        assert emu.ua2a_emu_kernel_count(9) == (1 if fused_expected else 0), mode
         assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
         assert all(b.guards_intact() for b in bufs), mode
         assert np.array_equal(bufs[2].view.reshape(w, -1), y.reshape(w, B, -1)[:, B - 1]), mode
@@ -502,6 +551,12 @@ def test_emulated_kernels_under_asan(tmp_path):
                 cases.append((*shape, mode, 1, path, 2, 0))
     for mode in (0, 1):      # more partial-chunk slots than lanes
         cases.append((130, 2, 5, 260, 3, 2, mode, 0, ua.UA2A_PATH_LDS, 2, 0))
+    # the LDS path's one-launch chunked kernel: partial chunks, several planes, a capped grid
+    for shape in [(4, 3, 64, 4, 7, 2), (130, 2, 8, 260, 3, 2), (2, 5, 4, 6, 5, 4), (8, 2, 257, 8, 24, 2),
+                  (3, 2, 16, 3, 5, 1)]:
+        for mode in (0, 1):
+            for mis, blocks in ((0, 0), (2, 0), (0, 5)):
+                cases.append((*shape, mode, 1, ua.UA2A_PATH_LDS, mis - mis % shape[5], blocks))
     # capped flat grids: groups of four tiles per workgroup, partial groups, remainders
     for shape in [(4, 3, 50, 8, 16, 2), (3, 2, 33, 12, 80, 4), (2, 2, 37, 2, 1024, 2)]:
         for mode in (0, 1):

@@ -551,6 +551,138 @@ def test_chunked_exchange_in_one_launch(shape):
     plan.close()
 
 
+LDS_CHUNKED_SHAPES = [            # a plane of one rank is a multiple of 16 bytes in each
+    (3, 4, 8, 3, 7, "bf16"),          # run 14 B: 2-byte pieces
+    (4, 3, 64, 4, 7, "bf16"),         # run 14 B, line-aligned tiles
+    (2, 5, 4, 6, 5, "fp32"),          # run 60 B, 4-byte pieces
+    (2, 3, 80, 2, 12, "fp16"),        # run 24 B, spans of whole chunks
+    (8, 2, 257, 8, 24, "bf16"),       # run 48 B, 8-byte pieces, odd S_local
+    (2, 9, 300, 4, 16, "bf16"),       # run 64 B, 16-byte pieces, nine planes
+    (3, 2, 16, 3, 5, "u8"),           # run 5 B: 1-byte pieces
+    (130, 2, 8, 260, 3, "bf16"),      # more partial-chunk slots than lanes
+    (8, 4, 4096, 8, 32, "bf16"),      # run 64 B, 33 MB: thousands of tiles per plane
+    (4, 4, 20000, 4, 7, "bf16"),      # run 14 B, 9 MB
+]
+
+
+@pytest.mark.parametrize("mis", [0, 1], ids=["aligned", "offset"])
+@pytest.mark.parametrize("shape", LDS_CHUNKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_chunked_lds_in_one_launch(shape, mis):
+    """Chunked exchanges on the LDS path (runs under 128 B or off the 16-byte
+    grid; 16/8/4/2/1-byte pieces, 2-9 planes) run as one launch of the chunked
+    LDS kernel: each workgroup fills LDS from a plane of the input, drains it
+    into its window spans, and after a barrier copies them to that plane of
+    the output.  With `offset`, input, output and window all start one
+    element past a 256-byte boundary, so spans begin and end inside 16-byte
+    chunks (the one-launch form still applies: output and window agree modulo
+    16).  The output matches the oracle, and the window ends holding the last
+    plane of every rank in the output's layout."""
+    w, B, S, H, D, dtype = shape
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32, "u8": torch.uint8}[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    assert (S * H * D * e) % 16 == 0
+    n, wb = lay["tensor_elems"], lay["window_bytes"]
+    win = torch.full((wb + 512,), 0x5A, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=win[mis * e:mis * e + wb])
+    plan.set_path(ua.UA2A_PATH_LDS)
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 51 + mode)
+        want = oracle_out(x, mode, w)
+        xin = torch.zeros(n + 64, dtype=dt, device=DEV)
+        xin[mis:mis + n] = x.reshape(-1).to(DEV)
+        outbuf = poisoned((n + 64,), dt)
+        xi = xin[mis:mis + n].view(in_shape(w, B, S, H, D, mode))
+        yo = outbuf[mis:mis + n].view(plan.out_shape(mode))
+        info = plan.describe(xi, mode, True, out=yo)
+        assert info["path"] == ua.UA2A_PATH_LDS
+        assert info["launches"] == 1 and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
+        note(f"chunked lds one launch {shape} mis={mis} mode={mode} {info}")
+        plan.exchange(xi, mode, True, out=yo)
+        torch.cuda.synchronize()
+        assert_same_bits(yo, want, f"chunked lds one launch {shape} mis {mis} mode {mode}")
+        guard = bits(outbuf.cpu())
+        full = 255 if guard.dtype == torch.uint8 else POISON
+        assert (guard[:mis] == full).all() and (guard[mis + n:] == full).all()
+        wcpu = win.cpu()
+        last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+        assert torch.equal(wcpu[mis * e:mis * e + wb].reshape(w, -1), last), f"window {shape} {mode}"
+        assert (wcpu[:mis * e] == 0x5A).all() and (wcpu[mis * e + wb:] == 0x5A).all()
+    plan.close()
+
+
+def _random_lds_chunked_cases(n, seed):
+    """Seeded chunked exchanges of 2-9 planes on the LDS path, bases off the
+    16-byte grid: the window offset from the output by a multiple of 16
+    bytes (one launch) or not (a permute and a copy per plane)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in _random_chunked_cases(n, seed):
+        c.update(path="lds", mis_win=int(rng.choice([0, c["mis_out"] * c["e"], 2, 6])))
+        c["mis_win"] -= c["mis_win"] % c["e"]
+        cases.append(c)
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_lds_chunked_cases(24, 5151), ids=lambda c: (
+    f"w{c['w']}B{c['B']}S{c['S']}H{c['H']}D{c['D']}{c['name']}m{c['mode']}"
+    f"{c['mis_in']}{c['mis_out']}{c['mis_win']}"))
+def test_random_chunked_lds(case):
+    w, B, S, H, D, dt = case["w"], case["B"], case["S"], case["H"], case["D"], case["dt"]
+    n = w * B * S * H * D
+    mode, e = case["mode"], case["e"]
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    wb, mw = lay["window_bytes"], case["mis_win"]
+    window = torch.full((wb + 512,), 0x3C, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, window=window[mw:mw + wb])
+    plan.set_path(ua.UA2A_PATH_LDS)
+    x = make_tensor(in_shape(w, B, S, H, D, mode), case["name"], "bytes", n % 6007)
+    want = oracle_out(x, mode, w)
+    xin = torch.zeros(n + 8, dtype=dt, device=DEV)
+    xin[case["mis_in"]:case["mis_in"] + n] = x.reshape(-1).to(DEV)
+    outbuf = poisoned((n + 8,), dt)
+    xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
+    yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
+    info = plan.describe(xi, mode, True, out=yo)
+    same = (S * H * D * e) % 16 == 0 and (yo.data_ptr() - window.data_ptr() - mw) % 16 == 0
+    if info["path"] == ua.UA2A_PATH_LDS:
+        assert info["chunked_form"] == (ua.UA2A_CHUNKED_ONE_LAUNCH if same else ua.UA2A_CHUNKED_PER_PLANE)
+    note(f"random chunked lds {case} {info}")
+    plan.exchange(xi, mode, True, out=yo)
+    torch.cuda.synchronize()
+    assert_same_bits(yo, want, f"random chunked lds case {case}")
+    guard = bits(outbuf.cpu())
+    full = 255 if guard.dtype == torch.uint8 else POISON
+    assert (guard[:case["mis_out"]] == full).all() and (guard[case["mis_out"] + n:] == full).all()
+    wcpu = window.cpu()
+    assert (wcpu[:mw] == 0x3C).all() and (wcpu[mw + wb:] == 0x3C).all()
+    last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+    assert torch.equal(wcpu[mw:mw + wb].reshape(w, -1), last), f"window after {case}"
+    plan.close()
+
+
+def test_chunked_lds_full_size_run64():
+    """A 537 MB chunked exchange on the LDS path (64-byte runs, four planes of
+    134 MB, window larger than the on-package cache), both modes, against the
+    oracle at full size."""
+    w, B, S, H, D = 8, 4, 32768, 8, 32
+    lay = ua.ua2a_layout(w, B, S, H, D, 2)
+    win = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16, window=win)
+    for mode in (0, 1):
+        x = make_tensor(in_shape(w, B, S, H, D, mode), "bf16", "normal", 61 + mode)
+        want = oracle_out(x, mode, w)
+        xd = x.to(DEV)
+        info = plan.describe(xd, mode, True)
+        assert info["path"] == ua.UA2A_PATH_LDS and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
+        note(f"chunked lds full size mode={mode} {info}")
+        y = plan.exchange(xd, mode, True, out=poisoned(plan.out_shape(mode), torch.bfloat16))
+        torch.cuda.synchronize()
+        assert_same_bits(y, want, f"chunked lds full size mode {mode}")
+        del x, xd, y, want
+    plan.close()
+
+
 # ------------------------------------------------------------- argument checks
 
 def test_argument_checks_on_device_tensors():

@@ -434,6 +434,7 @@ struct LdsTile {
     uint32_t a_len;    // rows * run (each of the w A spans)
     uint32_t head;     // (p_ptr + p_start) mod 16: LDS position of the span's first byte
     uint32_t stride;   // chunk slots per A span in the flat (span, chunk) index
+    uint32_t j;        // P-side rank of the tile
     Div32 d_stride;
 };
 
@@ -443,6 +444,35 @@ struct StackedBases {
     const LdsGeom& g;
     UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return g.p_ptr + static_cast<int64_t>(j) * g.p_rank; }
     UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return g.a_ptr + static_cast<int64_t>(r) * g.a_rank; }
+};
+
+// Rank-stacked tensors with one side moved by a byte offset: a one-launch
+// chunked exchange on the LDS path reads batch plane p of its input (offset
+// p * plane on the input side) and writes the one-plane window (offset 0).
+struct PlaneBases {
+    static constexpr bool kStacked = true;
+    const LdsGeom& g;
+    int64_t p_off, a_off;
+    UA2A_HD uint8_t* p_rank_base(uint32_t j) const { return g.p_ptr + static_cast<int64_t>(j) * g.p_rank + p_off; }
+    UA2A_HD uint8_t* a_rank_base(uint32_t r) const { return g.a_ptr + static_cast<int64_t>(r) * g.a_rank + a_off; }
+};
+
+// A chunked exchange in one launch on the LDS path.  LdsGeom describes plane
+// 0 of every rank and the window ([w][one plane] in the layout of the output
+// side: the A side in mode 0, the P side in mode 1).  Each workgroup keeps
+// its LDS tile for all planes: per plane p it fills LDS from the input moved
+// by p * plane bytes, drains LDS into the tile's window spans, and, after a
+// workgroup barrier, copies those spans to plane p of the output.  Window
+// byte x of block k lands at out + x + k * rank_step + p * plane (block k is
+// head block r in mode 0, the tile's rank j in mode 1; rank_step = the
+// output's rank stride minus the window's, plane bytes).  The host takes
+// this form only when the window and the output agree modulo 16 and plane
+// is a multiple of 16, so a span has the same 16-byte chunks on both sides.
+struct LdsChunkGeom {
+    uint8_t* out;          // the output: plane 0 of rank 0
+    int64_t rank_step;     // B * plane - plane
+    int64_t plane;         // bytes of one batch plane of one rank
+    uint32_t planes;       // B
 };
 
 // Per-rank allocations: one base pointer per rank and side (the rank strides
@@ -500,6 +530,7 @@ UA2A_HD LdsTile lds_tile(const LdsGeom& g, const Bases& bases, uint32_t t)
     const bool full = rows == g.rows_per_tile;
     d.stride = full ? g.stride_full : g.stride_last;
     d.d_stride = full ? g.d_stride_full : g.d_stride_last;
+    d.j = j;
     return d;
 }
 
@@ -611,15 +642,27 @@ UA2A_HD void scatter_a_chunk(const LdsGeom& g, const LdsTile& d, uint32_t r, uin
 // Partial A-span chunk (the first or last of a span): move its in-span
 // G-byte pieces one by one.  achunk0 = the span's 16-aligned first chunk
 // in global memory, ahead = the span's offset inside it.
-template <int G>
+template <class Mem, int G>
 UA2A_HD void a_partial_from_lds(const LdsGeom& g, const LdsTile& d, uint32_t r, uint32_t lo,
                                 uint32_t ahead, const uint8_t* lds, uint8_t* achunk0)
 {
     typedef typename Piece<G>::T T;
     const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
     for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
-        *reinterpret_cast<T*>(achunk0 + x) =
-            *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead));
+        Mem::st_piece(reinterpret_cast<T*>(achunk0 + x),
+                      *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead)));
+}
+
+// Partial P-span chunk, LDS image -> global (the P span's first or last
+// chunk when its base is not 16-aligned): its in-span G-byte pieces.
+template <class Mem, int G>
+UA2A_HD void p_partial_from_lds(const uint8_t* lds, uint8_t* pchunk0, uint32_t lo, uint32_t head,
+                                uint32_t len)
+{
+    typedef typename Piece<G>::T T;
+    const uint32_t x1 = umin32(lo + 16, head + len);
+    for (uint32_t x = umax32(lo, head); x < x1; x += G)
+        Mem::st_piece(reinterpret_cast<T*>(pchunk0 + x), *reinterpret_cast<const T*>(lds + x));
 }
 
 // ------------------------------------------------------------------------

@@ -62,10 +62,12 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
 }
 
 // Everything one exchange launches.  A chunked exchange on the direct path
-// with its 3-D grid is one launch of the chunked kernel (`fused`: perm is
-// that launch).  Otherwise perm and copy describe plane 0 of a chunked
-// exchange, and plane p adds p * plane_bytes to the pointers named in
-// to_plane: B permutes into the window, each followed by a copy out.
+// with its 3-D grid is one launch of the chunked kernel, and on the LDS path
+// one launch of the chunked LDS kernel when the window and the output share
+// their 16-byte chunks (`fused`: perm is that launch).  Otherwise perm and
+// copy describe plane 0 of a chunked exchange, and plane p adds
+// p * plane_bytes to the pointers named in to_plane: B permutes into the
+// window, each followed by a copy out.
 struct Prepared {
     int32_t path;            // UA2A_PATH_DIRECT or UA2A_PATH_LDS
     int32_t chunked;
@@ -162,11 +164,12 @@ uint32_t lds_pad(const ua2a_plan_s* p, uint32_t G)
 // written in parts in mode 0 -- at least one row and within the largest tile
 // a workgroup may hold; 0 (no LDS path) if one row plus padding and the
 // alignment slack does not fit.
-uint32_t lds_rows(const ua2a_plan_s* p, int mode, uint32_t G)
+uint32_t lds_rows(const ua2a_plan_s* p, int mode, uint32_t G, bool chunked = false)
 {
     const int64_t row = p->layout.run_bytes * p->w + lds_pad(p, G);
     if (row + 16 > kLdsTileMax) return 0;
-    const int64_t target = mode == 0 ? kLdsTileMode0 : kLdsTileMode1;
+    const int64_t target = chunked ? (mode == 0 ? kLdsChunkTileMode0 : kLdsChunkTileMode1)
+                                   : (mode == 0 ? kLdsTileMode0 : kLdsTileMode1);
     int64_t rows = (target - 16) / row;
     int64_t g = p->layout.run_bytes, m = kLineBytes;
     while (m != 0) {
@@ -200,7 +203,8 @@ void set_lds_slots(LdsGeom* g)
 }
 
 LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uint8_t* a_ptr,
-                 int64_t p_rank, int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb)
+                 int64_t p_rank, int64_t p_plane, int64_t a_rank, int64_t a_plane, uint32_t nb,
+                 bool chunked = false)
 {
     LdsGeom g;
     memset(&g, 0, sizeof g);
@@ -215,7 +219,7 @@ LdsGeom make_lds(const ua2a_plan_s* p, int mode, uint32_t G, uint8_t* p_ptr, uin
     g.pad = lds_pad(p, G);
     g.lrow = g.row + g.pad;
     g.s_local = static_cast<uint32_t>(p->S_local);
-    g.rows_per_tile = lds_rows(p, mode, G);
+    g.rows_per_tile = lds_rows(p, mode, G, chunked);
     g.tiles_per_plane = (g.s_local + g.rows_per_tile - 1) / g.rows_per_tile;
     g.w = static_cast<uint32_t>(p->w);
     g.nb = nb;
@@ -407,6 +411,25 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     }
     pr->launches = 1;
     if (chunked) {
+        // LDS path in one launch when a span has the same 16-byte chunks in
+        // the window and in every plane of the output (and of the input):
+        // the output agrees with the window modulo 16, and a plane is a
+        // multiple of 16 bytes
+        const bool same_chunks =
+            plane % 16 == 0 &&
+            (reinterpret_cast<uintptr_t>(outb) - reinterpret_cast<uintptr_t>(window)) % 16 == 0;
+        if (L.kernel == Kernel::Lds && same_chunks) {
+            pr->fused = 1;
+            L.kernel = Kernel::LdsChunked;
+            L.lds = make_lds(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb, true);
+            L.lds_bytes = L.lds.lds_bytes;
+            L.grid = grid_for(L.lds.num_slots, p->blocks, kLdsBlock);
+            L.lds_chunk.out = outb;
+            L.lds_chunk.rank_step = rank_bytes - plane;
+            L.lds_chunk.plane = plane;
+            L.lds_chunk.planes = static_cast<uint32_t>(p->B);
+            return;
+        }
         if (L.kernel == Kernel::Direct && L.grid3d) {
             // one launch: every tile of the one-plane window moves through
             // all B planes (the 3-D grid's z coordinate is the window block)
@@ -1049,9 +1072,10 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     info->grid = static_cast<int64_t>(static_cast<uint64_t>(pr.perm.grid) * pr.perm.grid_y *
                                       pr.perm.grid_z);
     info->block = static_cast<int32_t>(pr.perm.block);
-    info->tiles = pr.perm.kernel == Kernel::Lds ? pr.perm.lds.num_tiles : pr.perm.direct.num_tiles;
+    const bool lds = pr.perm.kernel == Kernel::Lds || pr.perm.kernel == Kernel::LdsChunked;
+    info->tiles = lds ? pr.perm.lds.num_tiles : pr.perm.direct.num_tiles;
     info->launches = pr.launches;
-    info->lds_rows = pr.perm.kernel == Kernel::Lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
+    info->lds_rows = lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
     info->grid_dims = pr.perm.grid3d ? 3 : 1;
     info->chunked_form = !chunked ? 0 : pr.fused ? UA2A_CHUNKED_ONE_LAUNCH : UA2A_CHUNKED_PER_PLANE;
     return UA2A_OK;

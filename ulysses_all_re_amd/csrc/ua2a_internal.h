@@ -38,12 +38,16 @@ constexpr uint64_t kMaxGridWorkItems = (uint64_t(1) << 31);   // x extent of a l
 constexpr uint32_t kLdsTileMode0 = 8192;        // target LDS bytes per workgroup, mode 0
 constexpr uint32_t kLdsTileMode1 = 16384;       // target LDS bytes per workgroup, mode 1
 constexpr uint32_t kLdsTileMax = 65536;         // a tile holds at least one row, up to this
+constexpr uint32_t kLdsChunkTileMode0 = 8192;   // ... in a one-launch chunked exchange, mode 0
+constexpr uint32_t kLdsChunkTileMode1 = 8192;   // ... and mode 1 (half the unchunked tile: the
+                                                //   window spans in flight then stay within L2)
 constexpr int64_t kLineBytes = 128;             // cache line: LDS tiles align their A spans to it
 constexpr uint32_t kLdsXcdLog = 2;              // LDS tiles: 2^kLdsXcdLog consecutive tiles per XCD turn
+constexpr uint32_t kLdsReadback = 2;            // one-launch chunked LDS path: window chunks per lane in flight
 constexpr uint32_t kWaitBlock = 64;             // one wave polls (or signals) the counters
 
 enum class Kernel : int32_t { Direct = 0, Lds = 1, Copy = 2, Ranks = 3, Wait = 4, Signal = 5,
-                              LdsRanks = 6, Chunked = 7, Pack = 8 };
+                              LdsRanks = 6, Chunked = 7, Pack = 8, LdsChunked = 9 };
 
 // One kernel launch, fully described for the backend.
 struct Launch {
@@ -55,10 +59,11 @@ struct Launch {
     int32_t width;       // Direct/Copy/Ranks: bytes per lane vector; Lds: LDS piece bytes G
     int32_t mode;        // Direct/Lds/Ranks: 0 or 1
     uint32_t grid;       // workgroups along x
-    uint32_t lds_bytes;  // dynamic LDS (Lds kernel only)
+    uint32_t lds_bytes;  // dynamic LDS (the LDS kernels)
     DirectGeom direct;   // Direct; Chunked: plane 0 of every rank into the window
     ChunkedGeom chunk;   // Chunked: output, plane strides and plane count
-    LdsGeom lds;
+    LdsGeom lds;         // Lds, LdsRanks; LdsChunked: plane 0 of every rank and the window
+    LdsChunkGeom lds_chunk;   // LdsChunked: output, plane strides and plane count
     CopyGeom copy;
     RanksGeom ranks;
     PackGeom pack;       // Pack: blocks from the senders' tensors into the receivers' windows

@@ -20,9 +20,14 @@
 //    direct path: each workgroup owns one tile of the one-plane window and
 //    moves it through every batch plane (permute into the window, read back,
 //    store to the output).
-//  * ua2a_copy_kernel    -- strided block copy used by the chunked exchange
-//    on the LDS path (and with a capped grid) to move the one-plane window
-//    into the output after each plane's permutation launch.
+//  * ua2a_lds_chunked_kernel -- a whole chunked exchange in one launch on
+//    the LDS path: each workgroup keeps its LDS tile through every batch
+//    plane (fill from the input, drain into the window, barrier, copy the
+//    window spans to the output).
+//  * ua2a_copy_kernel    -- strided block copy used by the per-plane form of
+//    the chunked exchange (a capped grid, or window and output off each
+//    other's 16-byte grid on the LDS path) to move the one-plane window into
+//    the output after each plane's permutation launch.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
@@ -95,6 +100,27 @@ struct StreamMem {
     // bytes outside the span are mapped; they are never used, and only an
     // exchange's input, which nothing writes meanwhile, is read this way.
     __device__ static u32x4 ld_part(const u32x4* p, uint32_t, uint32_t) { return __builtin_nontemporal_load(p); }
+    // A span's partial first or last chunk is written piece by piece with
+    // plain stores (lines written partly through a buffer range and partly
+    // plainly measured 9-52 % slower).
+    template <class T>
+    __device__ static void st_piece(T* p, T v) { *p = v; }
+};
+
+// Window stores of a one-launch chunked exchange on the LDS path: the drain
+// writes the tile's window spans with the default cache policy, since the
+// workgroup reads them back right after the barrier that follows (the lines
+// stay in the XCD's L2 meanwhile).
+struct WinMem {
+    template <class T>
+    __device__ static void st(T* p, T v) { *p = v; }
+    template <class T>
+    __device__ static void st_tile(uint8_t* base, uint32_t, uint32_t off, T v)
+    {
+        *reinterpret_cast<T*>(base + off) = v;
+    }
+    template <class T>
+    __device__ static void st_piece(T* p, T v) { *p = v; }
 };
 
 // Kernel arguments up front.  A direct, copy or per-rank workgroup moves one
@@ -296,6 +322,36 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, Ld
     lds_tiles<G, MODE1>(g, StagedTableBases{tab, a_tab});
 }
 
+// A whole chunked exchange in one launch on the LDS path (see LdsChunkGeom):
+// each workgroup keeps its tile through all B planes -- fill LDS from plane p
+// of the input, drain it into the tile's window spans, and after a barrier
+// copy those spans to plane p of the output.  The barrier after the next
+// plane's fill orders this plane's window reads before the next drain
+// overwrites the spans; the one after the drain, the drain's LDS reads before
+// the next fill.
+template <int G, bool MODE1>
+__global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, LdsChunkGeom c)
+{
+    args_up_front(g);
+    asm volatile("" ::"s"(c.out), "s"(c.rank_step), "s"(c.plane), "s"(c.planes));
+    extern __shared__ u32x4 ua2a_lds_raw[];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
+    for (uint64_t slot = blockIdx.x; slot < g.num_slots; slot += gridDim.x) {
+        const uint32_t t = lds_slot_tile(g, static_cast<uint32_t>(slot));
+        if (t >= g.num_tiles) continue;      // the same for the whole workgroup
+        for (uint32_t p = 0; p < c.planes; ++p) {
+            const int64_t off = static_cast<int64_t>(p) * c.plane;
+            const PlaneBases bases{g, MODE1 ? 0 : off, MODE1 ? off : 0};     // the input side moves
+            const LdsTile d = lds_tile(g, bases, t);
+            lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
+            __syncthreads();
+            lds_drain<WinMem, G, MODE1, kLdsBlock>(g, bases, d, threadIdx.x, lds);
+            __syncthreads();   // the tile's window spans are whole; LDS is free for the next fill
+            lds_readback<StreamMem, G, MODE1, kLdsBlock, kLdsReadback>(g, bases, d, c, p, threadIdx.x);
+        }
+    }
+}
+
 // Per-rank allocations (pointer tables, sender range): one tile per
 // workgroup when the grid covers the slab grid, else each dimension loops.
 template <int VB, bool MODE1, bool TWO, bool PART>
@@ -417,6 +473,19 @@ const void* ranks_fn(int vb)
     }
 }
 
+template <bool MODE1>
+const void* lds_chunked_fn(int g)
+{
+    switch (g) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_lds_chunked_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_lds_chunked_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_lds_chunked_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_lds_chunked_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_lds_chunked_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
 const void* pack_fn(int vb)
 {
     switch (vb) {
@@ -505,6 +574,12 @@ int backend_launch(const Launch& L, void* stream)
     case Kernel::Lds:
         fn = L.mode ? lds_fn<true>(L.width) : lds_fn<false>(L.width);
         arg = &lg;
+        shmem = L.lds_bytes;
+        break;
+    case Kernel::LdsChunked:
+        fn = L.mode ? lds_chunked_fn<true>(L.width) : lds_chunked_fn<false>(L.width);
+        arg = &lg;
+        arg2 = const_cast<LdsChunkGeom*>(&L.lds_chunk);
         shmem = L.lds_bytes;
         break;
     case Kernel::LdsRanks:

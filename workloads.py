@@ -41,6 +41,10 @@ MEASURE = {
                       seed0=0, seed1=1, chunked=False),     # run 64 B, 537 MB per tensor
     "odd_run": dict(w=4, B=1, S_local=2097152, H=4, D=7, dtype="bf16", dist="normal",
                     seed0=0, seed1=1, chunked=False),       # run 14 B, 470 MB per tensor
+    # the short-run shape in four batch planes, for the chunked exchange on the LDS path
+    # (bench.py --chunked): window of one plane of every rank, 134 MB
+    "short_run_b4": dict(w=8, B=4, S_local=32768, H=8, D=32, dtype="bf16", dist="normal",
+                         seed0=0, seed1=1, chunked=True),   # run 64 B, 537 MB per tensor
 }
 
 # Shapes whose per-rank run (H/w * D elements) is not a multiple of 16 bytes,
