@@ -153,8 +153,9 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               the LDS path it is one launch too when `out` and the window
  *               lie at the same offset modulo 16 bytes and a plane of one
  *               rank (S_local*H*D*elem_bytes) is a multiple of 16: each
- *               workgroup stages its tile of every plane in LDS, writes it to
- *               the window, and after a workgroup barrier copies it to `out`.
+ *               workgroup stages its tile of every plane in LDS, and each
+ *               lane writes its chunks of the tile to the window, reads them
+ *               back and stores them to `out`.
  *               Otherwise (a `blocks` cap on the direct path, the grouped
  *               tile order, or an LDS-path call that does not meet those
  *               conditions) each plane is a permute launch and a copy launch

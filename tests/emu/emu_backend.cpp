@@ -72,26 +72,6 @@ struct CheckedMem : PlainMem {
     }
 };
 
-// Window stores of the LDS path's one-launch chunked kernel (its drain):
-// recorded like CheckedMem::st_win, with the id of the running workgroup and
-// plane.  That workgroup reads its window spans back after a barrier, so any
-// of its lanes may read what another stored, but only in the same plane.
-struct CheckedWinMem : CheckedMem {
-    template <class T>
-    static void st(T* p, T v) { CheckedMem::st_win(p, v); }
-    template <class T>
-    static void st_tile(uint8_t* base, uint32_t nbytes, uint32_t off, T v)
-    {
-        if (off % sizeof(T) != 0 || static_cast<uint64_t>(off) + sizeof(T) > nbytes) {
-            fprintf(stderr, "emu: window tile store at %u (+%zu) outside its %u bytes\n", off, sizeof(T), nbytes);
-            abort();
-        }
-        CheckedMem::st_win(reinterpret_cast<T*>(base + off), v);
-    }
-    template <class T>
-    static void st_piece(T* p, T v) { CheckedMem::st_win(p, v); }
-};
-
 namespace {
 int g_fail_next = 0;          // test hook: fail the next launch with this code
 int g_device = 0;             // device the emulation reports as current
@@ -242,9 +222,10 @@ void run_lds(const LdsGeom& g, const Bases& bases)
 }
 
 // The LDS path's one-launch chunked exchange: every launch slot's tile
-// through all planes -- fill for all lanes, drain into the window for all
-// lanes, then the read-back for all lanes (the two workgroup barriers), with
-// the window bytes' writers tracked per (tile, plane).
+// through all planes -- fill for all lanes (the workgroup barrier), then
+// each lane's drain through the window, with the window bytes' writers
+// tracked per (tile, plane, lane): a lane may read back only what it stored
+// in the same plane.
 template <int G, bool M1>
 void run_lds_chunked(const Launch& L)
 {
@@ -266,14 +247,14 @@ void run_lds_chunked(const Launch& L)
             const int64_t off = static_cast<int64_t>(p) * c.plane;
             const PlaneBases bases{g, M1 ? 0 : off, M1 ? off : 0};
             const LdsTile d = lds_tile(g, bases, t);
-            g_lane_id = static_cast<int64_t>(t) * c.planes + p;
             memset(lds.data(), 0xA5, lds.size());
             for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
                 lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
-            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-                lds_drain<CheckedWinMem, G, M1, kLdsBlock>(g, bases, d, tid, lds.data());
-            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-                lds_readback<CheckedMem, G, M1, kLdsBlock, kLdsReadback>(g, bases, d, c, p, tid);
+            for (uint32_t tid = 0; tid < kLdsBlock; ++tid) {
+                g_lane_id = (static_cast<int64_t>(t) * c.planes + p) * kLdsBlock + tid;
+                lds_drain_through_window<CheckedMem, G, M1, kLdsBlock, (M1 ? 1 : kLdsReadback)>(g, bases, d, c, p,
+                                                                                              tid, lds.data());
+            }
         }
     }
     for (uint32_t t = 0; t < g.num_tiles; ++t)

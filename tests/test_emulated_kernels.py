@@ -212,8 +212,8 @@ def test_emulated_chunked_forms(emu, shape):
     chunked kernel, in which every lane reads back only window bytes it
     stored itself (the emulation tracks each window byte's last writer); on
     the LDS path (aligned buffers, planes of whole 16-byte chunks) one launch
-    of the chunked LDS kernel, whose workgroups read back only window bytes
-    they stored in the same plane; a blocks hint (flat grid) and the grouped
+    of the chunked LDS kernel, whose lanes likewise read back only window
+    bytes they stored in the same plane; a blocks hint (flat grid) and the grouped
     tile order run a permute and a copy launch per plane.  Every form matches
     the oracle, leaves the guard bands alone and ends with the last plane in
     the window."""
@@ -280,7 +280,7 @@ def test_emulated_chunked_lds_one_launch(emu, shape, mis):
     output share their 16-byte chunks (same offset modulo 16, planes of whole
     chunks), else a permute and a copy per plane; both match the oracle,
     keep the guard bands and end with the last plane in the window.  In the
-    one-launch form the emulation checks that each workgroup reads back only
+    one-launch form the emulation checks that each lane reads back only
     window bytes that it stored in the same plane, and that every window byte
     is written."""
     w, B, S, H, D, e = shape

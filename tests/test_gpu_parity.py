@@ -570,9 +570,9 @@ LDS_CHUNKED_SHAPES = [            # a plane of one rank is a multiple of 16 byte
 def test_chunked_lds_in_one_launch(shape, mis):
     """Chunked exchanges on the LDS path (runs under 128 B or off the 16-byte
     grid; 16/8/4/2/1-byte pieces, 2-9 planes) run as one launch of the chunked
-    LDS kernel: each workgroup fills LDS from a plane of the input, drains it
-    into its window spans, and after a barrier copies them to that plane of
-    the output.  With `offset`, input, output and window all start one
+    LDS kernel: each workgroup fills LDS from a plane of the input, and each
+    lane stores its chunks of the tile's window spans, reads them back and
+    stores them to that plane of the output.  With `offset`, input, output and window all start one
     element past a 256-byte boundary, so spans begin and end inside 16-byte
     chunks (the one-launch form still applies: output and window agree modulo
     16).  The output matches the oracle, and the window ends holding the last

@@ -492,18 +492,21 @@ UA2A_HD void lds_drain(const LdsGeom& g, const Bases& bases, const LdsTile& d, u
     }
 }
 
-// One-launch chunked exchange on the LDS path, third phase of plane `p`
-// (after the workgroup barrier that follows lds_drain into the window): the
-// tile's window spans, written by any lane of the workgroup, are read back
-// and stored to plane p of the output (see LdsChunkGeom).  A span has the
-// same 16-byte chunks in the window and the output, so whole chunks move as
-// 16-byte vectors, U per lane loaded before any is stored, and a partial
-// first or last chunk as its in-span G-byte pieces.
-//   mode 0: the w A spans (window block r = head block r);
-//   mode 1: the P span (window block j = the tile's rank).
+// One-launch chunked exchange on the LDS path, second phase of plane `p`
+// (after the workgroup barrier that follows lds_fill): LDS image -> the
+// tile's window spans -> plane p of the output (see LdsChunkGeom).  Each lane
+// stores its chunks of the spans into the window, reads them back and stores
+// them to the output, U chunks at a time; the same lane handles the same
+// chunks in every plane, so a lane reads back only what it stored itself and
+// the window needs no barrier.  A span has the same 16-byte chunks in the
+// window and the output, so whole chunks move as 16-byte vectors and a
+// partial first or last chunk as its in-span G-byte pieces.
+//   mode 0: the w A spans (window block r = head block r), gathered from
+//           the image as lds_drain does;
+//   mode 1: the P span (window block j = the tile's rank), copied out of it.
 template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases>
-UA2A_HD void lds_readback(const LdsGeom& g, const Bases& bases, const LdsTile& d, const LdsChunkGeom& c,
-                          uint32_t p, uint32_t tid)
+UA2A_HD void lds_drain_through_window(const LdsGeom& g, const Bases& bases, const LdsTile& d,
+                                      const LdsChunkGeom& c, uint32_t p, uint32_t tid, const uint8_t* lds)
 {
     typedef typename Piece<G>::T T;
     // window -> output, for block 0 of plane p (plus rank_step per block)
@@ -514,58 +517,75 @@ UA2A_HD void lds_readback(const LdsGeom& g, const Bases& bases, const LdsTile& d
         const uint32_t stride = d.stride;
         const uint32_t total = g.w * stride;
         for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
-            u32x4 v[U];
+            u32x4 v[U] = {};
+            uint8_t* win[U];
             uint8_t* to[U];
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k) {
-                to[k] = nullptr;
+                win[k] = to[k] = nullptr;
                 const uint32_t i = i0 + k * BS;
                 if (i >= total) continue;
                 const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t ci = i - r * stride;
-                const uint8_t* wspan = bases.a_rank_base(r) + d.a_start0;
+                uint8_t* wspan = bases.a_rank_base(r) + d.a_start0;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wspan) & 15u);
                 if (ci >= span_chunks(ahead, d.a_len)) continue;
-                const uint8_t* wchunk0 = wspan - ahead;
+                uint8_t* wchunk0 = wspan - ahead;
                 uint8_t* ochunk0 = reinterpret_cast<uint8_t*>(
                     reinterpret_cast<uintptr_t>(wchunk0) + shift + static_cast<int64_t>(r) * c.rank_step);
                 const uint32_t lo = ci * 16;
                 if (chunk_full(lo, ahead, d.a_len)) {
-                    v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(wchunk0 + lo));
+                    win[k] = wchunk0 + lo;
                     to[k] = ochunk0 + lo;
+                    Mem::st_win(reinterpret_cast<u32x4*>(win[k]), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
                 } else {
                     const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
-                    for (uint32_t x = umax32(lo, ahead); x < x1; x += G)
-                        Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x),
-                                      Mem::ld_win(reinterpret_cast<const T*>(wchunk0 + x)));
+                    for (uint32_t x = umax32(lo, ahead); x < x1; x += G) {
+                        T* const wp = reinterpret_cast<T*>(wchunk0 + x);
+                        Mem::st_win(wp, *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead)));
+                        Mem::win_order();
+                        Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x), Mem::ld_win(wp));
+                    }
                 }
             }
+            Mem::win_order();
+#pragma unroll
+            for (uint32_t k = 0; k < U; ++k)
+                if (win[k] != nullptr) v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(win[k]));
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k)
                 if (to[k] != nullptr) Mem::st(reinterpret_cast<u32x4*>(to[k]), v[k]);
         }
     } else {
-        const uint8_t* wchunk0 = d.p_span - d.head;
+        uint8_t* wchunk0 = d.p_span - d.head;
         uint8_t* ochunk0 = reinterpret_cast<uint8_t*>(
             reinterpret_cast<uintptr_t>(wchunk0) + shift + static_cast<int64_t>(d.j) * c.rank_step);
         const uint32_t pch = span_chunks(d.head, d.p_len);
         for (uint32_t c0 = tid; c0 < pch; c0 += BS * U) {
-            u32x4 v[U];
+            u32x4 v[U] = {};
             bool full[U];
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k) {
                 const uint32_t ci = c0 + k * BS;
-                full[k] = ci < pch && chunk_full(ci * 16, d.head, d.p_len);
+                const uint32_t lo = ci * 16;
+                full[k] = ci < pch && chunk_full(lo, d.head, d.p_len);
                 if (full[k]) {
-                    v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(wchunk0 + ci * 16));
+                    Mem::st_win(reinterpret_cast<u32x4*>(wchunk0 + lo),
+                                *reinterpret_cast<const u32x4*>(lds + lds_pos_of_p(g, lo)));
                 } else if (ci < pch) {
-                    const uint32_t lo = ci * 16;
                     const uint32_t x1 = umin32(lo + 16, d.head + d.p_len);
-                    for (uint32_t x = umax32(lo, d.head); x < x1; x += G)
-                        Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x),
-                                      Mem::ld_win(reinterpret_cast<const T*>(wchunk0 + x)));
+                    for (uint32_t x = umax32(lo, d.head); x < x1; x += G) {
+                        T* const wp = reinterpret_cast<T*>(wchunk0 + x);
+                        Mem::st_win(wp, *reinterpret_cast<const T*>(lds + x));
+                        Mem::win_order();
+                        Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x), Mem::ld_win(wp));
+                    }
                 }
             }
+            Mem::win_order();
+#pragma unroll
+            for (uint32_t k = 0; k < U; ++k)
+                if (full[k]) v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(wchunk0 + (c0 + k * BS) * 16));
 #pragma unroll
             for (uint32_t k = 0; k < U; ++k)
                 if (full[k]) Mem::st_tile(ochunk0, pch * 16, (c0 + k * BS) * 16, v[k]);

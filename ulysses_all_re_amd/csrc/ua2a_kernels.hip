@@ -107,22 +107,6 @@ struct StreamMem {
     __device__ static void st_piece(T* p, T v) { *p = v; }
 };
 
-// Window stores of a one-launch chunked exchange on the LDS path: the drain
-// writes the tile's window spans with the default cache policy, since the
-// workgroup reads them back right after the barrier that follows (the lines
-// stay in the XCD's L2 meanwhile).
-struct WinMem {
-    template <class T>
-    __device__ static void st(T* p, T v) { *p = v; }
-    template <class T>
-    __device__ static void st_tile(uint8_t* base, uint32_t, uint32_t off, T v)
-    {
-        *reinterpret_cast<T*>(base + off) = v;
-    }
-    template <class T>
-    __device__ static void st_piece(T* p, T v) { *p = v; }
-};
-
 // Kernel arguments up front.  A direct, copy or per-rank workgroup moves one
 // 1 KiB tile, so how soon its first load leaves decides much of its life.
 // Left alone, the compiler loads each argument field where it is first used:
@@ -324,11 +308,11 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, Ld
 
 // A whole chunked exchange in one launch on the LDS path (see LdsChunkGeom):
 // each workgroup keeps its tile through all B planes -- fill LDS from plane p
-// of the input, drain it into the tile's window spans, and after a barrier
-// copy those spans to plane p of the output.  The barrier after the next
-// plane's fill orders this plane's window reads before the next drain
-// overwrites the spans; the one after the drain, the drain's LDS reads before
-// the next fill.
+// of the input, then every lane stores its chunks of the tile's window spans,
+// reads them back and stores them to plane p of the output.  A lane reads
+// back only window bytes that it stored, so the window needs no barrier; the
+// barrier after the drain keeps the next plane's fill from overwriting LDS
+// that a lane still reads.
 template <int G, bool MODE1>
 __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, LdsChunkGeom c)
 {
@@ -345,9 +329,9 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, 
             const LdsTile d = lds_tile(g, bases, t);
             lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
             __syncthreads();
-            lds_drain<WinMem, G, MODE1, kLdsBlock>(g, bases, d, threadIdx.x, lds);
-            __syncthreads();   // the tile's window spans are whole; LDS is free for the next fill
-            lds_readback<StreamMem, G, MODE1, kLdsBlock, kLdsReadback>(g, bases, d, c, p, threadIdx.x);
+            lds_drain_through_window<StreamMem, G, MODE1, kLdsBlock, (MODE1 ? 1 : kLdsReadback)>(
+                g, bases, d, c, p, threadIdx.x, lds);
+            __syncthreads();   // the next fill overwrites the LDS image
         }
     }
 }
