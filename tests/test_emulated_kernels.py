@@ -269,6 +269,7 @@ def test_emulated_chunked_one_launch_planes(emu, B, mis):
     ((3, 2, 16, 3, 5, 1), (3, 3, 3)),         # run 5 B: 1-byte pieces
     ((130, 2, 8, 260, 3, 2), (2, 2, 2)),      # 2w partial-chunk slots > 256 lanes
     ((3, 2, 16, 3, 5, 1), (0, 5, 5)),         # input off by 5, output and window agree
+    ((1, 3, 8, 4, 7, 2), (0, 2, 2)),          # w = 1: one head block, window = one plane
     ((3, 4, 8, 3, 7, 2), (0, 0, 2)),          # window 2 bytes off the output: per plane
     ((3, 4, 8, 3, 7, 2), (0, 4, 0)),          # output 4 bytes off the window: per plane
     ((3, 3, 7, 3, 7, 2), (0, 0, 0)),          # plane 294 B, not whole chunks: per plane

@@ -560,6 +560,7 @@ LDS_CHUNKED_SHAPES = [            # a plane of one rank is a multiple of 16 byte
     (2, 9, 300, 4, 16, "bf16"),       # run 64 B, 16-byte pieces, nine planes
     (3, 2, 16, 3, 5, "u8"),           # run 5 B: 1-byte pieces
     (130, 2, 8, 260, 3, "bf16"),      # more partial-chunk slots than lanes
+    (1, 3, 8, 4, 7, "bf16"),          # w = 1
     (8, 4, 4096, 8, 32, "bf16"),      # run 64 B, 33 MB: thousands of tiles per plane
     (4, 4, 20000, 4, 7, "bf16"),      # run 14 B, 9 MB
 ]
