@@ -684,6 +684,65 @@ def test_chunked_lds_full_size_run64():
     plan.close()
 
 
+def _wide_cases(n, seed):
+    """A wide seeded sweep of small exchanges (at most ~4 MB per tensor): every
+    element size, 1-12 ranks, 1-6 planes, runs from 1 byte up, all paths, both
+    modes, chunked or not, grid caps, and input, output and window bases off
+    the 16-byte grid by independent amounts."""
+    rng = np.random.default_rng(seed)
+    dts = [("u8", torch.uint8), ("bf16", torch.bfloat16), ("fp32", torch.float32), ("f64", torch.float64)]
+    cases = []
+    for _ in range(n):
+        name, dt = dts[int(rng.integers(0, len(dts)))]
+        e = torch.empty((), dtype=dt).element_size()
+        w, hl = int(rng.integers(1, 13)), int(rng.integers(1, 7))
+        B, D = int(rng.integers(1, 7)), int(rng.integers(1, 161))
+        S = max(1, min(int(rng.integers(1, 2000)), (4 << 20) // (w * B * w * hl * D * e)))
+        cases.append(dict(w=w, B=B, S=S, H=w * hl, D=D, name=name, dt=dt, e=e,
+                          mode=int(rng.integers(0, 2)), chunked=bool(rng.integers(0, 2)),
+                          path=["auto", "direct", "lds"][int(rng.integers(0, 3))],
+                          blocks=[0, 0, 0, 7, 300][int(rng.integers(0, 5))],
+                          mis_in=int(rng.integers(0, 4)), mis_out=int(rng.integers(0, 4)),
+                          mis_win=int(rng.integers(0, 4)) * e))
+    return cases
+
+
+@pytest.mark.parametrize("case", _wide_cases(160, 777), ids=lambda c: (
+    f"w{c['w']}B{c['B']}S{c['S']}H{c['H']}D{c['D']}{c['name']}m{c['mode']}"
+    f"{'c' if c['chunked'] else ''}{c['path']}b{c['blocks']}-{c['mis_in']}{c['mis_out']}{c['mis_win']}"))
+def test_wide_random_sweep(case):
+    """Each case against the oracle, with the output's guard band, and (chunked)
+    the window's guard band and its last plane."""
+    w, B, S, H, D, dt, e = case["w"], case["B"], case["S"], case["H"], case["D"], case["dt"], case["e"]
+    n = w * B * S * H * D
+    mode, chunked = case["mode"], case["chunked"]
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    wb, mw = lay["window_bytes"], case["mis_win"]
+    window = torch.full((wb + 256,), 0x3C, dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, blocks=case["blocks"], window=window[mw:mw + wb])
+    plan.set_path(PATHS[case["path"]])
+    x = make_tensor(in_shape(w, B, S, H, D, mode), case["name"], "bytes", n % 8191)
+    want = oracle_out(x, mode, w)
+    xin = torch.zeros(n + 8, dtype=dt, device=DEV)
+    xin[case["mis_in"]:case["mis_in"] + n] = x.reshape(-1).to(DEV)
+    outbuf = poisoned((n + 8,), dt)
+    xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
+    yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
+    note(f"wide {case} {plan.describe(xi, mode, chunked, out=yo)}")
+    plan.exchange(xi, mode, chunked, out=yo)
+    torch.cuda.synchronize()
+    assert_same_bits(yo, want, f"wide case {case}")
+    guard = bits(outbuf.cpu())
+    full = 255 if guard.dtype == torch.uint8 else POISON
+    assert (guard[:case["mis_out"]] == full).all() and (guard[case["mis_out"] + n:] == full).all()
+    wcpu = window.cpu()
+    assert (wcpu[:mw] == 0x3C).all() and (wcpu[mw + wb:] == 0x3C).all()
+    if chunked:
+        last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+        assert torch.equal(wcpu[mw:mw + wb].reshape(w, -1), last), f"window after {case}"
+    plan.close()
+
+
 # ------------------------------------------------------------- argument checks
 
 def test_argument_checks_on_device_tensors():
