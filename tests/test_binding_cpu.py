@@ -1,5 +1,6 @@
-"""The Python binding's host side that needs no GPU: a bound per-rank call
-keeps its plan alive and refuses to run once the plan is closed."""
+"""The Python binding's host side that needs no GPU: a bound call (per-rank
+or rank-stacked) keeps its plan alive and refuses to run once the plan is
+closed."""
 from __future__ import annotations
 
 import gc
@@ -45,3 +46,38 @@ def test_bound_call_after_close_raises():
     with pytest.raises(ua.UA2AError) as e:
         call()
     assert e.value.code == ua.UA2A_ERR_INVALID_ARG and "closed" in str(e.value)
+
+
+def _bound_stacked(plan):
+    x = torch.zeros(plan.in_shape(1), dtype=plan.dtype)
+    out = torch.zeros(plan.out_shape(1), dtype=plan.dtype)
+    return plan.bind(x, 1, out=out, stream=types.SimpleNamespace(cuda_stream=0))
+
+
+def test_bound_exchange_keeps_its_plan_alive():
+    call = _bound_stacked(_host_plan())
+    gc.collect()
+    assert call.plan.handle and call.out.shape == call.plan.out_shape(1)
+    call.plan.close()
+
+
+def test_bound_exchange_after_close_raises():
+    plan = _host_plan()
+    call = _bound_stacked(plan)
+    plan.close()
+    with pytest.raises(ua.UA2AError) as e:
+        call()
+    assert e.value.code == ua.UA2A_ERR_INVALID_ARG and "closed" in str(e.value)
+
+
+def test_bind_checks_like_exchange():
+    plan = _host_plan()
+    with pytest.raises(ValueError):
+        plan.bind(torch.zeros((1, 2, 3), dtype=plan.dtype), 0, out=torch.zeros(plan.out_shape(0), dtype=plan.dtype),
+                  stream=types.SimpleNamespace(cuda_stream=0))
+    x = torch.zeros(plan.in_shape(0), dtype=plan.dtype)
+    with pytest.raises(ua.UA2AError) as e:       # chunked with no window: the library's own check
+        plan.bind(x, 0, True, out=torch.zeros(plan.out_shape(0), dtype=plan.dtype),
+                  stream=types.SimpleNamespace(cuda_stream=0))
+    assert e.value.code == ua.UA2A_ERR_CAPACITY
+    plan.close()

@@ -743,6 +743,34 @@ def test_wide_random_sweep(case):
     plan.close()
 
 
+@pytest.mark.parametrize("shape,chunked", [((2, 1, 8, 4, 16, "bf16"), False), ((4, 3, 64, 4, 7, "bf16"), True),
+                                           ((4, 4, 32, 16, 64, "fp16"), True)], ids=["tiny", "lds-chunked", "chunked"])
+def test_bound_exchange_repeats_the_call(shape, chunked):
+    """Plan.bind checks a call once and returns a function that re-issues it:
+    new bytes written into the bound input between calls come out exchanged,
+    three times in a row, in both modes."""
+    w, B, S, H, D, dtype = shape
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    win = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV) if chunked else None
+    plan = ua.Plan(w, B, S, H, D, dt, window=win)
+    for mode in (0, 1):
+        xd = torch.empty(in_shape(w, B, S, H, D, mode), dtype=dt, device=DEV)
+        call = plan.bind(xd, mode, chunked)
+        for rep in range(3):
+            x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 70 + 2 * rep + mode)
+            xd.copy_(x.to(DEV))
+            call.out.view(BITS_VIEW[e]).fill_(-1)
+            note(f"bound {shape} chunked={chunked} mode={mode} rep={rep}")
+            call()
+            torch.cuda.synchronize()
+            assert_same_bits(call.out, oracle_out(x, mode, w), f"bound {shape} mode {mode} rep {rep}")
+    plan.close()
+    with pytest.raises(ua.UA2AError):
+        call()
+
+
 # ------------------------------------------------------------- argument checks
 
 def test_argument_checks_on_device_tensors():

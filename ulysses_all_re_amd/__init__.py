@@ -456,6 +456,41 @@ class Plan:
                         [None if o is None else o.data_ptr() for o in outs], first, count, stream.cuda_stream)
         return outs
 
+    def bind(self, x, mode: int, chunked: bool = False, out=None, stream=None):
+        """Check exchange(x, mode, chunked, out) once (nothing is launched) and
+        return a no-argument function that issues it on the current device --
+        the same tensors and stream every time -- for loops of small exchanges
+        where the per-call checks of exchange() cost more than the launch.  The
+        function keeps the tensors and this plan alive, reads the plan's handle
+        at every call, and raises UA2AError (invalid argument) once the plan is
+        closed; `call.out` is the output tensor."""
+        import torch
+        self._check(x, self.in_shape(mode), "input")
+        if out is None:
+            out = torch.empty(self.out_shape(mode), dtype=self.dtype, device=self.device)
+        else:
+            self._check(out, self.out_shape(mode), "output")
+        self.describe(x, mode, chunked, out=out)          # the library's own checks
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        fn = load_library().ua2a_exchange
+        xptr, optr, sptr = x.data_ptr(), out.data_ptr(), stream.cuda_stream or None
+        ck = int(chunked)
+        plan = self
+
+        def call():
+            handle = plan.handle
+            if not handle:
+                raise UA2AError(UA2A_ERR_INVALID_ARG, "ua2a_exchange", "the plan is closed")
+            rc = fn(handle, mode, ck, xptr, optr, sptr)
+            if rc != UA2A_OK:
+                raise UA2AError(rc, "ua2a_exchange", ua2a_plan_last_error(handle))
+
+        call.tensors = (x, out)
+        call.out = out
+        call.plan = plan
+        return call
+
     def bind_ranks(self, xs, mode: int, outs, first: int = 0, count=None, stream=None):
         """Check a per-rank call once (nothing is launched) and return a
         no-argument function that issues it on the current device -- the same
