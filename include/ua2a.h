@@ -150,16 +150,12 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               whole exchange is ONE launch: each workgroup owns one tile of
  *               the window and, plane after plane, writes the tile, reads it
  *               back and stores it to `out` (UA2A_CHUNKED_ONE_LAUNCH).  On
- *               the LDS path it is one launch too when `out` and the window
- *               lie at the same offset modulo 16 bytes and a plane of one
- *               rank (S_local*H*D*elem_bytes) is a multiple of 16: each
- *               workgroup stages its tile of every plane in LDS, and each
- *               lane writes its chunks of the tile to the window, reads them
- *               back and stores them to `out`.
- *               Otherwise (a `blocks` cap on the direct path, the grouped
- *               tile order, or an LDS-path call that does not meet those
- *               conditions) each plane is a permute launch and a copy launch
- *               (UA2A_CHUNKED_PER_PLANE).
+ *               the LDS path it is one launch too: each workgroup stages its
+ *               tile of every plane in LDS, and each lane writes its chunks
+ *               of the tile to the window, reads them back and stores them
+ *               to `out`.  Otherwise (a `blocks` cap or the grouped tile
+ *               order on the direct path) each plane is a permute launch and
+ *               a copy launch (UA2A_CHUNKED_PER_PLANE).
  *               After the call the window holds plane B-1 of every rank, in
  *               `out`'s layout.  Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]

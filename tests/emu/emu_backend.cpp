@@ -477,17 +477,18 @@ int backend_launch(const Launch& L, void*)
         return L.mode ? dispatch_lds<true>(L.lds, StackedBases{L.lds}, L.width)
                       : dispatch_lds<false>(L.lds, StackedBases{L.lds}, L.width);
     case Kernel::LdsChunked: {
-        // plane 0 of every rank <-> the window (one plane of every rank), the
-        // output sharing the window's 16-byte chunks
+        // plane 0 of every rank <-> the window (one plane of every rank); every
+        // window -> output offset a multiple of the piece size
         const LdsGeom& g = L.lds;
         const LdsChunkGeom& c = L.lds_chunk;
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
         if (L.lds_bytes != g.lds_bytes || g.lds_bytes < 16 + g.rows_per_tile * g.lrow || g.lrow != g.row + g.pad ||
             (g.pad && L.width != 16) || g.num_slots < g.num_tiles ||
             (g.xlog && g.num_slots % (kXcds << g.xlog) != 0) || L.grid > g.num_slots || g.nb != 1 ||
-            g.p_plane != 0 || g.a_plane != 0 || c.planes < 1 || c.plane % 16 != 0 ||
+            g.p_plane != 0 || g.a_plane != 0 || c.planes < 1 || c.plane % L.width != 0 ||
             (L.mode ? g.p_rank : g.a_rank) != c.plane ||
-            (reinterpret_cast<uintptr_t>(c.out) - reinterpret_cast<uintptr_t>(L.mode ? g.p_ptr : g.a_ptr)) % 16)
+            (reinterpret_cast<uintptr_t>(c.out) - reinterpret_cast<uintptr_t>(L.mode ? g.p_ptr : g.a_ptr)) %
+                static_cast<uintptr_t>(L.width))
             return 3;
         return L.mode ? dispatch_lds_chunked<true>(L) : dispatch_lds_chunked<false>(L);
     }

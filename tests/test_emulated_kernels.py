@@ -270,29 +270,27 @@ def test_emulated_chunked_one_launch_planes(emu, B, mis):
     ((130, 2, 8, 260, 3, 2), (2, 2, 2)),      # 2w partial-chunk slots > 256 lanes
     ((3, 2, 16, 3, 5, 1), (0, 5, 5)),         # input off by 5, output and window agree
     ((1, 3, 8, 4, 7, 2), (0, 2, 2)),          # w = 1: one head block, window = one plane
-    ((3, 4, 8, 3, 7, 2), (0, 0, 2)),          # window 2 bytes off the output: per plane
-    ((3, 4, 8, 3, 7, 2), (0, 4, 0)),          # output 4 bytes off the window: per plane
-    ((3, 3, 7, 3, 7, 2), (0, 0, 0)),          # plane 294 B, not whole chunks: per plane
-    ((4, 3, 61, 4, 7, 2), (6, 6, 6)),         # plane 3416 B: per plane
-    ((5, 2, 37, 10, 3, 1), (3, 3, 3)),        # plane 1110 B: per plane
+    ((3, 4, 8, 3, 7, 2), (0, 0, 2)),          # window 2 bytes off the output: pieces out
+    ((3, 4, 8, 3, 7, 2), (0, 4, 0)),          # output 4 bytes off the window: pieces out
+    ((3, 3, 7, 3, 7, 2), (0, 0, 0)),          # plane 294 B: the output's offset moves per plane
+    ((4, 3, 61, 4, 7, 2), (6, 6, 6)),         # plane 3416 B, bases 6 bytes off
+    ((5, 2, 37, 10, 3, 1), (3, 3, 3)),        # plane 1110 B, 1-byte pieces
+    ((2, 5, 3, 6, 5, 4), (4, 8, 12)),         # run 60 B, plane 360 B, three different offsets
 ], ids=lambda v: "x".join(map(str, v)))
 def test_emulated_chunked_lds_one_launch(emu, shape, mis):
-    """The LDS path's chunked exchange is one launch when the window and the
-    output share their 16-byte chunks (same offset modulo 16, planes of whole
-    chunks), else a permute and a copy per plane; both match the oracle,
-    keep the guard bands and end with the last plane in the window.  In the
-    one-launch form the emulation checks that each lane reads back only
-    window bytes that it stored in the same plane, and that every window byte
-    is written."""
+    """The LDS path's chunked exchange is one launch of the chunked LDS
+    kernel whatever the bases' offsets and the plane size: window chunks go to
+    the output as whole 16-byte stores where the output lies at the window's
+    offset modulo 16, else as pieces.  It matches the oracle, keeps the guard
+    bands and ends with the last plane in the window; the emulation checks
+    that each lane reads back only window bytes that it stored in the same
+    plane, and that every window byte is written."""
     w, B, S, H, D, e = shape
-    plane = S * H * D * e
-    fused_expected = plane % 16 == 0 and (mis[1] - mis[2]) % 16 == 0
     for mode in (0, 1):
         x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_LDS, *mis, seed=41 + B + mode)
         assert info.path == ua.UA2A_PATH_LDS, mode
-        assert info.chunked_form == (ua.UA2A_CHUNKED_ONE_LAUNCH if fused_expected
-                                     else ua.UA2A_CHUNKED_PER_PLANE), mode
-        assert emu.ua2a_emu_kernel_count(9) == (1 if fused_expected else 0), mode
+        assert info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH and info.launches == 1, mode
+        assert emu.ua2a_emu_kernel_count(9) == 1 and emu.ua2a_emu_kernel_count(2) == 0, mode
         assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
         assert all(b.guards_intact() for b in bufs), mode
         assert np.array_equal(bufs[2].view.reshape(w, -1), y.reshape(w, B, -1)[:, B - 1]), mode
@@ -552,9 +550,10 @@ def test_emulated_kernels_under_asan(tmp_path):
                 cases.append((*shape, mode, 1, path, 2, 0))
     for mode in (0, 1):      # more partial-chunk slots than lanes
         cases.append((130, 2, 5, 260, 3, 2, mode, 0, ua.UA2A_PATH_LDS, 2, 0))
-    # the LDS path's one-launch chunked kernel: partial chunks, several planes, a capped grid
+    # the LDS path's one-launch chunked kernel: partial chunks, several planes, a capped grid,
+    # planes that are not whole 16-byte chunks
     for shape in [(4, 3, 64, 4, 7, 2), (130, 2, 8, 260, 3, 2), (2, 5, 4, 6, 5, 4), (8, 2, 257, 8, 24, 2),
-                  (3, 2, 16, 3, 5, 1)]:
+                  (3, 2, 16, 3, 5, 1), (3, 3, 7, 3, 7, 2), (4, 3, 61, 4, 7, 2)]:
         for mode in (0, 1):
             for mis, blocks in ((0, 0), (2, 0), (0, 5)):
                 cases.append((*shape, mode, 1, ua.UA2A_PATH_LDS, mis - mis % shape[5], blocks))

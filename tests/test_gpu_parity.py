@@ -551,7 +551,7 @@ def test_chunked_exchange_in_one_launch(shape):
     plan.close()
 
 
-LDS_CHUNKED_SHAPES = [            # a plane of one rank is a multiple of 16 bytes in each
+LDS_CHUNKED_SHAPES = [
     (3, 4, 8, 3, 7, "bf16"),          # run 14 B: 2-byte pieces
     (4, 3, 64, 4, 7, "bf16"),         # run 14 B, line-aligned tiles
     (2, 5, 4, 6, 5, "fp32"),          # run 60 B, 4-byte pieces
@@ -563,29 +563,32 @@ LDS_CHUNKED_SHAPES = [            # a plane of one rank is a multiple of 16 byte
     (1, 3, 8, 4, 7, "bf16"),          # w = 1
     (8, 4, 4096, 8, 32, "bf16"),      # run 64 B, 33 MB: thousands of tiles per plane
     (4, 4, 20000, 4, 7, "bf16"),      # run 14 B, 9 MB
+    (3, 3, 7, 3, 7, "bf16"),          # plane 294 B: the output's offset moves with the plane
+    (5, 2, 37, 10, 3, "u8"),          # plane 1110 B, 1-byte pieces
 ]
 
 
-@pytest.mark.parametrize("mis", [0, 1], ids=["aligned", "offset"])
+@pytest.mark.parametrize("mis", [(0, 0), (1, 1), (0, 1)], ids=["aligned", "offset", "window-off"])
 @pytest.mark.parametrize("shape", LDS_CHUNKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_chunked_lds_in_one_launch(shape, mis):
     """Chunked exchanges on the LDS path (runs under 128 B or off the 16-byte
     grid; 16/8/4/2/1-byte pieces, 2-9 planes) run as one launch of the chunked
     LDS kernel: each workgroup fills LDS from a plane of the input, and each
     lane stores its chunks of the tile's window spans, reads them back and
-    stores them to that plane of the output.  With `offset`, input, output and window all start one
-    element past a 256-byte boundary, so spans begin and end inside 16-byte
-    chunks (the one-launch form still applies: output and window agree modulo
-    16).  The output matches the oracle, and the window ends holding the last
-    plane of every rank in the output's layout."""
+    stores them to that plane of the output.  With `offset`, input, output
+    and window all start one element past a 256-byte boundary, so spans begin
+    and end inside 16-byte chunks; with `window-off` only the window does, so
+    window chunks go to the output in pieces.  The output matches the oracle,
+    and the window ends holding the last plane of every rank in the output's
+    layout."""
     w, B, S, H, D, dtype = shape
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32, "u8": torch.uint8}[dtype]
     e = torch.empty((), dtype=dt).element_size()
     lay = ua.ua2a_layout(w, B, S, H, D, e)
-    assert (S * H * D * e) % 16 == 0
+    mis, mwe = mis[0], mis[1] * e         # input/output offset (elements), window offset (bytes)
     n, wb = lay["tensor_elems"], lay["window_bytes"]
     win = torch.full((wb + 512,), 0x5A, dtype=torch.uint8, device=DEV)
-    plan = ua.Plan(w, B, S, H, D, dt, window=win[mis * e:mis * e + wb])
+    plan = ua.Plan(w, B, S, H, D, dt, window=win[mwe:mwe + wb])
     plan.set_path(ua.UA2A_PATH_LDS)
     for mode in (0, 1):
         x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 51 + mode)
@@ -607,15 +610,15 @@ def test_chunked_lds_in_one_launch(shape, mis):
         assert (guard[:mis] == full).all() and (guard[mis + n:] == full).all()
         wcpu = win.cpu()
         last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
-        assert torch.equal(wcpu[mis * e:mis * e + wb].reshape(w, -1), last), f"window {shape} {mode}"
-        assert (wcpu[:mis * e] == 0x5A).all() and (wcpu[mis * e + wb:] == 0x5A).all()
+        assert torch.equal(wcpu[mwe:mwe + wb].reshape(w, -1), last), f"window {shape} {mode}"
+        assert (wcpu[:mwe] == 0x5A).all() and (wcpu[mwe + wb:] == 0x5A).all()
     plan.close()
 
 
 def _random_lds_chunked_cases(n, seed):
     """Seeded chunked exchanges of 2-9 planes on the LDS path, bases off the
     16-byte grid: the window offset from the output by a multiple of 16
-    bytes (one launch) or not (a permute and a copy per plane)."""
+    bytes (whole 16-byte stores out) or not (pieces)."""
     rng = np.random.default_rng(seed)
     cases = []
     for c in _random_chunked_cases(n, seed):
@@ -645,9 +648,8 @@ def test_random_chunked_lds(case):
     xi = xin[case["mis_in"]:case["mis_in"] + n].view(in_shape(w, B, S, H, D, mode))
     yo = outbuf[case["mis_out"]:case["mis_out"] + n].view(plan.out_shape(mode))
     info = plan.describe(xi, mode, True, out=yo)
-    same = (S * H * D * e) % 16 == 0 and (yo.data_ptr() - window.data_ptr() - mw) % 16 == 0
     if info["path"] == ua.UA2A_PATH_LDS:
-        assert info["chunked_form"] == (ua.UA2A_CHUNKED_ONE_LAUNCH if same else ua.UA2A_CHUNKED_PER_PLANE)
+        assert info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH and info["launches"] == 1
     note(f"random chunked lds {case} {info}")
     plan.exchange(xi, mode, True, out=yo)
     torch.cuda.synchronize()

@@ -62,10 +62,8 @@ def _emu_pair(lib, shape, mode, path=ua.UA2A_PATH_AUTO, seed=0):
                                    (3, 5, 7, 3, 7, 2), (8, 2, 13, 40, 128, 2)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_emulated_noalloc_equals_the_window_exchange(emu, shape):
-    """Every chunked form (one launch of the chunked kernel on the direct
-    path or of the chunked LDS kernel, and permute + copy per plane where a
-    plane is not whole 16-byte chunks), both modes, then a second, smaller
-    call."""
+    """Both one-launch chunked kernels (direct and LDS path), both modes,
+    then a second, smaller call."""
     for path in (ua.UA2A_PATH_AUTO, ua.UA2A_PATH_DIRECT, ua.UA2A_PATH_LDS):
         for mode in (0, 1):
             for s in (shape, (2, 2, 3, 4, 8, shape[5])):          # the second call is smaller
@@ -140,7 +138,7 @@ def _gpu_pair(shape, dtype, mode, mis=0, seed=0):
 @pytest.mark.parametrize("first,second", [
     (((4, 4, 2048, 16, 64), "fp16"), ((2, 3, 100, 4, 32), "bf16")),      # the 4-plane workload, then smaller
     (((3, 2, 4681, 12, 80), "fp32"), ((3, 2, 41, 3, 5), "fp32")),         # 54 MB window, then an odd shape
-    (((2, 1, 8, 4, 16), "bf16"), ((2, 1, 5, 2, 16), "bf16")),            # short runs: the LDS path (offset output: per plane)
+    (((2, 1, 8, 4, 16), "bf16"), ((2, 1, 5, 2, 16), "bf16")),            # short runs: the LDS path (offset output: pieces)
     (((8, 4, 1024, 8, 32), "bf16"), ((3, 4, 8, 3, 7), "bf16")),          # the chunked LDS kernel, 64 B then 14 B runs
 ], ids=["chunked-then-small", "awkward-then-odd", "tiny-then-tinier", "lds-then-odd"])
 def test_noalloc_matches_the_window_exchange(first, second):

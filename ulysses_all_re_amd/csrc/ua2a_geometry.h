@@ -465,9 +465,9 @@ struct PlaneBases {
 // workgroup barrier, copies those spans to plane p of the output.  Window
 // byte x of block k lands at out + x + k * rank_step + p * plane (block k is
 // head block r in mode 0, the tile's rank j in mode 1; rank_step = the
-// output's rank stride minus the window's, plane bytes).  The host takes
-// this form only when the window and the output agree modulo 16 and plane
-// is a multiple of 16, so a span has the same 16-byte chunks on both sides.
+// output's rank stride minus the window's, plane bytes).  Every such offset
+// is a multiple of the piece size G, so a window chunk goes to the output in
+// one 16-byte store when the two agree modulo 16, else in G-byte pieces.
 struct LdsChunkGeom {
     uint8_t* out;          // the output: plane 0 of rank 0
     int64_t rank_step;     // B * plane - plane

@@ -63,9 +63,9 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
 
 // Everything one exchange launches.  A chunked exchange on the direct path
 // with its 3-D grid is one launch of the chunked kernel, and on the LDS path
-// one launch of the chunked LDS kernel when the window and the output share
-// their 16-byte chunks (`fused`: perm is that launch).  Otherwise perm and
-// copy describe plane 0 of a chunked exchange, and plane p adds
+// one launch of the chunked LDS kernel (`fused`: perm is that launch).
+// Otherwise (a capped grid or the grouped tile order on the direct path)
+// perm and copy describe plane 0 of a chunked exchange, and plane p adds
 // p * plane_bytes to the pointers named in to_plane: B permutes into the
 // window, each followed by a copy out.
 struct Prepared {
@@ -411,14 +411,8 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     }
     pr->launches = 1;
     if (chunked) {
-        // LDS path in one launch when a span has the same 16-byte chunks in
-        // the window and in every plane of the output (and of the input):
-        // the output agrees with the window modulo 16, and a plane is a
-        // multiple of 16 bytes
-        const bool same_chunks =
-            plane % 16 == 0 &&
-            (reinterpret_cast<uintptr_t>(outb) - reinterpret_cast<uintptr_t>(window)) % 16 == 0;
-        if (L.kernel == Kernel::Lds && same_chunks) {
+        // the LDS path: one launch of the chunked LDS kernel
+        if (L.kernel == Kernel::Lds) {
             pr->fused = 1;
             L.kernel = Kernel::LdsChunked;
             L.lds = make_lds(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb, true);

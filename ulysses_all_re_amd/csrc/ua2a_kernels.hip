@@ -25,9 +25,9 @@
 //    plane (fill from the input, drain into the window, barrier, copy the
 //    window spans to the output).
 //  * ua2a_copy_kernel    -- strided block copy used by the per-plane form of
-//    the chunked exchange (a capped grid, or window and output off each
-//    other's 16-byte grid on the LDS path) to move the one-plane window into
-//    the output after each plane's permutation launch.
+//    the chunked exchange (a capped grid or the grouped tile order on the
+//    direct path) to move the one-plane window into the output after each
+//    plane's permutation launch.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
