@@ -153,9 +153,10 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               the LDS path it is one launch too: each workgroup stages its
  *               tile of every plane in LDS, and each lane writes its chunks
  *               of the tile to the window, reads them back and stores them
- *               to `out`.  Otherwise (a `blocks` cap or the grouped tile
- *               order on the direct path) each plane is a permute launch and
- *               a copy launch (UA2A_CHUNKED_PER_PLANE).
+ *               to `out`.  Otherwise (a `blocks` cap on the direct path, or
+ *               more ranks or slabs than a 3-D grid's y and z extents hold)
+ *               each plane is a permute launch and a copy launch
+ *               (UA2A_CHUNKED_PER_PLANE).
  *               After the call the window holds plane B-1 of every rank, in
  *               `out`'s layout.  Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]

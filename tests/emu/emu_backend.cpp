@@ -162,14 +162,16 @@ void run_chunked(const Launch& L)
     for (uint32_t z = 0; z < L.grid_z; ++z)
         for (uint32_t y = 0; y < L.grid_y; ++y)
             for (uint32_t x = 0; x < L.grid; ++x, ++tile) {
-                const DirectTile d = direct_tile_3d<M1>(g, x, y, z);
+                uint32_t block;
+                const DirectTile d = chunked_tile<M1>(g, x, y, z, block);
+                if (d.nvec == 0) continue;          // padding tile of the grouped order
                 const bool full = d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock;
                 for (uint32_t tid = 0; tid < kDirectBlock; ++tid) {
                     g_lane_id = tile * kDirectBlock + tid;
                     if (full)
-                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, true>(g, d, L.chunk, z, tid);
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, true>(g, d, L.chunk, block, tid);
                     else
-                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, false>(g, d, L.chunk, z, tid);
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, false>(g, d, L.chunk, block, tid);
                 }
             }
     // every window byte belongs to exactly one lane and was written
@@ -458,12 +460,17 @@ int backend_launch(const Launch& L, void*)
         }
         return L.mode ? dispatch_direct<true>(L, L.width) : dispatch_direct<false>(L, L.width);
     case Kernel::Chunked: {
-        // the 3-D grid of one plane's tiles of every rank, z = window block
+        // the 3-D grid of one plane's tiles of every rank, z = window block;
+        // or, mode 0 with the grouped order, x = (tile group, r, tile), y = j
         const DirectGeom& g = L.direct;
-        if (!L.grid3d || g.nb != 1 || g.sig_count != 0 || g.group != 0 || L.grid != g.tiles_per_slab ||
-            static_cast<uint64_t>(L.grid_y) * L.grid_z * g.tiles_per_slab != g.num_tiles ||
-            L.grid_y != (L.mode ? 1u : g.w) || L.grid_z != g.w || L.chunk.planes < 1 ||
+        if (!L.grid3d || g.nb != 1 || g.sig_count != 0 || L.chunk.planes < 1 ||
             L.chunk.plane != (L.mode ? g.p_rank : g.a_rank))
+            return 6;
+        if (g.group == 0 ? (L.grid != g.tiles_per_slab ||
+                            static_cast<uint64_t>(L.grid_y) * L.grid_z * g.tiles_per_slab != g.num_tiles ||
+                            L.grid_y != (L.mode ? 1u : g.w) || L.grid_z != g.w)
+                         : (L.mode || L.grid != g.groups * g.group * g.w || L.grid_y != g.w || L.grid_z != 1 ||
+                            static_cast<uint64_t>(L.grid) * L.grid_y != g.num_tiles))
             return 6;
         return L.mode ? dispatch_chunked<true>(L, L.width) : dispatch_chunked<false>(L, L.width);
     }

@@ -520,10 +520,12 @@ def test_window_is_reused_and_left_alone_outside_its_size():
 
 @pytest.mark.parametrize("shape", [(4, 5, 96, 8, 64, "bf16"), (3, 2, 50, 6, 5, "fp32"),
                                    (2, 4, 33, 4, 3, "bf16"), (4, 3, 40, 4, 3, "bf16"),
-                                   (3, 3, 41, 3, 5, "u8"), (8, 6, 17, 40, 128, "bf16")],
+                                   (3, 3, 41, 3, 5, "u8"), (8, 6, 17, 40, 128, "bf16"),
+                                   (8, 3, 40, 16, 128, "bf16"), (2, 3, 37, 2, 1024, "bf16")],
                          ids=lambda s: "x".join(map(str, s)))
 def test_chunked_exchange_in_one_launch(shape):
-    """Chunked exchanges on the direct path (16/8/4/2/1-byte vectors, 2-6 planes) run as
+    """Chunked exchanges on the direct path (16/8/4/2/1-byte vectors, 2-6 planes; 4 KiB
+    rows, whose mode 0 takes the grouped tile order, with a padded last group) run as
     one launch of the chunked kernel: each workgroup moves its window tile through
     every plane, reading each plane back from the window before storing it to the
     output.  The output matches the oracle, and the window ends holding the last

@@ -204,6 +204,34 @@ UA2A_HD DirectTile direct_tile_3d(const DirectGeom& g, uint32_t x, uint32_t y, u
     return d;
 }
 
+// The chunked kernel's tile on its 3-D grid, and the window block it feeds
+// (mode 0: the head block r; mode 1: the receiving rank j).  With the
+// grouped order (mode 0, g.group > 0) x runs over (tile group q, head block
+// r, tile within the group), the group fastest, and y is the sending rank j;
+// a padding tile of the last group has nvec = 0.  Otherwise the plain 3-D
+// grid of direct_tile_3d.
+template <bool MODE1>
+UA2A_HD DirectTile chunked_tile(const DirectGeom& g, uint32_t x, uint32_t y, uint32_t z, uint32_t& block)
+{
+    if (!MODE1 && g.group != 0) {
+        const uint32_t grp = fdiv(x, g.d_group);
+        const uint32_t lo = x - grp * g.group;
+        const uint32_t q = fdiv(grp, g.d_w);
+        const uint32_t r = grp - q * g.w;
+        const uint32_t tt = q * g.group + lo;
+        block = r;
+        if (tt >= g.tiles_per_slab) {
+            DirectTile d;
+            d.u0 = d.nvec = 0;
+            d.dst_slab = d.src_slab = 0;
+            return d;
+        }
+        return direct_tile_3d<false>(g, tt, y, r);
+    }
+    block = z;
+    return direct_tile_3d<MODE1>(g, x, y, z);
+}
+
 // Read- and write-side offsets of vector u (< slab_vecs) of the tile's slab.
 template <bool MODE1>
 UA2A_HD void direct_vector(const DirectGeom& g, const DirectTile& d, uint32_t u,

@@ -64,8 +64,9 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
 // Everything one exchange launches.  A chunked exchange on the direct path
 // with its 3-D grid is one launch of the chunked kernel, and on the LDS path
 // one launch of the chunked LDS kernel (`fused`: perm is that launch).
-// Otherwise (a capped grid or the grouped tile order on the direct path)
-// perm and copy describe plane 0 of a chunked exchange, and plane p adds
+// Otherwise (a capped grid on the direct path, or more slabs than a 3-D
+// grid's y/z extents) perm and copy describe plane 0 of a chunked exchange,
+// and plane p adds
 // p * plane_bytes to the pointers named in to_plane: B permutes into the
 // window, each followed by a copy out.
 struct Prepared {
@@ -424,9 +425,21 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
             L.lds_chunk.planes = static_cast<uint32_t>(p->B);
             return;
         }
+        // mode 0 with the grouped tile order (4 KiB-multiple rows): the chunked
+        // kernel takes it on a 3-D grid too, x running over (tile group, head
+        // block r, tile within the group) and y over the sending rank j
+        const DirectGeom& dg = L.direct;
+        if (L.kernel == Kernel::Direct && !L.grid3d && dg.group != 0 && p->blocks == 0 &&
+            p->w <= static_cast<int32_t>(kMaxGridYZ)) {
+            L.grid3d = 1;
+            L.grid = dg.groups * dg.group * dg.w;      // <= num_tiles (nb = 1), < 2^32
+            L.grid_y = dg.w;
+            L.grid_z = 1;
+        }
         if (L.kernel == Kernel::Direct && L.grid3d) {
             // one launch: every tile of the one-plane window moves through
-            // all B planes (the 3-D grid's z coordinate is the window block)
+            // all B planes (the window block is the head block r in mode 0,
+            // the receiving rank j in mode 1)
             pr->fused = 1;
             L.kernel = Kernel::Chunked;
             L.chunk.out = outb;

@@ -25,9 +25,9 @@
 //    plane (fill from the input, drain into the window, barrier, copy the
 //    window spans to the output).
 //  * ua2a_copy_kernel    -- strided block copy used by the per-plane form of
-//    the chunked exchange (a capped grid or the grouped tile order on the
-//    direct path) to move the one-plane window into the output after each
-//    plane's permutation launch.
+//    the chunked exchange (a capped grid on the direct path) to move the
+//    one-plane window into the output after each plane's permutation
+//    launch.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
@@ -237,11 +237,13 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_chunked_kernel(DirectGeom g
 {
     args_up_front(g);
     asm volatile("" ::"s"(c.out), "s"(c.step), "s"(c.plane), "s"(c.planes));
-    const DirectTile d = direct_tile_3d<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z);
+    uint32_t block;
+    const DirectTile d = chunked_tile<MODE1>(g, blockIdx.x, blockIdx.y, blockIdx.z, block);
+    if (d.nvec == 0) return;                                  // padding tile of the grouped order
     if (d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock)      // the same for the whole workgroup
-        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, true>(g, d, c, blockIdx.z, threadIdx.x);
+        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, true>(g, d, c, block, threadIdx.x);
     else
-        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, false>(g, d, c, blockIdx.z, threadIdx.x);
+        chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, false>(g, d, c, block, threadIdx.x);
 }
 
 // The credits of a publishing exchange's last part.
