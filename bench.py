@@ -379,11 +379,12 @@ def run(args):
         traffic = None
     dom_mode, dom_avg = (0, avg0) if avg0 >= avg1 else (1, avg1)
     dom_info = info0 if dom_mode == 0 else info1
-    per_plane = chunked and dom_info.get("chunked_form") == ua.UA2A_CHUNKED_PER_PLANE
     if args.ranks is not None:
         kname = "ua2a_ranks_kernel"
-    elif chunked and not per_plane:
-        kname = "ua2a_chunked_kernel" if dom_info["path"] == ua.UA2A_PATH_DIRECT else "ua2a_lds_chunked_kernel"
+    elif chunked and dom_info["path"] == ua.UA2A_PATH_DIRECT:
+        kname = "ua2a_chunked_kernel" if dom_info["grid_dims"] == 3 else "ua2a_chunked_flat_kernel"
+    elif chunked:
+        kname = "ua2a_lds_chunked_kernel"
     elif dom_info["path"] == ua.UA2A_PATH_DIRECT:
         kname = "ua2a_direct3d_kernel" if dom_info["grid_dims"] == 3 else "ua2a_direct_kernel"
     else:
@@ -391,7 +392,6 @@ def run(args):
     roofline = {
         "bound": "hbm",
         "kernel": f"{kname}<{dom_info['vector_bytes']}, mode {dom_mode}>"
-                  + (" + ua2a_copy_kernel, per plane" if per_plane else "")
                   + (f", {w} launches of one sender each" if args.ranks == "one" else ""),
         "achieved": round(gbps(dom_avg), 1),
         "peak": PEAK_HBM_GBPS,

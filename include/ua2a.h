@@ -83,23 +83,21 @@ typedef struct ua2a_layout_s {
 #define UA2A_PATH_DIRECT  1  /* one pass, each lane moves whole vectors of a run */
 #define UA2A_PATH_LDS     2  /* rows staged through LDS, both sides moved as contiguous spans */
 
-/* How a chunked exchange is launched (ua2a_launch_info_t.chunked_form). */
-#define UA2A_CHUNKED_ONE_LAUNCH  1  /* one launch of the chunked kernel (direct path, 3-D grid)
-                                       or of the chunked LDS kernel (LDS path) */
-#define UA2A_CHUNKED_PER_PLANE   2  /* per plane: a permute into the window, then a copy out */
+/* How a chunked exchange is launched (ua2a_launch_info_t.chunked_form): one
+ * launch of the chunked kernel (direct path) or of the chunked LDS kernel. */
+#define UA2A_CHUNKED_ONE_LAUNCH  1
 
 /* What an exchange would launch (ua2a_describe). */
 typedef struct ua2a_launch_info_s {
     int32_t path;          /* UA2A_PATH_DIRECT or UA2A_PATH_LDS */
     int32_t vector_bytes;  /* bytes per lane access of the permutation kernel (1..16) */
     int32_t block;         /* threads per workgroup */
-    int32_t launches;      /* kernel launches per exchange; chunked: 1 (UA2A_CHUNKED_ONE_LAUNCH)
-                              or B permutes + B copies, 2*B (UA2A_CHUNKED_PER_PLANE) */
+    int32_t launches;      /* kernel launches per exchange: 1, chunked or not */
     int64_t grid;          /* workgroups of the permutation kernel per launch (all dimensions) */
     int64_t tiles;         /* work tiles per launch */
     int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
     int32_t grid_dims;     /* 3: a 3-D grid (direct path by default, every per-rank launch); else 1 */
-    int32_t chunked_form;  /* 0: not chunked; else UA2A_CHUNKED_ONE_LAUNCH or UA2A_CHUNKED_PER_PLANE */
+    int32_t chunked_form;  /* 0: not chunked; else UA2A_CHUNKED_ONE_LAUNCH */
 } ua2a_launch_info_t;
 
 /*
@@ -146,17 +144,14 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               window, then a copy of the window into plane p of `out`;
  *               plane p+1 overwrites a window byte only after plane p's copy
  *               has read it, and every byte of `out` is read from the
- *               window.  On the direct path with its default 3-D grid the
- *               whole exchange is ONE launch: each workgroup owns one tile of
- *               the window and, plane after plane, writes the tile, reads it
- *               back and stores it to `out` (UA2A_CHUNKED_ONE_LAUNCH).  On
- *               the LDS path it is one launch too: each workgroup stages its
- *               tile of every plane in LDS, and each lane writes its chunks
- *               of the tile to the window, reads them back and stores them
- *               to `out`.  Otherwise (a `blocks` cap on the direct path, or
- *               more ranks or slabs than a 3-D grid's y and z extents hold)
- *               each plane is a permute launch and a copy launch
- *               (UA2A_CHUNKED_PER_PLANE).
+ *               window.  The whole exchange is ONE launch
+ *               (UA2A_CHUNKED_ONE_LAUNCH).  On the direct path each
+ *               workgroup owns one tile of the window (or, under a `blocks`
+ *               cap, several in turn) and, plane after plane, writes the
+ *               tile, reads it back and stores it to `out`.  On the LDS path
+ *               each workgroup stages its tile of every plane in LDS, and
+ *               each lane writes its chunks of the tile to the window, reads
+ *               them back and stores them to `out`.
  *               After the call the window holds plane B-1 of every rank, in
  *               `out`'s layout.  Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]

@@ -158,8 +158,30 @@ void run_chunked(const Launch& L)
     g_win = g.dst;
     g_win_bytes = static_cast<size_t>(g.w) * static_cast<size_t>(L.chunk.plane) * VB;
     g_win_owner.assign(g_win_bytes, -1);
+    if (!L.grid3d) {
+        // the flat kernel's loop: workgroup bx takes tiles bx, bx + grid, ...
+        std::vector<uint8_t> seen(g.num_tiles, 0);
+        for (uint32_t bx = 0; bx < L.grid; ++bx)
+            for (uint64_t t = bx; t < g.num_tiles; t += L.grid) {
+                if (seen[t]++) abort();
+                uint32_t slab;
+                const DirectTile d = direct_tile<M1>(g, static_cast<uint32_t>(t), &slab);
+                if (d.nvec == 0) continue;
+                const uint32_t block = chunked_block<M1>(g, slab);
+                const bool full = d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock;
+                for (uint32_t tid = 0; tid < kDirectBlock; ++tid) {
+                    g_lane_id = static_cast<int64_t>(t) * kDirectBlock + tid;
+                    if (full)
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, true>(g, d, L.chunk, block, tid);
+                    else
+                        chunked_tile_body<CheckedMem, VB, M1, kDirectBlock, false>(g, d, L.chunk, block, tid);
+                }
+            }
+        for (uint32_t t = 0; t < g.num_tiles; ++t)
+            if (!seen[t]) abort();
+    }
     int64_t tile = 0;
-    for (uint32_t z = 0; z < L.grid_z; ++z)
+    for (uint32_t z = 0; L.grid3d && z < L.grid_z; ++z)
         for (uint32_t y = 0; y < L.grid_y; ++y)
             for (uint32_t x = 0; x < L.grid; ++x, ++tile) {
                 uint32_t block;
@@ -463,10 +485,13 @@ int backend_launch(const Launch& L, void*)
         // the 3-D grid of one plane's tiles of every rank, z = window block;
         // or, mode 0 with the grouped order, x = (tile group, r, tile), y = j
         const DirectGeom& g = L.direct;
-        if (!L.grid3d || g.nb != 1 || g.sig_count != 0 || L.chunk.planes < 1 ||
+        if (g.nb != 1 || g.sig_count != 0 || L.chunk.planes < 1 ||
             L.chunk.plane != (L.mode ? g.p_rank : g.a_rank))
             return 6;
-        if (g.group == 0 ? (L.grid != g.tiles_per_slab ||
+        if (!L.grid3d) {
+            // flat grid: workgroups loop over the tiles
+            if (L.grid_y != 1 || L.grid_z != 1 || L.grid > g.num_tiles) return 7;
+        } else if (g.group == 0 ? (L.grid != g.tiles_per_slab ||
                             static_cast<uint64_t>(L.grid_y) * L.grid_z * g.tiles_per_slab != g.num_tiles ||
                             L.grid_y != (L.mode ? 1u : g.w) || L.grid_z != g.w)
                          : (L.mode || L.grid != g.groups * g.group * g.w || L.grid_y != g.w || L.grid_z != 1 ||

@@ -208,15 +208,14 @@ def test_emulated_round_trip_and_chunked_launch_count(emu):
                                    (5, 2, 4, 10, 2, 1), (4, 3, 7, 8, 3, 8), (2, 3, 37, 2, 1024, 2)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_emulated_chunked_forms(emu, shape):
-    """Chunked exchanges on the direct path's 3-D grid are one launch of the
-    chunked kernel, in which every lane reads back only window bytes it
-    stored itself (the emulation tracks each window byte's last writer); on
-    the LDS path (aligned buffers, planes of whole 16-byte chunks) one launch
-    of the chunked LDS kernel, whose lanes likewise read back only window
-    bytes they stored in the same plane; a blocks hint (flat grid) and the grouped
-    tile order run a permute and a copy launch per plane.  Every form matches
-    the oracle, leaves the guard bands alone and ends with the last plane in
-    the window."""
+    """Every chunked exchange is one launch: of the chunked kernel on the
+    direct path (its 3-D grid, the grouped order's 3-D grid for 4 KiB rows in
+    mode 0, or a flat grid under a blocks hint, whose workgroups loop over
+    tiles), in which every lane reads back only window bytes it stored itself
+    (the emulation tracks each window byte's last writer), or of the chunked
+    LDS kernel, whose lanes likewise read back only window bytes they stored
+    in the same plane.  Every form matches the oracle, leaves the guard bands
+    alone and ends with the last plane in the window."""
     w, B, S, H, D, e = shape
     assert (S * H * D * e) % 16 == 0
     for mode in (0, 1):
@@ -225,16 +224,14 @@ def test_emulated_chunked_forms(emu, shape):
             x, y, info, bufs = emu_exchange(emu, shape, mode, True, path, blocks=blocks, seed=11 + mode)
             assert np.array_equal(y, oracle_bytes(x, shape, mode)), (mode, path, blocks)
             assert all(b.guards_intact() for b in bufs), (mode, path, blocks)
-            direct = info.path == ua.UA2A_PATH_DIRECT and info.grid_dims == 3
             lds = info.path == ua.UA2A_PATH_LDS
-            fused = direct or lds
-            assert info.chunked_form == (ua.UA2A_CHUNKED_ONE_LAUNCH if fused else ua.UA2A_CHUNKED_PER_PLANE)
-            assert info.launches == (1 if fused else 2 * B), (mode, path, blocks)
-            assert emu.ua2a_emu_kernel_count(7) == (1 if direct else 0)
+            assert info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH and info.launches == 1, (mode, path, blocks)
+            assert emu.ua2a_emu_kernel_count(7) == (0 if lds else 1)
             assert emu.ua2a_emu_kernel_count(9) == (1 if lds else 0)
-            assert emu.ua2a_emu_kernel_count(2) == (0 if fused else B)
-            if lds and blocks:
-                assert info.grid == blocks
+            assert emu.ua2a_emu_kernel_count(2) == 0
+            assert info.grid_dims == (1 if lds or blocks else 3), (mode, path, blocks)
+            if blocks:
+                assert 1 <= info.grid <= blocks, (mode, path, blocks)
             # the window holds the last plane of every rank, in the output's layout
             out = y.reshape(w, B, -1)
             assert np.array_equal(bufs[2].view.reshape(w, -1), out[:, B - 1]), (mode, path, blocks)

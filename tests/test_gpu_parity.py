@@ -417,6 +417,37 @@ def test_blocks_hint_gives_identical_bytes(blocks):
         plan.close()
 
 
+@pytest.mark.parametrize("blocks", [1, 7, 300, 5000])
+@pytest.mark.parametrize("shape", [(4, 4, 2048, 16, 64, "fp16"), (2, 3, 37, 2, 1024, "bf16"),
+                                   (3, 2, 41, 3, 5, "fp32")], ids=lambda s: "x".join(map(str, s)))
+def test_chunked_under_a_blocks_hint(shape, blocks):
+    """A chunked exchange on a grid capped by a blocks hint stays one launch: on the
+    direct path the chunked kernel's flat form, each workgroup moving several window
+    tiles in turn (4 KiB rows: in the grouped tile order, padding tiles included); on
+    the LDS path the chunked LDS kernel's slot loop.  Bytes and window as without it."""
+    w, B, S, H, D, dtype = shape
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+    e = torch.empty((), dtype=dt).element_size()
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    win = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
+    plan = ua.Plan(w, B, S, H, D, dt, blocks=blocks, window=win)
+    for path in ("direct", "lds"):
+        plan.set_path(PATHS[path])
+        for mode in (0, 1):
+            x = make_tensor(in_shape(w, B, S, H, D, mode), dtype, "bytes", 80 + mode)
+            want = oracle_out(x, mode, w)
+            xd = x.to(DEV)
+            info = plan.describe(xd, mode, True)
+            assert info["launches"] == 1 and info["grid"] <= blocks
+            note(f"chunked blocks={blocks} {shape} {path} mode={mode} {info}")
+            y = plan.exchange(xd, mode, True, out=poisoned(plan.out_shape(mode), dt))
+            torch.cuda.synchronize()
+            assert_same_bits(y, want, f"chunked blocks={blocks} {shape} {path} mode {mode}")
+            last = want.view(torch.uint8).reshape(w, B, -1)[:, B - 1]
+            assert torch.equal(win.cpu().reshape(w, -1), last), f"window {shape} {path} {mode}"
+    plan.close()
+
+
 def test_back_to_back_on_one_stream_and_side_stream():
     """mode 0 -> mode 1 -> mode 0 queued without host syncs, on a non-default stream."""
     w, B, S, H, D = cfg_shape(CONFIGS["chunked"])

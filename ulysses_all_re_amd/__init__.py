@@ -47,7 +47,6 @@ UA2A_PATH_DIRECT = 1
 UA2A_PATH_LDS = 2
 
 UA2A_CHUNKED_ONE_LAUNCH = 1
-UA2A_CHUNKED_PER_PLANE = 2
 
 UA2A_NOALLOC_WINDOW_BYTES = 64 * 1024 * 1024   # the library's own window (no-allocation entry point)
 

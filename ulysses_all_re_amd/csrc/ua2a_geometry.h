@@ -130,8 +130,9 @@ struct ChunkedGeom {
     uint32_t planes;    // B
 };
 
+// (`slab_out`, if given, receives the tile's slab index.)
 template <bool MODE1>
-UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
+UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t, uint32_t* slab_out = nullptr)
 {
     uint32_t slab, tt;
     if (g.group == 0) {
@@ -149,6 +150,7 @@ UA2A_HD DirectTile direct_tile(const DirectGeom& g, uint32_t t)
         slab = (r * g.nb + b) * g.w + j;          // the mode-0 slab numbering
         tt = hi * g.group + lo;
     }
+    if (slab_out != nullptr) *slab_out = slab;
     DirectTile d;
     if (tt >= g.tiles_per_slab) {      // padding tile of the grouped order
         d.u0 = 0;
@@ -205,7 +207,9 @@ UA2A_HD DirectTile direct_tile_3d(const DirectGeom& g, uint32_t x, uint32_t y, u
 }
 
 // The chunked kernel's tile on its 3-D grid, and the window block it feeds
-// (mode 0: the head block r; mode 1: the receiving rank j).  With the
+// (mode 0: the head block r; mode 1: the receiving rank j).  The chunked
+// kernel's geometry has one plane (nb = 1), so on a flat grid the block is
+// the slab's r = slab / w (mode 0) or j = slab (mode 1): chunked_block.  With the
 // grouped order (mode 0, g.group > 0) x runs over (tile group q, head block
 // r, tile within the group), the group fastest, and y is the sending rank j;
 // a padding tile of the last group has nvec = 0.  Otherwise the plain 3-D
@@ -230,6 +234,12 @@ UA2A_HD DirectTile chunked_tile(const DirectGeom& g, uint32_t x, uint32_t y, uin
     }
     block = z;
     return direct_tile_3d<MODE1>(g, x, y, z);
+}
+
+template <bool MODE1>
+UA2A_HD uint32_t chunked_block(const DirectGeom& g, uint32_t slab)
+{
+    return MODE1 ? slab : fdiv(slab, g.d_w);
 }
 
 // Read- and write-side offsets of vector u (< slab_vecs) of the tile's slab.

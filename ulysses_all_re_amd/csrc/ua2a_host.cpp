@@ -61,22 +61,12 @@ uint32_t grid_for(uint32_t tiles, int32_t hint, uint32_t block)
     return static_cast<uint32_t>(g);
 }
 
-// Everything one exchange launches.  A chunked exchange on the direct path
-// with its 3-D grid is one launch of the chunked kernel, and on the LDS path
-// one launch of the chunked LDS kernel (`fused`: perm is that launch).
-// Otherwise (a capped grid on the direct path, or more slabs than a 3-D
-// grid's y/z extents) perm and copy describe plane 0 of a chunked exchange,
-// and plane p adds
-// p * plane_bytes to the pointers named in to_plane: B permutes into the
-// window, each followed by a copy out.
+// The one launch of an exchange: the permutation kernel, or for a chunked
+// exchange the chunked kernel (direct path: on the 3-D grid, or on a flat
+// grid under a `blocks` cap) or the chunked LDS kernel.
 struct Prepared {
     int32_t path;            // UA2A_PATH_DIRECT or UA2A_PATH_LDS
-    int32_t chunked;
-    int32_t fused;           // chunked exchange in one launch
     Launch perm;
-    Launch copy;
-    int64_t plane_bytes;     // S_local * H * D * elem_bytes
-    int32_t launches;
 };
 
 // `recv` receiving ranks from the ones at the given bases (w for a whole
@@ -394,8 +384,6 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     }
 
     pr->path = path;
-    pr->chunked = chunked;
-    pr->plane_bytes = plane;
     Launch& L = pr->perm;
     L.mode = mode;
     L.grid_y = L.grid_z = 1;
@@ -410,11 +398,9 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         L.lds_bytes = L.lds.lds_bytes;
         L.grid = grid_for(L.lds.num_slots, p->blocks, kLdsBlock);
     }
-    pr->launches = 1;
     if (chunked) {
         // the LDS path: one launch of the chunked LDS kernel
         if (L.kernel == Kernel::Lds) {
-            pr->fused = 1;
             L.kernel = Kernel::LdsChunked;
             L.lds = make_lds(p, mode, g, p_ptr, a_ptr, p_rank, p_plane, a_rank, a_plane, nb, true);
             L.lds_bytes = L.lds.lds_bytes;
@@ -429,55 +415,23 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
         // kernel takes it on a 3-D grid too, x running over (tile group, head
         // block r, tile within the group) and y over the sending rank j
         const DirectGeom& dg = L.direct;
-        if (L.kernel == Kernel::Direct && !L.grid3d && dg.group != 0 && p->blocks == 0 &&
+        if (!L.grid3d && dg.group != 0 && p->blocks == 0 &&
             p->w <= static_cast<int32_t>(kMaxGridYZ)) {
             L.grid3d = 1;
             L.grid = dg.groups * dg.group * dg.w;      // <= num_tiles (nb = 1), < 2^32
             L.grid_y = dg.w;
             L.grid_z = 1;
         }
-        if (L.kernel == Kernel::Direct && L.grid3d) {
-            // one launch: every tile of the one-plane window moves through
-            // all B planes (the window block is the head block r in mode 0,
-            // the receiving rank j in mode 1)
-            pr->fused = 1;
-            L.kernel = Kernel::Chunked;
-            L.chunk.out = outb;
-            L.chunk.step = (rank_bytes - plane) / L.width;
-            L.chunk.plane = plane / L.width;
-            L.chunk.planes = static_cast<uint32_t>(p->B);
-            return;
-        }
-        // window -> plane 0 of every rank of `out`: w blocks of one plane
-        uint32_t vb = pow2_align(static_cast<uint64_t>(plane));
-        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(window)));
-        vb = umin32(vb, pow2_align(reinterpret_cast<uintptr_t>(out)));
-        Launch& C = pr->copy;
-        C.kernel = Kernel::Copy;
-        C.block = kCopyBlock;
-        C.grid_y = C.grid_z = 1;
-        C.width = static_cast<int32_t>(vb);
-        C.copy = make_copy(vb, window, outb, plane, rank_bytes, plane,
-                           static_cast<uint32_t>(p->w));
-        C.grid = grid_for(C.copy.num_tiles, 0, kCopyBlock);
-        pr->launches = static_cast<int32_t>(2 * p->B);
+        // the direct path: one launch of the chunked kernel, each tile of the
+        // one-plane window moved through all B planes (the window block is
+        // the head block r in mode 0, the receiving rank j in mode 1); on the
+        // 3-D grid, or on a flat grid whose workgroups loop over the tiles
+        L.kernel = Kernel::Chunked;
+        L.chunk.out = outb;
+        L.chunk.step = (rank_bytes - plane) / L.width;
+        L.chunk.plane = plane / L.width;
+        L.chunk.planes = static_cast<uint32_t>(p->B);
     }
-}
-
-// Shift plane-0 launches of a per-plane chunked exchange to plane `pl`.
-void to_plane(const Prepared& pr, int32_t mode, int64_t pl, Launch* perm, Launch* copy)
-{
-    *perm = pr.perm;
-    *copy = pr.copy;
-    const int64_t off = pl * pr.plane_bytes;
-    // the input side walks the planes; the window side stays put
-    if (perm->kernel == Kernel::Direct)
-        perm->direct.src += off;
-    else if (mode == 0)
-        perm->lds.p_ptr += off;
-    else
-        perm->lds.a_ptr += off;
-    copy->copy.dst += off;
 }
 
 // Per-rank tables: only the entries a call uses are looked at -- the inputs
@@ -742,36 +696,10 @@ int launch_exchange(ua2a_plan_s* plan, int32_t mode, int32_t chunked, const void
 {
     Prepared pr;
     prepare(plan, mode, chunked, in, out, &pr, UA2A_PATH_AUTO, window);
-    int err;
-    if (!chunked) {
-        err = backend_launch(pr.perm, stream);
-        if (err != 0) {
-            disable(plan, "launching the exchange kernel", err);
-            return UA2A_ERR_HIP;
-        }
-        return UA2A_OK;
-    }
-    // Chunked: one launch on the direct path's 3-D grid; otherwise per
-    // plane a permute into the window, then a copy of the window out.
-    // Stream order makes plane p's copy finish before plane p+1 overwrites
-    // the window.
-    if (pr.fused) {
-        err = backend_launch(pr.perm, stream);
-        if (err != 0) {
-            disable(plan, "launching the chunked exchange kernel", err);
-            return UA2A_ERR_HIP;
-        }
-        return UA2A_OK;
-    }
-    for (int64_t pl = 0; pl < plan->B; ++pl) {
-        Launch perm, copy;
-        to_plane(pr, mode, pl, &perm, &copy);
-        err = backend_launch(perm, stream);
-        if (err == 0) err = backend_launch(copy, stream);
-        if (err != 0) {
-            disable(plan, "launching a chunked-plane kernel", err);
-            return UA2A_ERR_HIP;
-        }
+    const int err = backend_launch(pr.perm, stream);
+    if (err != 0) {
+        disable(plan, chunked ? "launching the chunked exchange kernel" : "launching the exchange kernel", err);
+        return UA2A_ERR_HIP;
     }
     return UA2A_OK;
 }
@@ -1081,10 +1009,10 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     info->block = static_cast<int32_t>(pr.perm.block);
     const bool lds = pr.perm.kernel == Kernel::Lds || pr.perm.kernel == Kernel::LdsChunked;
     info->tiles = lds ? pr.perm.lds.num_tiles : pr.perm.direct.num_tiles;
-    info->launches = pr.launches;
+    info->launches = 1;
     info->lds_rows = lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
     info->grid_dims = pr.perm.grid3d ? 3 : 1;
-    info->chunked_form = !chunked ? 0 : pr.fused ? UA2A_CHUNKED_ONE_LAUNCH : UA2A_CHUNKED_PER_PLANE;
+    info->chunked_form = chunked ? UA2A_CHUNKED_ONE_LAUNCH : 0;
     return UA2A_OK;
 }
 

@@ -19,15 +19,14 @@
 //  * ua2a_chunked_kernel -- a whole chunked exchange in one launch on the
 //    direct path: each workgroup owns one tile of the one-plane window and
 //    moves it through every batch plane (permute into the window, read back,
-//    store to the output).
+//    store to the output); ua2a_chunked_flat_kernel -- the same on a flat
+//    grid capped by a `blocks` hint, each workgroup looping over tiles.
 //  * ua2a_lds_chunked_kernel -- a whole chunked exchange in one launch on
 //    the LDS path: each workgroup keeps its LDS tile through every batch
-//    plane (fill from the input, drain into the window, barrier, copy the
-//    window spans to the output).
-//  * ua2a_copy_kernel    -- strided block copy used by the per-plane form of
-//    the chunked exchange (a capped grid on the direct path) to move the
-//    one-plane window into the output after each plane's permutation
-//    launch.
+//    plane (fill from the input, then each lane stores its chunks into the
+//    window, reads them back and stores them to the output).
+//  * ua2a_copy_kernel    -- contiguous block copy: mode 0's unpack of a
+//    receiver's window into its output.
 //  * ua2a_ranks_kernel   -- the direct kernel's scheme over per-rank
 //    allocations (pointer tables) and a range of sending ranks;
 //    ua2a_lds_ranks_kernel -- the LDS kernel over them.
@@ -246,6 +245,25 @@ __global__ __launch_bounds__(kDirectBlock) void ua2a_chunked_kernel(DirectGeom g
         chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, false>(g, d, c, block, threadIdx.x);
 }
 
+// The same on a flat grid capped below the tile count (a `blocks` hint):
+// workgroup b moves tiles b, b + gridDim.x, ... each through all B planes.
+template <int VB, bool MODE1>
+__global__ __launch_bounds__(kDirectBlock) void ua2a_chunked_flat_kernel(DirectGeom g, ChunkedGeom c)
+{
+    flat_args_up_front(g);
+    asm volatile("" ::"s"(c.out), "s"(c.step), "s"(c.plane), "s"(c.planes));
+    for (uint64_t t = blockIdx.x; t < g.num_tiles; t += gridDim.x) {
+        uint32_t slab;
+        const DirectTile d = direct_tile<MODE1>(g, static_cast<uint32_t>(t), &slab);
+        if (d.nvec == 0) continue;                                // padding tile of the grouped order
+        const uint32_t block = chunked_block<MODE1>(g, slab);
+        if (d.nvec == ChunkedLane<VB>::kVecs * kDirectBlock)
+            chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, true>(g, d, c, block, threadIdx.x);
+        else
+            chunked_tile_body<StreamMem, VB, MODE1, kDirectBlock, false>(g, d, c, block, threadIdx.x);
+    }
+}
+
 // The credits of a publishing exchange's last part.
 __global__ __launch_bounds__(kWaitBlock) void ua2a_signal_kernel(SignalGeom g)
 {
@@ -460,6 +478,19 @@ const void* ranks_fn(int vb)
 }
 
 template <bool MODE1>
+const void* chunked_flat_fn(int vb)
+{
+    switch (vb) {
+    case 16: return reinterpret_cast<const void*>(&ua2a_chunked_flat_kernel<16, MODE1>);
+    case 8: return reinterpret_cast<const void*>(&ua2a_chunked_flat_kernel<8, MODE1>);
+    case 4: return reinterpret_cast<const void*>(&ua2a_chunked_flat_kernel<4, MODE1>);
+    case 2: return reinterpret_cast<const void*>(&ua2a_chunked_flat_kernel<2, MODE1>);
+    case 1: return reinterpret_cast<const void*>(&ua2a_chunked_flat_kernel<1, MODE1>);
+    default: return nullptr;
+    }
+}
+
+template <bool MODE1>
 const void* lds_chunked_fn(int g)
 {
     switch (g) {
@@ -552,8 +583,11 @@ int backend_launch(const Launch& L, void* stream)
         arg = &dg;
         break;
     case Kernel::Chunked:
-        if (!L.grid3d || L.direct.sig_count) return static_cast<int>(hipErrorInvalidValue);
-        fn = L.mode ? chunked_fn<true>(L.width) : chunked_fn<false>(L.width);
+        if (L.direct.sig_count) return static_cast<int>(hipErrorInvalidValue);
+        if (L.grid3d)
+            fn = L.mode ? chunked_fn<true>(L.width) : chunked_fn<false>(L.width);
+        else
+            fn = L.mode ? chunked_flat_fn<true>(L.width) : chunked_flat_fn<false>(L.width);
         arg = &dg;
         arg2 = const_cast<ChunkedGeom*>(&L.chunk);
         break;
