@@ -98,6 +98,8 @@ typedef struct ua2a_launch_info_s {
     int32_t lds_rows;      /* rows per LDS tile (LDS path), else 0 */
     int32_t grid_dims;     /* 3: a 3-D grid (direct path by default, every per-rank launch); else 1 */
     int32_t chunked_form;  /* 0: not chunked; else UA2A_CHUNKED_ONE_LAUNCH */
+    int32_t lds_bytes;     /* dynamic LDS per workgroup (LDS path), else 0 */
+    int32_t lds_planes;    /* chunked LDS path: batch planes held in LDS at once (1..B), else 0 */
 } ua2a_launch_info_t;
 
 /*

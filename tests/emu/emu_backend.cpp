@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "ua2a_bodies.h"
@@ -28,6 +29,9 @@ const uint8_t* g_win = nullptr;
 size_t g_win_bytes = 0;
 std::vector<int64_t> g_win_owner;     // -1: never stored
 int64_t g_lane_id = 0;                // tile * 64 + lane of the running body
+// LDS chunked kernel: the running lane's tile and lane; CheckedMem::win_plane
+// makes its writer id (tile, plane, lane)
+uint32_t g_lane_tile = 0, g_lane_tid = 0, g_lane_planes = 0;
 }  // namespace
 
 // PlainMem, with every tile store checked against the tile's written range
@@ -41,7 +45,19 @@ struct CheckedMem : PlainMem {
             fprintf(stderr, "emu: window access outside the window\n");
             abort();
         }
+        if (g_lane_id == -2) {
+            fprintf(stderr, "emu: window access before the lane named its plane\n");
+            abort();
+        }
         return static_cast<size_t>(b - g_win);
+    }
+    static void win_plane(uint32_t p)
+    {
+        if (p >= g_lane_planes) {
+            fprintf(stderr, "emu: window plane %u of %u\n", p, g_lane_planes);
+            abort();
+        }
+        g_lane_id = (static_cast<int64_t>(g_lane_tile) * g_lane_planes + p) * kLdsBlock + g_lane_tid;
     }
     template <class T>
     static void st_win(T* p, T v)
@@ -258,7 +274,9 @@ void run_lds_chunked(const Launch& L)
     g_win = M1 ? g.p_ptr : g.a_ptr;
     g_win_bytes = static_cast<size_t>(g.w) * static_cast<size_t>(c.plane);
     g_win_owner.assign(g_win_bytes, -1);
-    std::vector<uint8_t> lds(g.lds_bytes);
+    // exactly the launch's LDS (stage images), so an access past it is a heap
+    // overflow under the sanitizer build
+    std::vector<uint8_t> lds(L.lds_bytes);
     std::vector<uint8_t> seen(g.num_tiles, 0);
     for (uint32_t slot = 0; slot < g.num_slots; ++slot) {
         const uint32_t t = lds_slot_tile(g, slot);
@@ -267,17 +285,26 @@ void run_lds_chunked(const Launch& L)
             fprintf(stderr, "emu: LDS tile %u visited twice\n", t);
             abort();
         }
-        for (uint32_t p = 0; p < c.planes; ++p) {
-            const int64_t off = static_cast<int64_t>(p) * c.plane;
-            const PlaneBases bases{g, M1 ? 0 : off, M1 ? off : 0};
-            const LdsTile d = lds_tile(g, bases, t);
+        // as the kernel: `stage` planes filled (one image each), a barrier,
+        // then each lane drains them plane after plane, then a barrier
+        for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
+            const uint32_t n = std::min(c.stage, c.planes - p0);
             memset(lds.data(), 0xA5, lds.size());
-            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-                lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid, lds.data());
+            for (uint32_t k = 0; k < n; ++k) {
+                const int64_t off = static_cast<int64_t>(p0 + k) * c.plane;
+                const PlaneBases bases{g, M1 ? 0 : off, M1 ? off : 0};
+                const LdsTile d = lds_tile(g, bases, t);
+                for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+                    lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid,
+                                                                                      lds.data() + k * c.image);
+            }
             for (uint32_t tid = 0; tid < kLdsBlock; ++tid) {
-                g_lane_id = (static_cast<int64_t>(t) * c.planes + p) * kLdsBlock + tid;
-                lds_drain_through_window<CheckedMem, G, M1, kLdsBlock, (M1 ? 1 : kLdsReadback)>(g, bases, d, c, p,
-                                                                                              tid, lds.data());
+                g_lane_tile = t;
+                g_lane_tid = tid;
+                g_lane_planes = c.planes;
+                g_lane_id = -2;      // win_plane() must name the plane before any window access
+                lds_chunked_drain<CheckedMem, G, M1, kLdsBlock, kLdsReadback, kLdsChunkStage>(g, c, t, p0, n, tid,
+                                                                                          lds.data());
             }
         }
     }
@@ -514,7 +541,10 @@ int backend_launch(const Launch& L, void*)
         const LdsGeom& g = L.lds;
         const LdsChunkGeom& c = L.lds_chunk;
         if (L.grid_y != 1 || L.grid_z != 1) return 7;
-        if (L.lds_bytes != g.lds_bytes || g.lds_bytes < 16 + g.rows_per_tile * g.lrow || g.lrow != g.row + g.pad ||
+        if (c.image != g.lds_bytes || c.image % 16 != 0 || c.stage < 1 || c.stage > c.planes ||
+            c.stage > kLdsChunkStage || (c.stage > 1 && c.plane % 16 != 0) ||
+            static_cast<uint64_t>(L.lds_bytes) != static_cast<uint64_t>(c.stage) * c.image ||
+            L.lds_bytes > 65536 || g.lds_bytes < 16 + g.rows_per_tile * g.lrow || g.lrow != g.row + g.pad ||
             (g.pad && L.width != 16) || g.num_slots < g.num_tiles ||
             (g.xlog && g.num_slots % (kXcds << g.xlog) != 0) || L.grid > g.num_slots || g.nb != 1 ||
             g.p_plane != 0 || g.a_plane != 0 || c.planes < 1 || c.plane % L.width != 0 ||

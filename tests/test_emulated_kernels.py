@@ -278,15 +278,20 @@ def test_emulated_chunked_lds_one_launch(emu, shape, mis):
     """The LDS path's chunked exchange is one launch of the chunked LDS
     kernel whatever the bases' offsets and the plane size: window chunks go to
     the output as whole 16-byte stores where the output lies at the window's
-    offset modulo 16, else as pieces.  It matches the oracle, keeps the guard
-    bands and ends with the last plane in the window; the emulation checks
-    that each lane reads back only window bytes that it stored in the same
-    plane, and that every window byte is written."""
+    offset modulo 16, else as pieces.  LDS holds two planes at once when a
+    plane is a multiple of 16 bytes (one otherwise, and at the end of an odd
+    count).  It matches the oracle, keeps the guard bands and ends with the
+    last plane in the window; the emulation checks that each lane reads back
+    only window bytes that it stored in the same plane, and that every window
+    byte is written."""
     w, B, S, H, D, e = shape
+    plane = S * H * D * e
     for mode in (0, 1):
         x, y, info, bufs = emu_exchange(emu, shape, mode, True, ua.UA2A_PATH_LDS, *mis, seed=41 + B + mode)
         assert info.path == ua.UA2A_PATH_LDS, mode
         assert info.chunked_form == ua.UA2A_CHUNKED_ONE_LAUNCH and info.launches == 1, mode
+        assert info.lds_planes == (min(B, 2) if plane % 16 == 0 else 1), mode
+        assert info.lds_bytes % 16 == 0 and info.lds_bytes <= 65536, mode
         assert emu.ua2a_emu_kernel_count(9) == 1 and emu.ua2a_emu_kernel_count(2) == 0, mode
         assert np.array_equal(y, oracle_bytes(x, shape, mode)), mode
         assert all(b.guards_intact() for b in bufs), mode

@@ -634,6 +634,7 @@ def test_chunked_lds_in_one_launch(shape, mis):
         info = plan.describe(xi, mode, True, out=yo)
         assert info["path"] == ua.UA2A_PATH_LDS
         assert info["launches"] == 1 and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
+        assert info["lds_planes"] == (min(B, 2) if lay["tensor_bytes"] // (w * B) % 16 == 0 else 1)
         note(f"chunked lds one launch {shape} mis={mis} mode={mode} {info}")
         plan.exchange(xi, mode, True, out=yo)
         torch.cuda.synchronize()

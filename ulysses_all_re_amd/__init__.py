@@ -72,7 +72,8 @@ class ua2a_launch_info_t(ctypes.Structure):
                 ("block", ctypes.c_int32), ("launches", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("tiles", ctypes.c_int64),
                 ("lds_rows", ctypes.c_int32), ("grid_dims", ctypes.c_int32),
-                ("chunked_form", ctypes.c_int32)]
+                ("chunked_form", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("lds_planes", ctypes.c_int32)]
 
 
 class UA2AError(RuntimeError):

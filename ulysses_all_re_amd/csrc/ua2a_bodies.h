@@ -27,6 +27,9 @@ struct PlainMem {
     template <class T>
     UA2A_HD static void st_win(T* p, T v) { *p = v; }
     UA2A_HD static void win_order() {}
+    // The plane whose window accesses follow (the host emulation records
+    // it with each window byte's writer; nothing to do elsewhere).
+    UA2A_HD static void win_plane(uint32_t) {}
     // A store at byte `off` of a tile's written range [base, base + nbytes).
     template <class T>
     UA2A_HD static void st_tile(uint8_t* base, uint32_t, uint32_t off, T v)
@@ -506,129 +509,198 @@ UA2A_HD void st_chunk(uint8_t* to, u32x4 v)
     for (uint32_t o = 0; o < 16; o += G) Mem::st_piece(reinterpret_cast<T*>(to + o), PieceOf<G>::get(v, o));
 }
 
-// Mode 1 of lds_drain_through_window: the tile's P span, LDS image ->
-// window (at wchunk0) -> output (at ochunk0); OUT16: the two share their
-// 16-byte chunks, so whole chunks go out through the span's buffer range.
-template <class Mem, int G, uint32_t BS, uint32_t U, bool OUT16>
-UA2A_HD void p_span_through_window(const LdsGeom& g, const LdsTile& d, uint32_t tid, const uint8_t* lds,
-                                   uint8_t* wchunk0, uint8_t* ochunk0)
+// Mode 1 of lds_drain_through_window: the tile's P span, LDS images ->
+// window (at wchunk0) -> output (at ochunk0 for the first plane, plane bytes
+// further for each next one); OUT16: the output shares the window's 16-byte
+// chunks, so whole chunks go out through the span's buffer range.
+template <class Mem, int G, uint32_t BS, uint32_t U, uint32_t S, bool OUT16>
+UA2A_HD void p_span_through_window(const LdsGeom& g, const LdsTile& d, const LdsChunkGeom& c, uint32_t p0,
+                                   uint32_t n, uint32_t tid, const uint8_t* lds, uint8_t* wchunk0,
+                                   uint8_t* ochunk0)
 {
     typedef typename Piece<G>::T T;
     const uint32_t pch = span_chunks(d.head, d.p_len);
     for (uint32_t c0 = tid; c0 < pch; c0 += BS * U) {
-        u32x4 v[U] = {};
+        u32x4 v[S][U] = {};
         bool full[U];
 #pragma unroll
-        for (uint32_t k = 0; k < U; ++k) {
-            const uint32_t ci = c0 + k * BS;
-            const uint32_t lo = ci * 16;
-            full[k] = ci < pch && chunk_full(lo, d.head, d.p_len);
-            if (full[k]) {
-                Mem::st_win(reinterpret_cast<u32x4*>(wchunk0 + lo),
-                            *reinterpret_cast<const u32x4*>(lds + lds_pos_of_p(g, lo)));
-            } else if (ci < pch) {
-                const uint32_t x1 = umin32(lo + 16, d.head + d.p_len);
-                for (uint32_t x = umax32(lo, d.head); x < x1; x += G) {
-                    T* const wp = reinterpret_cast<T*>(wchunk0 + x);
-                    Mem::st_win(wp, *reinterpret_cast<const T*>(lds + x));
-                    Mem::win_order();
-                    Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x), Mem::ld_win(wp));
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t ci = c0 + u * BS;
+            full[u] = ci < pch && chunk_full(ci * 16, d.head, d.p_len);
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < S; ++k) {
+            if (k >= n) break;
+            Mem::win_plane(p0 + k);
+            const uint8_t* img = lds + k * c.image;
+            uint8_t* const och = ochunk0 + static_cast<int64_t>(k) * c.plane;
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u) {
+                const uint32_t ci = c0 + u * BS;
+                const uint32_t lo = ci * 16;
+                if (full[u]) {
+                    Mem::st_win(reinterpret_cast<u32x4*>(wchunk0 + lo),
+                                *reinterpret_cast<const u32x4*>(img + lds_pos_of_p(g, lo)));
+                } else if (ci < pch) {
+                    const uint32_t x1 = umin32(lo + 16, d.head + d.p_len);
+                    for (uint32_t x = umax32(lo, d.head); x < x1; x += G) {
+                        T* const wp = reinterpret_cast<T*>(wchunk0 + x);
+                        Mem::st_win(wp, *reinterpret_cast<const T*>(img + x));
+                        Mem::win_order();
+                        Mem::st_piece(reinterpret_cast<T*>(och + x), Mem::ld_win(wp));
+                    }
                 }
             }
+            Mem::win_order();
+#pragma unroll
+            for (uint32_t u = 0; u < U; ++u)
+                if (full[u]) v[k][u] = Mem::ld_win(reinterpret_cast<const u32x4*>(wchunk0 + (c0 + u * BS) * 16));
         }
-        Mem::win_order();
 #pragma unroll
-        for (uint32_t k = 0; k < U; ++k)
-            if (full[k]) v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(wchunk0 + (c0 + k * BS) * 16));
+        for (uint32_t k = 0; k < S; ++k) {
+            if (k >= n) break;
+            uint8_t* const och = ochunk0 + static_cast<int64_t>(k) * c.plane;
 #pragma unroll
-        for (uint32_t k = 0; k < U; ++k) {
-            if (!full[k]) continue;
-            if (OUT16)
-                Mem::st_tile(ochunk0, pch * 16, (c0 + k * BS) * 16, v[k]);
-            else
-                st_chunk<Mem, G>(ochunk0 + (c0 + k * BS) * 16, v[k]);
+            for (uint32_t u = 0; u < U; ++u) {
+                if (!full[u]) continue;
+                if (OUT16)
+                    Mem::st_tile(och, pch * 16, (c0 + u * BS) * 16, v[k][u]);
+                else
+                    st_chunk<Mem, G>(och + (c0 + u * BS) * 16, v[k][u]);
+            }
         }
     }
 }
 
-// One-launch chunked exchange on the LDS path, second phase of plane `p`
-// (after the workgroup barrier that follows lds_fill): LDS image -> the
-// tile's window spans -> plane p of the output (see LdsChunkGeom).  Each lane
-// stores its chunks of the spans into the window, reads them back and stores
-// them to the output, U chunks at a time; the same lane handles the same
-// chunks in every plane, so a lane reads back only what it stored itself and
-// the window needs no barrier.  Window chunks are aligned 16-byte chunks of
-// the window, read back as 16-byte vectors; each goes to the output in one
-// 16-byte store when the output lies at the same offset modulo 16 (the
-// usual case), else in G-byte pieces (every offset between the two is a
-// multiple of G).  A partial first or last chunk moves as its in-span G-byte
-// pieces.
+// One-launch chunked exchange on the LDS path, second phase for planes p0 ..
+// p0 + n - 1 (after the workgroup barrier that follows their fills; image k
+// of LDS, image bytes apart, holds plane p0 + k): LDS images -> the tile's
+// window spans -> those planes of the output (see LdsChunkGeom).  Each lane
+// takes U of its chunks of the spans at a time and, plane after plane,
+// stores them into the window and reads them back, then stores what it read
+// to the planes' output.  The same lane handles the same chunks in every
+// plane, so a lane reads back only what it stored itself and the window
+// needs no barrier; a later plane's store to a window chunk follows the
+// earlier plane's load of it in the lane's program order, which the hardware
+// keeps for accesses of one lane to one address.  Window chunks are aligned
+// 16-byte chunks of the window, read back as 16-byte vectors; each goes to
+// the output in one 16-byte store when the output lies at the same offset
+// modulo 16 (the usual case), else in G-byte pieces (every offset between
+// the two is a multiple of G).  A partial first or last chunk moves as its
+// in-span G-byte pieces.  With n > 1 the host guarantees that a plane is a
+// multiple of 16 bytes, so `d` (the tile as seen from plane p0) places every
+// plane's image alike and the output's offset modulo 16 is the same in
+// every plane.
 //   mode 0: the w A spans (window block r = head block r), gathered from
 //           the image as lds_drain does;
 //   mode 1: the P span (window block j = the tile's rank), copied out of it.
-template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases>
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, uint32_t S, class Bases>
 UA2A_HD void lds_drain_through_window(const LdsGeom& g, const Bases& bases, const LdsTile& d,
-                                      const LdsChunkGeom& c, uint32_t p, uint32_t tid, const uint8_t* lds)
+                                      const LdsChunkGeom& c, uint32_t p0, uint32_t n, uint32_t tid,
+                                      const uint8_t* lds)
 {
     typedef typename Piece<G>::T T;
-    // window -> output, for block 0 of plane p (plus rank_step per block)
+    // window -> output, for block 0 of plane p0 (plus rank_step per block)
     const uintptr_t wbase = reinterpret_cast<uintptr_t>(MODE1 ? g.p_ptr : g.a_ptr);
     const int64_t shift = static_cast<int64_t>(reinterpret_cast<uintptr_t>(c.out) - wbase) +
-                          static_cast<int64_t>(p) * c.plane;
+                          static_cast<int64_t>(p0) * c.plane;
     if (!MODE1) {
         const uint32_t stride = d.stride;
         const uint32_t total = g.w * stride;
         for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
-            u32x4 v[U] = {};
-            uint8_t* win[U];
-            uint8_t* to[U];
+            u32x4 v[S][U] = {};
+            uint8_t* wc[U];        // the chunk's 16-aligned window span base
+            uint8_t* oc[U];        // ... and the output's, plane p0
+            uint32_t rr[U], lo[U], ah[U];
+            int kind[U];           // 0: no chunk, 1: whole chunk, 2: partial chunk
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k) {
-                win[k] = to[k] = nullptr;
-                const uint32_t i = i0 + k * BS;
+            for (uint32_t u = 0; u < U; ++u) {
+                kind[u] = 0;
+                wc[u] = oc[u] = nullptr;
+                rr[u] = lo[u] = ah[u] = 0;
+                const uint32_t i = i0 + u * BS;
                 if (i >= total) continue;
                 const uint32_t r = fdiv(i, d.d_stride);
                 const uint32_t ci = i - r * stride;
                 uint8_t* wspan = bases.a_rank_base(r) + d.a_start0;
                 const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(wspan) & 15u);
                 if (ci >= span_chunks(ahead, d.a_len)) continue;
-                uint8_t* wchunk0 = wspan - ahead;
-                uint8_t* ochunk0 = reinterpret_cast<uint8_t*>(
-                    reinterpret_cast<uintptr_t>(wchunk0) + shift + static_cast<int64_t>(r) * c.rank_step);
-                const uint32_t lo = ci * 16;
-                if (chunk_full(lo, ahead, d.a_len)) {
-                    win[k] = wchunk0 + lo;
-                    to[k] = ochunk0 + lo;
-                    Mem::st_win(reinterpret_cast<u32x4*>(win[k]), gather_a_chunk<G>(g, d, r, lo - ahead, lds));
-                } else {
-                    const uint32_t x1 = umin32(lo + 16, ahead + d.a_len);
-                    for (uint32_t x = umax32(lo, ahead); x < x1; x += G) {
-                        T* const wp = reinterpret_cast<T*>(wchunk0 + x);
-                        Mem::st_win(wp, *reinterpret_cast<const T*>(lds + lds_pos_of_a(g, d, r, x - ahead)));
-                        Mem::win_order();
-                        Mem::st_piece(reinterpret_cast<T*>(ochunk0 + x), Mem::ld_win(wp));
+                wc[u] = wspan - ahead;
+                oc[u] = reinterpret_cast<uint8_t*>(
+                    reinterpret_cast<uintptr_t>(wc[u]) + shift + static_cast<int64_t>(r) * c.rank_step);
+                rr[u] = r;
+                lo[u] = ci * 16;
+                ah[u] = ahead;
+                kind[u] = chunk_full(lo[u], ahead, d.a_len) ? 1 : 2;
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+                Mem::win_plane(p0 + k);
+                const uint8_t* img = lds + k * c.image;
+                const int64_t pk = static_cast<int64_t>(k) * c.plane;
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u) {
+                    if (kind[u] == 1) {
+                        Mem::st_win(reinterpret_cast<u32x4*>(wc[u] + lo[u]),
+                                    gather_a_chunk<G>(g, d, rr[u], lo[u] - ah[u], img));
+                    } else if (kind[u] == 2) {
+                        const uint32_t x1 = umin32(lo[u] + 16, ah[u] + d.a_len);
+                        for (uint32_t x = umax32(lo[u], ah[u]); x < x1; x += G) {
+                            T* const wp = reinterpret_cast<T*>(wc[u] + x);
+                            Mem::st_win(wp, *reinterpret_cast<const T*>(img + lds_pos_of_a(g, d, rr[u], x - ah[u])));
+                            Mem::win_order();
+                            Mem::st_piece(reinterpret_cast<T*>(oc[u] + pk + x), Mem::ld_win(wp));
+                        }
                     }
                 }
+                Mem::win_order();
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u)
+                    if (kind[u] == 1) v[k][u] = Mem::ld_win(reinterpret_cast<const u32x4*>(wc[u] + lo[u]));
             }
-            Mem::win_order();
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k)
-                if (win[k] != nullptr) v[k] = Mem::ld_win(reinterpret_cast<const u32x4*>(win[k]));
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+                const int64_t pk = static_cast<int64_t>(k) * c.plane;
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k)
-                if (to[k] != nullptr) st_chunk<Mem, G>(to[k], v[k]);
+                for (uint32_t u = 0; u < U; ++u)
+                    if (kind[u] == 1) st_chunk<Mem, G>(oc[u] + pk + lo[u], v[k][u]);
+            }
         }
     } else {
         uint8_t* wchunk0 = d.p_span - d.head;
         uint8_t* ochunk0 = reinterpret_cast<uint8_t*>(
             reinterpret_cast<uintptr_t>(wchunk0) + shift + static_cast<int64_t>(d.j) * c.rank_step);
         // whether the output span's chunks line up with the window's (the
-        // same for the whole tile; a loop of its own for each case, since a
-        // per-store test measured 6-13 % slower)
+        // same for the whole tile and every plane of the stage; a loop of its
+        // own for each case, since a per-store test measured 6-13 % slower)
         if (G == 16 || (reinterpret_cast<uintptr_t>(ochunk0) & 15u) == 0)
-            p_span_through_window<Mem, G, BS, U, true>(g, d, tid, lds, wchunk0, ochunk0);
+            p_span_through_window<Mem, G, BS, U, S, true>(g, d, c, p0, n, tid, lds, wchunk0, ochunk0);
         else
-            p_span_through_window<Mem, G, BS, U, false>(g, d, tid, lds, wchunk0, ochunk0);
+            p_span_through_window<Mem, G, BS, U, S, false>(g, d, c, p0, n, tid, lds, wchunk0, ochunk0);
+    }
+}
+
+// The second phase of one stage of the LDS chunked kernel: planes p0 ..
+// p0 + n - 1 of tile t, whose images fill LDS (image bytes apart).  Mode 0
+// drains them in one pass (each lane's chunks through the window plane after
+// plane, then their output stores; U0 chunks per lane at a time, S >= n);
+// mode 1 one plane after the other, one chunk per lane at a time (the
+// one-pass form measured 2-6 % slower there, 2.5-6 % faster in mode 0).
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U0, uint32_t S>
+UA2A_HD void lds_chunked_drain(const LdsGeom& g, const LdsChunkGeom& c, uint32_t t, uint32_t p0, uint32_t n,
+                               uint32_t tid, const uint8_t* lds)
+{
+    if (!MODE1) {
+        const PlaneBases bases{g, static_cast<int64_t>(p0) * c.plane, 0};
+        lds_drain_through_window<Mem, G, false, BS, U0, S>(
+            g, bases, lds_tile(g, bases, t), c, p0, n, tid, lds);
+    } else {
+        const PlaneBases bases{g, 0, 0};     // the drain reads no input: the tile as plane 0 sees it
+        const LdsTile d = lds_tile(g, bases, t);
+        for (uint32_t k = 0; k < n; ++k)
+            lds_drain_through_window<Mem, G, true, BS, 1, 1>(g, bases, d, c, p0 + k, 1, tid, lds + k * c.image);
     }
 }
 

@@ -498,19 +498,23 @@ struct PlaneBases {
 // A chunked exchange in one launch on the LDS path.  LdsGeom describes plane
 // 0 of every rank and the window ([w][one plane] in the layout of the output
 // side: the A side in mode 0, the P side in mode 1).  Each workgroup keeps
-// its LDS tile for all planes: per plane p it fills LDS from the input moved
-// by p * plane bytes, drains LDS into the tile's window spans, and, after a
-// workgroup barrier, copies those spans to plane p of the output.  Window
-// byte x of block k lands at out + x + k * rank_step + p * plane (block k is
-// head block r in mode 0, the tile's rank j in mode 1; rank_step = the
-// output's rank stride minus the window's, plane bytes).  Every such offset
-// is a multiple of the piece size G, so a window chunk goes to the output in
-// one 16-byte store when the two agree modulo 16, else in G-byte pieces.
+// its LDS tile for all planes, `stage` planes at a time: it fills one LDS
+// image per plane (image bytes apart) from the input moved by p * plane
+// bytes, and after a workgroup barrier each lane, plane after plane, stores
+// its chunks of the tile's window spans into the window, reads them back and
+// stores them to plane p of the output.  Window byte x of block k lands at
+// out + x + k * rank_step + p * plane (block k is head block r in mode 0, the
+// tile's rank j in mode 1; rank_step = the output's rank stride minus the
+// window's, plane bytes).  Every such offset is a multiple of the piece size
+// G, so a window chunk goes to the output in one 16-byte store when the two
+// agree modulo 16, else in G-byte pieces.
 struct LdsChunkGeom {
     uint8_t* out;          // the output: plane 0 of rank 0
     int64_t rank_step;     // B * plane - plane
     int64_t plane;         // bytes of one batch plane of one rank
     uint32_t planes;       // B
+    uint32_t stage;        // planes filled into LDS before they are drained, 1..B
+    uint32_t image;        // LDS bytes of one plane's image (LdsGeom::lds_bytes)
 };
 
 // Per-rank allocations: one base pointer per rank and side (the rank strides

@@ -409,6 +409,16 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
             L.lds_chunk.rank_step = rank_bytes - plane;
             L.lds_chunk.plane = plane;
             L.lds_chunk.planes = static_cast<uint32_t>(p->B);
+            // planes staged per fill: up to kLdsChunkStage, as many images as
+            // fit kLdsChunkLds, at least one (an image alone is within the tile
+            // limit); several only when a plane is a multiple of 16 bytes, so
+            // that every plane's image is laid out alike
+            L.lds_chunk.image = L.lds.lds_bytes;            // a multiple of 16
+            uint32_t stage = plane % 16 == 0 ? kLdsChunkLds / L.lds.lds_bytes : 1u;
+            if (stage > kLdsChunkStage) stage = kLdsChunkStage;
+            if (stage > L.lds_chunk.planes) stage = L.lds_chunk.planes;
+            L.lds_chunk.stage = stage < 1 ? 1 : stage;
+            L.lds_bytes = L.lds_chunk.stage * L.lds_chunk.image;
             return;
         }
         // mode 0 with the grouped tile order (4 KiB-multiple rows): the chunked
@@ -1013,6 +1023,8 @@ int ua2a_describe(ua2a_plan_t plan, int32_t mode, int32_t chunked, const void* i
     info->lds_rows = lds ? static_cast<int32_t>(pr.perm.lds.rows_per_tile) : 0;
     info->grid_dims = pr.perm.grid3d ? 3 : 1;
     info->chunked_form = chunked ? UA2A_CHUNKED_ONE_LAUNCH : 0;
+    info->lds_bytes = lds ? static_cast<int32_t>(pr.perm.lds_bytes) : 0;
+    info->lds_planes = pr.perm.kernel == Kernel::LdsChunked ? static_cast<int32_t>(pr.perm.lds_chunk.stage) : 0;
     return UA2A_OK;
 }
 
@@ -1036,6 +1048,7 @@ int ua2a_describe_ranks(ua2a_plan_t plan, int32_t mode, const void* const* in_pt
     info->launches = 1;
     info->lds_rows = lds ? static_cast<int32_t>(L.lds.rows_per_tile) : 0;
     info->grid_dims = lds ? 1 : 3;
+    info->lds_bytes = lds ? static_cast<int32_t>(L.lds_bytes) : 0;
     return UA2A_OK;
 }
 

@@ -43,6 +43,8 @@ constexpr uint32_t kLdsChunkTileMode1 = 8192;   // ... and mode 1 (half the unch
                                                 //   window spans in flight then stay within L2)
 constexpr int64_t kLineBytes = 128;             // cache line: LDS tiles align their A spans to it
 constexpr uint32_t kLdsXcdLog = 2;              // LDS tiles: 2^kLdsXcdLog consecutive tiles per XCD turn
+constexpr uint32_t kLdsChunkStage = 2;          // one-launch chunked LDS path: planes per LDS fill
+constexpr uint32_t kLdsChunkLds = 65536;        // ... within this much LDS per workgroup
 constexpr uint32_t kLdsReadback = 2;            // one-launch chunked LDS path: window chunks per lane in
                                                 //   flight, mode 0 (mode 1: one; measured 5 % faster there,
                                                 //   6 % slower in mode 0; four: slower in both)

@@ -74,6 +74,7 @@ struct StreamMem {
     template <class T>
     __device__ static void st_win(T* p, T v) { *p = v; }
     __device__ static void win_order() { asm volatile("" ::: "memory"); }
+    __device__ static void win_plane(uint32_t) {}
     // A store at byte `off` of a tile's written range [base, base + nbytes),
     // through a buffer resource over that range (a store outside it would be
     // dropped by the hardware rather than land elsewhere).
@@ -327,31 +328,34 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, Ld
 }
 
 // A whole chunked exchange in one launch on the LDS path (see LdsChunkGeom):
-// each workgroup keeps its tile through all B planes -- fill LDS from plane p
-// of the input, then every lane stores its chunks of the tile's window spans,
-// reads them back and stores them to plane p of the output.  A lane reads
-// back only window bytes that it stored, so the window needs no barrier; the
-// barrier after the drain keeps the next plane's fill from overwriting LDS
-// that a lane still reads.
+// each workgroup keeps its tile through all B planes, `stage` planes at a
+// time -- fill one LDS image per plane, then every lane, plane after plane,
+// stores its chunks of the tile's window spans into the window and reads them
+// back, and stores them to that plane of the output.  A lane reads back only window bytes that
+// it stored, so the window needs no barrier; the barrier after the drain
+// keeps the next stage's fill from overwriting LDS that a lane still reads.
 template <int G, bool MODE1>
 __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, LdsChunkGeom c)
 {
     args_up_front(g);
-    asm volatile("" ::"s"(c.out), "s"(c.rank_step), "s"(c.plane), "s"(c.planes));
+    asm volatile("" ::"s"(c.out), "s"(c.rank_step), "s"(c.plane), "s"(c.planes), "s"(c.stage), "s"(c.image));
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
     for (uint64_t slot = blockIdx.x; slot < g.num_slots; slot += gridDim.x) {
         const uint32_t t = lds_slot_tile(g, static_cast<uint32_t>(slot));
         if (t >= g.num_tiles) continue;      // the same for the whole workgroup
-        for (uint32_t p = 0; p < c.planes; ++p) {
-            const int64_t off = static_cast<int64_t>(p) * c.plane;
-            const PlaneBases bases{g, MODE1 ? 0 : off, MODE1 ? off : 0};     // the input side moves
-            const LdsTile d = lds_tile(g, bases, t);
-            lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, threadIdx.x, lds);
+        for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
+            const uint32_t n = umin32(c.stage, c.planes - p0);
+            for (uint32_t k = 0; k < n; ++k) {
+                const int64_t off = static_cast<int64_t>(p0 + k) * c.plane;
+                const PlaneBases bases{g, MODE1 ? 0 : off, MODE1 ? off : 0};     // the input side moves
+                lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(
+                    g, bases, lds_tile(g, bases, t), threadIdx.x, lds + k * c.image);
+            }
             __syncthreads();
-            lds_drain_through_window<StreamMem, G, MODE1, kLdsBlock, (MODE1 ? 1 : kLdsReadback)>(
-                g, bases, d, c, p, threadIdx.x, lds);
-            __syncthreads();   // the next fill overwrites the LDS image
+            lds_chunked_drain<StreamMem, G, MODE1, kLdsBlock, kLdsReadback, kLdsChunkStage>(g, c, t, p0, n,
+                                                                                    threadIdx.x, lds);
+            __syncthreads();   // the next stage's fill overwrites the LDS images
         }
     }
 }
