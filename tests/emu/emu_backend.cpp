@@ -290,14 +290,9 @@ void run_lds_chunked(const Launch& L)
         for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
             const uint32_t n = std::min(c.stage, c.planes - p0);
             memset(lds.data(), 0xA5, lds.size());
-            for (uint32_t k = 0; k < n; ++k) {
-                const int64_t off = static_cast<int64_t>(p0 + k) * c.plane;
-                const PlaneBases bases{g, M1 ? 0 : off, M1 ? off : 0};
-                const LdsTile d = lds_tile(g, bases, t);
-                for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
-                    lds_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(g, bases, d, tid,
-                                                                                      lds.data() + k * c.image);
-            }
+            for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
+                lds_chunked_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1), kLdsChunkStage>(
+                    g, c, t, p0, n, tid, lds.data());
             for (uint32_t tid = 0; tid < kLdsBlock; ++tid) {
                 g_lane_tile = t;
                 g_lane_tid = tid;

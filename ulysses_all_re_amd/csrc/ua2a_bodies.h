@@ -357,36 +357,57 @@ UA2A_HD void place_a_part_chunk(const LdsGeom& g, const LdsTile& d, const PartCh
 // span's partial chunks piece by piece in its loop: a P span starts and ends
 // on a row, so they occur only with a misaligned base, and every other form
 // measured slower on aligned spans.
-template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases>
+// With S > 1 (the one-launch chunked kernel) one call fills the images of n
+// <= S batch planes: plane k's spans are the tile's moved by k * plane bytes,
+// its image lies k * image bytes into LDS, and every plane's loads go out
+// before any of their LDS stores.  The caller guarantees that plane is a
+// multiple of 16 bytes when n > 1, so `d` (the tile as the first plane sees
+// it) places every plane alike.
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, class Bases, uint32_t S = 1>
 UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, uint32_t tid,
-                      uint8_t* lds)
+                      uint8_t* lds, int64_t plane = 0, uint32_t image = 0, uint32_t n = 1)
 {
     if (!MODE1) {
         const uint8_t* pchunk0 = d.p_span - d.head;   // 16-aligned
         const uint32_t pch = span_chunks(d.head, d.p_len);
         for (uint32_t c0 = tid; c0 < pch; c0 += BS * U) {
-            u32x4 v[U] = {};
+            u32x4 v[S][U] = {};
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t c = c0 + k * BS;
-                if (c < pch && chunk_full(c * 16, d.head, d.p_len))
-                    v[k] = Mem::ld(reinterpret_cast<const u32x4*>(pchunk0 + c * 16));
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u) {
+                    const uint32_t c = c0 + u * BS;
+                    if (c < pch && chunk_full(c * 16, d.head, d.p_len))
+                        v[k][u] = Mem::ld(reinterpret_cast<const u32x4*>(pchunk0 + k * plane + c * 16));
+                }
             }
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t c = c0 + k * BS;
-                if (c >= pch) continue;
-                if (chunk_full(c * 16, d.head, d.p_len))
-                    *reinterpret_cast<u32x4*>(lds + lds_pos_of_p(g, c * 16)) = v[k];
-                else
-                    copy_partial_chunk<G>(pchunk0, lds, c * 16, d.head, d.p_len);
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+                uint8_t* const img = lds + k * image;
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u) {
+                    const uint32_t c = c0 + u * BS;
+                    if (c >= pch) continue;
+                    if (chunk_full(c * 16, d.head, d.p_len))
+                        *reinterpret_cast<u32x4*>(img + lds_pos_of_p(g, c * 16)) = v[k][u];
+                    else
+                        copy_partial_chunk<G>(pchunk0 + k * plane, img, c * 16, d.head, d.p_len);
+                }
             }
         }
     } else {
         // with G = 16 every A span is 16-aligned and has no partial chunk
         const PartChunk pc = G < 16 ? a_part_chunk(g, bases, d, tid) : PartChunk{};
-        u32x4 pv = {0u, 0u, 0u, 0u};
-        if (G < 16 && pc.valid) pv = Mem::ld_part(pc.src, pc.lo, pc.hi);
+        u32x4 pv[S] = {};
+#pragma unroll
+        for (uint32_t k = 0; k < S; ++k) {
+            if (k >= n) break;
+            if (G < 16 && pc.valid)
+                pv[k] = Mem::ld_part(reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(pc.src) + k * plane),
+                                     pc.lo, pc.hi);
+        }
         // the w spans' chunks as one flat index space, so every lane has work
         // even when one span is shorter than the workgroup; neighbouring lanes
         // take neighbouring chunks of one span (measured faster than putting
@@ -394,35 +415,53 @@ UA2A_HD void lds_fill(const LdsGeom& g, const Bases& bases, const LdsTile& d, ui
         const uint32_t stride = d.stride;      // chunk slots of the longest span
         const uint32_t total = g.w * stride;
         for (uint32_t i0 = tid; i0 < total; i0 += BS * U) {
-            u32x4 v[U] = {};
+            u32x4 v[S][U] = {};
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t i = i0 + k * BS;
-                if (i >= total) continue;
-                const uint32_t r = fdiv(i, d.d_stride);
-                const uint32_t c = i - r * stride;
-                const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
-                const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-                if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
-                    v[k] = Mem::ld(reinterpret_cast<const u32x4*>(aspan - ahead + c * 16));
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u) {
+                    const uint32_t i = i0 + u * BS;
+                    if (i >= total) continue;
+                    const uint32_t r = fdiv(i, d.d_stride);
+                    const uint32_t c = i - r * stride;
+                    const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
+                    const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+                    if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
+                        v[k][u] = Mem::ld(reinterpret_cast<const u32x4*>(aspan - ahead + k * plane + c * 16));
+                }
             }
 #pragma unroll
-            for (uint32_t k = 0; k < U; ++k) {
-                const uint32_t i = i0 + k * BS;
-                if (i >= total) continue;
-                const uint32_t r = fdiv(i, d.d_stride);
-                const uint32_t c = i - r * stride;
-                const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
-                const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
-                if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
-                    scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k], lds);
+            for (uint32_t k = 0; k < S; ++k) {
+                if (k >= n) break;
+                uint8_t* const img = lds + k * image;
+#pragma unroll
+                for (uint32_t u = 0; u < U; ++u) {
+                    const uint32_t i = i0 + u * BS;
+                    if (i >= total) continue;
+                    const uint32_t r = fdiv(i, d.d_stride);
+                    const uint32_t c = i - r * stride;
+                    const uint8_t* aspan = bases.a_rank_base(r) + d.a_start0;
+                    const uint32_t ahead = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(aspan) & 15u);
+                    if (c < span_chunks(ahead, d.a_len) && chunk_full(c * 16, ahead, d.a_len))
+                        scatter_a_chunk<G>(g, d, r, c * 16 - ahead, v[k][u], img);
+                }
             }
         }
-        if (G < 16 && pc.valid) place_a_part_chunk<G>(g, d, pc, pv, lds);
+#pragma unroll
+        for (uint32_t k = 0; k < S; ++k) {
+            if (k >= n) break;
+            if (G < 16 && pc.valid) place_a_part_chunk<G>(g, d, pc, pv[k], lds + k * image);
+        }
         for (uint32_t slot = tid + BS; G < 16 && slot < 2 * g.w; slot += BS) {
             const PartChunk more = a_part_chunk(g, bases, d, slot);
-            if (more.valid)
-                place_a_part_chunk<G>(g, d, more, Mem::ld_part(more.src, more.lo, more.hi), lds);
+            if (!more.valid) continue;
+            for (uint32_t k = 0; k < n; ++k)
+                place_a_part_chunk<G>(g, d, more,
+                                      Mem::ld_part(reinterpret_cast<const u32x4*>(
+                                                       reinterpret_cast<const uint8_t*>(more.src) + k * plane),
+                                                   more.lo, more.hi),
+                                      lds + k * image);
         }
     }
 }
@@ -679,6 +718,30 @@ UA2A_HD void lds_drain_through_window(const LdsGeom& g, const Bases& bases, cons
             p_span_through_window<Mem, G, BS, U, S, true>(g, d, c, p0, n, tid, lds, wchunk0, ochunk0);
         else
             p_span_through_window<Mem, G, BS, U, S, false>(g, d, c, p0, n, tid, lds, wchunk0, ochunk0);
+    }
+}
+
+// The first phase of one stage of the LDS chunked kernel: the images of
+// planes p0 .. p0 + n - 1 of tile t, image k at lds + k * image.  Every
+// plane's loads go out before any of their LDS stores (one lds_fill over
+// the n planes; with two planes of 16-byte pieces 10-18 % faster than one
+// plane after the other), except for mode 1 with narrower pieces, whose
+// scatter of pieces measured 1.5-3 % slower that way and fills one plane
+// after the other.
+template <class Mem, int G, bool MODE1, uint32_t BS, uint32_t U, uint32_t S>
+UA2A_HD void lds_chunked_fill(const LdsGeom& g, const LdsChunkGeom& c, uint32_t t, uint32_t p0, uint32_t n,
+                              uint32_t tid, uint8_t* lds)
+{
+    if (!MODE1 || G == 16) {
+        const int64_t off = static_cast<int64_t>(p0) * c.plane;
+        const PlaneBases bases{g, MODE1 ? 0 : off, MODE1 ? off : 0};     // the input side moves
+        lds_fill<Mem, G, MODE1, BS, U, PlaneBases, S>(g, bases, lds_tile(g, bases, t), tid, lds, c.plane,
+                                                      c.image, n);
+    } else {
+        for (uint32_t k = 0; k < n; ++k) {
+            const PlaneBases bases{g, 0, static_cast<int64_t>(p0 + k) * c.plane};
+            lds_fill<Mem, G, true, BS, U>(g, bases, lds_tile(g, bases, t), tid, lds + k * c.image);
+        }
     }
 }
 

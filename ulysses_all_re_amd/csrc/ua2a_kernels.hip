@@ -330,10 +330,11 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_ranks_kernel(LdsGeom g, Ld
 // A whole chunked exchange in one launch on the LDS path (see LdsChunkGeom):
 // each workgroup keeps its tile through all B planes, `stage` planes at a
 // time -- fill one LDS image per plane, then every lane, plane after plane,
-// stores its chunks of the tile's window spans into the window and reads them
-// back, and stores them to that plane of the output.  A lane reads back only window bytes that
-// it stored, so the window needs no barrier; the barrier after the drain
-// keeps the next stage's fill from overwriting LDS that a lane still reads.
+// stores its chunks of the tile's window spans into the window and reads
+// them back, and stores them to that plane of the output.  A lane reads back
+// only window bytes that it stored, so the window needs no barrier; the
+// barrier after the drain keeps the next stage's fill from overwriting LDS
+// that a lane still reads.
 template <int G, bool MODE1>
 __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, LdsChunkGeom c)
 {
@@ -346,12 +347,8 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, 
         if (t >= g.num_tiles) continue;      // the same for the whole workgroup
         for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
             const uint32_t n = umin32(c.stage, c.planes - p0);
-            for (uint32_t k = 0; k < n; ++k) {
-                const int64_t off = static_cast<int64_t>(p0 + k) * c.plane;
-                const PlaneBases bases{g, MODE1 ? 0 : off, MODE1 ? off : 0};     // the input side moves
-                lds_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1)>(
-                    g, bases, lds_tile(g, bases, t), threadIdx.x, lds + k * c.image);
-            }
+            lds_chunked_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1), kLdsChunkStage>(
+                g, c, t, p0, n, threadIdx.x, lds);
             __syncthreads();
             lds_chunked_drain<StreamMem, G, MODE1, kLdsBlock, kLdsReadback, kLdsChunkStage>(g, c, t, p0, n,
                                                                                     threadIdx.x, lds);
