@@ -151,9 +151,10 @@ int ua2a_plan(ua2a_plan_t* plan_out, int32_t w, int64_t B, int64_t S_local,
  *               workgroup owns one tile of the window (or, under a `blocks`
  *               cap, several in turn) and, plane after plane, writes the
  *               tile, reads it back and stores it to `out`.  On the LDS path
- *               each workgroup stages its tile of every plane in LDS, and
- *               each lane writes its chunks of the tile to the window, reads
- *               them back and stores them to `out`.
+ *               each workgroup stages its tile of every plane in LDS (two
+ *               planes at a time when a plane of one rank is a multiple of
+ *               16 bytes), and each lane writes its chunks of the tile to
+ *               the window, reads them back and stores them to `out`.
  *               After the call the window holds plane B-1 of every rank, in
  *               `out`'s layout.  Needs window_bytes >= layout.window_bytes.
  *   in       mode 0: [w][B][S_local][H][D]; mode 1: [w][B][S_local*w][H/w][D]

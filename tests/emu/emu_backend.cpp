@@ -287,8 +287,9 @@ void run_lds_chunked(const Launch& L)
         }
         // as the kernel: `stage` planes filled (one image each), a barrier,
         // then each lane drains them plane after plane, then a barrier
-        for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
-            const uint32_t n = std::min(c.stage, c.planes - p0);
+        const uint32_t per = c.stage == 0 ? 1u : std::min(c.stage, kLdsChunkStage);
+        for (uint32_t p0 = 0, n = 0; p0 < c.planes; p0 += n) {
+            n = std::min(per, c.planes - p0);
             memset(lds.data(), 0xA5, lds.size());
             for (uint32_t tid = 0; tid < kLdsBlock; ++tid)
                 lds_chunked_fill<CheckedMem, G, M1, kLdsBlock, (G == 16 ? kLdsUnroll : 1), kLdsChunkStage>(

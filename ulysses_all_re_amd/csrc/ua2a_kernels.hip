@@ -342,11 +342,13 @@ __global__ __launch_bounds__(kLdsBlock) void ua2a_lds_chunked_kernel(LdsGeom g, 
     asm volatile("" ::"s"(c.out), "s"(c.rank_step), "s"(c.plane), "s"(c.planes), "s"(c.stage), "s"(c.image));
     extern __shared__ u32x4 ua2a_lds_raw[];
     uint8_t* lds = reinterpret_cast<uint8_t*>(ua2a_lds_raw);
+    // planes per stage: at least one, at most what the bodies hold
+    const uint32_t per = c.stage == 0 ? 1u : umin32(c.stage, kLdsChunkStage);
     for (uint64_t slot = blockIdx.x; slot < g.num_slots; slot += gridDim.x) {
         const uint32_t t = lds_slot_tile(g, static_cast<uint32_t>(slot));
         if (t >= g.num_tiles) continue;      // the same for the whole workgroup
-        for (uint32_t p0 = 0; p0 < c.planes; p0 += c.stage) {
-            const uint32_t n = umin32(c.stage, c.planes - p0);
+        for (uint32_t p0 = 0, n = 0; p0 < c.planes; p0 += n) {
+            n = umin32(per, c.planes - p0);
             lds_chunked_fill<StreamMem, G, MODE1, kLdsBlock, (G == 16 ? kLdsUnroll : 1), kLdsChunkStage>(
                 g, c, t, p0, n, threadIdx.x, lds);
             __syncthreads();
