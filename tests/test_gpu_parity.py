@@ -698,11 +698,16 @@ def test_random_chunked_lds(case):
     plan.close()
 
 
-def test_chunked_lds_full_size_run64():
-    """A 537 MB chunked exchange on the LDS path (64-byte runs, four planes of
-    134 MB, window larger than the on-package cache), both modes, against the
-    oracle at full size."""
-    w, B, S, H, D = 8, 4, 32768, 8, 32
+@pytest.mark.parametrize("shape,planes_held", [
+    ((8, 4, 32768, 8, 32), 2),      # 64-byte runs, 537 MB, four planes of 134 MB, two per fill
+    ((4, 3, 524287, 4, 7), 1),      # 14-byte runs, 352 MB, a plane 8 bytes off the 16-byte grid
+    ((4, 5, 524288, 4, 7), 2),      # 14-byte runs, 587 MB, five planes: two stages and a single
+], ids=["run64", "run14-odd-plane", "run14-five-planes"])
+def test_chunked_lds_full_size(shape, planes_held):
+    """Chunked exchanges on the LDS path at full size (windows larger than the
+    on-package cache), both modes, against the oracle: LDS holds two planes at
+    once when a plane is a multiple of 16 bytes, one otherwise."""
+    w, B, S, H, D = shape
     lay = ua.ua2a_layout(w, B, S, H, D, 2)
     win = torch.empty(lay["window_bytes"], dtype=torch.uint8, device=DEV)
     plan = ua.Plan(w, B, S, H, D, torch.bfloat16, window=win)
@@ -712,10 +717,12 @@ def test_chunked_lds_full_size_run64():
         xd = x.to(DEV)
         info = plan.describe(xd, mode, True)
         assert info["path"] == ua.UA2A_PATH_LDS and info["chunked_form"] == ua.UA2A_CHUNKED_ONE_LAUNCH
-        note(f"chunked lds full size mode={mode} {info}")
+        assert info["lds_planes"] == planes_held
+        note(f"chunked lds full size {shape} mode={mode} {info}")
         y = plan.exchange(xd, mode, True, out=poisoned(plan.out_shape(mode), torch.bfloat16))
         torch.cuda.synchronize()
-        assert_same_bits(y, want, f"chunked lds full size mode {mode}")
+        assert_same_bits(y, want, f"chunked lds full size {shape} mode {mode}")
+        assert torch.equal(win.cpu().view(w, -1), want.view(torch.uint8).reshape(w, B, -1)[:, B - 1])
         del x, xd, y, want
     plan.close()
 
