@@ -767,7 +767,7 @@ UA2A_HD void lds_chunked_drain(const LdsGeom& g, const LdsChunkGeom& c, uint32_t
     }
 }
 
-// Strided block copy (chunked exchange: window -> planes of the output).
+// Strided block copy (mode 0's unpack: a receiver's window -> its output).
 template <class Mem, int VB, uint32_t BS, uint32_t U>
 UA2A_HD void copy_tile_body(const CopyGeom& g, uint32_t t, uint32_t tid)
 {

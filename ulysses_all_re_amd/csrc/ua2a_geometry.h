@@ -708,9 +708,9 @@ UA2A_HD void p_partial_from_lds(const uint8_t* lds, uint8_t* pchunk0, uint32_t l
 }
 
 // ------------------------------------------------------------------------
-// Plain strided block copy (window <-> one plane of every rank in the
-// chunked exchange): `count` blocks of span vectors, block k at
-// src + k*src_stride -> dst + k*dst_stride.  Units: VB-byte vectors.
+// Plain strided block copy: `count` blocks of span vectors, block k at
+// src + k*src_stride -> dst + k*dst_stride (units: VB-byte vectors).  Used
+// for mode 0's unpack of a receiver's window into its output, one block.
 struct CopyGeom {
     const uint8_t* src;
     uint8_t* dst;
