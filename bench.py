@@ -969,8 +969,7 @@ def traffic_from(d):
 def summarize_trace(d, workload, ranks=None, chunked=False):
     """Markdown table of a rocprofv3 --kernel-trace --stats --output-format csv run
     (with ranks == "one", each exchange launch moves one sender's share, 1/w;
-    with chunked, a per-plane launch moves one plane, 1/B, and the one-launch
-    chunked kernel the whole exchange)."""
+    a chunked exchange is one launch, its rate on the algorithmic bytes)."""
     paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not paths:
         raise SystemExit(f"no kernel_stats.csv under {d}")
@@ -981,10 +980,9 @@ def summarize_trace(d, workload, ranks=None, chunked=False):
     c = {**CONFIGS, **MEASURE}[workload]
     e = torch.empty((), dtype=DTYPES[c["dtype"]]).element_size()
     moved = ua.ua2a_layout(c["w"], c["B"], c["S_local"], c["H"], c["D"], e)["moved_bytes"]
-    share = moved // c["w"] if ranks == "one" else moved // c["B"] if chunked else moved
+    share = moved // c["w"] if ranks == "one" else moved
     print(f"| kernel | calls | avg us | min us | max us | GB/s at avg (2 x {share // 2} B"
-          + (", one sender" if ranks == "one" else ", one plane" if chunked else "")
-          + ("; B x for the one-launch chunked kernel" if chunked else "") + ") |")
+          + (", one sender" if ranks == "one" else ", algorithmic" if chunked else "") + ") |")
     print("|---|---|---|---|---|---|")
     with open(paths[0], newline="") as f:
         for r in csv.DictReader(f):
@@ -994,8 +992,7 @@ def summarize_trace(d, workload, ranks=None, chunked=False):
             avg = float(r["AverageNs"])
             rate = ""
             if "ua2a_" in r["Name"]:
-                k = c["B"] if chunked and "chunked_kernel" in r["Name"] else 1
-                rate = f"{k * share / (avg * 1e-9) / 1e9:.1f}"
+                rate = f"{share / (avg * 1e-9) / 1e9:.1f}"
             elif COPY_KERNEL_HINT in r["Name"] and ranks is None:   # per-rank runs also clone ranks
                 rate = f"{moved / (avg * 1e-9) / 1e9:.1f}"
             print(f"| `{name}` | {r['Calls']} | {avg / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
