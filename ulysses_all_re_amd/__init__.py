@@ -279,6 +279,16 @@ def ua2a_describe(plan: int, mode: int, chunked: int, inp: int, out: int) -> dic
 
 # ------------------------------------------------------------- torch wrapper
 
+def _current_raw_stream(device) -> int:
+    """torch's current stream on `device` as a raw hipStream_t (0: the null
+    stream), without building a Stream object where torch offers that."""
+    import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
 class Plan:
     """A ua2a plan bound to torch tensors on one device.
 
@@ -333,7 +343,7 @@ class Plan:
             raise TypeError(f"{what} has dtype {t.dtype}, plan expects {self.dtype}")
         if t.device != self.device:
             raise ValueError(f"{what} is on {t.device}, plan is on {self.device}")
-        if tuple(t.shape) != tuple(shape):
+        if t.shape != shape:
             raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{what} must be contiguous")
@@ -346,10 +356,17 @@ class Plan:
             out = torch.empty(self.out_shape(mode), dtype=self.dtype, device=self.device)
         else:
             self._check(out, self.out_shape(mode), "output")
-        if stream is None:
-            stream = torch.cuda.current_stream(self.device)
-        self._on_device(ua2a_exchange, self.handle, mode, int(chunked), x.data_ptr(), out.data_ptr(),
-                        stream.cuda_stream)
+        sptr = _current_raw_stream(self.device) if stream is None else stream.cuda_stream
+        handle = self.handle
+        args = (handle, mode, int(chunked), x.data_ptr(), out.data_ptr(), sptr or None)
+        lib = load_library()
+        rc = lib.ua2a_exchange(*args)
+        if rc == UA2A_ERR_DEVICE and handle:
+            # another device is current: the library changed nothing; retry on the plan's
+            with torch.cuda.device(self.device):
+                rc = lib.ua2a_exchange(*args)
+        if rc != UA2A_OK:
+            raise UA2AError(rc, "ua2a_exchange", ua2a_plan_last_error(handle) if handle else "")
         return out
 
     def exchange_noalloc(self, x, mode: int, out, stream=None):
