@@ -143,6 +143,29 @@ def test_tile_counts_near_2_32_are_exact(lib, shape, blocks, dims):
         ua.ua2a_destroy(h)
 
 
+@pytest.mark.parametrize("shape,mode,want", [
+    ((8, 1, 16384, 8, 32, 2), 1, ua.UA2A_PATH_DIRECT),   # 64-byte runs, 67 MB a side: direct
+    ((8, 1, 32768, 8, 32, 2), 1, ua.UA2A_PATH_LDS),      # 134 MB a side: LDS
+    ((8, 1, 20480, 8, 32, 2), 1, ua.UA2A_PATH_LDS),      # exactly 80 MiB a side: LDS
+    ((8, 1, 20479, 8, 32, 2), 1, ua.UA2A_PATH_DIRECT),   # one token less: direct
+    ((8, 1, 16384, 8, 32, 2), 0, ua.UA2A_PATH_LDS),      # mode 0 keeps the LDS kernel
+    ((4, 1, 2 ** 16, 4, 7, 2), 1, ua.UA2A_PATH_LDS),     # 14-byte runs: no 16-byte pieces
+    ((8, 1, 9450, 40, 128, 2), 1, ua.UA2A_PATH_DIRECT),  # long runs: direct at any size
+])
+def test_automatic_path_by_launch_size(lib, shape, mode, want):
+    """Mode 1 on short 16-byte-multiple runs takes the direct kernel below
+    80 MiB a side and the LDS kernel from there on (measured crossover)."""
+    w, B, S, H, D, e = shape
+    lay = ua.ua2a_layout(w, B, S, H, D, e)
+    h = ua.ua2a_plan(w, B, S, H, D, e, 0)
+    try:
+        base = 1 << 44
+        info = ua.ua2a_describe(h, mode, 0, base, base + lay["tensor_bytes"])
+        assert info["path"] == want, (shape, mode, info)
+    finally:
+        ua.ua2a_destroy(h)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ua, "_lib", None)
     monkeypatch.setattr(ua, "LIBRARY", str(tmp_path / "libua2a.so"))

@@ -349,22 +349,25 @@ def test_workload_pack_unpack_parity(name):
     plan.close()
 
 
+@pytest.mark.parametrize("path", ["auto", "lds"])
 @pytest.mark.parametrize("shape", TAIL_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_tail_pack_unpack_parity(shape):
+def test_tail_pack_unpack_parity(shape, path):
     """Runs that are short or not a multiple of 16 bytes, misaligned
     per-rank bases, a partial sender range (the other windows' blocks keep
-    their poison) and a partial receiver range."""
+    their poison) and a partial receiver range; the automatic kernel choice
+    and the LDS kernel forced (small mode-1 unpacks otherwise go direct)."""
     w, B, S, H, D, dtype = shape
     dt = DTYPES[dtype]
     e = torch.empty((), dtype=dt).element_size()
     plan = ua.Plan(w, B, S, H, D, dt)
+    plan.set_path(ua.UA2A_PATH_LDS if path == "lds" else ua.UA2A_PATH_AUTO)
     offsets = [(k % 3, (k + 1) % 3, (k + 2) % 3) for k in range(w)] if e < 8 else None
     for mode in (0, 1):
         ish, _ = stacked_shapes(w, B, S, H, D, mode)
         x = make_tensor(ish, dtype, "bytes", 60 + mode)
         senders = list(range(w)) if w < 3 else [0, w - 1]
         receivers = list(range(w)) if w < 3 else list(range(1, w))
-        note(f"pack/unpack tail {shape} mode {mode} senders {senders} receivers {receivers}")
+        note(f"pack/unpack tail {shape} path {path} mode {mode} senders {senders} receivers {receivers}")
         gw, ww, go, wo = run_pack_unpack(plan, x, mode, senders, receivers, offsets)
         assert_ranks_equal(gw, ww, f"{shape} mode {mode} windows")
         assert_ranks_equal(go, wo, f"{shape} mode {mode} outputs")

@@ -138,6 +138,18 @@ bool direct_reads_whole_lines(int mode, int64_t w, int64_t run)
     return kTileBytes % row == 0 && kTileBytes / w >= kDirectMinRun;
 }
 
+// Whether a mode-1 launch of short 16-byte-multiple runs is small enough that
+// the direct kernel beats the LDS kernel (measured rule): a launch moving
+// under kDirectMode1Bytes per side runs few rounds of LDS workgroups, so the
+// round at each end (fill, barrier, drain) costs more than the direct
+// kernel's half-line reads.  Measured with runs of 32, 64 and 96 bytes and w
+// of 4 and 8: direct ahead by 25 % at 17 MB per side, 10 % at 34 MB and 4 %
+// at 67 MB; LDS ahead by 2-9 % from 100 MB up.
+bool direct_for_small_mode1(int mode, uint32_t g, int64_t bytes_per_side)
+{
+    return mode == 1 && g == 16 && bytes_per_side < kDirectMode1Bytes;
+}
+
 // LDS padding per row for piece size G: with G = 16 every span is 16-aligned
 // and a row may be padded so that its LDS stride equals run modulo 256 bytes
 // (consecutive rows' runs on disjoint banks); otherwise rows stay packed.
@@ -354,6 +366,8 @@ void prepare(const ua2a_plan_s* p, int32_t mode, int32_t chunked, const void* in
     else if (want == UA2A_PATH_LDS)
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
     else if (g == 16 && direct_reads_whole_lines(mode, p->w, run))
+        path = UA2A_PATH_DIRECT;
+    else if (!chunked && direct_for_small_mode1(mode, g, rank_bytes * p->w))
         path = UA2A_PATH_DIRECT;
     else
         path = rows > 0 ? UA2A_PATH_LDS : UA2A_PATH_DIRECT;
@@ -654,7 +668,7 @@ void prepare_unpack(const ua2a_plan_s* p, int32_t mode, const void* win, void* o
     else if (p->path == UA2A_PATH_LDS)
         lds = true;
     else
-        lds = !(g == 16 && direct_reads_whole_lines(1, p->w, run));
+        lds = !(g == 16 && direct_reads_whole_lines(1, p->w, run)) && !direct_for_small_mode1(1, g, rank_bytes);
     if (!lds) {
         direct_launch(p, 1, g, outb, winb, 0, p_plane, block, a_plane, static_cast<uint32_t>(p->B), 1, false, L);
         return;

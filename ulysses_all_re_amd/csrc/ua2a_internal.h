@@ -31,6 +31,7 @@ constexpr uint32_t kCapInFlight = 8192;         // ... used while grid * kCapTil
 constexpr uint32_t kTileBytes = 1024;           // bytes per direct / copy tile
 constexpr uint32_t kLdsUnroll = 2;              // 16-byte chunks per lane per pass (LDS fill, G = 16)
 constexpr uint32_t kDirectMinRun = 256;         // auto path, mode 1: least contiguous read per head block
+constexpr int64_t kDirectMode1Bytes = int64_t(80) << 20;   // auto path, mode 1 short runs: direct below this per side
 constexpr uint32_t kDirectGroup = 8;            // grouped tile order (mode 0, 4 KiB-multiple rows)
 constexpr uint32_t kDirectGroupRowAlign = 4096;
 constexpr uint32_t kMaxGridYZ = 65535;          // largest y / z grid extent used
