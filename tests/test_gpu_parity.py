@@ -196,6 +196,29 @@ def test_power_of_two_rows(shape):
     plan.close()
 
 
+@pytest.mark.parametrize("S", [20479, 20480], ids=["under-80MiB", "at-80MiB"])
+def test_mode1_kernel_choice_at_its_size_boundary(S):
+    """Mode 1 on 64-byte runs takes the direct kernel just under 80 MiB a side
+    and the LDS kernel at 80 MiB; either way the output equals the oracle's and
+    mode 0 on it returns the input."""
+    w, B, H, D = 8, 1, 8, 32
+    plan = ua.Plan(w, B, S, H, D, torch.bfloat16)
+    x = make_tensor(in_shape(w, B, S, H, D, 1), "bf16", "bytes", 880 + S % 2)
+    want = oracle_out(x, 1, w)
+    xd = x.to(DEV)
+    info = plan.describe(xd, 1, False)
+    assert info["path"] == (ua.UA2A_PATH_DIRECT if S < 20480 else ua.UA2A_PATH_LDS), info
+    note(f"mode 1 size boundary S={S} path={info['path']}")
+    y = plan.exchange(xd, 1, out=poisoned(plan.out_shape(1), torch.bfloat16))
+    torch.cuda.synchronize()
+    assert_same_bits(y, want, f"mode 1 S={S}")
+    note(f"mode 0 round trip S={S}")
+    z = plan.exchange(y, 0, out=poisoned(plan.out_shape(0), torch.bfloat16))
+    torch.cuda.synchronize()
+    assert_same_bits(z, bits(x), f"round trip S={S}")
+    plan.close()
+
+
 def test_large_tensor_sampled():
     """16 GiB per tensor (2^31 eight-byte elements): byte offsets far past 2^32.
     Each element holds its own input position, so a sampled output position
