@@ -303,13 +303,20 @@ def run(args):
     log(f"mode 0 launch {info0}")
     log(f"mode 1 launch {info1}")
 
-    for _ in range(max(args.warmup, rotate)):
+    # one round trip through every buffer set, checked before anything is timed
+    for _ in range(rotate):
         ex0()
         ex1()
     torch.cuda.synchronize(dev)
     if not round_trips_ok():
         raise SystemExit("round trip did not return the input; refusing to report a number")
-    log(f"warmup done ({args.warmup} steps), round trip bit-exact")
+    log(f"round trip bit-exact on {rotate} buffer set(s)")
+    # the W warm-up steps come right before the timed region, with no check or
+    # host wait between them (a pause there left the first timed steps slower)
+    for _ in range(args.warmup):
+        ex0()
+        ex1()
+    log(f"warmup done ({args.warmup} steps)")
 
     K = args.steps
 
@@ -370,6 +377,9 @@ def run(args):
 
     timed(copy_leg, 3)
     avgc = timed(copy_leg, K) / K
+    if not round_trips_ok():
+        raise SystemExit("round trip no longer returns the input after the timed steps; "
+                         "refusing to report a number")
     log(f"per exchange: mode 0 {avg0 * 1e3:.1f} us, mode 1 {avg1 * 1e3:.1f} us, "
         f"copy {avgc * 1e3:.1f} us")
 
