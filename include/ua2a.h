@@ -79,6 +79,11 @@ typedef struct ua2a_layout_s {
 } ua2a_layout_t;
 
 /* Which kernel family runs an exchange (ua2a_plan_set_path, ua2a_describe). */
+/* UA2A_PATH_AUTO (default) takes the direct path when runs are whole 128-byte
+ * lines and the bases are 16-byte aligned (mode 1: when each 1 KiB tile reads at
+ * least 256 contiguous bytes per head block, or, for runs that are multiples of
+ * 16 bytes, when an unchunked launch moves under 80 MiB a side), the LDS path
+ * otherwise; ua2a_describe reports the choice. */
 #define UA2A_PATH_AUTO    0  /* the library chooses (default) */
 #define UA2A_PATH_DIRECT  1  /* one pass, each lane moves whole vectors of a run */
 #define UA2A_PATH_LDS     2  /* rows staged through LDS, both sides moved as contiguous spans */
